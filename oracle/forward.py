@@ -1,0 +1,135 @@
+"""The W4A4 routed-expert layer, step by step, in fp64.
+
+Steps (the layer that [P1] measures as one fused kernel; the pages print only
+pre_dispatch and the buffer, [P3] "Key source snippets", so the stage list is
+the plain reading of a routed SwiGLU expert layer with activation="swiglu" and
+MXFP4 operands on both sides):
+
+  1. pre_dispatch: quantize every token row of x to MXFP4 (group 32) once.
+  2. route: stable counting sort of the routed rows by expert (oracle.route).
+  3. GEMM1 per expert e over its rows:  acc = x_hat[t] . W1_hat[e]^T  (fp64);
+     gate = acc[:, :I], up = acc[:, I:]  -- W1 rows [0, I) are gate and
+     [I, 2I) are up, the split that _interleave_mega_moe_gate_up slices ([P3]
+     "Key source snippets");  h = silu(gate) * up = gate / (1 + exp(-gate)) * up.
+  4. requantize h to MXFP4 along I (same rule as step 1).  The pages leave the
+     precision of h open; the device keeps h in fp32, so the code decision is
+     taken on h rounded to fp32 on both sides (h itself is kept in fp64).
+  5. GEMM2: y = h_hat . W2_hat[e]^T  (fp64).
+  6. combine: out[t] = sum over valid slots j, in slot order, of w[t, j] * y[pos(t, j)],
+     in fp64, then rounded once to bfloat16.  A token with no valid slot gives +0.
+
+The top-k weights are applied in the combine only and are used as given.
+
+Weight operands are passed either as arrays (w1_codes [E, 2I, H/2],
+w1_scales [E, 2I, H/32], w2_codes [E, H, I/2], w2_scales [E, H, I/32]) or as a
+callable e -> (w1_codes[e], w1_scales[e], w2_codes[e], w2_scales[e]) so that a
+caller can supply experts lazily.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import bf16, mxfp4
+from .route import route
+
+
+def _expert_getter(weights):
+    if callable(weights):
+        return weights
+    w1c, w1s, w2c, w2s = weights
+    return lambda e: (w1c[e], w1s[e], w2c[e], w2s[e])
+
+
+def to_f32(v):
+    """Round fp64 values to the nearest fp32 (ties to even) and return them as fp64."""
+    return np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def silu_mul(gate, up):
+    """SwiGLU: gate / (1 + exp(-gate)) * up, no clamp, no bias, fp64."""
+    with np.errstate(over="ignore"):
+        return gate / (1.0 + np.exp(-gate)) * up
+
+
+def forward(x_bf16, topk_ids, topk_weights, weights, num_experts: int, inter: int,
+            tokens=None):
+    """Run the layer.
+
+    x_bf16        uint16 [T, H] bfloat16 bit patterns
+    topk_ids      int    [T, k]
+    topk_weights  float  [T, k]
+    weights       arrays or callable (see module doc)
+    tokens        optional iterable of token indices: compute y only for the
+                  routed rows of these tokens and out only for them (other
+                  rows of y / out are NaN).  None = all tokens.
+
+    Returns a dict with every intermediate:
+      xq, xsf          packed codes [T, H/2] and scale bytes [T, H/32] of x
+      counts, offsets, sorted_rows, pos
+      h                fp64 [n_valid, I] (NaN where not computed), in sorted order
+      hq, hsf          packed codes [n_valid, I/2], scale bytes [n_valid, I/32]
+      y                fp64 [n_valid, H]
+      out_f64          fp64 [T, H]
+      out              uint16 [T, H] bfloat16 bits
+    """
+    x_bits = np.asarray(x_bf16, dtype=np.uint16)
+    ids = np.asarray(topk_ids)
+    w = np.asarray(topk_weights, dtype=np.float64)
+    T, H = x_bits.shape
+    k = ids.shape[1]
+    E, I = int(num_experts), int(inter)
+    get = _expert_getter(weights)
+
+    xv = bf16.decode(x_bits)
+    xq, xsf = mxfp4.quantize_packed(xv)                        # step 1
+    x_hat = mxfp4.dequantize(xq, xsf)
+
+    counts, offsets, sorted_rows, pos = route(ids, E)          # step 2
+    nv = int(offsets[E])
+
+    if tokens is None:
+        want = np.ones(T, dtype=bool)
+    else:
+        want = np.zeros(T, dtype=bool)
+        want[np.asarray(list(tokens), dtype=np.int64)] = True
+
+    h = np.full((nv, I), np.nan)
+    hq = np.zeros((nv, I // 2), dtype=np.uint8)
+    hsf = np.zeros((nv, I // mxfp4.GROUP), dtype=np.uint8)
+    y = np.full((nv, H), np.nan)
+
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if lo == hi:
+            continue
+        p_idx = np.arange(lo, hi)
+        rows = sorted_rows[lo:hi]
+        tok = rows // k
+        sel = want[tok]
+        if not sel.any():
+            continue
+        p_idx, tok = p_idx[sel], tok[sel]
+        w1c, w1s, w2c, w2s = get(e)
+        W1 = mxfp4.dequantize(w1c, w1s)                        # [2I, H]
+        acc = x_hat[tok] @ W1.T                                # step 3
+        h_e = silu_mul(acc[:, :I], acc[:, I:])
+        hq_e, hsf_e = mxfp4.quantize_packed(to_f32(h_e))      # step 4
+        W2 = mxfp4.dequantize(w2c, w2s)                        # [H, I]
+        y_e = mxfp4.dequantize(hq_e, hsf_e) @ W2.T             # step 5
+        h[p_idx], hq[p_idx], hsf[p_idx], y[p_idx] = h_e, hq_e, hsf_e, y_e
+
+    out = np.full((T, H), np.nan)                              # step 6
+    for t in range(T):
+        if not want[t]:
+            continue
+        acc = np.zeros(H)
+        for j in range(k):
+            p = pos[t * k + j]
+            if p >= 0:
+                acc = acc + w[t, j] * y[p]
+        out[t] = acc
+    out_bits = np.zeros((T, H), dtype=np.uint16)
+    out_bits[want] = bf16.encode(out[want])
+
+    return dict(xq=xq, xsf=xsf, counts=counts, offsets=offsets, sorted_rows=sorted_rows,
+                pos=pos, h=h, hq=hq, hsf=hsf, y=y, out_f64=out, out=out_bits)
