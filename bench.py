@@ -1,0 +1,208 @@
+"""Benchmark of the W4A4 MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one whole forward of the layer (pre-dispatch quantization, routing,
+GEMM1 + SwiGLU + requant, GEMM2, combine) on one batch of synthetic tokens whose
+inputs are already resident in HBM.  The default workload is the pages'
+single-rank operating point: DeepSeek-V4-Flash shape (hidden 4096, inter 2048,
+256 experts, top-6), ntok = 512, uniform routing, all 256 experts' MXFP4
+weights resident.
+
+Prints ONE JSON line.  `value` is the time of one layer forward in us (lower is
+better); throughput in TFLOP/s and algorithmic HBM GB/s ride along.  The
+"roofline" object is for GEMM1, the dominant kernel, timed with HIP events on
+the stream it is launched on, inside the timed steps.  "cpu_baseline" times the
+fp64 CPU oracle on a bounded slice of the same workload (a few experts with all
+their routed rows) and scales it to one layer.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "mega-MoE layer µs + TFLOPS + HBM GB/s at ntok=512/4096, DSV4-Flash shape"
+HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E
+FP4_PEAK_TFLOPS = 10100.0         # MI355X dense MXFP4 MFMA
+PAGES_US_NTOK512 = 537.6          # W4A4 mega-MoE kernel, 1 B200, 1-rank isolation, ntok=512 (context)
+
+
+def expert_bytes(H, I):
+    """MXFP4 bytes of one expert: W1 (2I x H) and W2 (H x I) codes + scales."""
+    return 2 * I * H // 2 + 2 * I * H // 32 + H * I // 2 + H * I // 32
+
+
+def algorithmic(cfg, counts):
+    H, I, k, T = cfg.hidden, cfg.inter, cfg.topk, cfg.tokens
+    active = int((counts > 0).sum())
+    R = int(counts.sum())
+    layer_bytes = active * expert_bytes(H, I) + T * (2 * H + 8 * k + 2 * H)
+    flops = R * (2 * H * 2 * I + 2 * I * H)
+    w1 = 2 * I * H // 2 + 2 * I * H // 32
+    gemm1_bytes = active * w1 + T * (H // 2 + H // 32) + R * (I // 2 + I // 32)
+    return dict(active=active, R=R, layer_bytes=layer_bytes, flops=flops, gemm1_bytes=gemm1_bytes,
+                gemm1_flops=R * 2 * H * 2 * I)
+
+
+def cpu_baseline(cfg, x, ids, w, n_experts_sample=4):
+    """The oracle as it stands, on a slice: quantize + route of the whole batch,
+    then GEMM1/SwiGLU/requant/GEMM2 for all routed rows of a few experts; the
+    per-expert time is scaled to the active experts of the layer."""
+    try:
+        import threadpoolctl
+        blas = threadpoolctl.threadpool_info()
+        cores = max([b.get("num_threads", 1) for b in blas] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    import synth
+    from oracle import mxfp4
+    from oracle.forward import forward
+    from oracle.route import route
+
+    counts = route(ids, cfg.experts)[0]
+    active = [e for e in range(cfg.experts) if counts[e] > 0]
+    sample = active[:n_experts_sample]
+    weights = {}
+    for e in sample:                       # weight quantization is load-time work: not timed
+        w1, w2 = synth.expert_weights_f32(cfg, e)
+        weights[e] = mxfp4.quantize_packed(w1) + mxfp4.quantize_packed(w2)
+    t0 = time.perf_counter()
+    forward(x, ids, w, lambda e: weights[e], cfg.experts, cfg.inter, experts=[])
+    t_common = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    forward(x, ids, w, lambda e: weights[e], cfg.experts, cfg.inter, experts=sample)
+    t_sample = time.perf_counter() - t0 - t_common
+    us = (t_common + t_sample / len(sample) * len(active)) * 1e6
+    rows = int(sum(counts[e] for e in sample))
+    return {"value": round(us, 1), "unit": "us", "cores": int(cores), "kind": "oracle",
+            "sample": f"quantize+route of all {cfg.tokens} tokens, then experts {sample} "
+                      f"({rows} routed rows) through GEMM1/SwiGLU/requant/GEMM2; expert time scaled "
+                      f"to {len(active)} active experts",
+            "measured_s": round(t_common + t_sample, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv4flash_t512")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--threads", type=int, default=16)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this layer runs on one GPU (all experts resident); --gpus {args.gpus} is not "
+              f"supported.  Sharding is by expert and is described, not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from block_scaled_fp4_pre_amd import _lib
+    from block_scaled_fp4_pre_amd.layer import MoeW4A4Layer
+
+    cfg = {c.name: c for c in synth.CONFIGS}[args.workload]
+    torch.cuda.set_device(0)
+    t_setup = time.perf_counter()
+    layer = MoeW4A4Layer(cfg.hidden, cfg.inter, cfg.experts, cfg.topk, cfg.tokens)
+    layer.load_fp32(lambda e: synth.expert_weights_f32(cfg, e), threads=args.threads)
+    x_h = synth.make_tokens(cfg)
+    ids_h, w_h = synth.make_routing(cfg)
+    x = torch.from_numpy(x_h.view(np.int16)).cuda().view(torch.bfloat16)
+    ids = torch.from_numpy(ids_h).cuda()
+    w = torch.from_numpy(w_h).cuda()
+    out = torch.empty((cfg.tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    print(f"[bench] setup {time.perf_counter() - t_setup:.1f}s workload={cfg.name}", file=sys.stderr, flush=True)
+
+    T = cfg.tokens
+    S_A = _lib.MOE_STAGE_QUANT | _lib.MOE_STAGE_ROUTE
+    S_B = _lib.MOE_STAGE_GEMM1
+    S_C = _lib.MOE_STAGE_GEMM2 | _lib.MOE_STAGE_COMBINE
+
+    def step(ev=None):
+        # The same launches as moe_w4a4_forward, split in three calls so that
+        # GEMM1 can be bracketed by events on the stream it runs on.
+        layer.run_stages(S_A, T, x=x, topk_ids=ids)
+        if ev is not None:
+            ev[0].record()
+        layer.run_stages(S_B, T)
+        if ev is not None:
+            ev[1].record()
+        layer.run_stages(S_C, T, topk_weights=w, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = start.elapsed_time(end) / args.steps
+    gemm1_us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+
+    # forward through the single entry point, for comparison (same kernels)
+    fwd_s, fwd_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fwd_s.record()
+    for _ in range(args.steps):
+        layer.forward(x, ids, w, out)
+    fwd_e.record()
+    torch.cuda.synchronize()
+    fwd_ms = fwd_s.elapsed_time(fwd_e) / args.steps
+
+    counts = layer.ws("counts", (cfg.experts,), torch.int32).cpu().numpy()
+    alg = algorithmic(cfg, counts)
+    us = ms_per_step * 1e3
+    tflops = alg["flops"] / (us * 1e-6) / 1e12
+    gbps = alg["layer_bytes"] / (us * 1e-6) / 1e9
+    g1_gbps = alg["gemm1_bytes"] / (gemm1_us * 1e-6) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": round(us, 2),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": round(us / PAGES_US_NTOK512, 4) if cfg.name == "dsv4flash_t512" else None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": T, "hidden": cfg.hidden, "inter": cfg.inter,
+                   "experts": cfg.experts, "topk": cfg.topk, "routing": cfg.routing,
+                   "active_experts": alg["active"], "routed_rows": alg["R"]},
+        "tflops": round(tflops, 2),
+        "tflops_frac": round(tflops / FP4_PEAK_TFLOPS, 4),
+        "hbm_gbps": round(gbps, 1),
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "forward_entry_us": round(fwd_ms * 1e3, 2),
+        "roofline": {"kernel": "gemm1_swiglu_kernel", "bound": "hbm", "achieved": round(g1_gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(g1_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "avg_us": round(gemm1_us, 2),
+                     "bytes_per_launch": alg["gemm1_bytes"]},
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle slice)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(cfg, x_h, ids_h, w_h)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,157 @@
+"""ctypes binding of libmoe_w4a4.so (C ABI in include/moe_w4a4.h).
+
+Argument marshalling only: tensors are passed as raw device pointers, the
+current torch stream as the HIP stream, and status codes become MoeError.
+Every step of the layer runs in the library's HIP kernels; if the library is
+missing this module raises at import time -- there is no other code path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_w4a4.so")
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ECAPACITY, MOE_EWORKSPACE, MOE_ENODEVICE, MOE_EHIP = range(7)
+MOE_MMA_MXF4_X_MXF4 = 0
+MOE_ACT_SWIGLU = 0
+MOE_STAGE_QUANT, MOE_STAGE_ROUTE, MOE_STAGE_GEMM1, MOE_STAGE_GEMM2, MOE_STAGE_COMBINE = 1, 2, 4, 8, 16
+MOE_STAGE_ALL = 31
+
+# Every symbol include/moe_w4a4.h declares.
+EXPORTED = (
+    "moe_w4a4_query",
+    "moe_w4a4_quantize",
+    "moe_w4a4_prepare_weights",
+    "moe_w4a4_forward",
+    "moe_w4a4_status_string",
+    "moe_w4a4_workspace_layout",
+    "moe_w4a4_run_stages",
+)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+
+
+class moe_w4a4_cfg(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "hidden", "inter", "num_experts", "topk", "max_tokens", "group_size", "mma_type", "activation")]
+
+
+class moe_w4a4_ws_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in (
+        "xq", "xsf", "counts", "offsets", "sorted_rows", "pos", "hist", "hq", "hsf", "y", "total")]
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                      "(python -m block_scaled_fp4_pre_amd.build)")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.c_void_p
+_sz = ctypes.c_size_t
+_i32 = ctypes.c_int32
+_CFG = ctypes.POINTER(moe_w4a4_cfg)
+_lib.moe_w4a4_query.argtypes = [_CFG, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]
+_lib.moe_w4a4_quantize.argtypes = [_i32, _P, ctypes.c_int64, _i32, _P, _P, _P]
+_lib.moe_w4a4_prepare_weights.argtypes = [_CFG, _P, _P, _P, _P, _P, _sz, _P]
+_lib.moe_w4a4_forward.argtypes = [_CFG, _P, _i32, _P, _P, _P, _P, _P, _sz, _P]
+_lib.moe_w4a4_status_string.argtypes = [ctypes.c_int]
+_lib.moe_w4a4_status_string.restype = ctypes.c_char_p
+_lib.moe_w4a4_workspace_layout.argtypes = [_CFG, ctypes.POINTER(moe_w4a4_ws_layout)]
+_lib.moe_w4a4_run_stages.argtypes = [_CFG, _P, _i32, _P, _P, _P, _P, _P, _sz, ctypes.c_uint32, _P, _P]
+for _n in EXPORTED:
+    if _n != "moe_w4a4_status_string":
+        getattr(_lib, _n).restype = ctypes.c_int
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return _lib.moe_w4a4_status_string(int(status)).decode()
+
+
+def _check(st: int, where: str) -> None:
+    if st != MOE_OK:
+        raise MoeError(st, where)
+
+
+def _ptr(t) -> int | None:
+    """Device address of a tensor (None -> NULL); no copies, no conversions."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is not None:
+        return int(stream)
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def make_cfg(hidden: int, inter: int, num_experts: int, topk: int, max_tokens: int,
+             group_size: int = 32, mma_type: int = MOE_MMA_MXF4_X_MXF4,
+             activation: int = MOE_ACT_SWIGLU) -> moe_w4a4_cfg:
+    return moe_w4a4_cfg(hidden, inter, num_experts, topk, max_tokens, group_size, mma_type, activation)
+
+
+def moe_w4a4_query(cfg: moe_w4a4_cfg):
+    """(prepared_bytes, workspace_bytes)."""
+    p, w = _sz(), _sz()
+    _check(_lib.moe_w4a4_query(ctypes.byref(cfg), ctypes.byref(p), ctypes.byref(w)), "moe_w4a4_query")
+    return p.value, w.value
+
+
+def moe_w4a4_workspace_layout(cfg: moe_w4a4_cfg) -> dict:
+    lay = moe_w4a4_ws_layout()
+    _check(_lib.moe_w4a4_workspace_layout(ctypes.byref(cfg), ctypes.byref(lay)), "moe_w4a4_workspace_layout")
+    return {n: getattr(lay, n) for n, _ in moe_w4a4_ws_layout._fields_}
+
+
+def moe_w4a4_quantize(src, codes, scales, stream=None) -> None:
+    """src: device bf16 (or uint16 bit patterns) / float32 [rows, cols]."""
+    import torch
+    if src.dtype in (torch.bfloat16, torch.uint16, torch.int16):
+        dt = 0
+    elif src.dtype == torch.float32:
+        dt = 1
+    else:
+        raise ValueError(f"unsupported dtype {src.dtype}")
+    rows, cols = src.shape
+    _check(_lib.moe_w4a4_quantize(dt, _ptr(src), rows, cols, _ptr(codes), _ptr(scales), _stream(stream)),
+           "moe_w4a4_quantize")
+
+
+def moe_w4a4_prepare_weights(cfg, w1_codes, w1_scales, w2_codes, w2_scales, prepared, stream=None) -> None:
+    _check(_lib.moe_w4a4_prepare_weights(ctypes.byref(cfg), _ptr(w1_codes), _ptr(w1_scales), _ptr(w2_codes),
+                                         _ptr(w2_scales), _ptr(prepared), prepared.numel() * prepared.element_size(),
+                                         _stream(stream)), "moe_w4a4_prepare_weights")
+
+
+def moe_w4a4_forward(cfg, prepared, num_tokens: int, x, topk_ids, topk_weights, out, workspace,
+                     stream=None) -> None:
+    _check(_lib.moe_w4a4_forward(ctypes.byref(cfg), _ptr(prepared), int(num_tokens), _ptr(x), _ptr(topk_ids),
+                                 _ptr(topk_weights), _ptr(out), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)),
+           "moe_w4a4_forward")
+
+
+def moe_w4a4_run_stages(cfg, prepared, num_tokens: int, x, topk_ids, topk_weights, out, workspace,
+                        stages: int, gemm1_acc=None, stream=None) -> None:
+    _check(_lib.moe_w4a4_run_stages(ctypes.byref(cfg), _ptr(prepared), int(num_tokens), _ptr(x), _ptr(topk_ids),
+                                    _ptr(topk_weights), _ptr(out), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), int(stages), _ptr(gemm1_acc),
+                                    _stream(stream)), "moe_w4a4_run_stages")

@@ -1,0 +1,232 @@
+// C ABI of the W4A4 MoE layer (declared in include/moe_w4a4.h): argument
+// validation on the host, workspace/prepared layouts, and the stage sequence.
+// The pages' interface ([P3] prhub digest of sglang PR "bump sgl-deep-gemm to
+// 0.1.7, MegaMoE uses the mma_type API for MXFP4", "Key source snippets") is a
+// Python one: a buffer factory keyed by (tokens capacity, experts, topk,
+// hidden, inter, mma_type) with activation="swiglu", a pre_dispatch call that
+// takes the live num_tokens and group_size=32, and a weight transform.  Here
+// the buffer is a caller-owned workspace sized by moe_w4a4_query and the types
+// are explicit integers; nothing is cached across calls except whether a device
+// is a gfx950.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/moe_w4a4.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int kMaxExperts = 512;
+constexpr int kMaxTopk = 16;
+constexpr int kRouteRows = 1024;
+std::atomic<int> g_is_gfx950[kMaxDevices];  // 0 unknown, 1 yes, 2 no
+
+inline uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_cfg(const moe_w4a4_cfg* c) {
+  if (c == nullptr) return MOE_EINVAL;
+  if (c->hidden <= 0 || c->inter <= 0 || c->num_experts <= 0 || c->topk <= 0 || c->max_tokens < 0)
+    return MOE_EINVAL;
+  if (c->hidden % 256 != 0 || c->inter % 128 != 0) return MOE_EUNSUPPORTED;
+  if (c->hidden > (1 << 16) || c->inter > (1 << 16)) return MOE_EUNSUPPORTED;
+  if (c->num_experts > kMaxExperts || c->topk > kMaxTopk) return MOE_EUNSUPPORTED;
+  if (c->group_size != 32 || c->mma_type != MOE_MMA_MXF4_X_MXF4 || c->activation != MOE_ACT_SWIGLU)
+    return MOE_EUNSUPPORTED;
+  if ((int64_t)c->max_tokens * c->topk >= (int64_t)1 << 31) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+struct Prepared {
+  uint64_t w1c, w1s, w2c, w2s, total;
+};
+
+Prepared prepared_layout(const moe_w4a4_cfg* c) {
+  const uint64_t H = c->hidden, I = c->inter, E = c->num_experts;
+  Prepared p{};
+  uint64_t off = 0;
+  p.w1c = off; off = align256(off + E * 2 * I * H / 2);
+  p.w1s = off; off = align256(off + E * 2 * I * H / 32);
+  p.w2c = off; off = align256(off + E * H * I / 2);
+  p.w2s = off; off = align256(off + E * H * I / 32);
+  p.total = off;
+  return p;
+}
+
+moe_w4a4_ws_layout ws_layout(const moe_w4a4_cfg* c) {
+  const uint64_t H = c->hidden, I = c->inter, E = c->num_experts, M = c->max_tokens;
+  const uint64_t R = M * c->topk;
+  const uint64_t nb = (R + kRouteRows - 1) / kRouteRows;
+  moe_w4a4_ws_layout L{};
+  uint64_t off = 0;
+  L.xq = off; off = align256(off + M * H / 2);
+  L.xsf = off; off = align256(off + M * H / 32);
+  L.counts = off; off = align256(off + E * 4);
+  L.offsets = off; off = align256(off + (E + 1) * 4);
+  L.sorted_rows = off; off = align256(off + R * 4);
+  L.pos = off; off = align256(off + R * 4);
+  L.hist = off; off = align256(off + nb * E * 4);
+  L.hq = off; off = align256(off + R * I / 2);
+  L.hsf = off; off = align256(off + R * I / 32);
+  L.y = off; off = align256(off + R * H * 4);
+  L.total = off;
+  return L;
+}
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOE_ENODEVICE;
+  if (dev < kMaxDevices) {
+    const int known = g_is_gfx950[dev].load(std::memory_order_relaxed);
+    if (known != 0) return known == 1 ? MOE_OK : MOE_ENODEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ENODEVICE;
+  const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_is_gfx950[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? MOE_OK : MOE_ENODEVICE;
+}
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_w4a4_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument (null or misaligned pointer, or negative size)";
+    case MOE_EUNSUPPORTED: return "unsupported configuration (shape, group size, mma_type or activation)";
+    case MOE_ECAPACITY: return "num_tokens exceeds the configured max_tokens";
+    case MOE_EWORKSPACE: return "buffer smaller than moe_w4a4_query requires";
+    case MOE_ENODEVICE: return "current HIP device is not a gfx950";
+    case MOE_EHIP: return "HIP runtime call or kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_w4a4_query(const moe_w4a4_cfg* cfg, size_t* prepared_bytes, size_t* workspace_bytes) {
+  const int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (prepared_bytes) *prepared_bytes = (size_t)prepared_layout(cfg).total;
+  if (workspace_bytes) *workspace_bytes = (size_t)ws_layout(cfg).total;
+  return MOE_OK;
+}
+
+int moe_w4a4_workspace_layout(const moe_w4a4_cfg* cfg, moe_w4a4_ws_layout* out) {
+  const int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (out == nullptr) return MOE_EINVAL;
+  *out = ws_layout(cfg);
+  return MOE_OK;
+}
+
+int moe_w4a4_quantize(int32_t src_dtype, const void* src, int64_t rows, int32_t cols, uint8_t* codes,
+                      uint8_t* scales, void* stream) {
+  if (src_dtype != 0 && src_dtype != 1) return MOE_EUNSUPPORTED;
+  if (rows < 0 || cols <= 0) return MOE_EINVAL;
+  if (cols % 32 != 0) return MOE_EUNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (src == nullptr || codes == nullptr || scales == nullptr) return MOE_EINVAL;
+  if (!aligned(src, 16) || !aligned(codes, 16)) return MOE_EINVAL;
+  const int dv = check_device();
+  if (dv != MOE_OK) return dv;
+  return hip_status(moe::launch_quantize(src_dtype == 0, src, rows * (int64_t)(cols / 32), codes, scales,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int moe_w4a4_prepare_weights(const moe_w4a4_cfg* cfg, const uint8_t* w1_codes, const uint8_t* w1_scales,
+                             const uint8_t* w2_codes, const uint8_t* w2_scales, void* prepared,
+                             size_t prepared_bytes, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!w1_codes || !w1_scales || !w2_codes || !w2_scales || !prepared) return MOE_EINVAL;
+  if (!aligned(w1_codes, 16) || !aligned(w2_codes, 16) || !aligned(prepared, 256)) return MOE_EINVAL;
+  const Prepared P = prepared_layout(cfg);
+  if (prepared_bytes < P.total) return MOE_EWORKSPACE;
+  st = check_device();
+  if (st != MOE_OK) return st;
+  uint8_t* base = static_cast<uint8_t*>(prepared);
+  return hip_status(moe::launch_prepare(w1_codes, w1_scales, w2_codes, w2_scales, cfg->hidden, cfg->inter,
+                                        cfg->num_experts, base + P.w1c, base + P.w1s, base + P.w2c,
+                                        base + P.w2s, static_cast<hipStream_t>(stream)));
+}
+
+int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t num_tokens, const uint16_t* x,
+                        const int32_t* topk_ids, const float* topk_weights, uint16_t* out, void* workspace,
+                        size_t workspace_bytes, uint32_t stages, float* gemm1_acc, void* stream) {
+  int st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (num_tokens < 0) return MOE_EINVAL;
+  if (num_tokens > cfg->max_tokens) return MOE_ECAPACITY;
+  if ((stages & ~uint32_t(MOE_STAGE_ALL)) != 0) return MOE_EINVAL;
+  if (num_tokens == 0 || stages == 0) return MOE_OK;   // nothing to do; empty tensors may be NULL
+  if (workspace == nullptr || !aligned(workspace, 256)) return MOE_EINVAL;
+  const moe_w4a4_ws_layout L = ws_layout(cfg);
+  if (workspace_bytes < L.total) return MOE_EWORKSPACE;
+  if ((stages & MOE_STAGE_QUANT) && (x == nullptr || !aligned(x, 16))) return MOE_EINVAL;
+  if ((stages & MOE_STAGE_ROUTE) && (topk_ids == nullptr || !aligned(topk_ids, 4))) return MOE_EINVAL;
+  if ((stages & (MOE_STAGE_GEMM1 | MOE_STAGE_GEMM2)) && (prepared == nullptr || !aligned(prepared, 256)))
+    return MOE_EINVAL;
+  if ((stages & MOE_STAGE_COMBINE) &&
+      (topk_weights == nullptr || out == nullptr || !aligned(topk_weights, 4) || !aligned(out, 16)))
+    return MOE_EINVAL;
+  if (gemm1_acc != nullptr && !aligned(gemm1_acc, 16)) return MOE_EINVAL;
+  st = check_device();
+  if (st != MOE_OK) return st;
+
+  const int H = cfg->hidden, I = cfg->inter, E = cfg->num_experts, k = cfg->topk;
+  const int T = num_tokens, R = T * k;
+  const int rows_hint = (int)(((int64_t)R + E - 1) / E);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* xq = ws + L.xq;
+  uint8_t* xsf = ws + L.xsf;
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* sorted_rows = reinterpret_cast<int32_t*>(ws + L.sorted_rows);
+  int32_t* pos = reinterpret_cast<int32_t*>(ws + L.pos);
+  int32_t* hist = reinterpret_cast<int32_t*>(ws + L.hist);
+  uint8_t* hq = ws + L.hq;
+  uint8_t* hsf = ws + L.hsf;
+  float* y = reinterpret_cast<float*>(ws + L.y);
+  const Prepared P = prepared_layout(cfg);
+  const uint8_t* pw = static_cast<const uint8_t*>(prepared);
+
+  if (stages & MOE_STAGE_QUANT) {
+    st = hip_status(moe::launch_quantize(true, x, (int64_t)T * (H / 32), xq, xsf, s));
+    if (st != MOE_OK) return st;
+  }
+  if (stages & MOE_STAGE_ROUTE) {
+    st = hip_status(moe::launch_route(topk_ids, R, E, hist, counts, offsets, sorted_rows, pos, s));
+    if (st != MOE_OK) return st;
+  }
+  if (stages & MOE_STAGE_GEMM1) {
+    st = hip_status(moe::launch_gemm1(pw + P.w1c, pw + P.w1s, xq, xsf, counts, offsets, sorted_rows, H, I,
+                                      E, k, rows_hint, hq, hsf, gemm1_acc, s));
+    if (st != MOE_OK) return st;
+  }
+  if (stages & MOE_STAGE_GEMM2) {
+    st = hip_status(
+        moe::launch_gemm2(pw + P.w2c, pw + P.w2s, hq, hsf, counts, offsets, H, I, E, rows_hint, y, s));
+    if (st != MOE_OK) return st;
+  }
+  if (stages & MOE_STAGE_COMBINE) {
+    st = hip_status(moe::launch_combine(y, pos, topk_weights, T, H, k, out, s));
+    if (st != MOE_OK) return st;
+  }
+  return MOE_OK;
+}
+
+int moe_w4a4_forward(const moe_w4a4_cfg* cfg, const void* prepared, int32_t num_tokens, const uint16_t* x,
+                     const int32_t* topk_ids, const float* topk_weights, uint16_t* out, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  return moe_w4a4_run_stages(cfg, prepared, num_tokens, x, topk_ids, topk_weights, out, workspace,
+                             workspace_bytes, MOE_STAGE_ALL, nullptr, stream);
+}
+
+}  // extern "C"

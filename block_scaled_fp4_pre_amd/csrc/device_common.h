@@ -1,0 +1,67 @@
+// Device helpers shared by the gfx950 kernels of the W4A4 MoE layer.
+//
+// MXFP4 ([OCP-MX] = OCP Microscaling Formats v1.0): E2M1 codes (bit 3 sign,
+// bits 2..1 exponent with bias 1, bit 0 mantissa; magnitudes 0, .5, 1, 1.5, 2,
+// 3, 4, 6), one UE8M0 scale byte 2^(b-127) per 32 elements, two codes per byte
+// with the even element in the low nibble.  Block scale: 2^e with e the
+// smallest integer such that amax <= 6 * 2^e, clamped to [-127, 127].
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// Scale exponent of a block from the fp32 bits of its absolute maximum.
+// amax = m * 2^E with 1 <= m < 2: the smallest e with amax <= 6 * 2^e is E - 2
+// when m <= 1.5 (mantissa field <= 0x400000) and E - 1 otherwise.  Zero and
+// fp32 subnormals (amax < 2^-126) land on the -127 clamp.
+__device__ __forceinline__ int mx_scale_exp(uint32_t amax_bits) {
+  const uint32_t ef = amax_bits >> 23;
+  if (ef == 0) return -127;
+  int e = (int)ef - 129 + ((amax_bits & 0x7FFFFFu) > 0x400000u ? 1 : 0);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Magnitude index (0..7) of the E2M1 value nearest to a >= 0 (a <= 6), ties to
+// the even index: the thresholds are the midpoints 0.25, 0.75, 1.25, 1.75, 2.5,
+// 3.5, 5 with '>' where the lower neighbour is even and '>=' where the upper is.
+__device__ __forceinline__ uint32_t e2m1_index(float a) {
+  return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+         (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+         (uint32_t)(a > 5.0f);
+}
+
+// 4-bit code of v under block exponent e: sign bit copied from v.
+__device__ __forceinline__ uint32_t e2m1_code(float v, int e) {
+  const uint32_t bits = __float_as_uint(v);
+  const float a = ldexpf(__uint_as_float(bits & 0x7FFFFFFFu), -e);
+  return e2m1_index(a) | ((bits >> 31) << 3);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// fp32 -> bfloat16 bits, round to nearest even; NaN becomes a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// One gfx950 block-scaled MFMA, FP4 x FP4 (format code 4 on both sides),
+// 16x16 output, K = 128.  Lane l supplies row (l % 16) and K elements
+// [32 * (l / 16), +32) of each operand as 16 bytes of packed codes, and the
+// UE8M0 scale of that 32-element block in byte OA / OB of its scale register.
+// Output: lane l holds C[4 * (l / 16) + i][l % 16] in element i.
+template <int OA, int OB>
+__device__ __forceinline__ v4f mfma_fp4(const uint4& a, const uint4& b, const v4f& c, int sa, int sb) {
+  const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const v8i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, OA, sa, OB, sb);
+}
+
+}  // namespace moe

@@ -1,0 +1,195 @@
+// Stage S2: per-expert GEMM1 (tokens x W1^T over gate and up) with fp32
+// accumulation on the gfx950 block-scaled FP4 MFMA, then SwiGLU
+// h = silu(gate) * up and requantization of h to MXFP4 along the inter axis.
+//
+// [P1] sglang PR "[deepseek-v4] Bump sgl-deep-gemm for packed FP4xFP4 mega-MoE
+// (W4A4)": title (both operands packed FP4) and section B "NCU Speed-of-Light"
+// (the layer is memory-bound at ntok=512: the weight data path sets the time).
+// [P3] prhub digest of sglang PR "bump sgl-deep-gemm to 0.1.7, MegaMoE uses the
+// mma_type API for MXFP4", "Key source snippets": activation="swiglu"; W1 rows
+// [0, I) are gate and [I, 2I) are up (the split _interleave_mega_moe_gate_up
+// slices).  The pages' gate/up interleave is tied to their MMA layout; here the
+// pairing is by MFMA block instead (tiles.h).
+//
+// Grid: one workgroup of 4 waves per (expert, 128 inter columns); wave w owns
+// the unit of 32 columns u = 4g + w (64 weight rows).  A workgroup whose
+// expert has no rows exits at once.  Per pass it takes up to NT*16 of the
+// expert's rows: their quantized tokens are gathered into LDS (B operand),
+// while the wave streams its weight tiles HBM -> VGPR with a D-step register
+// prefetch ring, 4 MFMAs (one per 16-row block) per token tile per step.
+// Epilogue per lane: gate/up of 8 columns for one token; the 32-column absmax
+// is reduced over the 4 lanes holding that token (xor 16, xor 32).
+#include "device_common.h"
+#include "launch.h"
+#include "tiles.h"
+
+namespace moe {
+
+template <int NT, int D>
+__global__ void __launch_bounds__(256) gemm1_swiglu_kernel(
+    const uint8_t* __restrict__ w1c, const uint8_t* __restrict__ w1s, const uint8_t* __restrict__ xq,
+    const uint8_t* __restrict__ xsf, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows, int H, int I, int k,
+    uint8_t* __restrict__ hq, uint8_t* __restrict__ hsf, float* __restrict__ acc_out) {
+  const int groups = I / 128;
+  const int e = blockIdx.x / groups;
+  const int g = blockIdx.x - e * groups;
+  const int n_e = counts[e];
+  if (n_e == 0) return;
+  const int base = offsets[e];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int u = g * 4 + wave;
+  const int S = H / kStepK;
+  const int row_bytes = H / 2, row_stride = H / 2 + 16, sc_row = H / 32;
+
+  extern __shared__ __align__(16) uint8_t lds[];
+  uint8_t* lds_codes = lds;                               // [NT*16][row_stride]
+  uint8_t* lds_scales = lds + NT * 16 * row_stride;       // [NT*16][sc_row]
+
+  const uint4* wc = reinterpret_cast<const uint4*>(w1c + w1_code_offset(e, u, 0, H, I)) + lane;
+  const uint32_t* ws = reinterpret_cast<const uint32_t*>(w1s + w1_scale_offset(e, u, 0, H, I)) + lane;
+  const int tok_lane = lane & 15, kb = lane >> 4;
+
+  for (int t0 = 0; t0 < n_e; t0 += NT * 16) {
+    uint4 a[D][4];
+    uint32_t sa[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (d < S) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) a[d][rb] = wc[(d * 4 + rb) * 64];
+        sa[d] = ws[d * 64];
+      }
+    }
+    const int nrows = min(NT * 16, n_e - t0);
+    __syncthreads();  // the previous pass has finished reading LDS
+    const int chunks = row_bytes / 16;
+    for (int idx = threadIdx.x; idx < NT * 16 * chunks; idx += 256) {
+      const int n = idx / chunks, c = idx - n * chunks;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (n < nrows) {
+        const int t = sorted_rows[base + t0 + n] / k;
+        v = reinterpret_cast<const uint4*>(xq + (size_t)t * row_bytes)[c];
+      }
+      *reinterpret_cast<uint4*>(lds_codes + n * row_stride + c * 16) = v;
+    }
+    for (int idx = threadIdx.x; idx < NT * 16 * sc_row; idx += 256) {
+      const int n = idx / sc_row, c = idx - n * sc_row;
+      uint8_t v = 0;
+      if (n < nrows) {
+        const int t = sorted_rows[base + t0 + n] / k;
+        v = xsf[(size_t)t * sc_row + c];
+      }
+      lds_scales[n * sc_row + c] = v;
+    }
+    __syncthreads();
+
+    v4f acc[NT][4];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) acc[nt][rb] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    for (int s0 = 0; s0 < S; s0 += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        const int s = s0 + d;
+        if (s < S) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const int n = nt * 16 + tok_lane;
+            const uint4 b = *reinterpret_cast<const uint4*>(lds_codes + n * row_stride + s * 64 + kb * 16);
+            const int sb = lds_scales[n * sc_row + s * 4 + kb];
+            acc[nt][0] = mfma_fp4<0, 0>(a[d][0], b, acc[nt][0], (int)sa[d], sb);
+            acc[nt][1] = mfma_fp4<1, 0>(a[d][1], b, acc[nt][1], (int)sa[d], sb);
+            acc[nt][2] = mfma_fp4<2, 0>(a[d][2], b, acc[nt][2], (int)sa[d], sb);
+            acc[nt][3] = mfma_fp4<3, 0>(a[d][3], b, acc[nt][3], (int)sa[d], sb);
+          }
+          const int sn = s + D;
+          if (sn < S) {
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) a[d][rb] = wc[(sn * 4 + rb) * 64];
+            sa[d] = ws[sn * 64];
+          }
+        }
+      }
+    }
+
+    // Epilogue.  acc[nt][0|1][i]: gate of column 32u + 16*(0|1) + 4*kb + i for
+    // token row t0 + nt*16 + tok_lane; acc[nt][2|3][i]: the matching up values.
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int n = nt * 16 + tok_lane;
+      const bool live = n < nrows;
+      const int p = base + t0 + n;
+      float h[8];
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float gt = acc[nt][half][i], up = acc[nt][2 + half][i];
+          h[half * 4 + i] = gt / (1.0f + expf(-gt)) * up;
+        }
+      uint32_t amax = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = max(amax, __float_as_uint(h[i]) & 0x7FFFFFFFu);
+      amax = max(amax, (uint32_t)__shfl_xor((int)amax, 16, 64));
+      amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32, 64));
+      const int ex = mx_scale_exp(amax);
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo |= e2m1_code(h[i], ex) << (4 * i);
+        hi |= e2m1_code(h[4 + i], ex) << (4 * i);
+      }
+      if (live) {
+        uint8_t* row = hq + (size_t)p * (I / 2) + u * 16;
+        *reinterpret_cast<uint16_t*>(row + 2 * kb) = (uint16_t)lo;
+        *reinterpret_cast<uint16_t*>(row + 8 + 2 * kb) = (uint16_t)hi;
+        if (kb == 0) hsf[(size_t)p * (I / 32) + u] = (uint8_t)(ex + 127);
+        if (acc_out != nullptr) {
+          float* arow = acc_out + (size_t)p * (2 * I) + 32 * u + 4 * kb;
+#pragma unroll
+          for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              arow[16 * half + i] = acc[nt][half][i];
+              arow[I + 16 * half + i] = acc[nt][2 + half][i];
+            }
+        }
+      }
+    }
+  }
+}
+
+template <int NT, int D>
+static hipError_t launch_gemm1_t(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq,
+                                 const uint8_t* xsf, const int32_t* counts, const int32_t* offsets,
+                                 const int32_t* sorted_rows, int H, int I, int E, int k, uint8_t* hq,
+                                 uint8_t* hsf, float* acc_out, hipStream_t stream) {
+  const size_t lds = (size_t)NT * 16 * (H / 2 + 16) + (size_t)NT * 16 * (H / 32);
+  auto kern = gemm1_swiglu_kernel<NT, D>;
+  if (lds > 65536) {
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(kern, dim3(E * (I / 128)), dim3(256), lds, stream, w1c, w1s, xq, xsf, counts,
+                     offsets, sorted_rows, H, I, k, hq, hsf, acc_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm1(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq, const uint8_t* xsf,
+                        const int32_t* counts, const int32_t* offsets, const int32_t* sorted_rows,
+                        int H, int I, int E, int k, int rows_hint, uint8_t* hq, uint8_t* hsf,
+                        float* acc_out, hipStream_t stream) {
+  // rows_hint: expected routed rows per expert; two token tiles per pass once
+  // a 16-row tile would often overflow.
+  if (rows_hint > 8)
+    return launch_gemm1_t<2, 8>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hq, hsf,
+                                acc_out, stream);
+  return launch_gemm1_t<1, 8>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hq, hsf,
+                              acc_out, stream);
+}
+
+}  // namespace moe

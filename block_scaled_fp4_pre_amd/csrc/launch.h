@@ -1,0 +1,37 @@
+// Host-side launchers of the gfx950 kernels (one translation unit per stage).
+// Every launcher only enqueues on `stream`; shapes were validated by the caller.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Stage S1a: MXFP4 quantization of rows of bf16 (src_is_bf16) or fp32 values.
+hipError_t launch_quantize(bool src_is_bf16, const void* src, int64_t ngroups,
+                           uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
+// Stage S1b: stable counting sort of R routed rows over E experts.
+hipError_t launch_route(const int32_t* ids, int R, int E, int32_t* hist, int32_t* counts,
+                        int32_t* offsets, int32_t* sorted_rows, int32_t* pos, hipStream_t stream);
+
+// Stage S2: grouped GEMM1 over the prepared W1 tiles + SwiGLU + MXFP4 requant.
+hipError_t launch_gemm1(const uint8_t* w1_codes, const uint8_t* w1_scales, const uint8_t* xq,
+                        const uint8_t* xsf, const int32_t* counts, const int32_t* offsets,
+                        const int32_t* sorted_rows, int H, int I, int E, int k, int rows_hint,
+                        uint8_t* hq, uint8_t* hsf, float* acc_out, hipStream_t stream);
+
+// Stage S3: grouped GEMM2 over the prepared W2 tiles -> fp32 y in sorted order.
+hipError_t launch_gemm2(const uint8_t* w2_codes, const uint8_t* w2_scales, const uint8_t* hq,
+                        const uint8_t* hsf, const int32_t* counts, const int32_t* offsets, int H,
+                        int I, int E, int rows_hint, float* y, hipStream_t stream);
+
+// Stage S4: top-k weighted combine back to token order, bf16 output.
+hipError_t launch_combine(const float* y, const int32_t* pos, const float* w, int T, int H, int k,
+                          uint16_t* out, hipStream_t stream);
+
+// Stage S0: canonical MXFP4 weights -> device tile order.
+hipError_t launch_prepare(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* w2c,
+                          const uint8_t* w2s, int H, int I, int E, uint8_t* p_w1c, uint8_t* p_w1s,
+                          uint8_t* p_w2c, uint8_t* p_w2s, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,87 @@
+"""MoeW4A4Layer: owns the device buffers of one layer and calls the C ABI.
+
+PyTorch provides the device memory and the stream; every computation runs in
+the library's HIP kernels.  Weights can be loaded either as canonical MXFP4
+(codes + scale bytes) or as fp32 matrices, which are quantized on the device by
+moe_w4a4_quantize and then re-laid by moe_w4a4_prepare_weights.
+"""
+from __future__ import annotations
+
+import concurrent.futures
+
+import torch
+
+from . import _lib
+
+
+class MoeW4A4Layer:
+    def __init__(self, hidden: int, inter: int, num_experts: int, topk: int, max_tokens: int,
+                 device: str | torch.device = "cuda"):
+        self.H, self.I, self.E, self.k, self.max_tokens = hidden, inter, num_experts, topk, max_tokens
+        self.device = torch.device(device)
+        self.cfg = _lib.make_cfg(hidden, inter, num_experts, topk, max_tokens)
+        pb, wb = _lib.moe_w4a4_query(self.cfg)
+        self.prepared = torch.empty(pb, dtype=torch.uint8, device=self.device)
+        self.workspace = torch.empty(wb, dtype=torch.uint8, device=self.device)
+        self.layout = _lib.moe_w4a4_workspace_layout(self.cfg)
+
+    # ---- weights ------------------------------------------------------------
+    def canonical_buffers(self):
+        H, I, E = self.H, self.I, self.E
+        u8 = dict(dtype=torch.uint8, device=self.device)
+        return (torch.empty((E, 2 * I, H // 2), **u8), torch.empty((E, 2 * I, H // 32), **u8),
+                torch.empty((E, H, I // 2), **u8), torch.empty((E, H, I // 32), **u8))
+
+    def load_canonical(self, w1_codes, w1_scales, w2_codes, w2_scales) -> None:
+        _lib.moe_w4a4_prepare_weights(self.cfg, w1_codes, w1_scales, w2_codes, w2_scales, self.prepared)
+
+    def quantize_fp32_weights(self, expert_source, threads: int = 16):
+        """expert_source(e) -> (W1 [2I, H], W2 [H, I]) fp32 arrays (host or device).
+        Returns the canonical MXFP4 buffers (w1c, w1s, w2c, w2s) on the device."""
+        bufs = self.canonical_buffers()
+        w1c, w1s, w2c, w2s = bufs
+        with concurrent.futures.ThreadPoolExecutor(max(1, threads)) as ex:
+            futs = [ex.submit(expert_source, e) for e in range(min(self.E, 2 * threads))]
+            nxt = len(futs)
+            for e in range(self.E):
+                w1, w2 = futs[e].result()
+                futs[e] = None
+                if nxt < self.E:
+                    futs.append(ex.submit(expert_source, nxt))
+                    nxt += 1
+                d1 = torch.as_tensor(w1).to(self.device, torch.float32)
+                d2 = torch.as_tensor(w2).to(self.device, torch.float32)
+                _lib.moe_w4a4_quantize(d1, w1c[e], w1s[e])
+                _lib.moe_w4a4_quantize(d2, w2c[e], w2s[e])
+        return bufs
+
+    def load_fp32(self, expert_source, threads: int = 16, keep_canonical: bool = False):
+        bufs = self.quantize_fp32_weights(expert_source, threads)
+        self.load_canonical(*bufs)
+        if keep_canonical:
+            return bufs
+        del bufs
+        return None
+
+    # ---- forward ------------------------------------------------------------
+    def forward(self, x, topk_ids, topk_weights, out=None, stream=None):
+        T = x.shape[0]
+        if out is None:
+            out = torch.empty((T, self.H), dtype=torch.bfloat16, device=self.device)
+        _lib.moe_w4a4_forward(self.cfg, self.prepared, T, x, topk_ids, topk_weights, out, self.workspace,
+                              stream=stream)
+        return out
+
+    def run_stages(self, stages, num_tokens, x=None, topk_ids=None, topk_weights=None, out=None,
+                   gemm1_acc=None, stream=None):
+        _lib.moe_w4a4_run_stages(self.cfg, self.prepared, num_tokens, x, topk_ids, topk_weights, out,
+                                 self.workspace, stages, gemm1_acc=gemm1_acc, stream=stream)
+
+    def ws(self, name: str, shape, dtype) -> torch.Tensor:
+        """A view of one intermediate region of the workspace (see moe_w4a4_ws_layout)."""
+        off = self.layout[name]
+        n = 1
+        for s in shape:
+            n *= s
+        nbytes = n * torch.empty((), dtype=dtype).element_size()
+        return self.workspace[off:off + nbytes].view(dtype).view(*shape)

@@ -1,0 +1,186 @@
+/*
+ * moe_w4a4.h -- C ABI of the MI355X (gfx950) W4A4 routed-expert MoE layer.
+ *
+ * The layer is the fused "mega-MoE" W4A4 layer of a DeepSeek-V4-Flash-shaped
+ * model (hidden 4096, inter 2048, 256 experts, top-6): tokens and expert
+ * weights are both MXFP4 (E2M1 codes, one UE8M0 scale per 32 elements), the
+ * expert MLP is SwiGLU.  Sources:
+ *   [P1] sglang PR "[deepseek-v4] Bump sgl-deep-gemm for packed FP4xFP4
+ *        mega-MoE (W4A4)": title (packed FP4 x FP4 operands), Appendix
+ *        "measured data" (the layer shape).
+ *   [P3] prhub digest of sglang PR "bump sgl-deep-gemm to 0.1.7, MegaMoE uses
+ *        the mma_type API for MXFP4": "Key source snippets" (the symmetric
+ *        buffer factory with mma_type and activation="swiglu"; the mxf4xmxf4
+ *        pre_dispatch call with group_size=32 and a live num_tokens below the
+ *        buffer capacity; the gate/up split of the L1 weights), and
+ *        "Implementation breakdown" item 4 (weights are transformed once at
+ *        load time for the chosen mma_type).
+ *   [OCP-MX] OCP Microscaling Formats (MX) v1.0: E2M1 element and E8M0 scale
+ *        encodings.
+ *
+ * Conventions for every entry point
+ *   - Device pointers are allocated and owned by the caller; the library never
+ *     allocates, frees or synchronizes, and reads no environment variables.
+ *     A call only enqueues work on `stream` (a hipStream_t; NULL = the null
+ *     stream), so it can be captured into a HIP graph.
+ *   - Arguments are validated on the host before any HIP call; a failed check
+ *     returns a status code and enqueues nothing.
+ *   - Faults while kernels execute surface at the caller's next synchronization.
+ *   - The library is stateless apart from a per-device cache of "is this a
+ *     gfx950"; calls on different streams with distinct workspaces may run
+ *     concurrently.
+ *
+ * MXFP4 encoding used throughout ([OCP-MX]; the scale rule is the reading
+ * taken where the pages are silent):
+ *   code (4 bits): bit 3 sign, bits 2..1 exponent (bias 1), bit 0 mantissa;
+ *                  magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+ *   packing:       two codes per byte, the even element in the low nibble.
+ *   scale byte b:  value 2^(b-127); for a block with absolute maximum a the
+ *                  scale is 2^e with e the smallest integer such that
+ *                  a <= 6*2^e, clamped to [-127, 127] (a == 0 gives b = 0).
+ *   rounding:      nearest code to v/2^e, ties to the even mantissa; the sign
+ *                  bit is copied from v (so -0 encodes as 0x8).
+ */
+#ifndef MOE_W4A4_H
+#define MOE_W4A4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,        /* null or misaligned pointer, negative size            */
+  MOE_EUNSUPPORTED = 2,  /* shape, group size, mma_type or activation not built   */
+  MOE_ECAPACITY = 3,     /* num_tokens > cfg->max_tokens                          */
+  MOE_EWORKSPACE = 4,    /* a buffer is smaller than moe_w4a4_query() requires    */
+  MOE_ENODEVICE = 5,     /* the current HIP device is not a gfx950                */
+  MOE_EHIP = 6           /* a HIP runtime call or kernel launch failed            */
+};
+
+/* mma_type: the pairing of activation and weight formats.  Only MXFP4 x MXFP4
+ * ("mxf4xmxf4" in [P3]) is implemented; the FP8-activation pairing is not. */
+enum { MOE_MMA_MXF4_X_MXF4 = 0 };
+/* activation: SwiGLU, silu(gate) * up, with no clamp or bias ([P3]). */
+enum { MOE_ACT_SWIGLU = 0 };
+
+/* Layer configuration.  Supported: hidden % 256 == 0, inter % 128 == 0,
+ * 1 <= num_experts <= 512, 1 <= topk <= 16, 0 <= max_tokens and
+ * max_tokens * topk < 2^31, group_size == 32, mma_type == MOE_MMA_MXF4_X_MXF4,
+ * activation == MOE_ACT_SWIGLU.  max_tokens is the capacity the workspace is
+ * sized for (num_max_tokens_per_rank in [P3]); each forward passes the live
+ * token count. */
+typedef struct moe_w4a4_cfg {
+  int32_t hidden;       /* H */
+  int32_t inter;        /* I */
+  int32_t num_experts;  /* E */
+  int32_t topk;         /* k */
+  int32_t max_tokens;   /* capacity */
+  int32_t group_size;   /* must be 32 */
+  int32_t mma_type;     /* MOE_MMA_MXF4_X_MXF4 */
+  int32_t activation;   /* MOE_ACT_SWIGLU */
+} moe_w4a4_cfg;
+
+/* Sizes in bytes of the prepared-weights buffer and of the forward workspace
+ * for `cfg`.  Either output pointer may be NULL.  Pure host function. */
+int moe_w4a4_query(const moe_w4a4_cfg* cfg, size_t* prepared_bytes, size_t* workspace_bytes);
+
+/* Quantize `rows` rows of `cols` values to MXFP4 along each row.
+ * src_dtype: 0 = bfloat16 (uint16 bit patterns), 1 = float32.  Values must be
+ * finite.  src: device [rows, cols], 16-byte aligned.  codes: device uint8
+ * [rows, cols/2] (packed, 16-byte aligned); scales: device uint8 [rows, cols/32].
+ * cols % 32 == 0, rows >= 0.  This is the activation quantizer of the
+ * pre-dispatch step ([P3] "Key source snippets": pre_dispatch packs E2M1 with
+ * group_size=32) and the load-time quantizer for fp32 expert weights. */
+int moe_w4a4_quantize(int32_t src_dtype, const void* src, int64_t rows, int32_t cols,
+                      uint8_t* codes, uint8_t* scales, void* stream);
+
+/* Re-lay canonical MXFP4 expert weights into the device tile order used by the
+ * forward ([P3] "Implementation breakdown" item 4: a one-off weight transform at
+ * load time).  A pure byte permutation.
+ *   w1_codes  [E, 2I, H/2], w1_scales [E, 2I, H/32]: rows [0, I) are gate and
+ *             rows [I, 2I) are up ([P3] gate/up split of the L1 weights);
+ *   w2_codes  [E, H, I/2],  w2_scales [E, H, I/32].
+ * All device pointers; codes 16-byte aligned.  prepared: device buffer of at
+ * least moe_w4a4_query()'s prepared_bytes, 256-byte aligned; owned by the
+ * caller and read by every later forward. */
+int moe_w4a4_prepare_weights(const moe_w4a4_cfg* cfg,
+                             const uint8_t* w1_codes, const uint8_t* w1_scales,
+                             const uint8_t* w2_codes, const uint8_t* w2_scales,
+                             void* prepared, size_t prepared_bytes, void* stream);
+
+/* One forward of the layer for num_tokens (0 <= num_tokens <= cfg->max_tokens):
+ *   1. pre-dispatch: each token row of x quantized once to MXFP4;
+ *   2. route: stable counting sort of the routed rows r = t*k + j by expert
+ *      (ids outside [0, E) are skipped; duplicates are separate rows);
+ *   3. GEMM1 per expert with fp32 accumulation, SwiGLU, requantization of h to
+ *      MXFP4 along I;
+ *   4. GEMM2 per expert, fp32 result per routed row;
+ *   5. combine: out[t] = sum over valid slots j (in slot order, fp32, from +0)
+ *      of topk_weights[t, j] * y[row (t, j)], rounded once to bfloat16.
+ * x:            device bfloat16 [num_tokens, H], 16-byte aligned
+ * topk_ids:     device int32 [num_tokens, k]
+ * topk_weights: device float32 [num_tokens, k], used as given
+ * out:          device bfloat16 [num_tokens, H], 16-byte aligned
+ * workspace:    device buffer of at least query()'s workspace_bytes, 256-byte
+ *               aligned; holds the intermediates (layout: moe_w4a4_workspace_layout)
+ * num_tokens == 0 returns MOE_OK and enqueues nothing, without looking at
+ * any pointer (empty tensors may have NULL data).
+ * The result is deterministic: no floating-point atomics, stable sort. */
+int moe_w4a4_forward(const moe_w4a4_cfg* cfg, const void* prepared, int32_t num_tokens,
+                     const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
+                     uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable text of a status code (static storage). */
+const char* moe_w4a4_status_string(int status);
+
+/* ---- inspection and stage-by-stage execution (tests, profiling) -------- */
+
+/* Byte offsets of each intermediate inside the forward workspace; every region
+ * is 256-byte aligned and sized for cfg->max_tokens. */
+typedef struct moe_w4a4_ws_layout {
+  uint64_t xq;           /* uint8  [max_tokens, H/2]   quantized tokens (packed)    */
+  uint64_t xsf;          /* uint8  [max_tokens, H/32]  their scale bytes            */
+  uint64_t counts;       /* int32  [E]                 routed rows per expert       */
+  uint64_t offsets;      /* int32  [E+1]               exclusive prefix of counts   */
+  uint64_t sorted_rows;  /* int32  [max_tokens*k]      r = t*k+j in (expert, r) order */
+  uint64_t pos;          /* int32  [max_tokens*k]      index of r in sorted_rows or -1 */
+  uint64_t hist;         /* int32  [ceil(max_tokens*k/1024), E] per-block counts   */
+  uint64_t hq;           /* uint8  [max_tokens*k, I/2] requantized h (sorted order) */
+  uint64_t hsf;          /* uint8  [max_tokens*k, I/32]                             */
+  uint64_t y;            /* float  [max_tokens*k, H]   GEMM2 result (sorted order)  */
+  uint64_t total;        /* == workspace_bytes                                      */
+} moe_w4a4_ws_layout;
+
+int moe_w4a4_workspace_layout(const moe_w4a4_cfg* cfg, moe_w4a4_ws_layout* out);
+
+/* Stage bits for moe_w4a4_run_stages. */
+enum {
+  MOE_STAGE_QUANT = 1,    /* x -> xq, xsf                                  */
+  MOE_STAGE_ROUTE = 2,    /* topk_ids -> counts, offsets, sorted_rows, pos */
+  MOE_STAGE_GEMM1 = 4,    /* xq, route -> hq, hsf                          */
+  MOE_STAGE_GEMM2 = 8,    /* hq, route -> y                                */
+  MOE_STAGE_COMBINE = 16, /* y, pos, topk_weights -> out                   */
+  MOE_STAGE_ALL = 31
+};
+
+/* Run the selected stages of a forward on the workspace, reading whatever the
+ * skipped stages would have written from the workspace as the caller left it
+ * (a test can fill an intermediate and run a single stage).  Arguments as for
+ * moe_w4a4_forward; a pointer only some stages read may be NULL when those
+ * stages are not selected.  gemm1_acc: NULL, or a device float buffer
+ * [max_tokens*k, 2I] into which GEMM1 also writes its raw fp32 accumulators
+ * (gate in columns [0, I), up in [I, 2I)), in sorted-row order. */
+int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t num_tokens,
+                        const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
+                        uint16_t* out, void* workspace, size_t workspace_bytes,
+                        uint32_t stages, float* gemm1_acc, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_W4A4_H */

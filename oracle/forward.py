@@ -52,7 +52,7 @@ def silu_mul(gate, up):
 
 
 def forward(x_bf16, topk_ids, topk_weights, weights, num_experts: int, inter: int,
-            tokens=None):
+            tokens=None, keep_acc: bool = False, experts=None):
     """Run the layer.
 
     x_bf16        uint16 [T, H] bfloat16 bit patterns
@@ -62,10 +62,14 @@ def forward(x_bf16, topk_ids, topk_weights, weights, num_experts: int, inter: in
     tokens        optional iterable of token indices: compute y only for the
                   routed rows of these tokens and out only for them (other
                   rows of y / out are NaN).  None = all tokens.
+    experts       optional iterable of expert indices: run steps 3-5 only for
+                  these experts' rows and skip step 6 (out stays NaN); used to
+                  time a bounded slice of the layer.  None = all experts.
 
     Returns a dict with every intermediate:
       xq, xsf          packed codes [T, H/2] and scale bytes [T, H/32] of x
       counts, offsets, sorted_rows, pos
+      acc              fp64 [n_valid, 2I] GEMM1 result (gate | up), only with keep_acc
       h                fp64 [n_valid, I] (NaN where not computed), in sorted order
       hq, hsf          packed codes [n_valid, I/2], scale bytes [n_valid, I/32]
       y                fp64 [n_valid, H]
@@ -97,8 +101,10 @@ def forward(x_bf16, topk_ids, topk_weights, weights, num_experts: int, inter: in
     hq = np.zeros((nv, I // 2), dtype=np.uint8)
     hsf = np.zeros((nv, I // mxfp4.GROUP), dtype=np.uint8)
     y = np.full((nv, H), np.nan)
+    acc_all = np.full((nv, 2 * I), np.nan) if keep_acc else None
 
-    for e in range(E):
+    expert_list = range(E) if experts is None else sorted(set(int(e) for e in experts))
+    for e in expert_list:
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if lo == hi:
             continue
@@ -117,10 +123,12 @@ def forward(x_bf16, topk_ids, topk_weights, weights, num_experts: int, inter: in
         W2 = mxfp4.dequantize(w2c, w2s)                        # [H, I]
         y_e = mxfp4.dequantize(hq_e, hsf_e) @ W2.T             # step 5
         h[p_idx], hq[p_idx], hsf[p_idx], y[p_idx] = h_e, hq_e, hsf_e, y_e
+        if keep_acc:
+            acc_all[p_idx] = acc
 
     out = np.full((T, H), np.nan)                              # step 6
     for t in range(T):
-        if not want[t]:
+        if not want[t] or experts is not None:
             continue
         acc = np.zeros(H)
         for j in range(k):
@@ -129,7 +137,8 @@ def forward(x_bf16, topk_ids, topk_weights, weights, num_experts: int, inter: in
                 acc = acc + w[t, j] * y[p]
         out[t] = acc
     out_bits = np.zeros((T, H), dtype=np.uint16)
-    out_bits[want] = bf16.encode(out[want])
+    if experts is None:
+        out_bits[want] = bf16.encode(out[want])
 
     return dict(xq=xq, xsf=xsf, counts=counts, offsets=offsets, sorted_rows=sorted_rows,
-                pos=pos, h=h, hq=hq, hsf=hsf, y=y, out_f64=out, out=out_bits)
+                pos=pos, acc=acc_all, h=h, hq=hq, hsf=hsf, y=y, out_f64=out, out=out_bits)

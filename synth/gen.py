@@ -7,9 +7,11 @@ The token counts are the decode size 64, the pages' single-rank operating point
 ntok=512 (same page, section B "NCU Speed-of-Light"), a 4x1024-token prefill and
 a 16384-token prefill with Zipf(1.1) expert popularity.
 
-Streams: every draw uses numpy PCG64 seeded with SeedSequence((1000*cfg + stream,
-*sub)); stream 0 = tokens, 1 = routing, 2 = weights (sub = expert index, so any
-single expert can be regenerated on its own).
+Streams: every draw uses numpy PCG64 seeded with SeedSequence((1000*idx + stream,
+*sub)); stream 0 = tokens, 1 = routing (idx = the config index), 2 = weights
+(idx = the config's weight set, sub = expert index, so any single expert can be
+regenerated on its own).  The four DeepSeek-V4-Flash-shaped configs are one
+layer at four token counts and share weight set 1; the tiny layer has set 0.
 
 Value distributions:
   x        fp32 ~ N(0, 1), rounded to bfloat16 (round to nearest, ties to even)
@@ -41,6 +43,7 @@ class LayerConfig:
     experts: int
     topk: int
     routing: str           # 'logits' | 'uniform' | 'zipf'
+    weight_set: int = 0
     zipf_s: float = 1.1
 
     @property
@@ -50,10 +53,10 @@ class LayerConfig:
 
 CONFIGS = (
     LayerConfig(0, "tiny_t16_h256_i128_e8_k2", 16, 256, 128, 8, 2, "logits"),
-    LayerConfig(1, "dsv4flash_t64_decode", 64, 4096, 2048, 256, 6, "uniform"),
-    LayerConfig(2, "dsv4flash_t512", 512, 4096, 2048, 256, 6, "uniform"),
-    LayerConfig(3, "dsv4flash_t4096_prefill", 4096, 4096, 2048, 256, 6, "uniform"),
-    LayerConfig(4, "dsv4flash_t16384_zipf1.1", 16384, 4096, 2048, 256, 6, "zipf"),
+    LayerConfig(1, "dsv4flash_t64_decode", 64, 4096, 2048, 256, 6, "uniform", 1),
+    LayerConfig(2, "dsv4flash_t512", 512, 4096, 2048, 256, 6, "uniform", 1),
+    LayerConfig(3, "dsv4flash_t4096_prefill", 4096, 4096, 2048, 256, 6, "uniform", 1),
+    LayerConfig(4, "dsv4flash_t16384_zipf1.1", 16384, 4096, 2048, 256, 6, "zipf", 1),
 )
 
 
@@ -112,7 +115,7 @@ def make_routing(cfg: LayerConfig, tokens: int | None = None):
 
 def expert_weights_f32(cfg: LayerConfig, e: int):
     """(W1 fp32 [2I, H], W2 fp32 [H, I]) for expert e; rows [0, I) of W1 are gate, [I, 2I) are up."""
-    rng = _rng(cfg.index, 2, e)
+    rng = _rng(cfg.weight_set, 2, e)
     std = np.float32(0.02)
     w1 = rng.standard_normal((2 * cfg.inter, cfg.hidden), dtype=np.float32)
     w1 *= std

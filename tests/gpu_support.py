@@ -1,0 +1,78 @@
+"""Device-side fixtures for the GPU tier: synthetic inputs copied to the GPU,
+weights quantized there by the library (moe_w4a4_quantize) and re-laid by
+moe_w4a4_prepare_weights.  The oracle side never sees a device result as an
+input: it regenerates the same synthetic values and quantizes them itself."""
+import functools
+import sys
+
+import numpy as np
+import torch
+
+import synth
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def dev(a, dtype=None) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def layer_for(H, I, E, k, max_tokens):
+    from block_scaled_fp4_pre_amd.layer import MoeW4A4Layer
+    return MoeW4A4Layer(H, I, E, k, max_tokens)
+
+
+@functools.lru_cache(maxsize=2)
+def synth_layer(weight_set_cfg_index: int, max_tokens: int):
+    """A layer holding the synthetic weights of the config's weight set."""
+    cfg = synth.CONFIGS[weight_set_cfg_index]
+    log(f"[gpu_support] building layer weight_set={cfg.weight_set} H={cfg.hidden} I={cfg.inter} "
+        f"E={cfg.experts} k={cfg.topk} max_tokens={max_tokens}")
+    layer = layer_for(cfg.hidden, cfg.inter, cfg.experts, cfg.topk, max_tokens)
+    layer.load_fp32(lambda e: synth.expert_weights_f32(cfg, e))
+    torch.cuda.synchronize()
+    log("[gpu_support] layer ready")
+    return layer
+
+
+def run_config(layer, cfg, tokens=None):
+    """Forward of config cfg on `layer`; returns host copies of every intermediate."""
+    x = synth.make_tokens(cfg, tokens)
+    ids, w = synth.make_routing(cfg, tokens)
+    T = x.shape[0]
+    out = layer.forward(dev_bf16(x), dev(ids), dev(w))
+    torch.cuda.synchronize()
+    return dict(x=x, ids=ids, w=w, out=host_bits(out), **workspace_host(layer, T))
+
+
+def workspace_host(layer, T):
+    H, I, E, k = layer.H, layer.I, layer.E, layer.k
+    R = T * k
+    ws = layer.ws
+    counts = ws("counts", (E,), torch.int32).cpu().numpy()
+    nv = int(counts.sum())
+    return dict(
+        xq=ws("xq", (layer.max_tokens, H // 2), torch.uint8)[:T].cpu().numpy(),
+        xsf=ws("xsf", (layer.max_tokens, H // 32), torch.uint8)[:T].cpu().numpy(),
+        counts=counts,
+        offsets=ws("offsets", (E + 1,), torch.int32).cpu().numpy(),
+        sorted_rows=ws("sorted_rows", (layer.max_tokens * k,), torch.int32)[:nv].cpu().numpy(),
+        pos=ws("pos", (layer.max_tokens * k,), torch.int32)[:R].cpu().numpy(),
+        hq=ws("hq", (layer.max_tokens * k, I // 2), torch.uint8)[:nv].cpu().numpy(),
+        hsf=ws("hsf", (layer.max_tokens * k, I // 32), torch.uint8)[:nv].cpu().numpy(),
+        y=ws("y", (layer.max_tokens * k, H), torch.float32)[:nv].cpu().numpy(),
+    )

@@ -1,0 +1,120 @@
+"""GPU tier, whole forward through moe_w4a4_forward, against the oracle:
+the tiny configuration, odd shapes and routing edge cases, determinism."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle.forward import forward
+from tests.gpu_support import dev, dev_bf16, host_bits, layer_for, log, run_config, synth_layer, workspace_host
+from tests.oracle_inputs import all_expert_weights
+from tests.parity import OUT_REL_L2, compare_requant, rel_l2
+
+pytestmark = pytest.mark.gpu
+TINY = synth.CONFIGS[0]
+
+
+def check_all_stages(got, ref, k):
+    from oracle import bf16
+    assert np.array_equal(got["xq"], ref["xq"]) and np.array_equal(got["xsf"], ref["xsf"])
+    for key in ("counts", "offsets", "sorted_rows", "pos"):
+        assert np.array_equal(got[key], ref[key]), key
+    stats = compare_requant(got["hq"], got["hsf"], ref["hq"], ref["hsf"], ref["h"])
+    y_err = rel_l2(got["y"], ref["y"]) if ref["y"].size else 0.0
+    o_err = rel_l2(bf16.decode(got["out"]), ref["out_f64"])
+    same = float(np.mean(got["out"] == ref["out"])) if got["out"].size else 1.0
+    log(f"    requant {stats}  y rel-L2 {y_err:.2e}  out rel-L2 {o_err:.2e}  out bit-identical {same:.4f}")
+    assert y_err <= 1e-3
+    assert o_err <= OUT_REL_L2
+    return o_err
+
+
+@pytest.fixture(scope="module")
+def tiny_layer():
+    layer = layer_for(TINY.hidden, TINY.inter, TINY.experts, TINY.topk, 1024)
+    layer.load_fp32(lambda e: synth.expert_weights_f32(TINY, e))
+    return layer
+
+
+@pytest.fixture(scope="module")
+def tiny_weights():
+    return all_expert_weights(TINY)
+
+
+def test_tiny_config_end_to_end(tiny_layer, tiny_weights):
+    log("[test] tiny config end to end")
+    got = run_config(tiny_layer, TINY)
+    ref = forward(got["x"], got["ids"], got["w"], tiny_weights, TINY.experts, TINY.inter)
+    check_all_stages(got, ref, TINY.topk)
+
+
+def _run_custom(layer, x, ids, w):
+    out = layer.forward(dev_bf16(x), dev(ids), dev(w))
+    torch.cuda.synchronize()
+    return dict(out=host_bits(out), **workspace_host(layer, x.shape[0]))
+
+
+@pytest.mark.parametrize("case", ["T1", "T3", "T129", "T1000", "one_expert", "masked_dups", "zero_x"])
+def test_tiny_dims_edge_cases(tiny_layer, tiny_weights, case):
+    log(f"[test] edge case {case}")
+    rng = np.random.default_rng(abs(hash(case)) % (1 << 31))
+    T = {"T1": 1, "T3": 3, "T129": 129, "T1000": 1000}.get(case, 200)
+    E, k = TINY.experts, TINY.topk
+    x = synth.f32_to_bf16_bits(rng.standard_normal((T, TINY.hidden)).astype(np.float32))
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    w /= w.sum(axis=1, keepdims=True)
+    if case == "one_expert":
+        ids[:, 0] = 5                       # 200 rows on one expert: many token tiles
+        ids[:, 1] = rng.integers(0, 2, T)   # experts 2,3,4,6,7 get nothing
+    if case == "masked_dups":
+        ids[::3, 1] = -1
+        ids[1::3, 1] = ids[1::3, 0]
+        ids[5, :] = -1
+        ids[7, 0] = E + 3
+    if case == "zero_x":
+        x[:] = 0
+    got = _run_custom(tiny_layer, x, ids, w)
+    ref = forward(x, ids, w, tiny_weights, E, TINY.inter)
+    check_all_stages(got, ref, k)
+    if case == "zero_x":
+        assert np.all(got["out"] == 0) and np.all(got["xsf"] == 0)
+
+
+def test_single_expert_single_slot():
+    log("[test] E=1, k=1 dense MXFP4 MLP")
+    H, I, T = 256, 128, 70
+    rng = np.random.default_rng(3)
+    W1 = (rng.standard_normal((1, 2 * I, H)) * 0.05).astype(np.float32)
+    W2 = (rng.standard_normal((1, H, I)) * 0.05).astype(np.float32)
+    layer = layer_for(H, I, 1, 1, T)
+    layer.load_fp32(lambda e: (W1[e], W2[e]))
+    x = synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    ids = np.zeros((T, 1), np.int32)
+    w = np.ones((T, 1), np.float32)
+    got = _run_custom(layer, x, ids, w)
+    from oracle import mxfp4
+    Wq = (*mxfp4.quantize_packed(W1[0].astype(np.float64)), *mxfp4.quantize_packed(W2[0].astype(np.float64)))
+    ref = forward(x, ids, w, tuple(a[None] for a in Wq), 1, I)
+    check_all_stages(got, ref, 1)
+
+
+def test_forward_is_deterministic(tiny_layer):
+    log("[test] determinism")
+    cfg = TINY
+    x = synth.make_tokens(cfg, 16)
+    ids, w = synth.make_routing(cfg, 16)
+    xs, idt, wt = dev_bf16(np.tile(x, (40, 1))), dev(np.tile(ids, (40, 1))), dev(np.tile(w, (40, 1)))
+    a = host_bits(tiny_layer.forward(xs, idt, wt))
+    b = host_bits(tiny_layer.forward(xs, idt, wt))
+    assert np.array_equal(a, b)
+
+
+def test_zero_tokens_is_a_no_op(tiny_layer):
+    out = torch.full((4, TINY.hidden), 7.0, dtype=torch.bfloat16, device="cuda")
+    x = torch.zeros((0, TINY.hidden), dtype=torch.bfloat16, device="cuda")
+    from block_scaled_fp4_pre_amd import _lib
+    _lib.moe_w4a4_forward(tiny_layer.cfg, tiny_layer.prepared, 0, x, torch.zeros((0, 2), dtype=torch.int32,
+                          device="cuda"), torch.zeros((0, 2), device="cuda"), out, tiny_layer.workspace)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
