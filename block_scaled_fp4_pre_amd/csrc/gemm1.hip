@@ -14,19 +14,19 @@
 // Grid: one workgroup of 4 waves per (expert, 128 inter columns); wave w owns
 // the unit of 32 columns u = 4g + w (64 weight rows).  A workgroup whose
 // expert has no rows exits at once.  Per pass it takes up to NT*16 of the
-// expert's rows: their quantized tokens are gathered into LDS (B operand),
-// while the wave streams its weight tiles HBM -> VGPR with a D-step register
-// prefetch ring, 4 MFMAs (one per 16-row block) per token tile per step.
+// expert's rows: their quantized tokens are gathered into LDS (B operand) by
+// direct-to-LDS loads while the wave's weight ring (gemm_common.h) fills;
+// then 4 MFMAs (one per 16-row block) per token tile per K step of 128.
 // Epilogue per lane: gate/up of 8 columns for one token; the 32-column absmax
 // is reduced over the 4 lanes holding that token (xor 16, xor 32).
-#include "device_common.h"
+#include "gemm_common.h"
 #include "launch.h"
 #include "tiles.h"
 
 namespace moe {
 
-template <int NT, int D>
-__global__ void __launch_bounds__(256) gemm1_swiglu_kernel(
+template <int NT, int D, int SWZ>
+__global__ void __launch_bounds__(256, 2) gemm1_swiglu_kernel(
     const uint8_t* __restrict__ w1c, const uint8_t* __restrict__ w1s, const uint8_t* __restrict__ xq,
     const uint8_t* __restrict__ xsf, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows, int H, int I, int k,
@@ -37,51 +37,37 @@ __global__ void __launch_bounds__(256) gemm1_swiglu_kernel(
   const int n_e = counts[e];
   if (n_e == 0) return;
   const int base = offsets[e];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps the buffer resources in SGPRs
   const int u = g * 4 + wave;
   const int S = H / kStepK;
-  const int row_bytes = H / 2, row_stride = H / 2 + 16, sc_row = H / 32;
+  const int row_bytes = H / 2, sc_bytes = H / 32;
 
   extern __shared__ __align__(16) uint8_t lds[];
-  uint8_t* lds_codes = lds;                               // [NT*16][row_stride]
-  uint8_t* lds_scales = lds + NT * 16 * row_stride;       // [NT*16][sc_row]
+  uint8_t* lds_codes = lds;                               // [NT*16][row_bytes], swizzled chunks
+  uint8_t* lds_scales = lds + NT * 16 * row_bytes;        // [NT*16][sc_bytes]
 
-  const uint4* wc = reinterpret_cast<const uint4*>(w1c + w1_code_offset(e, u, 0, H, I)) + lane;
-  const uint32_t* ws = reinterpret_cast<const uint32_t*>(w1s + w1_scale_offset(e, u, 0, H, I)) + lane;
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(w1c + w1_code_offset(e, u, 0, H, I), (uint32_t)S * kStepCodeBytes);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(w1s + w1_scale_offset(e, u, 0, H, I), (uint32_t)S * kStepScaleBytes);
+  const int voff = lane * 16, svoff = lane * 4;
   const int tok_lane = lane & 15, kb = lane >> 4;
 
   for (int t0 = 0; t0 < n_e; t0 += NT * 16) {
+    const int nrows = min(NT * 16, n_e - t0);
     uint4 a[D][4];
     uint32_t sa[D];
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      if (d < S) {
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) a[d][rb] = wc[(d * 4 + rb) * 64];
-        sa[d] = ws[d * 64];
-      }
+      for (int rb = 0; rb < 4; ++rb) a[d][rb] = buf_load16(wr, voff + rb * 1024, d * kStepCodeBytes);
+      sa[d] = buf_load4(sr, svoff, d * kStepScaleBytes);
     }
-    const int nrows = min(NT * 16, n_e - t0);
+    // token of each tile row: lane n < nrows holds it, broadcast by shuffle
+    const int my_tok = lane < nrows ? sorted_rows[base + t0 + lane] / k : 0;
     __syncthreads();  // the previous pass has finished reading LDS
-    const int chunks = row_bytes / 16;
-    for (int idx = threadIdx.x; idx < NT * 16 * chunks; idx += 256) {
-      const int n = idx / chunks, c = idx - n * chunks;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (n < nrows) {
-        const int t = sorted_rows[base + t0 + n] / k;
-        v = reinterpret_cast<const uint4*>(xq + (size_t)t * row_bytes)[c];
-      }
-      *reinterpret_cast<uint4*>(lds_codes + n * row_stride + c * 16) = v;
-    }
-    for (int idx = threadIdx.x; idx < NT * 16 * sc_row; idx += 256) {
-      const int n = idx / sc_row, c = idx - n * sc_row;
-      uint8_t v = 0;
-      if (n < nrows) {
-        const int t = sorted_rows[base + t0 + n] / k;
-        v = xsf[(size_t)t * sc_row + c];
-      }
-      lds_scales[n * sc_row + c] = v;
-    }
+    gather_tile<NT * 16, SWZ>(lds_codes, lds_scales, xq, xsf, row_bytes, sc_bytes, nrows,
+                              [&](int n) { return __shfl(my_tok, n, 64); }, wave, lane, 4);
+    wait_vmem_all();
     __syncthreads();
 
     v4f acc[NT][4];
@@ -90,28 +76,26 @@ __global__ void __launch_bounds__(256) gemm1_swiglu_kernel(
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) acc[nt][rb] = v4f{0.f, 0.f, 0.f, 0.f};
 
+    // Steady state without branches: D divides S, and the loads issued for
+    // steps S..S+D-1 fall outside the buffer range and return zeros unread.
     for (int s0 = 0; s0 < S; s0 += D) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         const int s = s0 + d;
-        if (s < S) {
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            const int n = nt * 16 + tok_lane;
-            const uint4 b = *reinterpret_cast<const uint4*>(lds_codes + n * row_stride + s * 64 + kb * 16);
-            const int sb = lds_scales[n * sc_row + s * 4 + kb];
-            acc[nt][0] = mfma_fp4<0, 0>(a[d][0], b, acc[nt][0], (int)sa[d], sb);
-            acc[nt][1] = mfma_fp4<1, 0>(a[d][1], b, acc[nt][1], (int)sa[d], sb);
-            acc[nt][2] = mfma_fp4<2, 0>(a[d][2], b, acc[nt][2], (int)sa[d], sb);
-            acc[nt][3] = mfma_fp4<3, 0>(a[d][3], b, acc[nt][3], (int)sa[d], sb);
-          }
-          const int sn = s + D;
-          if (sn < S) {
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) a[d][rb] = wc[(sn * 4 + rb) * 64];
-            sa[d] = ws[sn * 64];
-          }
+        for (int nt = 0; nt < NT; ++nt) {
+          const int n = nt * 16 + tok_lane;
+          const uint4 b = tile_operand<SWZ>(lds_codes, row_bytes, n, s, kb);
+          const int sb = lds_scales[n * sc_bytes + s * 4 + kb];
+          acc[nt][0] = mfma_fp4<0, 0>(a[d][0], b, acc[nt][0], (int)sa[d], sb);
+          acc[nt][1] = mfma_fp4<1, 0>(a[d][1], b, acc[nt][1], (int)sa[d], sb);
+          acc[nt][2] = mfma_fp4<2, 0>(a[d][2], b, acc[nt][2], (int)sa[d], sb);
+          acc[nt][3] = mfma_fp4<3, 0>(a[d][3], b, acc[nt][3], (int)sa[d], sb);
         }
+        const int sn = s + D;
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) a[d][rb] = buf_load16(wr, voff + rb * 1024, sn * kStepCodeBytes);
+        sa[d] = buf_load4(sr, svoff, sn * kStepScaleBytes);
       }
     }
 
@@ -162,13 +146,13 @@ __global__ void __launch_bounds__(256) gemm1_swiglu_kernel(
   }
 }
 
-template <int NT, int D>
+template <int NT, int D, int SWZ>
 static hipError_t launch_gemm1_t(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq,
                                  const uint8_t* xsf, const int32_t* counts, const int32_t* offsets,
                                  const int32_t* sorted_rows, int H, int I, int E, int k, uint8_t* hq,
                                  uint8_t* hsf, float* acc_out, hipStream_t stream) {
-  const size_t lds = (size_t)NT * 16 * (H / 2 + 16) + (size_t)NT * 16 * (H / 32);
-  auto kern = gemm1_swiglu_kernel<NT, D>;
+  const size_t lds = (size_t)NT * 16 * (H / 2) + (size_t)NT * 16 * (H / 32);
+  auto kern = gemm1_swiglu_kernel<NT, D, SWZ>;
   if (lds > 65536) {
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -179,17 +163,43 @@ static hipError_t launch_gemm1_t(const uint8_t* w1c, const uint8_t* w1s, const u
   return hipGetLastError();
 }
 
+template <int NT, int D>
+static hipError_t launch_gemm1_nt(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq,
+                                  const uint8_t* xsf, const int32_t* counts, const int32_t* offsets,
+                                  const int32_t* sorted_rows, int H, int I, int E, int k, uint8_t* hq,
+                                  uint8_t* hsf, float* acc_out, hipStream_t stream) {
+  const int chunks = H / 32;  // 16-byte chunks per token row; a multiple of 8
+  if (chunks % 16 == 0)
+    return launch_gemm1_t<NT, D, 16>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hq, hsf,
+                                     acc_out, stream);
+  return launch_gemm1_t<NT, D, 8>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hq, hsf,
+                                  acc_out, stream);
+}
+
+template <int NT>
+static hipError_t launch_gemm1_d(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq,
+                                 const uint8_t* xsf, const int32_t* counts, const int32_t* offsets,
+                                 const int32_t* sorted_rows, int H, int I, int E, int k, uint8_t* hq,
+                                 uint8_t* hsf, float* acc_out, hipStream_t stream) {
+  // The ring depth must divide the number of K steps H/128 (even, as H % 256 == 0).
+  if ((H / kStepK) % 4 == 0)
+    return launch_gemm1_nt<NT, 4>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hq, hsf,
+                                  acc_out, stream);
+  return launch_gemm1_nt<NT, 2>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hq, hsf,
+                                acc_out, stream);
+}
+
 hipError_t launch_gemm1(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq, const uint8_t* xsf,
                         const int32_t* counts, const int32_t* offsets, const int32_t* sorted_rows,
                         int H, int I, int E, int k, int rows_hint, uint8_t* hq, uint8_t* hsf,
                         float* acc_out, hipStream_t stream) {
-  // rows_hint: expected routed rows per expert; two token tiles per pass once
-  // a 16-row tile would often overflow.
+  // rows_hint: mean routed rows per expert; two token tiles per pass once a
+  // single 16-row tile would often overflow (and re-stream the weights).
   if (rows_hint > 8)
-    return launch_gemm1_t<2, 8>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hq, hsf,
-                                acc_out, stream);
-  return launch_gemm1_t<1, 8>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hq, hsf,
-                              acc_out, stream);
+    return launch_gemm1_d<2>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hq, hsf, acc_out,
+                             stream);
+  return launch_gemm1_d<1>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hq, hsf, acc_out,
+                           stream);
 }
 
 }  // namespace moe

@@ -8,16 +8,17 @@
 //
 // Grid: one workgroup of 4 waves per (expert, 256 hidden rows); wave w owns the
 // unit of 64 hidden rows v = 4g + w.  The expert's requantized rows are
-// already contiguous (sorted order), so the B tile is a plain copy into LDS.
-// Weights stream HBM -> VGPR with a D-step register prefetch ring as in GEMM1.
-#include "device_common.h"
+// already contiguous (sorted order), so the B tile is a plain copy into LDS by
+// direct-to-LDS loads; weights stream through the register ring of
+// gemm_common.h.
+#include "gemm_common.h"
 #include "launch.h"
 #include "tiles.h"
 
 namespace moe {
 
-template <int NT, int D>
-__global__ void __launch_bounds__(256) gemm2_kernel(
+template <int NT, int D, int SWZ>
+__global__ void __launch_bounds__(256, 2) gemm2_kernel(
     const uint8_t* __restrict__ w2c, const uint8_t* __restrict__ w2s, const uint8_t* __restrict__ hq,
     const uint8_t* __restrict__ hsf, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, int H, int I, float* __restrict__ y) {
@@ -27,43 +28,36 @@ __global__ void __launch_bounds__(256) gemm2_kernel(
   const int n_e = counts[e];
   if (n_e == 0) return;
   const int base = offsets[e];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps the buffer resources in SGPRs
   const int v = g * 4 + wave;
   const int S = I / kStepK;
-  const int row_bytes = I / 2, row_stride = I / 2 + 16, sc_row = I / 32;
+  const int row_bytes = I / 2, sc_bytes = I / 32;
 
   extern __shared__ __align__(16) uint8_t lds[];
   uint8_t* lds_codes = lds;
-  uint8_t* lds_scales = lds + NT * 16 * row_stride;
+  uint8_t* lds_scales = lds + NT * 16 * row_bytes;
 
-  const uint4* wc = reinterpret_cast<const uint4*>(w2c + w2_code_offset(e, v, 0, H, I)) + lane;
-  const uint32_t* ws = reinterpret_cast<const uint32_t*>(w2s + w2_scale_offset(e, v, 0, H, I)) + lane;
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(w2c + w2_code_offset(e, v, 0, H, I), (uint32_t)S * kStepCodeBytes);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(w2s + w2_scale_offset(e, v, 0, H, I), (uint32_t)S * kStepScaleBytes);
+  const int voff = lane * 16, svoff = lane * 4;
   const int tok_lane = lane & 15, kb = lane >> 4;
 
   for (int t0 = 0; t0 < n_e; t0 += NT * 16) {
+    const int nrows = min(NT * 16, n_e - t0);
     uint4 a[D][4];
     uint32_t sa[D];
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      if (d < S) {
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) a[d][rb] = wc[(d * 4 + rb) * 64];
-        sa[d] = ws[d * 64];
-      }
+      for (int rb = 0; rb < 4; ++rb) a[d][rb] = buf_load16(wr, voff + rb * 1024, d * kStepCodeBytes);
+      sa[d] = buf_load4(sr, svoff, d * kStepScaleBytes);
     }
-    const int nrows = min(NT * 16, n_e - t0);
     __syncthreads();
-    const int chunks = row_bytes / 16;
-    for (int idx = threadIdx.x; idx < NT * 16 * chunks; idx += 256) {
-      const int n = idx / chunks, c = idx - n * chunks;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (n < nrows) val = reinterpret_cast<const uint4*>(hq + (size_t)(base + t0 + n) * row_bytes)[c];
-      *reinterpret_cast<uint4*>(lds_codes + n * row_stride + c * 16) = val;
-    }
-    for (int idx = threadIdx.x; idx < NT * 16 * sc_row; idx += 256) {
-      const int n = idx / sc_row, c = idx - n * sc_row;
-      lds_scales[n * sc_row + c] = n < nrows ? hsf[(size_t)(base + t0 + n) * sc_row + c] : (uint8_t)0;
-    }
+    const int row0 = base + t0;
+    gather_tile<NT * 16, SWZ>(lds_codes, lds_scales, hq, hsf, row_bytes, sc_bytes, nrows,
+                              [&](int n) { return row0 + n; }, wave, lane, 4);
+    wait_vmem_all();
     __syncthreads();
 
     v4f acc[NT][4];
@@ -72,28 +66,26 @@ __global__ void __launch_bounds__(256) gemm2_kernel(
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) acc[nt][rb] = v4f{0.f, 0.f, 0.f, 0.f};
 
+    // Steady state without branches: D divides S, and the loads issued for
+    // steps S..S+D-1 fall outside the buffer range and return zeros unread.
     for (int s0 = 0; s0 < S; s0 += D) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         const int s = s0 + d;
-        if (s < S) {
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            const int n = nt * 16 + tok_lane;
-            const uint4 b = *reinterpret_cast<const uint4*>(lds_codes + n * row_stride + s * 64 + kb * 16);
-            const int sb = lds_scales[n * sc_row + s * 4 + kb];
-            acc[nt][0] = mfma_fp4<0, 0>(a[d][0], b, acc[nt][0], (int)sa[d], sb);
-            acc[nt][1] = mfma_fp4<1, 0>(a[d][1], b, acc[nt][1], (int)sa[d], sb);
-            acc[nt][2] = mfma_fp4<2, 0>(a[d][2], b, acc[nt][2], (int)sa[d], sb);
-            acc[nt][3] = mfma_fp4<3, 0>(a[d][3], b, acc[nt][3], (int)sa[d], sb);
-          }
-          const int sn = s + D;
-          if (sn < S) {
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) a[d][rb] = wc[(sn * 4 + rb) * 64];
-            sa[d] = ws[sn * 64];
-          }
+        for (int nt = 0; nt < NT; ++nt) {
+          const int n = nt * 16 + tok_lane;
+          const uint4 b = tile_operand<SWZ>(lds_codes, row_bytes, n, s, kb);
+          const int sb = lds_scales[n * sc_bytes + s * 4 + kb];
+          acc[nt][0] = mfma_fp4<0, 0>(a[d][0], b, acc[nt][0], (int)sa[d], sb);
+          acc[nt][1] = mfma_fp4<1, 0>(a[d][1], b, acc[nt][1], (int)sa[d], sb);
+          acc[nt][2] = mfma_fp4<2, 0>(a[d][2], b, acc[nt][2], (int)sa[d], sb);
+          acc[nt][3] = mfma_fp4<3, 0>(a[d][3], b, acc[nt][3], (int)sa[d], sb);
         }
+        const int sn = s + D;
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) a[d][rb] = buf_load16(wr, voff + rb * 1024, sn * kStepCodeBytes);
+        sa[d] = buf_load4(sr, svoff, sn * kStepScaleBytes);
       }
     }
 
@@ -112,12 +104,12 @@ __global__ void __launch_bounds__(256) gemm2_kernel(
   }
 }
 
-template <int NT, int D>
+template <int NT, int D, int SWZ>
 static hipError_t launch_gemm2_t(const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq,
                                  const uint8_t* hsf, const int32_t* counts, const int32_t* offsets,
                                  int H, int I, int E, float* y, hipStream_t stream) {
-  const size_t lds = (size_t)NT * 16 * (I / 2 + 16) + (size_t)NT * 16 * (I / 32);
-  auto kern = gemm2_kernel<NT, D>;
+  const size_t lds = (size_t)NT * 16 * (I / 2) + (size_t)NT * 16 * (I / 32);
+  auto kern = gemm2_kernel<NT, D, SWZ>;
   if (lds > 65536) {
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -128,11 +120,32 @@ static hipError_t launch_gemm2_t(const uint8_t* w2c, const uint8_t* w2s, const u
   return hipGetLastError();
 }
 
+template <int NT, int D>
+static hipError_t launch_gemm2_nt(const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq,
+                                  const uint8_t* hsf, const int32_t* counts, const int32_t* offsets,
+                                  int H, int I, int E, float* y, hipStream_t stream) {
+  const int chunks = I / 32;  // a multiple of 4
+  if (chunks % 16 == 0) return launch_gemm2_t<NT, D, 16>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, y, stream);
+  if (chunks % 8 == 0) return launch_gemm2_t<NT, D, 8>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, y, stream);
+  return launch_gemm2_t<NT, D, 4>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, y, stream);
+}
+
+template <int NT>
+static hipError_t launch_gemm2_d(const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq,
+                                 const uint8_t* hsf, const int32_t* counts, const int32_t* offsets,
+                                 int H, int I, int E, float* y, hipStream_t stream) {
+  // The ring depth must divide the number of K steps I/128.
+  const int S = I / kStepK;
+  if (S % 4 == 0) return launch_gemm2_nt<NT, 4>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, y, stream);
+  if (S % 2 == 0) return launch_gemm2_nt<NT, 2>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, y, stream);
+  return launch_gemm2_nt<NT, 1>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, y, stream);
+}
+
 hipError_t launch_gemm2(const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq, const uint8_t* hsf,
                         const int32_t* counts, const int32_t* offsets, int H, int I, int E,
                         int rows_hint, float* y, hipStream_t stream) {
-  if (rows_hint > 8) return launch_gemm2_t<2, 8>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, y, stream);
-  return launch_gemm2_t<1, 8>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, y, stream);
+  if (rows_hint > 8) return launch_gemm2_d<2>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, y, stream);
+  return launch_gemm2_d<1>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, y, stream);
 }
 
 }  // namespace moe

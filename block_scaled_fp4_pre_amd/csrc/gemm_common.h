@@ -1,0 +1,83 @@
+// Building blocks shared by the two grouped GEMM kernels (gemm1.hip, gemm2.hip).
+//
+// Weight stream: each wave walks its unit's tiles (tiles.h) through a buffer
+// resource -- lane offset in a VGPR, step offset in an SGPR, block offset as
+// the instruction immediate -- into a ring of D register slots, so D steps of
+// loads are in flight while the MFMAs consume the oldest slot.  Out-of-range
+// buffer reads return zero instead of faulting.
+//
+// Token tile: the B operand (up to NT*16 token rows of packed codes and their
+// scale bytes) is copied into LDS with gfx950 direct-to-LDS loads; each wave
+// instruction fills 1 KiB (codes) or 256 B (scales) of contiguous LDS.  Code
+// rows are unpadded; the 16-byte chunk c of row n sits at position
+// c ^ (n % SWZ) so that the 16 rows read by one MFMA operand load spread over
+// the LDS banks.
+#pragma once
+#include "device_common.h"
+
+namespace moe {
+
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit dwords (gfx9 descriptor word 3)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
+// Direct global -> LDS copy: lane l's 16 (or 4) bytes land at wave_dst + l*16 (l*4).
+__device__ __forceinline__ void lds_dma16(const void* src, void* wave_dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)wave_dst, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void* src, void* wave_dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)wave_dst, 4, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Copy ROWS token rows into LDS.  Row n (n < nrows) comes from global row
+// row_index(n) of `codes` (row_bytes per row) and `scales` (sc_bytes per row).
+// ROWS * row_bytes is a multiple of 1024 and sc_bytes a multiple of 4.
+template <int ROWS, int SWZ, class RowIndex>
+__device__ __forceinline__ void gather_tile(uint8_t* lds_codes, uint8_t* lds_scales, const uint8_t* codes,
+                                            const uint8_t* scales, int row_bytes, int sc_bytes, int nrows,
+                                            RowIndex row_index, int wave, int lane, int nwaves) {
+  const int chunks = row_bytes >> 4;
+  const int code_insts = ROWS * row_bytes >> 10;
+  for (int j = wave; j < code_insts; j += nwaves) {
+    const int slot = j * 64 + lane;
+    const int n = slot / chunks, pos = slot - n * chunks;
+    const int src = row_index(n);            // evaluated by every lane (it may shuffle)
+    if (n < nrows) {
+      const int c = pos ^ (n & (SWZ - 1));
+      lds_dma16(codes + (size_t)src * row_bytes + c * 16, lds_codes + j * 1024);
+    }
+  }
+  const int dws = sc_bytes >> 2;
+  const int sc_total = ROWS * dws;
+  for (int j = wave; j * 64 < sc_total; j += nwaves) {
+    const int slot = j * 64 + lane;
+    const int n = min(slot / dws, ROWS - 1), d = slot - (slot / dws) * dws;
+    const int src = row_index(n);
+    if (slot < sc_total && n < nrows) lds_dma4(scales + (size_t)src * sc_bytes + d * 4, lds_scales + j * 256);
+  }
+}
+
+// B operand of step s for token column n (row of the LDS tile) and K block kb.
+template <int SWZ>
+__device__ __forceinline__ uint4 tile_operand(const uint8_t* lds_codes, int row_bytes, int n, int s, int kb) {
+  const int pos = (s * 4 + kb) ^ (n & (SWZ - 1));
+  return *reinterpret_cast<const uint4*>(lds_codes + n * row_bytes + pos * 16);
+}
+
+}  // namespace moe
