@@ -44,12 +44,18 @@ class moe_w4a4_cfg(ctypes.Structure):
 
 class moe_w4a4_ws_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
-        "xq", "xsf", "counts", "offsets", "sorted_rows", "pos", "hist", "hq", "hsf", "y", "total")]
+        "xq", "xsf", "counts", "offsets", "sorted_rows", "pos", "hist", "hq", "hsf", "y", "tiles",
+        "num_tiles", "total")]
 
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
                       "(python -m block_scaled_fp4_pre_amd.build)")
+# torch ships its own HIP runtime.  Loading torch first makes the library bind
+# to that same runtime (same devices, streams and allocations); loading the
+# library first would bring in a second runtime next to torch's.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 _P = ctypes.c_void_p

@@ -12,6 +12,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/moe_w4a4.h"
 #include "launch.h"
@@ -22,6 +23,7 @@ constexpr int kMaxDevices = 64;
 constexpr int kMaxExperts = 512;
 constexpr int kMaxTopk = 16;
 constexpr int kRouteRows = 1024;
+constexpr int kStreamMaxRows = 16;  // mean routed rows per expert up to which the streaming GEMMs run
 std::atomic<int> g_is_gfx950[kMaxDevices];  // 0 unknown, 1 yes, 2 no
 
 inline uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
@@ -72,6 +74,8 @@ moe_w4a4_ws_layout ws_layout(const moe_w4a4_cfg* c) {
   L.hq = off; off = align256(off + R * I / 2);
   L.hsf = off; off = align256(off + R * I / 32);
   L.y = off; off = align256(off + R * H * 4);
+  L.tiles = off; off = align256(off + (R / 16 + E + 1) * 8);
+  L.num_tiles = off; off = align256(off + 4);
   L.total = off;
   return L;
 }
@@ -93,6 +97,26 @@ int check_device() {
 inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
 }  // namespace
+
+namespace moe {
+
+hipError_t raise_lds_limit(const void* kernel, size_t bytes) {
+  struct Entry { const void* kernel; int device; size_t bytes; };
+  static std::mutex mu;
+  static Entry done[64];
+  static int ndone = 0;
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < ndone; ++i)
+    if (done[i].kernel == kernel && done[i].device == dev && done[i].bytes >= bytes) return hipSuccess;
+  err = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (err == hipSuccess && ndone < 64) done[ndone++] = Entry{kernel, dev, bytes};
+  return err;
+}
+
+}  // namespace moe
 
 extern "C" {
 
@@ -182,6 +206,10 @@ int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t n
   const int H = cfg->hidden, I = cfg->inter, E = cfg->num_experts, k = cfg->topk;
   const int T = num_tokens, R = T * k;
   const int rows_hint = (int)(((int64_t)R + E - 1) / E);
+  // Few rows per expert: stream each expert's weights once with the whole
+  // token tile in LDS.  Many rows: tiled GEMMs over a device-built tile list.
+  const bool tiled = rows_hint > kStreamMaxRows;
+  const int max_tiles = moe::tiled_max_tiles(R, E);
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint8_t* xq = ws + L.xq;
@@ -191,6 +219,8 @@ int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t n
   int32_t* sorted_rows = reinterpret_cast<int32_t*>(ws + L.sorted_rows);
   int32_t* pos = reinterpret_cast<int32_t*>(ws + L.pos);
   int32_t* hist = reinterpret_cast<int32_t*>(ws + L.hist);
+  int2* tiles = reinterpret_cast<int2*>(ws + L.tiles);
+  int32_t* num_tiles = reinterpret_cast<int32_t*>(ws + L.num_tiles);
   uint8_t* hq = ws + L.hq;
   uint8_t* hsf = ws + L.hsf;
   float* y = reinterpret_cast<float*>(ws + L.y);
@@ -202,17 +232,23 @@ int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t n
     if (st != MOE_OK) return st;
   }
   if (stages & MOE_STAGE_ROUTE) {
-    st = hip_status(moe::launch_route(topk_ids, R, E, hist, counts, offsets, sorted_rows, pos, s));
+    st = hip_status(moe::launch_route(topk_ids, R, E, hist, counts, offsets, sorted_rows, pos,
+                                      tiled ? moe::kTiledRows : 0, tiles, num_tiles, s));
     if (st != MOE_OK) return st;
   }
   if (stages & MOE_STAGE_GEMM1) {
-    st = hip_status(moe::launch_gemm1(pw + P.w1c, pw + P.w1s, xq, xsf, counts, offsets, sorted_rows, H, I,
-                                      E, k, rows_hint, hq, hsf, gemm1_acc, s));
+    st = hip_status(tiled ? moe::launch_gemm1_tiled(pw + P.w1c, pw + P.w1s, xq, xsf, counts, offsets,
+                                                    sorted_rows, tiles, num_tiles, max_tiles, H, I, k, hq,
+                                                    hsf, gemm1_acc, s)
+                          : moe::launch_gemm1(pw + P.w1c, pw + P.w1s, xq, xsf, counts, offsets, sorted_rows,
+                                              H, I, E, k, rows_hint, hq, hsf, gemm1_acc, s));
     if (st != MOE_OK) return st;
   }
   if (stages & MOE_STAGE_GEMM2) {
-    st = hip_status(
-        moe::launch_gemm2(pw + P.w2c, pw + P.w2s, hq, hsf, counts, offsets, H, I, E, rows_hint, y, s));
+    st = hip_status(tiled ? moe::launch_gemm2_tiled(pw + P.w2c, pw + P.w2s, hq, hsf, counts, offsets, tiles,
+                                                    num_tiles, max_tiles, H, I, y, s)
+                          : moe::launch_gemm2(pw + P.w2c, pw + P.w2s, hq, hsf, counts, offsets, H, I, E,
+                                              rows_hint, y, s));
     if (st != MOE_OK) return st;
   }
   if (stages & MOE_STAGE_COMBINE) {

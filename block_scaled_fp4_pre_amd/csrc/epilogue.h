@@ -1,0 +1,91 @@
+// Epilogues of the two grouped GEMMs, shared by the streaming kernels
+// (gemm1.hip, gemm2.hip) and the tiled prefill kernels (gemm_tiled.hip).
+//
+// Accumulator layout (16x16x128 MFMA, swap-AB): acc[nt][rb][i] holds weight row
+// 16*rb + 4*(lane/16) + i of the wave's 64-row unit against token column
+// nt*16 + lane%16 of the tile.
+#pragma once
+#include "device_common.h"
+
+namespace moe {
+
+// GEMM1 unit u (inter columns [32u, 32u+32)): blocks 0,1 are gate, 2,3 up.
+// h = silu(gate) * up in fp32, requantized to MXFP4 per 32 columns: the absmax
+// over the 4 lanes of a token (xor 16, xor 32), then codes packed two per byte
+// (even column in the low nibble).  row0: sorted position of token column 0.
+template <int NT>
+__device__ __forceinline__ void gemm1_epilogue(v4f (&acc)[NT][4], int u, int row0, int nrows, int I,
+                                               int lane, uint8_t* __restrict__ hq, uint8_t* __restrict__ hsf,
+                                               float* __restrict__ acc_out) {
+  const int tok_lane = lane & 15, kb = lane >> 4;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int n = nt * 16 + tok_lane;
+    const bool live = n < nrows;
+    const int p = row0 + n;
+    float h[8];
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float gt = acc[nt][half][i], up = acc[nt][2 + half][i];
+        h[half * 4 + i] = gt / (1.0f + expf(-gt)) * up;
+      }
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = max(amax, __float_as_uint(h[i]) & 0x7FFFFFFFu);
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 16, 64));
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32, 64));
+    const int ex = mx_scale_exp(amax);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo |= e2m1_code(h[i], ex) << (4 * i);
+      hi |= e2m1_code(h[4 + i], ex) << (4 * i);
+    }
+    if (live) {
+      uint8_t* row = hq + (size_t)p * (I / 2) + u * 16;
+      *reinterpret_cast<uint16_t*>(row + 2 * kb) = (uint16_t)lo;
+      *reinterpret_cast<uint16_t*>(row + 8 + 2 * kb) = (uint16_t)hi;
+      if (kb == 0) hsf[(size_t)p * (I / 32) + u] = (uint8_t)(ex + 127);
+      if (acc_out != nullptr) {
+        float* arow = acc_out + (size_t)p * (2 * I) + 32 * u + 4 * kb;
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            arow[16 * half + i] = acc[nt][half][i];
+            arow[I + 16 * half + i] = acc[nt][2 + half][i];
+          }
+      }
+    }
+  }
+}
+
+// GEMM2 unit v (hidden rows [64v, 64v+64)): fp32 y rows in sorted order.
+template <int NT>
+__device__ __forceinline__ void gemm2_epilogue(const v4f (&acc)[NT][4], int v, int row0, int nrows, int H,
+                                               int lane, float* __restrict__ y) {
+  const int tok_lane = lane & 15, kb = lane >> 4;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int n = nt * 16 + tok_lane;
+    if (n < nrows) {
+      float* yrow = y + (size_t)(row0 + n) * H + 64 * v + 4 * kb;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+        *reinterpret_cast<float4*>(yrow + 16 * rb) =
+            make_float4(acc[nt][rb][0], acc[nt][rb][1], acc[nt][rb][2], acc[nt][rb][3]);
+    }
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void zero_acc(v4f (&acc)[NT][4]) {
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) acc[nt][rb] = v4f{0.f, 0.f, 0.f, 0.f};
+}
+
+}  // namespace moe

@@ -11,17 +11,23 @@
 // slices).  The pages' gate/up interleave is tied to their MMA layout; here the
 // pairing is by MFMA block instead (tiles.h).
 //
-// Grid: one workgroup of 4 waves per (expert, 128 inter columns); wave w owns
-// the unit of 32 columns u = 4g + w (64 weight rows).  A workgroup whose
+// Grid: one workgroup of 4 waves per (expert, 128*upw inter columns); wave w
+// owns upw consecutive units of 32 columns (64 weight rows each), whose tiles
+// are contiguous, and streams them as one sequence of K steps.  A workgroup whose
 // expert has no rows exits at once.  Per pass it takes up to NT*16 of the
 // expert's rows: their quantized tokens are gathered into LDS (B operand) by
 // direct-to-LDS loads while the wave's weight ring (gemm_common.h) fills;
 // then 4 MFMAs (one per 16-row block) per token tile per K step of 128.
 // Epilogue per lane: gate/up of 8 columns for one token; the 32-column absmax
 // is reduced over the 4 lanes holding that token (xor 16, xor 32).
+#include "epilogue.h"
 #include "gemm_common.h"
 #include "launch.h"
 #include "tiles.h"
+
+#ifndef MOE_GEMM1_UNITS_PER_WAVE
+#define MOE_GEMM1_UNITS_PER_WAVE 1
+#endif
 
 namespace moe {
 
@@ -30,8 +36,8 @@ __global__ void __launch_bounds__(256, 2) gemm1_swiglu_kernel(
     const uint8_t* __restrict__ w1c, const uint8_t* __restrict__ w1s, const uint8_t* __restrict__ xq,
     const uint8_t* __restrict__ xsf, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows, int H, int I, int k,
-    uint8_t* __restrict__ hq, uint8_t* __restrict__ hsf, float* __restrict__ acc_out) {
-  const int groups = I / 128;
+    int upw, uint8_t* __restrict__ hq, uint8_t* __restrict__ hsf, float* __restrict__ acc_out) {
+  const int groups = I / (128 * upw);
   const int e = blockIdx.x / groups;
   const int g = blockIdx.x - e * groups;
   const int n_e = counts[e];
@@ -39,16 +45,19 @@ __global__ void __launch_bounds__(256, 2) gemm1_swiglu_kernel(
   const int base = offsets[e];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps the buffer resources in SGPRs
-  const int u = g * 4 + wave;
+  const int u0 = (g * 4 + wave) * upw;  // first of this wave's upw consecutive units
   const int S = H / kStepK;
+  const int total_steps = upw * S;       // the units' tiles are contiguous: one stream
   const int row_bytes = H / 2, sc_bytes = H / 32;
 
   extern __shared__ __align__(16) uint8_t lds[];
   uint8_t* lds_codes = lds;                               // [NT*16][row_bytes], swizzled chunks
   uint8_t* lds_scales = lds + NT * 16 * row_bytes;        // [NT*16][sc_bytes]
 
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(w1c + w1_code_offset(e, u, 0, H, I), (uint32_t)S * kStepCodeBytes);
-  const __amdgpu_buffer_rsrc_t sr = make_rsrc(w1s + w1_scale_offset(e, u, 0, H, I), (uint32_t)S * kStepScaleBytes);
+  const __amdgpu_buffer_rsrc_t wr =
+      make_rsrc(w1c + w1_code_offset(e, u0, 0, H, I), (uint32_t)total_steps * kStepCodeBytes);
+  const __amdgpu_buffer_rsrc_t sr =
+      make_rsrc(w1s + w1_scale_offset(e, u0, 0, H, I), (uint32_t)total_steps * kStepScaleBytes);
   const int voff = lane * 16, svoff = lane * 4;
   const int tok_lane = lane & 15, kb = lane >> 4;
 
@@ -76,9 +85,10 @@ __global__ void __launch_bounds__(256, 2) gemm1_swiglu_kernel(
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) acc[nt][rb] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // Steady state without branches: D divides S, and the loads issued for
-    // steps S..S+D-1 fall outside the buffer range and return zeros unread.
-    for (int s0 = 0; s0 < S; s0 += D) {
+    // Steady state without branches: D divides S, and the loads issued past
+    // the wave's last step fall outside the buffer range and return zeros.
+    for (int j0 = 0; j0 < total_steps; j0 += D) {
+      const int s0 = j0 % S;
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         const int s = s0 + d;
@@ -92,56 +102,16 @@ __global__ void __launch_bounds__(256, 2) gemm1_swiglu_kernel(
           acc[nt][2] = mfma_fp4<2, 0>(a[d][2], b, acc[nt][2], (int)sa[d], sb);
           acc[nt][3] = mfma_fp4<3, 0>(a[d][3], b, acc[nt][3], (int)sa[d], sb);
         }
-        const int sn = s + D;
+        const int jn = j0 + d + D;
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) a[d][rb] = buf_load16(wr, voff + rb * 1024, sn * kStepCodeBytes);
-        sa[d] = buf_load4(sr, svoff, sn * kStepScaleBytes);
+        for (int rb = 0; rb < 4; ++rb) a[d][rb] = buf_load16(wr, voff + rb * 1024, jn * kStepCodeBytes);
+        sa[d] = buf_load4(sr, svoff, jn * kStepScaleBytes);
       }
-    }
+      if (s0 + D != S) continue;
 
-    // Epilogue.  acc[nt][0|1][i]: gate of column 32u + 16*(0|1) + 4*kb + i for
-    // token row t0 + nt*16 + tok_lane; acc[nt][2|3][i]: the matching up values.
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int n = nt * 16 + tok_lane;
-      const bool live = n < nrows;
-      const int p = base + t0 + n;
-      float h[8];
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float gt = acc[nt][half][i], up = acc[nt][2 + half][i];
-          h[half * 4 + i] = gt / (1.0f + expf(-gt)) * up;
-        }
-      uint32_t amax = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) amax = max(amax, __float_as_uint(h[i]) & 0x7FFFFFFFu);
-      amax = max(amax, (uint32_t)__shfl_xor((int)amax, 16, 64));
-      amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32, 64));
-      const int ex = mx_scale_exp(amax);
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lo |= e2m1_code(h[i], ex) << (4 * i);
-        hi |= e2m1_code(h[4 + i], ex) << (4 * i);
-      }
-      if (live) {
-        uint8_t* row = hq + (size_t)p * (I / 2) + u * 16;
-        *reinterpret_cast<uint16_t*>(row + 2 * kb) = (uint16_t)lo;
-        *reinterpret_cast<uint16_t*>(row + 8 + 2 * kb) = (uint16_t)hi;
-        if (kb == 0) hsf[(size_t)p * (I / 32) + u] = (uint8_t)(ex + 127);
-        if (acc_out != nullptr) {
-          float* arow = acc_out + (size_t)p * (2 * I) + 32 * u + 4 * kb;
-#pragma unroll
-          for (int half = 0; half < 2; ++half)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              arow[16 * half + i] = acc[nt][half][i];
-              arow[I + 16 * half + i] = acc[nt][2 + half][i];
-            }
-        }
-      }
+      // Unit finished: SwiGLU + requant of its 32 columns for the tile's rows.
+      gemm1_epilogue<NT>(acc, u0 + j0 / S, base + t0, nrows, I, lane, hq, hsf, acc_out);
+      zero_acc<NT>(acc);
     }
   }
 }
@@ -153,13 +123,13 @@ static hipError_t launch_gemm1_t(const uint8_t* w1c, const uint8_t* w1s, const u
                                  uint8_t* hsf, float* acc_out, hipStream_t stream) {
   const size_t lds = (size_t)NT * 16 * (H / 2) + (size_t)NT * 16 * (H / 32);
   auto kern = gemm1_swiglu_kernel<NT, D, SWZ>;
+  const int upw = units_per_wave(I / 32 / 4, MOE_GEMM1_UNITS_PER_WAVE);
   if (lds > 65536) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t err = raise_lds_limit(reinterpret_cast<const void*>(kern), lds);
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(kern, dim3(E * (I / 128)), dim3(256), lds, stream, w1c, w1s, xq, xsf, counts,
-                     offsets, sorted_rows, H, I, k, hq, hsf, acc_out);
+  hipLaunchKernelGGL(kern, dim3(E * (I / (128 * upw))), dim3(256), lds, stream, w1c, w1s, xq, xsf, counts,
+                     offsets, sorted_rows, H, I, k, upw, hq, hsf, acc_out);
   return hipGetLastError();
 }
 

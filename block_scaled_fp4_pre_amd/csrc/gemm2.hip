@@ -6,14 +6,20 @@
 // (W4A4)": title (packed FP4 x FP4) and section B "NCU Speed-of-Light" (the
 // weight stream bounds the layer at ntok=512).
 //
-// Grid: one workgroup of 4 waves per (expert, 256 hidden rows); wave w owns the
-// unit of 64 hidden rows v = 4g + w.  The expert's requantized rows are
+// Grid: one workgroup of 4 waves per (expert, 256*upw hidden rows); wave w owns
+// upw consecutive units of 64 hidden rows, whose tiles are contiguous, and
+// streams them as one sequence of K steps, writing y at each unit's end.  The expert's requantized rows are
 // already contiguous (sorted order), so the B tile is a plain copy into LDS by
 // direct-to-LDS loads; weights stream through the register ring of
 // gemm_common.h.
+#include "epilogue.h"
 #include "gemm_common.h"
 #include "launch.h"
 #include "tiles.h"
+
+#ifndef MOE_GEMM2_UNITS_PER_WAVE
+#define MOE_GEMM2_UNITS_PER_WAVE 1
+#endif
 
 namespace moe {
 
@@ -21,8 +27,8 @@ template <int NT, int D, int SWZ>
 __global__ void __launch_bounds__(256, 2) gemm2_kernel(
     const uint8_t* __restrict__ w2c, const uint8_t* __restrict__ w2s, const uint8_t* __restrict__ hq,
     const uint8_t* __restrict__ hsf, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ offsets, int H, int I, float* __restrict__ y) {
-  const int groups = H / 256;
+    const int32_t* __restrict__ offsets, int H, int I, int upw, float* __restrict__ y) {
+  const int groups = H / (256 * upw);
   const int e = blockIdx.x / groups;
   const int g = blockIdx.x - e * groups;
   const int n_e = counts[e];
@@ -30,16 +36,19 @@ __global__ void __launch_bounds__(256, 2) gemm2_kernel(
   const int base = offsets[e];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps the buffer resources in SGPRs
-  const int v = g * 4 + wave;
+  const int v0 = (g * 4 + wave) * upw;  // first of this wave's upw consecutive units
   const int S = I / kStepK;
+  const int total_steps = upw * S;       // the units' tiles are contiguous: one stream
   const int row_bytes = I / 2, sc_bytes = I / 32;
 
   extern __shared__ __align__(16) uint8_t lds[];
   uint8_t* lds_codes = lds;
   uint8_t* lds_scales = lds + NT * 16 * row_bytes;
 
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(w2c + w2_code_offset(e, v, 0, H, I), (uint32_t)S * kStepCodeBytes);
-  const __amdgpu_buffer_rsrc_t sr = make_rsrc(w2s + w2_scale_offset(e, v, 0, H, I), (uint32_t)S * kStepScaleBytes);
+  const __amdgpu_buffer_rsrc_t wr =
+      make_rsrc(w2c + w2_code_offset(e, v0, 0, H, I), (uint32_t)total_steps * kStepCodeBytes);
+  const __amdgpu_buffer_rsrc_t sr =
+      make_rsrc(w2s + w2_scale_offset(e, v0, 0, H, I), (uint32_t)total_steps * kStepScaleBytes);
   const int voff = lane * 16, svoff = lane * 4;
   const int tok_lane = lane & 15, kb = lane >> 4;
 
@@ -66,9 +75,10 @@ __global__ void __launch_bounds__(256, 2) gemm2_kernel(
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) acc[nt][rb] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // Steady state without branches: D divides S, and the loads issued for
-    // steps S..S+D-1 fall outside the buffer range and return zeros unread.
-    for (int s0 = 0; s0 < S; s0 += D) {
+    // Steady state without branches: D divides S, and the loads issued past
+    // the wave's last step fall outside the buffer range and return zeros.
+    for (int j0 = 0; j0 < total_steps; j0 += D) {
+      const int s0 = j0 % S;
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         const int s = s0 + d;
@@ -82,23 +92,15 @@ __global__ void __launch_bounds__(256, 2) gemm2_kernel(
           acc[nt][2] = mfma_fp4<2, 0>(a[d][2], b, acc[nt][2], (int)sa[d], sb);
           acc[nt][3] = mfma_fp4<3, 0>(a[d][3], b, acc[nt][3], (int)sa[d], sb);
         }
-        const int sn = s + D;
+        const int jn = j0 + d + D;
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) a[d][rb] = buf_load16(wr, voff + rb * 1024, sn * kStepCodeBytes);
-        sa[d] = buf_load4(sr, svoff, sn * kStepScaleBytes);
+        for (int rb = 0; rb < 4; ++rb) a[d][rb] = buf_load16(wr, voff + rb * 1024, jn * kStepCodeBytes);
+        sa[d] = buf_load4(sr, svoff, jn * kStepScaleBytes);
       }
-    }
-
-    // acc[nt][rb][i] = y[row t0 + nt*16 + tok_lane][64v + 16rb + 4kb + i]
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int n = nt * 16 + tok_lane;
-      if (n < nrows) {
-        float* yrow = y + (size_t)(base + t0 + n) * H + 64 * v + 4 * kb;
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-          *reinterpret_cast<float4*>(yrow + 16 * rb) =
-              make_float4(acc[nt][rb][0], acc[nt][rb][1], acc[nt][rb][2], acc[nt][rb][3]);
+      if (s0 + D == S) {
+        // unit finished: its 64 hidden columns of y for the tile's rows
+        gemm2_epilogue<NT>(acc, v0 + j0 / S, base + t0, nrows, H, lane, y);
+        zero_acc<NT>(acc);
       }
     }
   }
@@ -110,13 +112,13 @@ static hipError_t launch_gemm2_t(const uint8_t* w2c, const uint8_t* w2s, const u
                                  int H, int I, int E, float* y, hipStream_t stream) {
   const size_t lds = (size_t)NT * 16 * (I / 2) + (size_t)NT * 16 * (I / 32);
   auto kern = gemm2_kernel<NT, D, SWZ>;
+  const int upw = units_per_wave(H / kUnitRows / 4, MOE_GEMM2_UNITS_PER_WAVE);
   if (lds > 65536) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t err = raise_lds_limit(reinterpret_cast<const void*>(kern), lds);
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(kern, dim3(E * (H / 256)), dim3(256), lds, stream, w2c, w2s, hq, hsf, counts,
-                     offsets, H, I, y);
+  hipLaunchKernelGGL(kern, dim3(E * (H / (256 * upw))), dim3(256), lds, stream, w2c, w2s, hq, hsf, counts,
+                     offsets, H, I, upw, y);
   return hipGetLastError();
 }
 

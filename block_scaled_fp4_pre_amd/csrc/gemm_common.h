@@ -43,6 +43,18 @@ __device__ __forceinline__ void lds_dma4(const void* src, void* wave_dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)wave_dst, 4, 0, 0);
 }
 
+// Lets `kernel` use `bytes` (> 64 KiB) of dynamic LDS.  The attribute is per
+// kernel and process-wide, so it is set once per (kernel, device) and cached.
+hipError_t raise_lds_limit(const void* kernel, size_t bytes);
+
+// Largest power of two <= want that divides units (the units of one expert
+// handled by each wave of a 4-wave workgroup).
+inline int units_per_wave(int units, int want) {
+  int u = 1;
+  while (u * 2 <= want && units % (u * 2) == 0) u *= 2;
+  return u;
+}
+
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Copy ROWS token rows into LDS.  Row n (n < nrows) comes from global row

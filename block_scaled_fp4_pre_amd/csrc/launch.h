@@ -10,9 +10,28 @@ namespace moe {
 hipError_t launch_quantize(bool src_is_bf16, const void* src, int64_t ngroups,
                            uint8_t* codes, uint8_t* scales, hipStream_t stream);
 
-// Stage S1b: stable counting sort of R routed rows over E experts.
+// Stage S1b: stable counting sort of R routed rows over E experts.  With
+// tile_rows > 0 it also lists the (expert, first row) tiles of tile_rows rows
+// that the tiled GEMMs work on.
 hipError_t launch_route(const int32_t* ids, int R, int E, int32_t* hist, int32_t* counts,
-                        int32_t* offsets, int32_t* sorted_rows, int32_t* pos, hipStream_t stream);
+                        int32_t* offsets, int32_t* sorted_rows, int32_t* pos, int tile_rows, int2* tiles,
+                        int32_t* num_tiles, hipStream_t stream);
+
+// Tiled prefill GEMMs (gemm_tiled.hip): tiles of kTiledRows routed rows.
+#ifndef MOE_TILED_NT
+#define MOE_TILED_NT 4
+#endif
+constexpr int kTiledNT = MOE_TILED_NT;
+constexpr int kTiledRows = 16 * kTiledNT;
+int tiled_max_tiles(int R, int E);
+hipError_t launch_gemm1_tiled(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq, const uint8_t* xsf,
+                              const int32_t* counts, const int32_t* offsets, const int32_t* sorted_rows,
+                              const int2* tiles, const int32_t* num_tiles, int max_tiles, int H, int I, int k,
+                              uint8_t* hq, uint8_t* hsf, float* acc_out, hipStream_t stream);
+hipError_t launch_gemm2_tiled(const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq, const uint8_t* hsf,
+                              const int32_t* counts, const int32_t* offsets, const int2* tiles,
+                              const int32_t* num_tiles, int max_tiles, int H, int I, float* y,
+                              hipStream_t stream);
 
 // Stage S2: grouped GEMM1 over the prepared W1 tiles + SwiGLU + MXFP4 requant.
 hipError_t launch_gemm1(const uint8_t* w1_codes, const uint8_t* w1_scales, const uint8_t* xq,

@@ -61,7 +61,8 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int* wave_tot) {
 __global__ void __launch_bounds__(kRouteRows) route_scatter_kernel(
     const int32_t* __restrict__ ids, int R, int E, int nbits, int nblocks,
     const int32_t* __restrict__ hist, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted_rows, int32_t* __restrict__ pos) {
+    int32_t* __restrict__ sorted_rows, int32_t* __restrict__ pos, int tile_rows, int2* __restrict__ tiles,
+    int32_t* __restrict__ num_tiles) {
   extern __shared__ int smem[];
   int* base = smem;                       // [E]   first slot of this block's rows of e
   int* wcnt = smem + E;                   // [16][E] rows of e in each wave of this block
@@ -87,6 +88,15 @@ __global__ void __launch_bounds__(kRouteRows) route_scatter_kernel(
     }
   }
   __syncthreads();
+
+  if (b == 0 && tile_rows > 0) {
+    // Tile list for the tiled GEMMs: expert e gets ceil(count / tile_rows)
+    // consecutive entries (e, 0), (e, tile_rows), ...
+    const int nt_e = tid < E ? (tot + tile_rows - 1) / tile_rows : 0;
+    const int t_incl = block_inclusive_scan(nt_e, wave_tot);
+    for (int i = 0; i < nt_e; ++i) tiles[t_incl - nt_e + i] = make_int2(tid, i * tile_rows);
+    if (tid == kRouteRows - 1) *num_tiles = t_incl;
+  }
 
   const int r = b * kRouteRows + tid;
   const int e = r < R ? ids[r] : -1;
@@ -116,7 +126,8 @@ __global__ void __launch_bounds__(kRouteRows) route_scatter_kernel(
 }
 
 hipError_t launch_route(const int32_t* ids, int R, int E, int32_t* hist, int32_t* counts,
-                        int32_t* offsets, int32_t* sorted_rows, int32_t* pos, hipStream_t stream) {
+                        int32_t* offsets, int32_t* sorted_rows, int32_t* pos, int tile_rows, int2* tiles,
+                        int32_t* num_tiles, hipStream_t stream) {
   if (R <= 0) return hipSuccess;
   const int nblocks = (R + kRouteRows - 1) / kRouteRows;
   int nbits = 0;
@@ -127,7 +138,7 @@ hipError_t launch_route(const int32_t* ids, int R, int E, int32_t* hist, int32_t
   if (err != hipSuccess) return err;
   const size_t lds = (size_t)(E + kRouteWaves * E + kRouteWaves) * sizeof(int);
   hipLaunchKernelGGL(route_scatter_kernel, dim3(nblocks), dim3(kRouteRows), lds, stream, ids, R, E,
-                     nbits, nblocks, hist, counts, offsets, sorted_rows, pos);
+                     nbits, nblocks, hist, counts, offsets, sorted_rows, pos, tile_rows, tiles, num_tiles);
   return hipGetLastError();
 }
 

@@ -153,6 +153,8 @@ typedef struct moe_w4a4_ws_layout {
   uint64_t hq;           /* uint8  [max_tokens*k, I/2] requantized h (sorted order) */
   uint64_t hsf;          /* uint8  [max_tokens*k, I/32]                             */
   uint64_t y;            /* float  [max_tokens*k, H]   GEMM2 result (sorted order)  */
+  uint64_t tiles;        /* int32  [max_tokens*k/16 + E, 2] (expert, first row) work tiles */
+  uint64_t num_tiles;    /* int32  [1]                 number of valid tiles        */
   uint64_t total;        /* == workspace_bytes                                      */
 } moe_w4a4_ws_layout;
 

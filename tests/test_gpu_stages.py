@@ -70,6 +70,16 @@ def test_route_matches_oracle(T, k, E, masked):
     assert np.array_equal(ws("offsets", (E + 1,), torch.int32).cpu().numpy(), offsets)
     assert np.array_equal(ws("sorted_rows", (T * k,), torch.int32)[:srt.size].cpu().numpy(), srt)
     assert np.array_equal(ws("pos", (T * k,), torch.int32).cpu().numpy(), pos)
+    if (T * k + E - 1) // E > 16:
+        # many rows per expert: the route also lists equal-size (expert, first row)
+        # tiles, in expert order, covering every expert's rows exactly once
+        nt = int(ws("num_tiles", (1,), torch.int32).cpu().numpy()[0])
+        tiles = [tuple(t) for t in ws("tiles", (nt, 2), torch.int32).cpu().numpy().tolist()]
+        steps = {b[1] - a[1] for a, b in zip(tiles, tiles[1:]) if a[0] == b[0]}
+        assert len(steps) <= 1
+        rows_per_tile = steps.pop() if steps else max(int(counts.max()), 1)
+        want = [(e, i * rows_per_tile) for e in range(E) for i in range(-(-int(counts[e]) // rows_per_tile))]
+        assert tiles == want
 
 
 def _grid_group(rng, rows, K):
