@@ -91,8 +91,8 @@ __global__ void __launch_bounds__(256, 2) gemm_tiled_kernel(
 #pragma unroll
   for (int d = 0; d < D; ++d) {
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) a[d][rb] = buf_load16(wr, voff + rb * 1024, d * kStepCodeBytes);
-    sa[d] = buf_load4(sr, svoff, d * kStepScaleBytes);
+    for (int rb = 0; rb < 4; ++rb) a[d][rb] = buf_load16<kPolicyDefault>(wr, voff + rb * 1024, d * kStepCodeBytes);
+    sa[d] = buf_load4<kPolicyDefault>(sr, svoff, d * kStepScaleBytes);
   }
 
   // Fixed staging assignment: thread piece i = row n, piece c of every chunk.
@@ -161,8 +161,8 @@ __global__ void __launch_bounds__(256, 2) gemm_tiled_kernel(
       }
       const int jn = j + D;
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) a[slot][rb] = buf_load16(wr, voff + rb * 1024, jn * kStepCodeBytes);
-      sa[slot] = buf_load4(sr, svoff, jn * kStepScaleBytes);
+      for (int rb = 0; rb < 4; ++rb) a[slot][rb] = buf_load16<kPolicyDefault>(wr, voff + rb * 1024, jn * kStepCodeBytes);
+      sa[slot] = buf_load4<kPolicyDefault>(sr, svoff, jn * kStepScaleBytes);
       if (q == CK - 1) {
         // Chunk boundary.  Buffer (chunk+1)&1 was last read in chunk-1, which
         // every wave finished before the previous barrier.
