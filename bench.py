@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "mega-MoE layer µs + TFLOPS + HBM GB/s at ntok=512/4096, DSV4-Flash shape"
 HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E
 FP4_PEAK_TFLOPS = 10100.0         # MI355X dense MXFP4 MFMA
+COPY_BYTES = 256 << 20           # calibration copy size
 PAGES_US_NTOK512 = 537.6          # W4A4 mega-MoE kernel, 1 B200, 1-rank isolation, ntok=512 (context)
 
 
@@ -52,7 +53,36 @@ def algorithmic(cfg, counts):
                 gemm1_flops=R * 2 * H * 2 * I)
 
 
-def cpu_baseline(cfg, x, ids, w, n_experts_sample=4):
+GEMM1_SOURCES = ("gemm1.hip", "gemm_common.h", "epilogue.h", "device_common.h", "tiles.h")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemm1_swiglu_{}_hbm_counters.txt")
+
+
+def measured_traffic(workload):
+    """HBM bytes per GEMM1 launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE runs, each scaled by the same counter on a copy of known size;
+    None if there are none for this workload or the kernel changed since."""
+    import hashlib
+    path = COUNTERS_FILE.format(workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for name in GEMM1_SOURCES:
+        with open(os.path.join(ROOT, "block_scaled_fp4_pre_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    if kv.get("kernel_sources_sha256") != h.hexdigest():
+        return None
+    cb = float(kv["copy_bytes"])
+    fetch = float(kv["fetch_kib"]) * cb / float(kv["copy_fetch_kib"])
+    write = float(kv["write_kib"]) * cb / float(kv["copy_write_kib"])
+    return int(round(fetch + write))
+
+
+def cpu_baseline(cfg, x, ids, w, n_experts_sample=40):
     """The oracle as it stands, on a slice: quantize + route of the whole batch,
     then GEMM1/SwiGLU/requant/GEMM2 for all routed rows of a few experts; the
     per-expert time is scaled to the active experts of the layer."""
@@ -83,7 +113,8 @@ def cpu_baseline(cfg, x, ids, w, n_experts_sample=4):
     us = (t_common + t_sample / len(sample) * len(active)) * 1e6
     rows = int(sum(counts[e] for e in sample))
     return {"value": round(us, 1), "unit": "us", "cores": int(cores), "kind": "oracle",
-            "sample": f"quantize+route of all {cfg.tokens} tokens, then experts {sample} "
+            "sample": f"quantize+route of all {cfg.tokens} tokens, then the {len(sample)} lowest-numbered "
+                      f"active experts ({sample[0]}..{sample[-1]}) "
                       f"({rows} routed rows) through GEMM1/SwiGLU/requant/GEMM2; expert time scaled "
                       f"to {len(active)} active experts",
             "measured_s": round(t_common + t_sample, 2)}
@@ -97,6 +128,8 @@ def main():
     ap.add_argument("--workload", default="dsv4flash_t512")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--threads", type=int, default=16)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after timing, run a 256 MiB device-to-device copy (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this layer runs on one GPU (all experts resident); --gpus {args.gpus} is not "
@@ -164,6 +197,16 @@ def main():
     torch.cuda.synchronize()
     fwd_ms = fwd_s.elapsed_time(fwd_e) / args.steps
 
+    if args.calibrate_copy:
+        # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE per dispatch
+        # calibrate the counters read for the layer's kernels.
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     counts = layer.ws("counts", (cfg.experts,), torch.int32).cpu().numpy()
     alg = algorithmic(cfg, counts)
     us = ms_per_step * 1e3
@@ -194,7 +237,7 @@ def main():
         "forward_entry_us": round(fwd_ms * 1e3, 2),
         "roofline": {"kernel": "gemm1_swiglu_kernel", "bound": "hbm", "achieved": round(g1_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(g1_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "avg_us": round(gemm1_us, 2),
+                     "traffic": measured_traffic(cfg.name), "avg_us": round(gemm1_us, 2),
                      "bytes_per_launch": alg["gemm1_bytes"]},
         "wall_s": round(wall, 3),
     }
