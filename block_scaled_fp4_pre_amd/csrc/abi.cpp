@@ -24,6 +24,7 @@ constexpr int kMaxExperts = 512;
 constexpr int kMaxTopk = 16;
 constexpr int kRouteRows = 1024;
 constexpr int kStreamMaxRows = 16;  // mean routed rows per expert up to which the streaming GEMMs run
+constexpr int kFusedRouteMaxRows = 8192;  // routed rows up to which one block routes them all
 std::atomic<int> g_is_gfx950[kMaxDevices];  // 0 unknown, 1 yes, 2 no
 
 inline uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
@@ -227,14 +228,22 @@ int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t n
   const Prepared P = prepared_layout(cfg);
   const uint8_t* pw = static_cast<const uint8_t*>(prepared);
 
-  if (stages & MOE_STAGE_QUANT) {
-    st = hip_status(moe::launch_quantize(true, x, (int64_t)T * (H / 32), xq, xsf, s));
+  const int tile_rows = tiled ? moe::kTiledRows : 0;
+  if ((stages & MOE_STAGE_QUANT) && (stages & MOE_STAGE_ROUTE) && R <= kFusedRouteMaxRows) {
+    // pre-dispatch in one launch: one block routes, the others quantize
+    st = hip_status(moe::launch_predispatch(x, (int64_t)T * (H / 32), xq, xsf, topk_ids, R, E, counts, offsets,
+                                            sorted_rows, pos, tile_rows, tiles, num_tiles, s));
     if (st != MOE_OK) return st;
-  }
-  if (stages & MOE_STAGE_ROUTE) {
-    st = hip_status(moe::launch_route(topk_ids, R, E, hist, counts, offsets, sorted_rows, pos,
-                                      tiled ? moe::kTiledRows : 0, tiles, num_tiles, s));
-    if (st != MOE_OK) return st;
+  } else {
+    if (stages & MOE_STAGE_QUANT) {
+      st = hip_status(moe::launch_quantize(true, x, (int64_t)T * (H / 32), xq, xsf, s));
+      if (st != MOE_OK) return st;
+    }
+    if (stages & MOE_STAGE_ROUTE) {
+      st = hip_status(
+          moe::launch_route(topk_ids, R, E, hist, counts, offsets, sorted_rows, pos, tile_rows, tiles, num_tiles, s));
+      if (st != MOE_OK) return st;
+    }
   }
   if (stages & MOE_STAGE_GEMM1) {
     st = hip_status(tiled ? moe::launch_gemm1_tiled(pw + P.w1c, pw + P.w1s, xq, xsf, counts, offsets,

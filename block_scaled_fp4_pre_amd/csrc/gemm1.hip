@@ -25,6 +25,13 @@
 #include "launch.h"
 #include "tiles.h"
 
+#ifndef MOE_STREAM_RING_DEPTH
+#define MOE_STREAM_RING_DEPTH 4   // weight-ring slots of the streaming GEMMs (divides the K steps)
+#endif
+#ifndef MOE_STREAM_ROWS2
+#define MOE_STREAM_ROWS2 24       // token rows per pass of the two-tile variant (17..32)
+#endif
+
 #ifndef MOE_GEMM1_UNITS_PER_WAVE
 #define MOE_GEMM1_UNITS_PER_WAVE 1
 #endif
@@ -50,9 +57,14 @@ __global__ void __launch_bounds__(256, 2) gemm1_swiglu_kernel(
   const int total_steps = upw * S;       // the units' tiles are contiguous: one stream
   const int row_bytes = H / 2, sc_bytes = H / 32;
 
+  // Rows per pass: 16 for one token tile; MOE_STREAM_ROWS2 (<= 32) for two.  A
+  // cap below 32 trades a rare second pass for less LDS per workgroup; B-operand
+  // reads clamp the row so the second tile never reads past the cap.
+  constexpr int ROWS = NT == 1 ? 16 : MOE_STREAM_ROWS2;
+  static_assert(ROWS > 16 * (NT - 1) && ROWS <= 16 * NT, "rows per pass must need NT tiles");
   extern __shared__ __align__(16) uint8_t lds[];
   uint8_t* lds_codes = lds;                               // [NT*16][row_bytes], swizzled chunks
-  uint8_t* lds_scales = lds + NT * 16 * row_bytes;        // [NT*16][sc_bytes]
+  uint8_t* lds_scales = lds + ROWS * row_bytes;           // [ROWS][sc_bytes]
 
   const __amdgpu_buffer_rsrc_t wr =
       make_rsrc(w1c + w1_code_offset(e, u0, 0, H, I), (uint32_t)total_steps * kStepCodeBytes);
@@ -61,8 +73,8 @@ __global__ void __launch_bounds__(256, 2) gemm1_swiglu_kernel(
   const int voff = lane * 16, svoff = lane * 4;
   const int tok_lane = lane & 15, kb = lane >> 4;
 
-  for (int t0 = 0; t0 < n_e; t0 += NT * 16) {
-    const int nrows = min(NT * 16, n_e - t0);
+  for (int t0 = 0; t0 < n_e; t0 += ROWS) {
+    const int nrows = min(ROWS, n_e - t0);
     uint4 a[D][4];
     uint32_t sa[D];
 #pragma unroll
@@ -74,7 +86,7 @@ __global__ void __launch_bounds__(256, 2) gemm1_swiglu_kernel(
     // token of each tile row: lane n < nrows holds it, broadcast by shuffle
     const int my_tok = lane < nrows ? sorted_rows[base + t0 + lane] / k : 0;
     __syncthreads();  // the previous pass has finished reading LDS
-    gather_tile<NT * 16, SWZ>(lds_codes, lds_scales, xq, xsf, row_bytes, sc_bytes, nrows,
+    gather_tile<ROWS, SWZ>(lds_codes, lds_scales, xq, xsf, row_bytes, sc_bytes, nrows,
                               [&](int n) { return __shfl(my_tok, n, 64); }, wave, lane, 4);
     wait_vmem_all();
     __syncthreads();
@@ -94,7 +106,7 @@ __global__ void __launch_bounds__(256, 2) gemm1_swiglu_kernel(
         const int s = s0 + d;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const int n = nt * 16 + tok_lane;
+          const int n = min(nt * 16 + tok_lane, ROWS - 1);
           const uint4 b = tile_operand<SWZ>(lds_codes, row_bytes, n, s, kb);
           const int sb = lds_scales[n * sc_bytes + s * 4 + kb];
           acc[nt][0] = mfma_fp4<0, 0>(a[d][0], b, acc[nt][0], (int)sa[d], sb);
@@ -121,7 +133,8 @@ static hipError_t launch_gemm1_t(const uint8_t* w1c, const uint8_t* w1s, const u
                                  const uint8_t* xsf, const int32_t* counts, const int32_t* offsets,
                                  const int32_t* sorted_rows, int H, int I, int E, int k, uint8_t* hq,
                                  uint8_t* hsf, float* acc_out, hipStream_t stream) {
-  const size_t lds = (size_t)NT * 16 * (H / 2) + (size_t)NT * 16 * (H / 32);
+  constexpr int ROWS = NT == 1 ? 16 : MOE_STREAM_ROWS2;
+  const size_t lds = (size_t)ROWS * (H / 2) + (size_t)ROWS * (H / 32);
   auto kern = gemm1_swiglu_kernel<NT, D, SWZ>;
   const int upw = units_per_wave(I / 32 / 4, MOE_GEMM1_UNITS_PER_WAVE);
   if (lds > 65536) {
@@ -152,8 +165,8 @@ static hipError_t launch_gemm1_d(const uint8_t* w1c, const uint8_t* w1s, const u
                                  const int32_t* sorted_rows, int H, int I, int E, int k, uint8_t* hq,
                                  uint8_t* hsf, float* acc_out, hipStream_t stream) {
   // The ring depth must divide the number of K steps H/128 (even, as H % 256 == 0).
-  if ((H / kStepK) % 4 == 0)
-    return launch_gemm1_nt<NT, 4>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hq, hsf,
+  if ((H / kStepK) % MOE_STREAM_RING_DEPTH == 0)
+    return launch_gemm1_nt<NT, MOE_STREAM_RING_DEPTH>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hq, hsf,
                                   acc_out, stream);
   return launch_gemm1_nt<NT, 2>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hq, hsf,
                                 acc_out, stream);

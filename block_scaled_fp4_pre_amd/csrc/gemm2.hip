@@ -17,6 +17,13 @@
 #include "launch.h"
 #include "tiles.h"
 
+#ifndef MOE_STREAM_RING_DEPTH
+#define MOE_STREAM_RING_DEPTH 4   // weight-ring slots of the streaming GEMMs (divides the K steps)
+#endif
+#ifndef MOE_STREAM_ROWS2
+#define MOE_STREAM_ROWS2 24       // token rows per pass of the two-tile variant (17..32)
+#endif
+
 #ifndef MOE_GEMM2_UNITS_PER_WAVE
 #define MOE_GEMM2_UNITS_PER_WAVE 1
 #endif
@@ -41,9 +48,14 @@ __global__ void __launch_bounds__(256, 2) gemm2_kernel(
   const int total_steps = upw * S;       // the units' tiles are contiguous: one stream
   const int row_bytes = I / 2, sc_bytes = I / 32;
 
+  // Rows per pass: 16 for one token tile; MOE_STREAM_ROWS2 (<= 32) for two.  A
+  // cap below 32 trades a rare second pass for less LDS per workgroup; B-operand
+  // reads clamp the row so the second tile never reads past the cap.
+  constexpr int ROWS = NT == 1 ? 16 : MOE_STREAM_ROWS2;
+  static_assert(ROWS > 16 * (NT - 1) && ROWS <= 16 * NT, "rows per pass must need NT tiles");
   extern __shared__ __align__(16) uint8_t lds[];
   uint8_t* lds_codes = lds;
-  uint8_t* lds_scales = lds + NT * 16 * row_bytes;
+  uint8_t* lds_scales = lds + ROWS * row_bytes;
 
   const __amdgpu_buffer_rsrc_t wr =
       make_rsrc(w2c + w2_code_offset(e, v0, 0, H, I), (uint32_t)total_steps * kStepCodeBytes);
@@ -52,8 +64,8 @@ __global__ void __launch_bounds__(256, 2) gemm2_kernel(
   const int voff = lane * 16, svoff = lane * 4;
   const int tok_lane = lane & 15, kb = lane >> 4;
 
-  for (int t0 = 0; t0 < n_e; t0 += NT * 16) {
-    const int nrows = min(NT * 16, n_e - t0);
+  for (int t0 = 0; t0 < n_e; t0 += ROWS) {
+    const int nrows = min(ROWS, n_e - t0);
     uint4 a[D][4];
     uint32_t sa[D];
 #pragma unroll
@@ -64,7 +76,7 @@ __global__ void __launch_bounds__(256, 2) gemm2_kernel(
     }
     __syncthreads();
     const int row0 = base + t0;
-    gather_tile<NT * 16, SWZ>(lds_codes, lds_scales, hq, hsf, row_bytes, sc_bytes, nrows,
+    gather_tile<ROWS, SWZ>(lds_codes, lds_scales, hq, hsf, row_bytes, sc_bytes, nrows,
                               [&](int n) { return row0 + n; }, wave, lane, 4);
     wait_vmem_all();
     __syncthreads();
@@ -84,7 +96,7 @@ __global__ void __launch_bounds__(256, 2) gemm2_kernel(
         const int s = s0 + d;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const int n = nt * 16 + tok_lane;
+          const int n = min(nt * 16 + tok_lane, ROWS - 1);
           const uint4 b = tile_operand<SWZ>(lds_codes, row_bytes, n, s, kb);
           const int sb = lds_scales[n * sc_bytes + s * 4 + kb];
           acc[nt][0] = mfma_fp4<0, 0>(a[d][0], b, acc[nt][0], (int)sa[d], sb);
@@ -110,7 +122,8 @@ template <int NT, int D, int SWZ>
 static hipError_t launch_gemm2_t(const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq,
                                  const uint8_t* hsf, const int32_t* counts, const int32_t* offsets,
                                  int H, int I, int E, float* y, hipStream_t stream) {
-  const size_t lds = (size_t)NT * 16 * (I / 2) + (size_t)NT * 16 * (I / 32);
+  constexpr int ROWS = NT == 1 ? 16 : MOE_STREAM_ROWS2;
+  const size_t lds = (size_t)ROWS * (I / 2) + (size_t)ROWS * (I / 32);
   auto kern = gemm2_kernel<NT, D, SWZ>;
   const int upw = units_per_wave(H / kUnitRows / 4, MOE_GEMM2_UNITS_PER_WAVE);
   if (lds > 65536) {
@@ -138,7 +151,7 @@ static hipError_t launch_gemm2_d(const uint8_t* w2c, const uint8_t* w2s, const u
                                  int H, int I, int E, float* y, hipStream_t stream) {
   // The ring depth must divide the number of K steps I/128.
   const int S = I / kStepK;
-  if (S % 4 == 0) return launch_gemm2_nt<NT, 4>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, y, stream);
+  if (S % MOE_STREAM_RING_DEPTH == 0) return launch_gemm2_nt<NT, MOE_STREAM_RING_DEPTH>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, y, stream);
   if (S % 2 == 0) return launch_gemm2_nt<NT, 2>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, y, stream);
   return launch_gemm2_nt<NT, 1>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, y, stream);
 }

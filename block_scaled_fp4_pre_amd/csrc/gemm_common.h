@@ -68,13 +68,14 @@ __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(
 
 // Copy ROWS token rows into LDS.  Row n (n < nrows) comes from global row
 // row_index(n) of `codes` (row_bytes per row) and `scales` (sc_bytes per row).
-// ROWS * row_bytes is a multiple of 1024 and sc_bytes a multiple of 4.
+// sc_bytes is a multiple of 4.  Lanes whose slot lies past the last row are
+// masked off, so ROWS * row_bytes need not be a multiple of 1024.
 template <int ROWS, int SWZ, class RowIndex>
 __device__ __forceinline__ void gather_tile(uint8_t* lds_codes, uint8_t* lds_scales, const uint8_t* codes,
                                             const uint8_t* scales, int row_bytes, int sc_bytes, int nrows,
                                             RowIndex row_index, int wave, int lane, int nwaves) {
   const int chunks = row_bytes >> 4;
-  const int code_insts = ROWS * row_bytes >> 10;
+  const int code_insts = (ROWS * row_bytes + 1023) >> 10;
   for (int j = wave; j < code_insts; j += nwaves) {
     const int slot = j * 64 + lane;
     const int n = slot / chunks, pos = slot - n * chunks;

@@ -1,0 +1,50 @@
+// MXFP4 quantization of one 32-element group (pre-dispatch, stage S1a), shared
+// by the stand-alone quantize kernel and the fused pre-dispatch kernel.
+// [P3] prhub digest of sglang PR "bump sgl-deep-gemm to 0.1.7, MegaMoE uses the
+// mma_type API for MXFP4", "Key source snippets": pre_dispatch packs E2M1 with
+// group_size=32.  Formats per [OCP-MX] (OCP MX v1.0), scale rule in
+// device_common.h.
+#pragma once
+#include "device_common.h"
+
+namespace moe {
+
+// Group g of a row-major source (32 consecutive values) -> 16 bytes of packed
+// codes at codes + 16g and one scale byte at scales[g].  64 B (bf16) or 128 B
+// (fp32) in as 16-byte loads.
+template <bool BF16>
+__device__ __forceinline__ void quantize_group(const void* __restrict__ src, int64_t g,
+                                               uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  float v[32];
+  if (BF16) {
+    const uint4* p = reinterpret_cast<const uint4*>(src) + g * 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 w = p[q];
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[q * 8 + 2 * i] = bf16_to_f32(ws[i] & 0xFFFFu);
+        v[q * 8 + 2 * i + 1] = bf16_to_f32(ws[i] >> 16);
+      }
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(src) + g * 8;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float4 w = p[q];
+      v[4 * q] = w.x; v[4 * q + 1] = w.y; v[4 * q + 2] = w.z; v[4 * q + 3] = w.w;
+    }
+  }
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = max(amax, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+  const int e = mx_scale_exp(amax);
+  uint32_t packed[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) packed[i >> 3] |= e2m1_code(v[i], e) << (4 * (i & 7));
+  reinterpret_cast<uint4*>(codes)[g] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  scales[g] = (uint8_t)(e + 127);
+}
+
+}  // namespace moe
