@@ -33,7 +33,7 @@
 #endif
 
 #ifndef MOE_GEMM1_UNITS_PER_WAVE
-#define MOE_GEMM1_UNITS_PER_WAVE 1
+#define MOE_GEMM1_UNITS_PER_WAVE 2
 #endif
 
 namespace moe {
