@@ -74,7 +74,7 @@ moe_w4a4_ws_layout ws_layout(const moe_w4a4_cfg* c) {
   L.hist = off; off = align256(off + nb * E * 4);
   L.hq = off; off = align256(off + R * I / 2);
   L.hsf = off; off = align256(off + R * I / 32);
-  L.y = off; off = align256(off + R * H * 4);
+  L.y = off; off = align256(off + R * H * 2);
   L.tiles = off; off = align256(off + (R / 16 + E + 1) * 8);
   L.num_tiles = off; off = align256(off + 4);
   L.total = off;
@@ -224,7 +224,7 @@ int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t n
   int32_t* num_tiles = reinterpret_cast<int32_t*>(ws + L.num_tiles);
   uint8_t* hq = ws + L.hq;
   uint8_t* hsf = ws + L.hsf;
-  float* y = reinterpret_cast<float*>(ws + L.y);
+  uint16_t* y = reinterpret_cast<uint16_t*>(ws + L.y);
   const Prepared P = prepared_layout(cfg);
   const uint8_t* pw = static_cast<const uint8_t*>(prepared);
 

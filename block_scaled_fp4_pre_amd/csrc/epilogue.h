@@ -62,20 +62,23 @@ __device__ __forceinline__ void gemm1_epilogue(v4f (&acc)[NT][4], int u, int row
   }
 }
 
-// GEMM2 unit v (hidden rows [64v, 64v+64)): fp32 y rows in sorted order.
+// GEMM2 unit v (hidden rows [64v, 64v+64)): y rows in sorted order, the fp32
+// accumulators rounded to bfloat16 (nearest even) -- half the bytes of the
+// y round trip to the combine.
 template <int NT>
 __device__ __forceinline__ void gemm2_epilogue(const v4f (&acc)[NT][4], int v, int row0, int nrows, int H,
-                                               int lane, float* __restrict__ y) {
+                                               int lane, uint16_t* __restrict__ y) {
   const int tok_lane = lane & 15, kb = lane >> 4;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int n = nt * 16 + tok_lane;
     if (n < nrows) {
-      float* yrow = y + (size_t)(row0 + n) * H + 64 * v + 4 * kb;
+      uint16_t* yrow = y + (size_t)(row0 + n) * H + 64 * v + 4 * kb;
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
-        *reinterpret_cast<float4*>(yrow + 16 * rb) =
-            make_float4(acc[nt][rb][0], acc[nt][rb][1], acc[nt][rb][2], acc[nt][rb][3]);
+        *reinterpret_cast<uint2*>(yrow + 16 * rb) =
+            make_uint2(f32_to_bf16(acc[nt][rb][0]) | (f32_to_bf16(acc[nt][rb][1]) << 16),
+                       f32_to_bf16(acc[nt][rb][2]) | (f32_to_bf16(acc[nt][rb][3]) << 16));
     }
   }
 }

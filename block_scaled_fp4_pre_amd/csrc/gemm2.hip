@@ -1,6 +1,6 @@
 // Stage S3: per-expert GEMM2 (down projection) y = h_hat . W2_hat[e]^T with fp32
 // accumulation on the gfx950 block-scaled FP4 MFMA; y is written per routed row
-// in expert-sorted order for the combine.
+// in expert-sorted order, rounded to bfloat16, for the combine.
 //
 // [P1] sglang PR "[deepseek-v4] Bump sgl-deep-gemm for packed FP4xFP4 mega-MoE
 // (W4A4)": title (packed FP4 x FP4) and section B "NCU Speed-of-Light" (the
@@ -34,7 +34,7 @@ template <int NT, int D, int SWZ>
 __global__ void __launch_bounds__(256, 2) gemm2_kernel(
     const uint8_t* __restrict__ w2c, const uint8_t* __restrict__ w2s, const uint8_t* __restrict__ hq,
     const uint8_t* __restrict__ hsf, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ offsets, int H, int I, int upw, float* __restrict__ y) {
+    const int32_t* __restrict__ offsets, int H, int I, int upw, uint16_t* __restrict__ y) {
   const int groups = H / (256 * upw);
   const int e = blockIdx.x / groups;
   const int g = blockIdx.x - e * groups;
@@ -121,7 +121,7 @@ __global__ void __launch_bounds__(256, 2) gemm2_kernel(
 template <int NT, int D, int SWZ>
 static hipError_t launch_gemm2_t(const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq,
                                  const uint8_t* hsf, const int32_t* counts, const int32_t* offsets,
-                                 int H, int I, int E, float* y, hipStream_t stream) {
+                                 int H, int I, int E, uint16_t* y, hipStream_t stream) {
   constexpr int ROWS = NT == 1 ? 16 : MOE_STREAM_ROWS2;
   const size_t lds = (size_t)ROWS * (I / 2) + (size_t)ROWS * (I / 32);
   auto kern = gemm2_kernel<NT, D, SWZ>;
@@ -138,7 +138,7 @@ static hipError_t launch_gemm2_t(const uint8_t* w2c, const uint8_t* w2s, const u
 template <int NT, int D>
 static hipError_t launch_gemm2_nt(const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq,
                                   const uint8_t* hsf, const int32_t* counts, const int32_t* offsets,
-                                  int H, int I, int E, float* y, hipStream_t stream) {
+                                  int H, int I, int E, uint16_t* y, hipStream_t stream) {
   const int chunks = I / 32;  // a multiple of 4
   if (chunks % 16 == 0) return launch_gemm2_t<NT, D, 16>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, y, stream);
   if (chunks % 8 == 0) return launch_gemm2_t<NT, D, 8>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, y, stream);
@@ -148,7 +148,7 @@ static hipError_t launch_gemm2_nt(const uint8_t* w2c, const uint8_t* w2s, const 
 template <int NT>
 static hipError_t launch_gemm2_d(const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq,
                                  const uint8_t* hsf, const int32_t* counts, const int32_t* offsets,
-                                 int H, int I, int E, float* y, hipStream_t stream) {
+                                 int H, int I, int E, uint16_t* y, hipStream_t stream) {
   // The ring depth must divide the number of K steps I/128.
   const int S = I / kStepK;
   if (S % MOE_STREAM_RING_DEPTH == 0) return launch_gemm2_nt<NT, MOE_STREAM_RING_DEPTH>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, y, stream);
@@ -158,7 +158,7 @@ static hipError_t launch_gemm2_d(const uint8_t* w2c, const uint8_t* w2s, const u
 
 hipError_t launch_gemm2(const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq, const uint8_t* hsf,
                         const int32_t* counts, const int32_t* offsets, int H, int I, int E,
-                        int rows_hint, float* y, hipStream_t stream) {
+                        int rows_hint, uint16_t* y, hipStream_t stream) {
   if (rows_hint > 8) return launch_gemm2_d<2>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, y, stream);
   return launch_gemm2_d<1>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, y, stream);
 }

@@ -47,7 +47,7 @@ __global__ void __launch_bounds__(256, 2) gemm_tiled_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows,
     const int2* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int max_tiles, int H, int I,
     int k, uint8_t* __restrict__ hq, uint8_t* __restrict__ hsf, float* __restrict__ acc_out,
-    float* __restrict__ y) {
+    uint16_t* __restrict__ y) {
   constexpr int ROWS = NT * 16;
   constexpr int CHUNKS = CK * 4;                    // 16-byte pieces per row per chunk
   constexpr int CODE_BYTES = ROWS * CHUNKS * 16;    // one buffer of codes
@@ -184,7 +184,7 @@ static hipError_t launch_tiled_t(const uint8_t* wc, const uint8_t* wsc, const ui
                                  const uint8_t* act_sf, const int32_t* counts, const int32_t* offsets,
                                  const int32_t* sorted_rows, const int2* tiles, const int32_t* num_tiles,
                                  int max_tiles, int H, int I, int k, uint8_t* hq, uint8_t* hsf,
-                                 float* acc_out, float* y, hipStream_t stream) {
+                                 float* acc_out, uint16_t* y, hipStream_t stream) {
   constexpr int ROWS = NT * 16;
   const size_t lds = 2 * ((size_t)ROWS * CK * 64 + (size_t)ROWS * CK * 4);
   const int nwb = G1 ? I / 128 : H / 256;
@@ -213,7 +213,7 @@ hipError_t launch_gemm1_tiled(const uint8_t* w1c, const uint8_t* w1s, const uint
 
 hipError_t launch_gemm2_tiled(const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq, const uint8_t* hsf,
                               const int32_t* counts, const int32_t* offsets, const int2* tiles,
-                              const int32_t* num_tiles, int max_tiles, int H, int I, float* y,
+                              const int32_t* num_tiles, int max_tiles, int H, int I, uint16_t* y,
                               hipStream_t stream) {
   const int S = I / kStepK;
   if (S % 4 == 0)

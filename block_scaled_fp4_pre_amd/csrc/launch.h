@@ -36,7 +36,7 @@ hipError_t launch_gemm1_tiled(const uint8_t* w1c, const uint8_t* w1s, const uint
                               uint8_t* hq, uint8_t* hsf, float* acc_out, hipStream_t stream);
 hipError_t launch_gemm2_tiled(const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq, const uint8_t* hsf,
                               const int32_t* counts, const int32_t* offsets, const int2* tiles,
-                              const int32_t* num_tiles, int max_tiles, int H, int I, float* y,
+                              const int32_t* num_tiles, int max_tiles, int H, int I, uint16_t* y,
                               hipStream_t stream);
 
 // Stage S2: grouped GEMM1 over the prepared W1 tiles + SwiGLU + MXFP4 requant.
@@ -48,10 +48,10 @@ hipError_t launch_gemm1(const uint8_t* w1_codes, const uint8_t* w1_scales, const
 // Stage S3: grouped GEMM2 over the prepared W2 tiles -> fp32 y in sorted order.
 hipError_t launch_gemm2(const uint8_t* w2_codes, const uint8_t* w2_scales, const uint8_t* hq,
                         const uint8_t* hsf, const int32_t* counts, const int32_t* offsets, int H,
-                        int I, int E, int rows_hint, float* y, hipStream_t stream);
+                        int I, int E, int rows_hint, uint16_t* y, hipStream_t stream);
 
 // Stage S4: top-k weighted combine back to token order, bf16 output.
-hipError_t launch_combine(const float* y, const int32_t* pos, const float* w, int T, int H, int k,
+hipError_t launch_combine(const uint16_t* y, const int32_t* pos, const float* w, int T, int H, int k,
                           uint16_t* out, hipStream_t stream);
 
 // Stage S0: canonical MXFP4 weights -> device tile order.

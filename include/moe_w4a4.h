@@ -119,9 +119,10 @@ int moe_w4a4_prepare_weights(const moe_w4a4_cfg* cfg,
  *      (ids outside [0, E) are skipped; duplicates are separate rows);
  *   3. GEMM1 per expert with fp32 accumulation, SwiGLU, requantization of h to
  *      MXFP4 along I;
- *   4. GEMM2 per expert, fp32 result per routed row;
+ *   4. GEMM2 per expert with fp32 accumulation, the result per routed row
+ *      rounded to bfloat16;
  *   5. combine: out[t] = sum over valid slots j (in slot order, fp32, from +0)
- *      of topk_weights[t, j] * y[row (t, j)], rounded once to bfloat16.
+ *      of topk_weights[t, j] * y[row (t, j)], rounded to bfloat16.
  * x:            device bfloat16 [num_tokens, H], 16-byte aligned
  * topk_ids:     device int32 [num_tokens, k]
  * topk_weights: device float32 [num_tokens, k], used as given
@@ -152,7 +153,7 @@ typedef struct moe_w4a4_ws_layout {
   uint64_t hist;         /* int32  [ceil(max_tokens*k/1024), E] per-block counts   */
   uint64_t hq;           /* uint8  [max_tokens*k, I/2] requantized h (sorted order) */
   uint64_t hsf;          /* uint8  [max_tokens*k, I/32]                             */
-  uint64_t y;            /* float  [max_tokens*k, H]   GEMM2 result (sorted order)  */
+  uint64_t y;            /* bf16   [max_tokens*k, H]   GEMM2 result (sorted order)  */
   uint64_t tiles;        /* int32  [max_tokens*k/16 + E, 2] (expert, first row) work tiles */
   uint64_t num_tiles;    /* int32  [1]                 number of valid tiles        */
   uint64_t total;        /* == workspace_bytes                                      */

@@ -74,5 +74,5 @@ def workspace_host(layer, T):
         pos=ws("pos", (layer.max_tokens * k,), torch.int32)[:R].cpu().numpy(),
         hq=ws("hq", (layer.max_tokens * k, I // 2), torch.uint8)[:nv].cpu().numpy(),
         hsf=ws("hsf", (layer.max_tokens * k, I // 32), torch.uint8)[:nv].cpu().numpy(),
-        y=ws("y", (layer.max_tokens * k, H), torch.float32)[:nv].cpu().numpy(),
+        y=ws("y", (layer.max_tokens * k, H), torch.bfloat16)[:nv].float().cpu().numpy().astype(np.float64),
     )

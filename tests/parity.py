@@ -6,6 +6,9 @@
       difference at most one step on the signed E2M1 grid; a group whose scale
       bytes differ must have its oracle absmax within 1e-4 (relative) of a scale
       boundary 6 * 2^e
+  y (GEMM2 result, stored bf16) ............ relative L2 error <= 4e-3 against
+      the oracle's fp64 y, and >= 99.9 % of its bf16 values equal to the
+      oracle's y rounded to bf16
   final bf16 output ........................ relative L2 error <= 5e-3
 """
 import numpy as np
@@ -14,6 +17,7 @@ from oracle import mxfp4
 
 OUT_REL_L2 = 5e-3
 REQUANT_IDENTICAL = 0.999
+Y_REL_L2 = 4e-3          # y is stored in bfloat16: one rounding, relative error <= 2^-8
 
 
 def grid_index(codes):
@@ -48,3 +52,13 @@ def rel_l2(a, b):
     b = np.asarray(b, dtype=np.float64)
     den = np.linalg.norm(b)
     return float(np.linalg.norm(a - b) / den) if den > 0 else float(np.linalg.norm(a - b))
+
+
+def check_y(g_y, r_y):
+    """g_y: device y decoded to float; r_y: oracle fp64 y (same rows)."""
+    from oracle import bf16
+    err = rel_l2(g_y, r_y) if np.asarray(r_y).size else 0.0
+    same = float(np.mean(bf16.encode(np.asarray(g_y, np.float64)) == bf16.encode(r_y))) if np.asarray(r_y).size else 1.0
+    assert err <= Y_REL_L2, err
+    assert same >= 0.999, same
+    return err, same

@@ -31,7 +31,7 @@ def test_query_sizes_dsv4():
     lay = _lib.moe_w4a4_workspace_layout(cfg)
     assert lay["total"] == ws
     assert all(v % 256 == 0 for v in lay.values())
-    assert lay["y"] + 512 * 6 * 4096 * 4 <= ws
+    assert lay["y"] + 512 * 6 * 4096 * 2 <= ws               # y is bf16 [R, H]
 
 
 @pytest.mark.parametrize("field,value,status", [

@@ -6,7 +6,12 @@ import torch
 
 from oracle import bf16, mxfp4
 from oracle.route import route
+from synth import f32_to_bf16_bits as _f32_to_bf16_bits
 from tests.gpu_support import dev, dev_bf16, host_bits, layer_for, log
+
+
+def synth_bf16(v):
+    return _f32_to_bf16_bits(np.asarray(v, dtype=np.float32))
 
 pytestmark = pytest.mark.gpu
 
@@ -143,27 +148,31 @@ def test_gemm2_exact_on_injected_rows():
     ws("hsf", (T * k, I // 32), torch.uint8)[:srt.size].copy_(torch.from_numpy(hsf))
     layer.run_stages(8, T)
     torch.cuda.synchronize()
-    y = ws("y", (T * k, H), torch.float32)[:srt.size].cpu().numpy()
+    # the fp32 accumulators are exact here, so the stored bf16 y is the exact
+    # product rounded once to bf16 (nearest even)
+    y = host_bits(ws("y", (T * k, H), torch.bfloat16)[:srt.size])
     W2hat = mxfp4.dequantize(W[2], W[3])
     hhat = mxfp4.dequantize(hq, hsf)
     for e in range(E):
         lo, hi = offsets[e], offsets[e + 1]
-        assert np.array_equal(y[lo:hi].astype(np.float64), hhat[lo:hi] @ W2hat[e].T)
+        assert np.array_equal(y[lo:hi], bf16.encode(hhat[lo:hi] @ W2hat[e].T))
 
 
 def test_combine_exact_cases():
+    """y is injected as bf16; with k = 1 and w = 1 the output is y bit for bit."""
     log("[test] combine exact cases")
     H, I, E = 512, 256, 6
     rng = np.random.default_rng(9)
     for k, T in ((1, 50), (4, 33)):
         ids = rng.integers(-1, E, (T, k)).astype(np.int32)
         counts, offsets, srt, pos = route(ids, E)
-        y = (rng.standard_normal((max(srt.size, 1), H)) * 3).astype(np.float32)
+        y_bits = synth_bf16(rng.standard_normal((max(srt.size, 1), H)) * 3)
+        y = bf16.decode(y_bits)
         w = rng.random((T, k)).astype(np.float32) if k > 1 else np.ones((T, k), np.float32)
         layer = layer_for(H, I, E, k, T)
         ws = layer.ws
         ws("pos", (T * k,), torch.int32).copy_(torch.from_numpy(pos))
-        ws("y", (T * k, H), torch.float32)[:srt.size].copy_(torch.from_numpy(y[:srt.size]))
+        ws("y", (T * k, H), torch.int16)[:srt.size].copy_(torch.from_numpy(y_bits[:srt.size].view(np.int16)))
         out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
         outs = []
         for scale in (1.0, 2.0):
@@ -174,7 +183,7 @@ def test_combine_exact_cases():
         for t in range(T):
             for j in range(k):
                 if pos[t * k + j] >= 0:
-                    ref[t] = ref[t] + np.float64(w[t, j]) * y[pos[t * k + j]].astype(np.float64)
+                    ref[t] = ref[t] + np.float64(w[t, j]) * y[pos[t * k + j]]
         if k == 1:
             assert np.array_equal(outs[0], bf16.encode(ref))   # out = bf16(y) exactly
         else:
