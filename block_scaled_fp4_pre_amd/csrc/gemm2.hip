@@ -98,7 +98,7 @@ __global__ void __launch_bounds__(256, 2) gemm2_kernel(
         for (int nt = 0; nt < NT; ++nt) {
           const int n = min(nt * 16 + tok_lane, ROWS - 1);
           const uint4 b = tile_operand<SWZ>(lds_codes, row_bytes, n, s, kb);
-          const int sb = lds_scales[n * sc_bytes + s * 4 + kb];
+          const int sb = tile_scale(lds_scales, sc_bytes, n, s, kb);
           acc[nt][0] = mfma_fp4<0, 0>(a[d][0], b, acc[nt][0], (int)sa[d], sb);
           acc[nt][1] = mfma_fp4<1, 0>(a[d][1], b, acc[nt][1], (int)sa[d], sb);
           acc[nt][2] = mfma_fp4<2, 0>(a[d][2], b, acc[nt][2], (int)sa[d], sb);

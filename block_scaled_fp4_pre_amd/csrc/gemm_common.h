@@ -66,6 +66,16 @@ inline int units_per_wave(int units, int want) {
 
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Swizzle width of the scale rows in LDS: the largest power of two (at most
+// 32) dividing the dwords per row.  Row n keeps its step-s dword at position
+// s ^ (n % width), so the 16 token rows read by one MFMA scale load hit
+// different banks instead of two.
+__device__ __forceinline__ int scale_swizzle(int sc_bytes) {
+  const int dws = sc_bytes >> 2;
+  const int low = dws & (-dws);
+  return low > 32 ? 32 : low;
+}
+
 // Copy ROWS token rows into LDS.  Row n (n < nrows) comes from global row
 // row_index(n) of `codes` (row_bytes per row) and `scales` (sc_bytes per row).
 // sc_bytes is a multiple of 4.  Lanes whose slot lies past the last row are
@@ -85,14 +95,23 @@ __device__ __forceinline__ void gather_tile(uint8_t* lds_codes, uint8_t* lds_sca
       lds_dma16(codes + (size_t)src * row_bytes + c * 16, lds_codes + j * 1024);
     }
   }
+  // Scale dword d of row n sits at position d ^ (n % scale_swizzle(sc_bytes)).
   const int dws = sc_bytes >> 2;
+  const int scm = scale_swizzle(sc_bytes) - 1;
   const int sc_total = ROWS * dws;
   for (int j = wave; j * 64 < sc_total; j += nwaves) {
     const int slot = j * 64 + lane;
-    const int n = min(slot / dws, ROWS - 1), d = slot - (slot / dws) * dws;
+    const int n = min(slot / dws, ROWS - 1), dpos = slot - (slot / dws) * dws;
     const int src = row_index(n);
-    if (slot < sc_total && n < nrows) lds_dma4(scales + (size_t)src * sc_bytes + d * 4, lds_scales + j * 256);
+    if (slot < sc_total && n < nrows)
+      lds_dma4(scales + (size_t)src * sc_bytes + (dpos ^ (n & scm)) * 4, lds_scales + j * 256);
   }
+}
+
+// Scale byte of step s for token column n and K block kb.
+__device__ __forceinline__ int tile_scale(const uint8_t* lds_scales, int sc_bytes, int n, int s, int kb) {
+  const int scm = scale_swizzle(sc_bytes) - 1;
+  return lds_scales[n * sc_bytes + (s ^ (n & scm)) * 4 + kb];
 }
 
 // B operand of step s for token column n (row of the LDS tile) and K block kb.
