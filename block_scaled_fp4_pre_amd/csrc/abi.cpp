@@ -14,7 +14,7 @@
 #include <atomic>
 #include <mutex>
 
-#include "../../include/moe_w4a4.h"
+#include "moe_w4a4.h"
 #include "launch.h"
 
 namespace {

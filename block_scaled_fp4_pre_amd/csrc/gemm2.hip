@@ -24,6 +24,10 @@
 #define MOE_STREAM_ROWS2 24       // token rows per pass of the two-tile variant (17..32)
 #endif
 
+#ifndef MOE_GEMM2_MIN_BLOCKS
+#define MOE_GEMM2_MIN_BLOCKS 2    // launch bound: workgroups per CU the register budget must allow
+#endif
+
 #ifndef MOE_GEMM2_UNITS_PER_WAVE
 #define MOE_GEMM2_UNITS_PER_WAVE 1
 #endif
@@ -31,7 +35,7 @@
 namespace moe {
 
 template <int NT, int D, int SWZ>
-__global__ void __launch_bounds__(256, 2) gemm2_kernel(
+__global__ void __launch_bounds__(256, MOE_GEMM2_MIN_BLOCKS) gemm2_kernel(
     const uint8_t* __restrict__ w2c, const uint8_t* __restrict__ w2s, const uint8_t* __restrict__ hq,
     const uint8_t* __restrict__ hsf, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, int H, int I, int upw, uint16_t* __restrict__ y) {

@@ -27,8 +27,12 @@ hipError_t launch_predispatch(const uint16_t* x, int64_t ngroups, uint8_t* xq, u
 #ifndef MOE_TILED_NT
 #define MOE_TILED_NT 4
 #endif
-constexpr int kTiledNT = MOE_TILED_NT;
-constexpr int kTiledRows = 16 * kTiledNT;
+#ifndef MOE_TILED_HALVES
+#define MOE_TILED_HALVES 1
+#endif
+constexpr int kTiledNT = MOE_TILED_NT;          // token tiles of 16 rows per wave
+constexpr int kTiledHalves = MOE_TILED_HALVES;  // 4-wave groups per workgroup
+constexpr int kTiledRows = 16 * kTiledNT * kTiledHalves;
 int tiled_max_tiles(int R, int E);
 hipError_t launch_gemm1_tiled(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq, const uint8_t* xsf,
                               const int32_t* counts, const int32_t* offsets, const int32_t* sorted_rows,
