@@ -50,7 +50,7 @@ class moe_w4a4_ws_layout(ctypes.Structure):
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
-                      "(python -m block_scaled_fp4_pre_amd.build)")
+                      "(python block_scaled_fp4_pre_amd/build.py)")
 # torch ships its own HIP runtime.  Loading torch first makes the library bind
 # to that same runtime (same devices, streams and allocations); loading the
 # library first would bring in a second runtime next to torch's.

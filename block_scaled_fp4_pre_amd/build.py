@@ -1,6 +1,6 @@
 """Build libmoe_w4a4.so in-tree with hipcc for gfx950.
 
-    python -m block_scaled_fp4_pre_amd.build      (or __graft_entry__.build())
+    python block_scaled_fp4_pre_amd/build.py      (or __graft_entry__.build())
 
 Each source under csrc/ is compiled to an object in _build/ and the objects are
 linked into block_scaled_fp4_pre_amd/libmoe_w4a4.so next to the binding.

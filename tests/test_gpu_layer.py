@@ -1,5 +1,7 @@
 """GPU tier, whole forward through moe_w4a4_forward, against the oracle:
 the tiny configuration, odd shapes and routing edge cases, determinism."""
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -57,7 +59,7 @@ def _run_custom(layer, x, ids, w):
 @pytest.mark.parametrize("case", ["T1", "T3", "T129", "T1000", "one_expert", "masked_dups", "zero_x"])
 def test_tiny_dims_edge_cases(tiny_layer, tiny_weights, case):
     log(f"[test] edge case {case}")
-    rng = np.random.default_rng(abs(hash(case)) % (1 << 31))
+    rng = np.random.default_rng(zlib.crc32(case.encode()))
     T = {"T1": 1, "T3": 3, "T129": 129, "T1000": 1000}.get(case, 200)
     E, k = TINY.experts, TINY.topk
     x = synth.f32_to_bf16_bits(rng.standard_normal((T, TINY.hidden)).astype(np.float32))
