@@ -20,7 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe_w4a4.so")
 ARCH = "gfx950"
 
-DEVICE_SOURCES = ("quant.hip", "route.hip", "predispatch.hip", "gemm1.hip", "gemm2.hip", "gemm_tiled.hip", "combine.hip",
+DEVICE_SOURCES = ("quant.hip", "route.hip", "predispatch.hip", "gemm1.hip", "gemm2.hip", "gemm_lds.hip",
+                  "combine.hip",
                   "prepare.hip")
 HOST_SOURCES = ("abi.cpp",)
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include")]

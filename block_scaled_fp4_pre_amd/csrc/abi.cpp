@@ -25,6 +25,7 @@ constexpr int kMaxTopk = 16;
 constexpr int kRouteRows = 1024;
 constexpr int kStreamMaxRows = 16;  // mean routed rows per expert up to which the streaming GEMMs run
 constexpr int kFusedRouteMaxRows = 8192;  // routed rows up to which one block routes them all
+
 std::atomic<int> g_is_gfx950[kMaxDevices];  // 0 unknown, 1 yes, 2 no
 
 inline uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
@@ -208,9 +209,11 @@ int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t n
   const int T = num_tokens, R = T * k;
   const int rows_hint = (int)(((int64_t)R + E - 1) / E);
   // Few rows per expert: stream each expert's weights once with the whole
-  // token tile in LDS.  Many rows: tiled GEMMs over a device-built tile list.
+  // token tile in LDS.  Many rows: tiled GEMMs over a device-built tile list,
+  // both operands staged through LDS.
   const bool tiled = rows_hint > kStreamMaxRows;
-  const int max_tiles = moe::tiled_max_tiles(R, E);
+  const int tile_rows = tiled ? moe::lds_tile_rows(rows_hint) : 0;
+  const int max_tiles = tiled ? moe::lds_max_tiles(R, E, tile_rows) : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint8_t* xq = ws + L.xq;
@@ -228,7 +231,6 @@ int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t n
   const Prepared P = prepared_layout(cfg);
   const uint8_t* pw = static_cast<const uint8_t*>(prepared);
 
-  const int tile_rows = tiled ? moe::kTiledRows : 0;
   if ((stages & MOE_STAGE_QUANT) && (stages & MOE_STAGE_ROUTE) && R <= kFusedRouteMaxRows) {
     // pre-dispatch in one launch: one block routes, the others quantize
     st = hip_status(moe::launch_predispatch(x, (int64_t)T * (H / 32), xq, xsf, topk_ids, R, E, counts, offsets,
@@ -246,16 +248,16 @@ int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t n
     }
   }
   if (stages & MOE_STAGE_GEMM1) {
-    st = hip_status(tiled ? moe::launch_gemm1_tiled(pw + P.w1c, pw + P.w1s, xq, xsf, counts, offsets,
-                                                    sorted_rows, tiles, num_tiles, max_tiles, H, I, k, hq,
-                                                    hsf, gemm1_acc, s)
+    st = hip_status(tiled ? moe::launch_gemm1_lds(pw + P.w1c, pw + P.w1s, xq, xsf, counts, offsets, sorted_rows,
+                                                  tiles, num_tiles, max_tiles, rows_hint, H, I, k, hq, hsf,
+                                                  gemm1_acc, s)
                           : moe::launch_gemm1(pw + P.w1c, pw + P.w1s, xq, xsf, counts, offsets, sorted_rows,
                                               H, I, E, k, rows_hint, hq, hsf, gemm1_acc, s));
     if (st != MOE_OK) return st;
   }
   if (stages & MOE_STAGE_GEMM2) {
-    st = hip_status(tiled ? moe::launch_gemm2_tiled(pw + P.w2c, pw + P.w2s, hq, hsf, counts, offsets, tiles,
-                                                    num_tiles, max_tiles, H, I, y, s)
+    st = hip_status(tiled ? moe::launch_gemm2_lds(pw + P.w2c, pw + P.w2s, hq, hsf, counts, offsets, tiles,
+                                                  num_tiles, max_tiles, rows_hint, H, I, y, s)
                           : moe::launch_gemm2(pw + P.w2c, pw + P.w2s, hq, hsf, counts, offsets, H, I, E,
                                               rows_hint, y, s));
     if (st != MOE_OK) return st;

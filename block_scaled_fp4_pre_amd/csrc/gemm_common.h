@@ -28,9 +28,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 // Cache policy of a weight stream.  The streaming GEMMs read every weight byte
 // once per forward and load it non-temporal (NT bit), which measured ~9% more
-// sustained read bandwidth on gfx950 than the default policy.  The tiled GEMMs
-// reuse a weight block across the tiles that share it and keep the default.
-constexpr int kPolicyDefault = 0;
+// sustained read bandwidth on gfx950 than the default policy.
 constexpr int kPolicyStream = 2;
 
 template <int CP = kPolicyStream>

@@ -1,0 +1,260 @@
+// Stages S2 / S3 for many routed rows per expert (prefill): grouped GEMMs whose
+// two operands are both staged in LDS by direct-to-LDS loads through a ring of
+// P stages, one K step of 128 per stage.
+//
+// [P1] sglang PR "[deepseek-v4] Bump sgl-deep-gemm for packed FP4xFP4 mega-MoE
+// (W4A4)", Appendix A (prefill sweep with 1024-token inputs) and section B (the
+// fused layer on packed FP4 operands); [P3] prhub digest of sglang PR "bump
+// sgl-deep-gemm to 0.1.7, MegaMoE uses the mma_type API for MXFP4", "Key source
+// snippets" (activation="swiglu", gate rows then up rows in W1).
+//
+// Work item = (tile of up to NT*16 routed rows of one expert, from the route's
+// tile list) x (weight block of 4 units = 256 weight rows).  Wave w of the
+// 4-wave workgroup owns unit w (64 weight rows, the 16-row MFMA A side) and
+// all NT*16 token rows (the B side), so each stage feeds 4*NT MFMAs per wave.
+//
+// Per stage each wave issues its share of the DMA: its unit's 4 KiB of weight
+// codes and 256 B of weight scales (already in MFMA operand order), a quarter
+// of the token rows' 64-byte code pieces (gathered by row index; 16-byte piece
+// c of row n lands at position c ^ ((n / 4) % 4), so the 16 rows one MFMA
+// operand read touches fall on distinct banks) and a quarter of their scale
+// dwords.  The DMA is issued from inline assembly: the compiler cannot tell the
+// ring's stages apart and would otherwise wait for every DMA in flight before
+// each LDS read.  The wait is explicit instead: before step s a wave waits
+// until only the DMAs of the P-2 later stages it has issued remain
+// (vmcnt, in order), then the barrier makes the whole stage visible and
+// guarantees that stage s-1's buffer is no longer read, so the DMA of stage
+// s+P-1 can go into it.
+//
+// Block order: logical id L = (blockIdx % 8) * (grid / 8) + blockIdx / 8 runs
+// weight-block-major, tile-minor.  Workgroups are dealt round-robin to the 8
+// XCDs, so each XCD gets a contiguous range of L: the tiles that share a
+// weight block run on one XCD at about the same time and fetch it from HBM
+// once into that XCD's L2.  (Tile-major order, which keeps a tile's tokens in
+// L2 instead, measured 30% slower at 96 rows per expert.)
+//
+// Occupancy: two workgroups per CU (3 stages x 26 KiB of LDS each, 176 VGPRs
+// including the accumulators) measured faster than one workgroup with a
+// deeper ring; the second workgroup's MFMAs cover the first one's waits.
+#include "epilogue.h"
+#include "gemm_common.h"
+#include "launch.h"
+#include "tiles.h"
+
+namespace moe {
+
+template <int NT>
+struct LdsStage {
+  static constexpr int ROWS = NT * 16;
+  static constexpr int W_CODES = 0;                      // 4 units x 4 KiB
+  static constexpr int W_SCALES = 4 * kStepCodeBytes;    // 4 units x 256 B
+  static constexpr int T_CODES = W_SCALES + 4 * kStepScaleBytes;  // ROWS x 64 B
+  static constexpr int T_SCALES = T_CODES + ROWS * 64;   // ROWS x 4 B
+  static constexpr int BYTES = T_SCALES + ROWS * 4;
+};
+
+// Position of 16-byte piece c (0..3) of staged token row n.
+__device__ __forceinline__ int tok_pos(int n, int c) { return c ^ ((n >> 2) & 3); }
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// Direct global -> LDS copies: lane l's 16 (4) bytes land at LDS byte address
+// lds + 16*l (4*l).  M0 carries the wave's LDS address.
+__device__ __forceinline__ void dma16_asm(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_asm(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+// The same with the non-temporal hint (data read once).
+__device__ __forceinline__ void dma16_nt_asm(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_nt_asm(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off nt" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+#ifndef MOE_LDS_BLOCKS
+#define MOE_LDS_BLOCKS 2        // workgroups per CU the launch bound asks for
+#endif
+
+// WNT: weight DMA with the non-temporal hint (each weight byte is read by one
+// tile only).
+template <bool G1, int NT, int P, bool WNT>
+__global__ void __launch_bounds__(256, MOE_LDS_BLOCKS) gemm_lds_kernel(
+    const uint8_t* __restrict__ wc, const uint8_t* __restrict__ wsc, const uint8_t* __restrict__ act,
+    const uint8_t* __restrict__ act_sf, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows,
+    const int2* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int max_tiles, int H, int I, int k,
+    uint8_t* __restrict__ hq, uint8_t* __restrict__ hsf, float* __restrict__ acc_out, uint16_t* __restrict__ y) {
+  using L = LdsStage<NT>;
+  constexpr int ROWS = L::ROWS;
+  constexpr int TOK_INSTS = NT / 4;                    // token-code DMAs per wave per stage
+  constexpr int SC_LANES = ROWS / 4;                   // token-scale dwords per wave per stage
+  constexpr int DMA_PER_STAGE = 4 + 1 + TOK_INSTS + 1;
+  static_assert(NT % 4 == 0 && SC_LANES <= 64, "tile rows");
+  static_assert(DMA_PER_STAGE * (P - 2) <= 63, "vmcnt range");
+
+  const int K = G1 ? H : I;
+  const int nwb = G1 ? I / 128 : H / 256;
+  const int G = gridDim.x;
+  const int Lid = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  const int wb = Lid / max_tiles;
+  const int ti = Lid - wb * max_tiles;
+  if (wb >= nwb || ti >= *num_tiles) return;
+  const int2 tile = tiles[ti];
+  const int e = tile.x, t0 = tile.y;
+  const int nrows = min(ROWS, counts[e] - t0);
+  const int row0 = offsets[e] + t0;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int unit = wb * 4 + wave;
+  const int S = K / kStepK;
+  const int row_bytes = K / 2, sc_row = K / 32;
+
+  extern __shared__ __align__(16) uint8_t lds[];
+  const uint32_t lbase = (uint32_t)(uintptr_t)lds;
+
+  // DMA sources.  Rows past the tile's end re-read its last row (their
+  // results are never stored).
+  const uint8_t* wsrc = wc + (G1 ? w1_code_offset(e, unit, 0, H, I) : w2_code_offset(e, unit, 0, H, I)) + lane * 16;
+  const uint8_t* ssrc = wsc + (G1 ? w1_scale_offset(e, unit, 0, H, I) : w2_scale_offset(e, unit, 0, H, I)) + lane * 4;
+  auto src_row = [&](int n) -> int {
+    const int r = min(n, nrows - 1);
+    return G1 ? sorted_rows[row0 + r] / k : row0 + r;
+  };
+  const uint8_t* tsrc[TOK_INSTS];
+#pragma unroll
+  for (int i = 0; i < TOK_INSTS; ++i) {
+    const int slot = (wave * TOK_INSTS + i) * 64 + lane;
+    const int n = slot >> 2;
+    tsrc[i] = act + (size_t)src_row(n) * row_bytes + tok_pos(n, slot & 3) * 16;
+  }
+  const uint8_t* tssrc = act_sf + (size_t)src_row(wave * SC_LANES + min(lane, SC_LANES - 1)) * sc_row;
+
+  auto issue = [&](int s) {
+    const uint32_t sb = lbase + (uint32_t)((s % P) * L::BYTES);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      if constexpr (WNT)
+        dma16_nt_asm(wsrc + (size_t)s * kStepCodeBytes + rb * 1024, sb + L::W_CODES + wave * kStepCodeBytes + rb * 1024);
+      else
+        dma16_asm(wsrc + (size_t)s * kStepCodeBytes + rb * 1024, sb + L::W_CODES + wave * kStepCodeBytes + rb * 1024);
+    }
+    if constexpr (WNT)
+      dma4_nt_asm(ssrc + (size_t)s * kStepScaleBytes, sb + L::W_SCALES + wave * kStepScaleBytes);
+    else
+      dma4_asm(ssrc + (size_t)s * kStepScaleBytes, sb + L::W_SCALES + wave * kStepScaleBytes);
+#pragma unroll
+    for (int i = 0; i < TOK_INSTS; ++i)
+      dma16_asm(tsrc[i] + s * 64, sb + L::T_CODES + (wave * TOK_INSTS + i) * 1024);
+    if (lane < SC_LANES) dma4_asm(tssrc + s * 4, sb + L::T_SCALES + wave * SC_LANES * 4);
+  };
+
+  for (int s = 0; s < P - 1 && s < S; ++s) issue(s);
+
+  v4f acc[NT][4];
+  zero_acc<NT>(acc);
+  const int tok_lane = lane & 15, kb = lane >> 4;
+  for (int s = 0; s < S; ++s) {
+    if (s + P - 2 < S)
+      wait_vm<DMA_PER_STAGE * (P - 2)>();   // stage s landed; the P-2 later ones may be in flight
+    else
+      wait_vm<0>();
+    stage_barrier();
+    if (s + P - 1 < S) issue(s + P - 1);    // into the buffer of stage s-1, read by nobody now
+
+    const uint8_t* st = lds + (s % P) * L::BYTES;
+    uint4 a[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+      a[rb] = *reinterpret_cast<const uint4*>(st + L::W_CODES + wave * kStepCodeBytes + rb * 1024 + lane * 16);
+    const int sa = *reinterpret_cast<const int*>(st + L::W_SCALES + wave * kStepScaleBytes + lane * 4);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int n = nt * 16 + tok_lane;
+      const uint4 b = *reinterpret_cast<const uint4*>(st + L::T_CODES + n * 64 + tok_pos(n, kb) * 16);
+      const int sb = (int)(*reinterpret_cast<const uint32_t*>(st + L::T_SCALES + n * 4) >> (8 * kb));
+      acc[nt][0] = mfma_fp4<0, 0>(a[0], b, acc[nt][0], sa, sb);
+      acc[nt][1] = mfma_fp4<1, 0>(a[1], b, acc[nt][1], sa, sb);
+      acc[nt][2] = mfma_fp4<2, 0>(a[2], b, acc[nt][2], sa, sb);
+      acc[nt][3] = mfma_fp4<3, 0>(a[3], b, acc[nt][3], sa, sb);
+    }
+  }
+
+  if constexpr (G1)
+    gemm1_epilogue<NT>(acc, unit, row0, nrows, I, lane, hq, hsf, acc_out);
+  else
+    gemm2_epilogue<NT>(acc, unit, row0, nrows, H, lane, y);
+}
+
+#ifndef MOE_LDS_STAGES
+#define MOE_LDS_STAGES 3      // ring stages: two workgroups of 3 x 26 KiB fit a CU's LDS
+#endif
+
+constexpr int kLdsNT = 8;     // token tiles of 16 rows per wave: 128-row work tiles
+
+template <bool G1, bool WNT>
+static hipError_t launch_prefill_t(const uint8_t* wc, const uint8_t* wsc, const uint8_t* act,
+                                   const uint8_t* act_sf, const int32_t* counts, const int32_t* offsets,
+                                   const int32_t* sorted_rows, const int2* tiles, const int32_t* num_tiles,
+                                   int max_tiles, int H, int I, int k, uint8_t* hq, uint8_t* hsf, float* acc_out,
+                                   uint16_t* y, hipStream_t stream) {
+  constexpr int P = MOE_LDS_STAGES;
+  auto kern = gemm_lds_kernel<G1, kLdsNT, P, WNT>;
+  const size_t lds = (size_t)P * LdsStage<kLdsNT>::BYTES;
+  if (lds > 65536) {
+    hipError_t err = raise_lds_limit(reinterpret_cast<const void*>(kern), lds);
+    if (err != hipSuccess) return err;
+  }
+  const int nwb = G1 ? I / 128 : H / 256;
+  const int64_t blocks = ((int64_t)max_tiles * nwb + 7) / 8 * 8;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), lds, stream, wc, wsc, act, act_sf, counts, offsets,
+                     sorted_rows, tiles, num_tiles, max_tiles, H, I, k, hq, hsf, acc_out, y);
+  return hipGetLastError();
+}
+
+int lds_tile_rows(int) { return kLdsNT * 16; }
+
+int lds_max_tiles(int R, int E, int tile_rows) { return (R + tile_rows - 1) / tile_rows + E; }
+
+// With mean rows per expert within one tile every weight block is read by a
+// single tile: it streams non-temporal.  Otherwise the tiles of an expert
+// share each weight block through L2 and the loads keep the default policy.
+template <bool G1>
+static hipError_t launch_prefill(const uint8_t* wc, const uint8_t* wsc, const uint8_t* act, const uint8_t* act_sf,
+                                 const int32_t* counts, const int32_t* offsets, const int32_t* sorted_rows,
+                                 const int2* tiles, const int32_t* num_tiles, int max_tiles, int rows_hint, int H,
+                                 int I, int k, uint8_t* hq, uint8_t* hsf, float* acc_out, uint16_t* y,
+                                 hipStream_t stream) {
+  if (rows_hint <= kLdsNT * 16)
+    return launch_prefill_t<G1, true>(wc, wsc, act, act_sf, counts, offsets, sorted_rows, tiles, num_tiles, max_tiles,
+                                      H, I, k, hq, hsf, acc_out, y, stream);
+  return launch_prefill_t<G1, false>(wc, wsc, act, act_sf, counts, offsets, sorted_rows, tiles, num_tiles, max_tiles,
+                                     H, I, k, hq, hsf, acc_out, y, stream);
+}
+
+hipError_t launch_gemm1_lds(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq, const uint8_t* xsf,
+                            const int32_t* counts, const int32_t* offsets, const int32_t* sorted_rows,
+                            const int2* tiles, const int32_t* num_tiles, int max_tiles, int rows_hint, int H, int I,
+                            int k, uint8_t* hq, uint8_t* hsf, float* acc_out, hipStream_t stream) {
+  return launch_prefill<true>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, tiles, num_tiles, max_tiles, rows_hint,
+                              H, I, k, hq, hsf, acc_out, nullptr, stream);
+}
+
+hipError_t launch_gemm2_lds(const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq, const uint8_t* hsf,
+                            const int32_t* counts, const int32_t* offsets, const int2* tiles,
+                            const int32_t* num_tiles, int max_tiles, int rows_hint, int H, int I, uint16_t* y,
+                            hipStream_t stream) {
+  return launch_prefill<false>(w2c, w2s, hq, hsf, counts, offsets, nullptr, tiles, num_tiles, max_tiles, rows_hint, H,
+                               I, 1, nullptr, nullptr, nullptr, y, stream);
+}
+
+}  // namespace moe

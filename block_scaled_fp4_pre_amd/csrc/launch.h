@@ -23,25 +23,19 @@ hipError_t launch_predispatch(const uint16_t* x, int64_t ngroups, uint8_t* xq, u
                               int R, int E, int32_t* counts, int32_t* offsets, int32_t* sorted_rows,
                               int32_t* pos, int tile_rows, int2* tiles, int32_t* num_tiles, hipStream_t stream);
 
-// Tiled prefill GEMMs (gemm_tiled.hip): tiles of kTiledRows routed rows.
-#ifndef MOE_TILED_NT
-#define MOE_TILED_NT 4
-#endif
-#ifndef MOE_TILED_HALVES
-#define MOE_TILED_HALVES 1
-#endif
-constexpr int kTiledNT = MOE_TILED_NT;          // token tiles of 16 rows per wave
-constexpr int kTiledHalves = MOE_TILED_HALVES;  // 4-wave groups per workgroup
-constexpr int kTiledRows = 16 * kTiledNT * kTiledHalves;
-int tiled_max_tiles(int R, int E);
-hipError_t launch_gemm1_tiled(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq, const uint8_t* xsf,
-                              const int32_t* counts, const int32_t* offsets, const int32_t* sorted_rows,
-                              const int2* tiles, const int32_t* num_tiles, int max_tiles, int H, int I, int k,
-                              uint8_t* hq, uint8_t* hsf, float* acc_out, hipStream_t stream);
-hipError_t launch_gemm2_tiled(const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq, const uint8_t* hsf,
-                              const int32_t* counts, const int32_t* offsets, const int2* tiles,
-                              const int32_t* num_tiles, int max_tiles, int H, int I, uint16_t* y,
-                              hipStream_t stream);
+// Prefill GEMMs with both operands staged in LDS (gemm_lds.hip): tiles of
+// lds_tile_rows(mean rows per expert) routed rows; rows_hint (the mean) also
+// picks the weight load policy and the work order.
+int lds_tile_rows(int rows_hint);
+int lds_max_tiles(int R, int E, int tile_rows);
+hipError_t launch_gemm1_lds(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq, const uint8_t* xsf,
+                            const int32_t* counts, const int32_t* offsets, const int32_t* sorted_rows,
+                            const int2* tiles, const int32_t* num_tiles, int max_tiles, int rows_hint, int H, int I,
+                            int k, uint8_t* hq, uint8_t* hsf, float* acc_out, hipStream_t stream);
+hipError_t launch_gemm2_lds(const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq, const uint8_t* hsf,
+                            const int32_t* counts, const int32_t* offsets, const int2* tiles,
+                            const int32_t* num_tiles, int max_tiles, int rows_hint, int H, int I, uint16_t* y,
+                            hipStream_t stream);
 
 // Stage S2: grouped GEMM1 over the prepared W1 tiles + SwiGLU + MXFP4 requant.
 hipError_t launch_gemm1(const uint8_t* w1_codes, const uint8_t* w1_scales, const uint8_t* xq,
