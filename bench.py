@@ -13,9 +13,11 @@ Prints ONE JSON line.  `value` is the time of one layer forward in us (lower is
 better): K calls of moe_w4a4_forward, bracketed by synchronizations and HIP
 events on the stream the kernels run on.  Throughput in TFLOP/s and
 algorithmic HBM GB/s ride along.  The "roofline" object is for GEMM1, the
-dominant kernel: its duration comes from K further steps of the same launches
-in which events on the same stream bracket the GEMM1 launch ("split_step_us"
-is the step time of that loop).  "cpu_baseline" times the fp64 CPU oracle on a
+dominant kernel (gemm1_swiglu_kernel up to 16 routed rows per expert,
+gemm_lds_kernel above), against the HBM or the FP4 MFMA peak, whichever bounds
+its algorithmic bytes and flops: its duration comes from K further steps of the
+same launches in which events on the same stream bracket the GEMM1 launch
+("split_step_us" is the step time of that loop).  "cpu_baseline" times the fp64 CPU oracle on a
 bounded slice of the same workload (a few experts with all their routed rows)
 and scales it to one layer.
 """
@@ -56,16 +58,27 @@ def algorithmic(cfg, counts):
                 gemm1_flops=R * 2 * H * 2 * I)
 
 
-GEMM1_SOURCES = ("gemm1.hip", "gemm_common.h", "epilogue.h", "device_common.h", "tiles.h")
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemm1_swiglu_{}_hbm_counters.txt")
+STREAM_MAX_ROWS = 16              # mean routed rows per expert up to which GEMM1 is the streaming kernel
+# GEMM1 kernel of each path, with the sources its code comes from.
+GEMM1_KERNELS = {
+    "stream": ("gemm1_swiglu_kernel", ("gemm1.hip", "gemm_common.h", "epilogue.h", "device_common.h", "tiles.h")),
+    "prefill": ("gemm_lds_kernel", ("gemm_lds.hip", "gemm_common.h", "epilogue.h", "device_common.h", "tiles.h")),
+}
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "{}_{}_hbm_counters.txt")
 
 
-def measured_traffic(workload):
+def gemm1_path(cfg):
+    rows_hint = -(-cfg.tokens * cfg.topk // cfg.experts)
+    return "stream" if rows_hint <= STREAM_MAX_ROWS else "prefill"
+
+
+def measured_traffic(workload, path):
     """HBM bytes per GEMM1 launch from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE runs, each scaled by the same counter on a copy of known size;
     None if there are none for this workload or the kernel changed since."""
     import hashlib
-    path = COUNTERS_FILE.format(workload)
+    kernel, sources = GEMM1_KERNELS[path]
+    path = COUNTERS_FILE.format(kernel, workload)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -74,7 +87,7 @@ def measured_traffic(workload):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
     h = hashlib.sha256()
-    for name in GEMM1_SOURCES:
+    for name in sources:
         with open(os.path.join(ROOT, "block_scaled_fp4_pre_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     if kv.get("kernel_sources_sha256") != h.hexdigest():
@@ -126,8 +139,8 @@ def cpu_baseline(cfg, x, ids, w, n_experts_sample=40):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="dsv4flash_t512")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--threads", type=int, default=16)
@@ -222,7 +235,15 @@ def main():
     us = ms_per_step * 1e3
     tflops = alg["flops"] / (us * 1e-6) / 1e12
     gbps = alg["layer_bytes"] / (us * 1e-6) / 1e9
-    g1_gbps = alg["gemm1_bytes"] / (gemm1_us * 1e-6) / 1e9
+    # GEMM1's roofline: HBM-bound unless its flops take longer at the FP4 MFMA
+    # peak than its algorithmic bytes at the HBM peak.
+    path = gemm1_path(cfg)
+    g1_kernel = GEMM1_KERNELS[path][0]
+    mfma_bound = alg["gemm1_flops"] / (FP4_PEAK_TFLOPS * 1e12) > alg["gemm1_bytes"] / (HBM_PEAK_GBPS * 1e9)
+    if mfma_bound:
+        g1_ach, g1_peak, g1_unit = alg["gemm1_flops"] / (gemm1_us * 1e-6) / 1e12, FP4_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        g1_ach, g1_peak, g1_unit = alg["gemm1_bytes"] / (gemm1_us * 1e-6) / 1e9, HBM_PEAK_GBPS, "GB/s"
 
     res = {
         "metric": METRIC,
@@ -245,10 +266,10 @@ def main():
         "hbm_gbps": round(gbps, 1),
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "split_step_us": round(split_ms * 1e3, 2),
-        "roofline": {"kernel": "gemm1_swiglu_kernel", "bound": "hbm", "achieved": round(g1_gbps, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(g1_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(cfg.name), "avg_us": round(gemm1_us, 2),
-                     "bytes_per_launch": alg["gemm1_bytes"]},
+        "roofline": {"kernel": g1_kernel, "bound": "mfma" if mfma_bound else "hbm", "achieved": round(g1_ach, 1),
+                     "peak": g1_peak, "unit": g1_unit, "frac": round(g1_ach / g1_peak, 4),
+                     "traffic": measured_traffic(cfg.name, path), "avg_us": round(gemm1_us, 2),
+                     "bytes_per_launch": alg["gemm1_bytes"], "flops_per_launch": alg["gemm1_flops"]},
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:

@@ -27,20 +27,21 @@ __device__ __forceinline__ int mx_scale_exp(uint32_t amax_bits) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
-// Magnitude index (0..7) of the E2M1 value nearest to a >= 0 (a <= 6), ties to
-// the even index: the thresholds are the midpoints 0.25, 0.75, 1.25, 1.75, 2.5,
-// 3.5, 5 with '>' where the lower neighbour is even and '>=' where the upper is.
-__device__ __forceinline__ uint32_t e2m1_index(float a) {
-  return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-         (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-         (uint32_t)(a > 5.0f);
+// The block scale 2^e as an fp32 value, e in [-127, 127] (2^-127 is denormal).
+__device__ __forceinline__ float exp2_scale(int e) {
+  return e > -127 ? __uint_as_float((uint32_t)(e + 127) << 23) : __uint_as_float(0x00400000u);
 }
 
-// 4-bit code of v under block exponent e: sign bit copied from v.
-__device__ __forceinline__ uint32_t e2m1_code(float v, int e) {
-  const uint32_t bits = __float_as_uint(v);
-  const float a = ldexpf(__uint_as_float(bits & 0x7FFFFFFFu), -e);
-  return e2m1_index(a) | ((bits >> 31) << 3);
+// E2M1 codes of v0 and v1 under block scale sc = 2^e, as one byte (v0 in the
+// low nibble) written into byte SEL of old.  gfx950's v_cvt_scalef32_pk_fp4_f32
+// rounds |v| / sc to the nearest E2M1 magnitude, ties to the even mantissa,
+// and keeps the sign bit (so -0 and negatives that round to zero give 0x8):
+// the rule above.  An exhaustive check on MI355X found no difference from the
+// rule for any fp32 magnitude up to 8 * 2^e at e = -127, -126, -100, -20, -3,
+// 0, 5, 20, 126, 127, both signs.
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_pack2(uint32_t old, float v0, float v1, float sc) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, v0, v1, sc, SEL);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }

@@ -81,6 +81,9 @@ __device__ __forceinline__ void wait_vm() {
 }
 __device__ __forceinline__ void stage_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+#ifndef MOE_LDS_PAIRED
+#define MOE_LDS_PAIRED 1        // 1: per-XCD weight blocks, tile-major inside an XCD
+#endif
 #ifndef MOE_LDS_BLOCKS
 #define MOE_LDS_BLOCKS 2        // workgroups per CU the launch bound asks for
 #endif
@@ -105,9 +108,18 @@ __global__ void __launch_bounds__(256, MOE_LDS_BLOCKS) gemm_lds_kernel(
   const int K = G1 ? H : I;
   const int nwb = G1 ? I / 128 : H / 256;
   const int G = gridDim.x;
-  const int Lid = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-  const int wb = Lid / max_tiles;
-  const int ti = Lid - wb * max_tiles;
+  int wb, ti;
+  if (MOE_LDS_PAIRED && nwb % 8 == 0) {
+    // XCD x owns weight blocks [x*q, x*q+q); its workgroups run tile-major
+    // over them, so the q workgroups of a tile share its token lines in L2.
+    const int q = nwb >> 3, j = blockIdx.x >> 3;
+    ti = j / q;
+    wb = (blockIdx.x & 7) * q + (j - ti * q);
+  } else {
+    const int Lid = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    wb = Lid / max_tiles;
+    ti = Lid - wb * max_tiles;
+  }
   if (wb >= nwb || ti >= *num_tiles) return;
   const int2 tile = tiles[ti];
   const int e = tile.x, t0 = tile.y;

@@ -40,9 +40,15 @@ __device__ __forceinline__ void quantize_group(const void* __restrict__ src, int
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = max(amax, __float_as_uint(v[i]) & 0x7FFFFFFFu);
   const int e = mx_scale_exp(amax);
-  uint32_t packed[4] = {0, 0, 0, 0};
+  const float sc = exp2_scale(e);
+  uint32_t packed[4];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) packed[i >> 3] |= e2m1_code(v[i], e) << (4 * (i & 7));
+  for (int q = 0; q < 4; ++q) {
+    uint32_t w = e2m1_pack2<0>(0u, v[8 * q], v[8 * q + 1], sc);
+    w = e2m1_pack2<1>(w, v[8 * q + 2], v[8 * q + 3], sc);
+    w = e2m1_pack2<2>(w, v[8 * q + 4], v[8 * q + 5], sc);
+    packed[q] = e2m1_pack2<3>(w, v[8 * q + 6], v[8 * q + 7], sc);
+  }
   reinterpret_cast<uint4*>(codes)[g] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
   scales[g] = (uint8_t)(e + 127);
 }
