@@ -43,13 +43,14 @@
 
 namespace moe {
 
-template <int NT>
+// One stage of the ring for WAVES waves (one weight unit each) and NT*16 token rows.
+template <int NT, int WAVES>
 struct LdsStage {
   static constexpr int ROWS = NT * 16;
-  static constexpr int W_CODES = 0;                      // 4 units x 4 KiB
-  static constexpr int W_SCALES = 4 * kStepCodeBytes;    // 4 units x 256 B
-  static constexpr int T_CODES = W_SCALES + 4 * kStepScaleBytes;  // ROWS x 64 B
-  static constexpr int T_SCALES = T_CODES + ROWS * 64;   // ROWS x 4 B
+  static constexpr int W_CODES = 0;                          // WAVES units x 4 KiB
+  static constexpr int W_SCALES = WAVES * kStepCodeBytes;    // WAVES units x 256 B
+  static constexpr int T_CODES = W_SCALES + WAVES * kStepScaleBytes;  // ROWS x 64 B
+  static constexpr int T_SCALES = T_CODES + ROWS * 64;       // ROWS x 4 B
   static constexpr int BYTES = T_SCALES + ROWS * 4;
 };
 
@@ -89,24 +90,29 @@ __device__ __forceinline__ void stage_barrier() { asm volatile("s_waitcnt lgkmcn
 #endif
 
 // WNT: weight DMA with the non-temporal hint (each weight byte is read by one
-// tile only).
-template <bool G1, int NT, int P, bool WNT>
-__global__ void __launch_bounds__(256, MOE_LDS_BLOCKS) gemm_lds_kernel(
+// tile only).  WB: weight blocks per workgroup (4*WB waves, one unit each), so
+// each staged token piece feeds WB weight blocks.
+template <bool G1, int NT, int P, bool WNT, int WB>
+__global__ void __launch_bounds__(256 * WB, WB == 1 ? MOE_LDS_BLOCKS : 1) gemm_lds_kernel(
     const uint8_t* __restrict__ wc, const uint8_t* __restrict__ wsc, const uint8_t* __restrict__ act,
     const uint8_t* __restrict__ act_sf, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows,
     const int2* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int max_tiles, int H, int I, int k,
     uint8_t* __restrict__ hq, uint8_t* __restrict__ hsf, float* __restrict__ acc_out, uint16_t* __restrict__ y) {
-  using L = LdsStage<NT>;
+  constexpr int WAVES = 4 * WB;
+  using L = LdsStage<NT, WAVES>;
   constexpr int ROWS = L::ROWS;
-  constexpr int TOK_INSTS = NT / 4;                    // token-code DMAs per wave per stage
-  constexpr int SC_LANES = ROWS / 4;                   // token-scale dwords per wave per stage
+  constexpr int TOK_INSTS = NT / WAVES;                // token-code DMAs (1 KiB each) per wave per stage
+  constexpr int SC_LANES = ROWS / WAVES;               // token-scale dwords per wave per stage
   constexpr int DMA_PER_STAGE = 4 + 1 + TOK_INSTS + 1;
-  static_assert(NT % 4 == 0 && SC_LANES <= 64, "tile rows");
+  // The waves' token DMAs tile the stage's token region exactly: ROWS rows x
+  // 64 B of codes, ROWS x 4 B of scales.
+  static_assert(TOK_INSTS >= 1 && TOK_INSTS * WAVES * 1024 == ROWS * 64, "token code DMAs");
+  static_assert(SC_LANES * WAVES == ROWS && SC_LANES <= 64, "token scale DMAs");
   static_assert(DMA_PER_STAGE * (P - 2) <= 63, "vmcnt range");
 
   const int K = G1 ? H : I;
-  const int nwb = G1 ? I / 128 : H / 256;
+  const int nwb = (G1 ? I / 128 : H / 256) / WB;      // weight-block groups per expert
   const int G = gridDim.x;
   int wb, ti;
   if (MOE_LDS_PAIRED && nwb % 8 == 0) {
@@ -127,7 +133,7 @@ __global__ void __launch_bounds__(256, MOE_LDS_BLOCKS) gemm_lds_kernel(
   const int row0 = offsets[e] + t0;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int unit = wb * 4 + wave;
+  const int unit = wb * WAVES + wave;
   const int S = K / kStepK;
   const int row_bytes = K / 2, sc_row = K / 32;
 
@@ -213,22 +219,22 @@ __global__ void __launch_bounds__(256, MOE_LDS_BLOCKS) gemm_lds_kernel(
 
 constexpr int kLdsNT = 8;     // token tiles of 16 rows per wave: 128-row work tiles
 
-template <bool G1, bool WNT>
-static hipError_t launch_prefill_t(const uint8_t* wc, const uint8_t* wsc, const uint8_t* act,
-                                   const uint8_t* act_sf, const int32_t* counts, const int32_t* offsets,
-                                   const int32_t* sorted_rows, const int2* tiles, const int32_t* num_tiles,
-                                   int max_tiles, int H, int I, int k, uint8_t* hq, uint8_t* hsf, float* acc_out,
-                                   uint16_t* y, hipStream_t stream) {
+template <bool G1, bool WNT, int WB>
+static hipError_t launch_prefill_wb(const uint8_t* wc, const uint8_t* wsc, const uint8_t* act,
+                                    const uint8_t* act_sf, const int32_t* counts, const int32_t* offsets,
+                                    const int32_t* sorted_rows, const int2* tiles, const int32_t* num_tiles,
+                                    int max_tiles, int H, int I, int k, uint8_t* hq, uint8_t* hsf, float* acc_out,
+                                    uint16_t* y, hipStream_t stream) {
   constexpr int P = MOE_LDS_STAGES;
-  auto kern = gemm_lds_kernel<G1, kLdsNT, P, WNT>;
-  const size_t lds = (size_t)P * LdsStage<kLdsNT>::BYTES;
+  auto kern = gemm_lds_kernel<G1, kLdsNT, P, WNT, WB>;
+  const size_t lds = (size_t)P * LdsStage<kLdsNT, 4 * WB>::BYTES;
   if (lds > 65536) {
     hipError_t err = raise_lds_limit(reinterpret_cast<const void*>(kern), lds);
     if (err != hipSuccess) return err;
   }
-  const int nwb = G1 ? I / 128 : H / 256;
+  const int nwb = (G1 ? I / 128 : H / 256) / WB;
   const int64_t blocks = ((int64_t)max_tiles * nwb + 7) / 8 * 8;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), lds, stream, wc, wsc, act, act_sf, counts, offsets,
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256 * WB), lds, stream, wc, wsc, act, act_sf, counts, offsets,
                      sorted_rows, tiles, num_tiles, max_tiles, H, I, k, hq, hsf, acc_out, y);
   return hipGetLastError();
 }
@@ -237,20 +243,27 @@ int lds_tile_rows(int) { return kLdsNT * 16; }
 
 int lds_max_tiles(int R, int E, int tile_rows) { return (R + tile_rows - 1) / tile_rows + E; }
 
-// With mean rows per expert within one tile every weight block is read by a
-// single tile: it streams non-temporal.  Otherwise the tiles of an expert
-// share each weight block through L2 and the loads keep the default policy.
+// Mean rows per expert within one tile (the weight stream bounds the GEMM):
+// every weight block is read by a single tile, so it streams non-temporal, and
+// GEMM1 pairs two weight blocks per workgroup so each staged token piece feeds
+// both (half the token traffic; measured 6% faster GEMM1 at 96 rows per
+// expert).  More rows: the tiles of an expert share each weight block through
+// L2, loads keep the default policy, and single-block workgroups (two per CU,
+// each with its own barrier) keep the MFMAs busier.
 template <bool G1>
 static hipError_t launch_prefill(const uint8_t* wc, const uint8_t* wsc, const uint8_t* act, const uint8_t* act_sf,
                                  const int32_t* counts, const int32_t* offsets, const int32_t* sorted_rows,
                                  const int2* tiles, const int32_t* num_tiles, int max_tiles, int rows_hint, int H,
                                  int I, int k, uint8_t* hq, uint8_t* hsf, float* acc_out, uint16_t* y,
                                  hipStream_t stream) {
-  if (rows_hint <= kLdsNT * 16)
-    return launch_prefill_t<G1, true>(wc, wsc, act, act_sf, counts, offsets, sorted_rows, tiles, num_tiles, max_tiles,
-                                      H, I, k, hq, hsf, acc_out, y, stream);
-  return launch_prefill_t<G1, false>(wc, wsc, act, act_sf, counts, offsets, sorted_rows, tiles, num_tiles, max_tiles,
-                                     H, I, k, hq, hsf, acc_out, y, stream);
+#define MOE_PREFILL_ARGS wc, wsc, act, act_sf, counts, offsets, sorted_rows, tiles, num_tiles, max_tiles, H, I, k, \
+                         hq, hsf, acc_out, y, stream
+  const bool single = rows_hint <= kLdsNT * 16;
+  const int nwb = G1 ? I / 128 : H / 256;
+  if (single && G1 && nwb % 2 == 0) return launch_prefill_wb<G1, true, 2>(MOE_PREFILL_ARGS);
+  if (single) return launch_prefill_wb<G1, true, 1>(MOE_PREFILL_ARGS);
+  return launch_prefill_wb<G1, false, 1>(MOE_PREFILL_ARGS);
+#undef MOE_PREFILL_ARGS
 }
 
 hipError_t launch_gemm1_lds(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq, const uint8_t* xsf,
