@@ -23,8 +23,10 @@ constexpr int kMaxDevices = 64;
 constexpr int kMaxExperts = 512;
 constexpr int kMaxTopk = 16;
 constexpr int kRouteRows = 1024;
-constexpr int kStreamMaxRows = 16;  // mean routed rows per expert up to which the streaming GEMMs run
-constexpr int kFusedRouteMaxRows = 8192;  // routed rows up to which one block routes them all
+#ifndef MOE_STREAM_MAX_ROWS
+#define MOE_STREAM_MAX_ROWS 16   // mean routed rows per expert up to which the VGPR-streaming GEMMs run
+#endif
+constexpr int kStreamMaxRows = MOE_STREAM_MAX_ROWS;
 
 std::atomic<int> g_is_gfx950[kMaxDevices];  // 0 unknown, 1 yes, 2 no
 
@@ -231,7 +233,7 @@ int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t n
   const Prepared P = prepared_layout(cfg);
   const uint8_t* pw = static_cast<const uint8_t*>(prepared);
 
-  if ((stages & MOE_STAGE_QUANT) && (stages & MOE_STAGE_ROUTE) && R <= kFusedRouteMaxRows) {
+  if ((stages & MOE_STAGE_QUANT) && (stages & MOE_STAGE_ROUTE) && R <= moe::kPredispatchMaxRows) {
     // pre-dispatch in one launch: one block routes, the others quantize
     st = hip_status(moe::launch_predispatch(x, (int64_t)T * (H / 32), xq, xsf, topk_ids, R, E, counts, offsets,
                                             sorted_rows, pos, tile_rows, tiles, num_tiles, s));

@@ -17,8 +17,9 @@ hipError_t launch_route(const int32_t* ids, int R, int E, int32_t* hist, int32_t
                         int32_t* offsets, int32_t* sorted_rows, int32_t* pos, int tile_rows, int2* tiles,
                         int32_t* num_tiles, hipStream_t stream);
 
-// Stages S1a + S1b in one launch: block 0 routes all R rows (R small), the
-// other blocks quantize the bf16 tokens.
+// Stages S1a + S1b in one launch: block 0 routes all R <= kPredispatchMaxRows
+// rows, the other blocks quantize the bf16 tokens.
+constexpr int kPredispatchMaxRows = 8192;
 hipError_t launch_predispatch(const uint16_t* x, int64_t ngroups, uint8_t* xq, uint8_t* xsf, const int32_t* ids,
                               int R, int E, int32_t* counts, int32_t* offsets, int32_t* sorted_rows,
                               int32_t* pos, int tile_rows, int2* tiles, int32_t* num_tiles, hipStream_t stream);

@@ -4,16 +4,19 @@
 // that packs the tokens to E2M1 with group_size=32 and hands over the top-k ids
 // and weights).
 //
-// Block 0 routes all R rows by itself: an LDS histogram (integer atomics only
-// count), one block scan for counts/offsets (and the tile list), then the rows
-// in chunks of 1024 in order, each placed with the in-block stable ranks of
-// route_common.h while a running base per expert carries the chunks before it.
-// Blocks 1.. quantize one 32-element group of x per thread meanwhile.
+// Block 0 routes all R <= 8192 rows by itself: every thread reads its (up to 8)
+// ids once, then an LDS histogram (integer atomics only count), one block scan
+// for counts/offsets (and the tile list), then the rows in chunks of 1024 in
+// order, each placed with the in-block stable ranks of route_common.h while a
+// running base per expert carries the chunks before it.  Blocks 1.. quantize
+// one 32-element group of x per thread meanwhile.
 #include "launch.h"
 #include "quant_group.h"
 #include "route_common.h"
 
 namespace moe {
+
+constexpr int kPredispatchChunks = kPredispatchMaxRows / kRouteRows;
 
 __global__ void __launch_bounds__(kRouteRows) predispatch_kernel(
     const uint16_t* __restrict__ x, int64_t ngroups, uint8_t* __restrict__ xq, uint8_t* __restrict__ xsf,
@@ -30,13 +33,18 @@ __global__ void __launch_bounds__(kRouteRows) predispatch_kernel(
   int* base = smem;                        // [E] next free slot of expert e
   int* wcnt = smem + E;                    // [16][E]
   int* wave_tot = wcnt + kRouteWaves * E;  // [16]
+  int eid[kPredispatchChunks];
+#pragma unroll
+  for (int c = 0; c < kPredispatchChunks; ++c) {
+    const int r = c * kRouteRows + tid;
+    eid[c] = r < R ? ids[r] : -1;
+  }
   for (int i = tid; i < E; i += kRouteRows) base[i] = 0;
   for (int i = tid; i < kRouteWaves * E; i += kRouteRows) wcnt[i] = 0;
   __syncthreads();
-  for (int r = tid; r < R; r += kRouteRows) {
-    const int e = ids[r];
-    if (e >= 0 && e < E) atomicAdd(&base[e], 1);
-  }
+#pragma unroll
+  for (int c = 0; c < kPredispatchChunks; ++c)
+    if (eid[c] >= 0 && eid[c] < E) atomicAdd(&base[eid[c]], 1);
   __syncthreads();
   const int tot = tid < E ? base[tid] : 0;
   const int incl = block_inclusive_scan(tot, wave_tot);  // also orders the reads of base above
@@ -48,17 +56,20 @@ __global__ void __launch_bounds__(kRouteRows) predispatch_kernel(
   }
   if (tile_rows > 0) write_tiles(tot, E, tile_rows, wave_tot, tiles, num_tiles);
   __syncthreads();
-  for (int r0 = 0; r0 < R; r0 += kRouteRows) {
-    place_chunk(ids, R, E, nbits, r0, base, wcnt, sorted_rows, pos);
+#pragma unroll
+  for (int c = 0; c < kPredispatchChunks; ++c) {
+    const int r0 = c * kRouteRows;
+    if (r0 >= R) break;
+    place_chunk(eid[c], R, E, nbits, r0, base, wcnt, sorted_rows, pos);
     __syncthreads();
     // advance the running bases past this chunk and clear the per-wave counts
     for (int e = tid; e < E; e += kRouteRows) {
-      int c = 0;
+      int cnt = 0;
       for (int w = 0; w < kRouteWaves; ++w) {
-        c += wcnt[w * E + e];
+        cnt += wcnt[w * E + e];
         wcnt[w * E + e] = 0;
       }
-      base[e] += c;
+      base[e] += cnt;
     }
     __syncthreads();
   }

@@ -62,7 +62,8 @@ __global__ void __launch_bounds__(kRouteRows) route_scatter_kernel(
   }
   if (b == 0 && tile_rows > 0) write_tiles(tot, E, tile_rows, wave_tot, tiles, num_tiles);
   __syncthreads();
-  place_chunk(ids, R, E, nbits, b * kRouteRows, base, wcnt, sorted_rows, pos);
+  const int r = b * kRouteRows + tid;
+  place_chunk(r < R ? ids[r] : -1, R, E, nbits, b * kRouteRows, base, wcnt, sorted_rows, pos);
 }
 
 hipError_t launch_route(const int32_t* ids, int R, int E, int32_t* hist, int32_t* counts,

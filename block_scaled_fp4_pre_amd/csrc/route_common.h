@@ -35,18 +35,17 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int* wave_tot) {
   return r;
 }
 
-// Places the rows [r0, r0 + 1024) of a chunk: row r of expert e goes to
-// base[e] + (rows of e before r in the chunk).  The rank inside a wave comes
-// from a 64-lane match (one ballot per id bit), across waves from per-wave
-// counts in wcnt[16][E], which must be zero on entry and are left holding the
-// chunk's per-wave counts.  Called by all 1024 threads.
-__device__ __forceinline__ void place_chunk(const int32_t* __restrict__ ids, int R, int E, int nbits, int r0,
-                                            const int* base, int* wcnt, int32_t* __restrict__ sorted_rows,
-                                            int32_t* __restrict__ pos) {
+// Places row r = r0 + threadIdx.x of a chunk of 1024 rows, whose expert id e
+// the caller read (-1 past the end): row r of expert e goes to base[e] + (rows
+// of e before r in the chunk).  The rank inside a wave comes from a 64-lane
+// match (one ballot per id bit), across waves from per-wave counts in
+// wcnt[16][E], which must be zero on entry and are left holding the chunk's
+// per-wave counts.  Called by all 1024 threads.
+__device__ __forceinline__ void place_chunk(int e, int R, int E, int nbits, int r0, const int* base, int* wcnt,
+                                            int32_t* __restrict__ sorted_rows, int32_t* __restrict__ pos) {
   const int tid = threadIdx.x;
   const int r = r0 + tid;
-  const int e = r < R ? ids[r] : -1;
-  const bool valid = e >= 0 && e < E;
+  const bool valid = r < R && e >= 0 && e < E;
   uint64_t match = __ballot(valid);
   for (int bit = 0; bit < nbits; ++bit) {
     const uint64_t m1 = __ballot(valid && ((e >> bit) & 1));

@@ -8,6 +8,8 @@ every intermediate, at shapes the oracle finishes in seconds:
   h256_i128   2 / 1 K steps: the one-item-per-workgroup kernel
   e16         about 125 rows per expert: weights loaded non-temporal (each
               expert's mean fits one tile), some experts spill into a second
+  t600_e8     about 150 rows per expert: several tiles per expert, default
+              load policy
 
 Zipf routing gives hot experts with several full 128-row tiles and a ragged
 last tile, and cold experts with a single short tile."""
@@ -28,6 +30,7 @@ SHAPES = [
     synth.LayerConfig(101, "prefill_h2048_i1024_e8_k2_t1500", 1500, 2048, 1024, 8, 2, "zipf", 101, 1.1),
     synth.LayerConfig(102, "prefill_h256_i128_e8_k2_t2000", 2000, 256, 128, 8, 2, "uniform", 102),
     synth.LayerConfig(103, "prefill_h512_i512_e16_k2_t1000", 1000, 512, 512, 16, 2, "uniform", 103),
+    synth.LayerConfig(104, "prefill_h512_i512_e8_k2_t600", 600, 512, 512, 8, 2, "uniform", 104),
 ]
 
 
