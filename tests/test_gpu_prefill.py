@@ -2,10 +2,11 @@
 with both operands staged in LDS), compared with the oracle on every token and
 every intermediate, at shapes the oracle finishes in seconds:
 
-  h512_i512   4 K steps per GEMM: the persistent kernel with the generic item
-              order (weight blocks not a multiple of the 8 XCDs)
-  h2048_i1024 16 / 8 K steps: the persistent kernel with the per-XCD paired order
-  h256_i128   2 / 1 K steps: the one-item-per-workgroup kernel
+  h512_i512   4 K steps per GEMM; the generic work order (weight blocks per
+              expert not a multiple of the 8 XCDs)
+  h2048_i1024 16 / 8 K steps; the per-XCD paired work order, GEMM1 with two
+              weight blocks per workgroup where rows fit one tile
+  h256_i128   2 / 1 K steps: fewer K steps than ring stages
   e16         about 125 rows per expert: weights loaded non-temporal (each
               expert's mean fits one tile), some experts spill into a second
   t600_e8     about 150 rows per expert: several tiles per expert, default
