@@ -4,11 +4,11 @@ every intermediate, at shapes the oracle finishes in seconds:
 
   h512_i512   4 K steps per GEMM; the generic work order (weight blocks per
               expert not a multiple of the 8 XCDs)
-  h2048_i1024 16 / 8 K steps; the per-XCD paired work order, GEMM1 with two
-              weight blocks per workgroup where rows fit one tile
+  h2048_i1024 16 / 8 K steps; the per-XCD paired work order
   h256_i128   2 / 1 K steps: fewer K steps than ring stages
-  e16         about 125 rows per expert: weights loaded non-temporal (each
-              expert's mean fits one tile), some experts spill into a second
+  e16         about 125 rows per expert: each expert's mean fits one tile, so
+              weights load non-temporal and GEMM1 takes two weight blocks per
+              workgroup; some experts spill into a second tile
   t600_e8     about 150 rows per expert: several tiles per expert, default
               load policy
 
