@@ -10,8 +10,9 @@
 //   kernel 1 (one block per 1024 rows): per-block expert histogram.  Integer
 //     LDS atomics only count, so the result does not depend on their order.
 //   kernel 2 (same blocks): every block sums the histograms of all blocks and
-//     of the blocks before it, scans the totals over experts, and places its
-//     rows at offsets[e] + (rows of e in earlier blocks) + (rank in block).
+//     of the blocks before it (several threads per expert, then an LDS
+//     reduction), scans the totals over experts, and places its rows at
+//     offsets[e] + (rows of e in earlier blocks) + (rank in block).
 #include "launch.h"
 #include "route_common.h"
 
@@ -37,20 +38,37 @@ __global__ void __launch_bounds__(kRouteRows) route_scatter_kernel(
     int32_t* __restrict__ sorted_rows, int32_t* __restrict__ pos, int tile_rows, int2* __restrict__ tiles,
     int32_t* __restrict__ num_tiles) {
   extern __shared__ int smem[];
+  const int Q = kRouteRows / E;            // threads per expert summing the histograms (E <= 512)
   int* base = smem;                        // [E]   first slot of this block's rows of e
   int* wcnt = smem + E;                    // [16][E] rows of e in each wave of this block
   int* wave_tot = wcnt + kRouteWaves * E;  // [16]
+  int* part_tot = wave_tot + kRouteWaves;  // [Q][E] partial sums over every Q-th block
+  int* part_bef = part_tot + Q * E;        // [Q][E] the same over the blocks before this one
   const int tid = threadIdx.x, b = blockIdx.x;
 
-  int tot = 0, before = 0;
-  if (tid < E) {
-    for (int bb = 0; bb < nblocks; ++bb) {
-      const int h = hist[(size_t)bb * E + tid];
-      tot += h;
-      if (bb < b) before += h;
+  // Thread (q, e) sums the counts of expert e in blocks q, q+Q, ...: Q
+  // independent load chains instead of one chain over every block.
+  if (tid < Q * E) {
+    const int e = tid % E, q = tid / E;
+    int t = 0, bf = 0;
+#pragma unroll 4
+    for (int bb = q; bb < nblocks; bb += Q) {
+      const int h = hist[(size_t)bb * E + e];
+      t += h;
+      bf += bb < b ? h : 0;
     }
+    part_tot[q * E + e] = t;
+    part_bef[q * E + e] = bf;
   }
   for (int i = tid; i < kRouteWaves * E; i += kRouteRows) wcnt[i] = 0;
+  __syncthreads();
+  int tot = 0, before = 0;
+  if (tid < E) {
+    for (int q = 0; q < Q; ++q) {
+      tot += part_tot[q * E + tid];
+      before += part_bef[q * E + tid];
+    }
+  }
   const int incl = block_inclusive_scan(tot, wave_tot);
   if (tid < E) {
     base[tid] = incl - tot + before;
@@ -75,7 +93,7 @@ hipError_t launch_route(const int32_t* ids, int R, int E, int32_t* hist, int32_t
                      R, E, hist);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const size_t lds = (size_t)(E + kRouteWaves * E + kRouteWaves) * sizeof(int);
+  const size_t lds = (size_t)(E + kRouteWaves * E + kRouteWaves + 2 * (kRouteRows / E) * E) * sizeof(int);
   hipLaunchKernelGGL(route_scatter_kernel, dim3(nblocks), dim3(kRouteRows), lds, stream, ids, R, E,
                      id_bits(E), nblocks, hist, counts, offsets, sorted_rows, pos, tile_rows, tiles, num_tiles);
   return hipGetLastError();
