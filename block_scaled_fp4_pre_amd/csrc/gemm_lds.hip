@@ -60,19 +60,21 @@ __device__ __forceinline__ int tok_pos(int n, int c) { return c ^ ((n >> 2) & 3)
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 // Direct global -> LDS copies: lane l's 16 (4) bytes land at LDS byte address
-// lds + 16*l (4*l).  M0 carries the wave's LDS address.
+// lds + 16*l (4*l).  M0 carries the wave's LDS address; a DMA that reads M0
+// right after a scalar write of it needs one wait state (the s_nop), which the
+// compiler cannot insert inside an asm statement.
 __device__ __forceinline__ void dma16_asm(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4_asm(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
 }
 // The same with the non-temporal hint (data read once).
 __device__ __forceinline__ void dma16_nt_asm(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(lds) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(lds) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4_nt_asm(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off nt" ::"v"(g), "s"(lds) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off nt" ::"v"(g), "s"(lds) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 

@@ -1,7 +1,8 @@
 """CPU check of the generated gfx950 code of the LDS-staged prefill GEMMs.
 
 Their direct-to-LDS loads are issued from inline assembly, with M0 set in the
-same statement and completion tracked by explicit in-order vmcnt waits.  That
+same statement (followed by the one wait state a DMA that reads a freshly
+written M0 needs) and completion tracked by explicit in-order vmcnt waits.  That
 is only sound while the compiler's own code neither uses M0 nor waits on
 vmcnt inside these kernels (a compiler wait would count only the loads it
 knows of and drain the ring), and while nothing spills to scratch.  The test
@@ -82,8 +83,10 @@ def test_m0_only_in_dma_statements(kernels):
         assert not [t for t in compiler if re.search(r"\bm0\b", t)], name
         for b in blocks:
             if any(re.search(r"\bm0\b", t) for t in b):
-                assert len(b) == 2 and b[0].startswith("s_mov_b32 m0,"), (name, b)
-                assert b[1].startswith("global_load_lds_dword"), (name, b)
+                # M0 written, one wait state, then the DMA that reads it
+                assert len(b) == 3 and b[0].startswith("s_mov_b32 m0,"), (name, b)
+                assert b[1].startswith("s_nop"), (name, b)
+                assert b[2].startswith("global_load_lds_dword"), (name, b)
 
 
 def test_no_compiler_vmcnt_waits_once_the_ring_runs(kernels):
