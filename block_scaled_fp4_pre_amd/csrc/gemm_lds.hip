@@ -54,27 +54,34 @@ struct LdsStage {
   static constexpr int BYTES = T_SCALES + ROWS * 4;
 };
 
+template <bool B>
+struct BoolConst {
+  static constexpr bool value = B;
+};
+
 // Position of 16-byte piece c (0..3) of staged token row n.
 __device__ __forceinline__ int tok_pos(int n, int c) { return c ^ ((n >> 2) & 3); }
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 // Direct global -> LDS copies: lane l's 16 (4) bytes land at LDS byte address
-// lds + 16*l (4*l).  M0 carries the wave's LDS address; a DMA that reads M0
+// lds + 16*l (4*l).  M0 carries the wave's LDS address (uniform; readfirstlane
+// keeps it in a scalar register wherever the compiler's divergence analysis
+// loses track of that).  A DMA that reads M0
 // right after a scalar write of it needs one wait state (the s_nop), which the
 // compiler cannot insert inside an asm statement.
 __device__ __forceinline__ void dma16_asm(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4_asm(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
 }
 // The same with the non-temporal hint (data read once).
 __device__ __forceinline__ void dma16_nt_asm(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(lds) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4_nt_asm(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off nt" ::"v"(g), "s"(lds) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off nt" ::"v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -86,6 +93,9 @@ __device__ __forceinline__ void stage_barrier() { asm volatile("s_waitcnt lgkmcn
 
 #ifndef MOE_LDS_PAIRED
 #define MOE_LDS_PAIRED 1        // 1: per-XCD weight blocks, tile-major inside an XCD
+#endif
+#ifndef MOE_LDS_INTERLEAVE
+#define MOE_LDS_INTERLEAVE 1    // 1: a stage's DMAs are issued between the MFMA groups of the step
 #endif
 #ifndef MOE_LDS_BLOCKS
 #define MOE_LDS_BLOCKS 2        // workgroups per CU the launch bound asks for
@@ -159,23 +169,32 @@ __global__ void __launch_bounds__(256 * WB, WB == 1 ? MOE_LDS_BLOCKS : 1) gemm_l
   }
   const uint8_t* tssrc = act_sf + (size_t)src_row(wave * SC_LANES + min(lane, SC_LANES - 1)) * sc_row;
 
-  auto issue = [&](int s) {
+  // DMA i (0 .. DMA_PER_STAGE-1) of stage s: the token scales (the one DMA
+  // that not every lane takes part in, first, so that no MFMA of the step is
+  // issued before that branch), the unit's four 1 KiB pieces of weight codes,
+  // its weight scales, the token-code pieces.
+  auto issue_one = [&](int s, int i) {
     const uint32_t sb = lbase + (uint32_t)((s % P) * L::BYTES);
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
+    if (i == 0) {
+      if (lane < SC_LANES) dma4_asm(tssrc + s * 4, sb + L::T_SCALES + wave * SC_LANES * 4);
+    } else if (i <= 4) {
+      const int rb = i - 1;
       if constexpr (WNT)
         dma16_nt_asm(wsrc + (size_t)s * kStepCodeBytes + rb * 1024, sb + L::W_CODES + wave * kStepCodeBytes + rb * 1024);
       else
         dma16_asm(wsrc + (size_t)s * kStepCodeBytes + rb * 1024, sb + L::W_CODES + wave * kStepCodeBytes + rb * 1024);
+    } else if (i == 5) {
+      if constexpr (WNT)
+        dma4_nt_asm(ssrc + (size_t)s * kStepScaleBytes, sb + L::W_SCALES + wave * kStepScaleBytes);
+      else
+        dma4_asm(ssrc + (size_t)s * kStepScaleBytes, sb + L::W_SCALES + wave * kStepScaleBytes);
+    } else {
+      dma16_asm(tsrc[i - 6] + s * 64, sb + L::T_CODES + (wave * TOK_INSTS + i - 6) * 1024);
     }
-    if constexpr (WNT)
-      dma4_nt_asm(ssrc + (size_t)s * kStepScaleBytes, sb + L::W_SCALES + wave * kStepScaleBytes);
-    else
-      dma4_asm(ssrc + (size_t)s * kStepScaleBytes, sb + L::W_SCALES + wave * kStepScaleBytes);
+  };
+  auto issue = [&](int s) {
 #pragma unroll
-    for (int i = 0; i < TOK_INSTS; ++i)
-      dma16_asm(tsrc[i] + s * 64, sb + L::T_CODES + (wave * TOK_INSTS + i) * 1024);
-    if (lane < SC_LANES) dma4_asm(tssrc + s * 4, sb + L::T_SCALES + wave * SC_LANES * 4);
+    for (int i = 0; i < DMA_PER_STAGE; ++i) issue_one(s, i);
   };
 
   for (int s = 0; s < P - 1 && s < S; ++s) issue(s);
@@ -183,16 +202,19 @@ __global__ void __launch_bounds__(256 * WB, WB == 1 ? MOE_LDS_BLOCKS : 1) gemm_l
   v4f acc[NT][4];
   zero_acc<NT>(acc);
   const int tok_lane = lane & 15, kb = lane >> 4;
-  for (int s = 0; s < S; ++s) {
-    if (s + P - 2 < S)
-      wait_vm<DMA_PER_STAGE * (P - 2)>();   // stage s landed; the P-2 later ones may be in flight
-    else
-      wait_vm<0>();
-    stage_barrier();
-    if (s + P - 1 < S) issue(s + P - 1);    // into the buffer of stage s-1, read by nobody now
-
+  // One K step from the stage in LDS; WITH_DMA also issues the DMAs of stage
+  // s+P-1.  With MOE_LDS_INTERLEAVE they go between the MFMA groups, one group
+  // of four MFMAs per 16 token rows, with scheduling fences so the compiler
+  // keeps them there: a wave never sits on a full memory queue with none of
+  // its MFMAs issued.  The operand reads come first, all of them.
+  auto step = [&](int s, auto with_dma) {
+    constexpr bool WITH_DMA = decltype(with_dma)::value;
+#if !MOE_LDS_INTERLEAVE
+    if constexpr (WITH_DMA) issue(s + P - 1);
+#endif
     const uint8_t* st = lds + (s % P) * L::BYTES;
-    uint4 a[4];
+    uint4 a[4], b[NT];
+    int sbv[NT];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
       a[rb] = *reinterpret_cast<const uint4*>(st + L::W_CODES + wave * kStepCodeBytes + rb * 1024 + lane * 16);
@@ -200,13 +222,43 @@ __global__ void __launch_bounds__(256 * WB, WB == 1 ? MOE_LDS_BLOCKS : 1) gemm_l
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int n = nt * 16 + tok_lane;
-      const uint4 b = *reinterpret_cast<const uint4*>(st + L::T_CODES + n * 64 + tok_pos(n, kb) * 16);
-      const int sb = (int)(*reinterpret_cast<const uint32_t*>(st + L::T_SCALES + n * 4) >> (8 * kb));
-      acc[nt][0] = mfma_fp4<0, 0>(a[0], b, acc[nt][0], sa, sb);
-      acc[nt][1] = mfma_fp4<1, 0>(a[1], b, acc[nt][1], sa, sb);
-      acc[nt][2] = mfma_fp4<2, 0>(a[2], b, acc[nt][2], sa, sb);
-      acc[nt][3] = mfma_fp4<3, 0>(a[3], b, acc[nt][3], sa, sb);
+      b[nt] = *reinterpret_cast<const uint4*>(st + L::T_CODES + n * 64 + tok_pos(n, kb) * 16);
+      sbv[nt] = (int)(*reinterpret_cast<const uint32_t*>(st + L::T_SCALES + n * 4) >> (8 * kb));
     }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#if MOE_LDS_INTERLEAVE
+      if constexpr (WITH_DMA) {
+#pragma unroll
+        for (int i = 0; i < DMA_PER_STAGE; ++i)
+          if (i * NT / DMA_PER_STAGE == nt) issue_one(s + P - 1, i);
+      }
+#endif
+      acc[nt][0] = mfma_fp4<0, 0>(a[0], b[nt], acc[nt][0], sa, sbv[nt]);
+      acc[nt][1] = mfma_fp4<1, 0>(a[1], b[nt], acc[nt][1], sa, sbv[nt]);
+      acc[nt][2] = mfma_fp4<2, 0>(a[2], b[nt], acc[nt][2], sa, sbv[nt]);
+      acc[nt][3] = mfma_fp4<3, 0>(a[3], b[nt], acc[nt][3], sa, sbv[nt]);
+#if MOE_LDS_INTERLEAVE
+      __builtin_amdgcn_sched_barrier(0);
+#endif
+    }
+  };
+  // Before step s a wave waits until only the DMAs of the P-2 stages after s
+  // that it issued are in flight; the barrier then makes stage s whole and
+  // frees the buffer of stage s-1, into which stage s+P-1 goes.
+  int s = 0;
+  for (; s + P - 1 < S; ++s) {
+    wait_vm<DMA_PER_STAGE * (P - 2)>();
+    stage_barrier();
+    step(s, BoolConst<true>{});
+  }
+  for (; s < S; ++s) {                      // the last P-1 steps issue nothing
+    if (s + P - 2 < S)
+      wait_vm<DMA_PER_STAGE * (P - 2)>();
+    else
+      wait_vm<0>();
+    stage_barrier();
+    step(s, BoolConst<false>{});
   }
 
   if constexpr (G1)
