@@ -11,9 +11,11 @@
 // slices).  The pages' gate/up interleave is tied to their MMA layout; here the
 // pairing is by MFMA block instead (tiles.h).
 //
-// Grid: one workgroup of 4 waves per (expert, 128*upw inter columns); wave w
-// owns upw consecutive units of 32 columns (64 weight rows each), whose tiles
-// are contiguous, and streams them as one sequence of K steps.  A workgroup whose
+// Grid: one workgroup of 4 waves per (expert, 128*upw inter columns), i.e. upw
+// groups of 4 units of 32 columns (64 weight rows each); wave w owns unit w of
+// each group.  In the tile order of tiles.h those units' chunks follow each
+// other at one fixed stride, so the wave streams them as one sequence of K
+// steps, and the 4 waves read one contiguous 16 KiB per step.  A workgroup whose
 // expert has no rows exits at once.  Per pass it takes up to NT*16 of the
 // expert's rows: their quantized tokens are gathered into LDS (B operand) by
 // direct-to-LDS loads while the wave's weight ring (gemm_common.h) fills;
@@ -52,9 +54,9 @@ __global__ void __launch_bounds__(256, 2) gemm1_swiglu_kernel(
   const int base = offsets[e];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps the buffer resources in SGPRs
-  const int u0 = (g * 4 + wave) * upw;  // first of this wave's upw consecutive units
+  const int u0 = g * 4 * upw + wave;   // wave w owns unit w of each of the workgroup's upw unit groups
   const int S = H / kStepK;
-  const int total_steps = upw * S;       // the units' tiles are contiguous: one stream
+  const int total_steps = upw * S;       // the wave's upw units: one stream at stride kUnitStepStride
   const int row_bytes = H / 2, sc_bytes = H / 32;
 
   // Rows per pass: 16 for one token tile; MOE_STREAM_ROWS2 (<= 32) for two.  A
@@ -67,9 +69,9 @@ __global__ void __launch_bounds__(256, 2) gemm1_swiglu_kernel(
   uint8_t* lds_scales = lds + ROWS * row_bytes;           // [ROWS][sc_bytes]
 
   const __amdgpu_buffer_rsrc_t wr =
-      make_rsrc(w1c + w1_code_offset(e, u0, 0, H, I), (uint32_t)total_steps * kStepCodeBytes);
+      make_rsrc(w1c + w1_code_offset(e, u0, 0, H, I), (uint32_t)(total_steps - 1) * kUnitStepStride + kStepCodeBytes);
   const __amdgpu_buffer_rsrc_t sr =
-      make_rsrc(w1s + w1_scale_offset(e, u0, 0, H, I), (uint32_t)total_steps * kStepScaleBytes);
+      make_rsrc(w1s + w1_scale_offset(e, u0, 0, H, I), (uint32_t)(total_steps - 1) * kUnitScaleStride + kStepScaleBytes);
   const int voff = lane * 16, svoff = lane * 4;
   const int tok_lane = lane & 15, kb = lane >> 4;
 
@@ -80,8 +82,8 @@ __global__ void __launch_bounds__(256, 2) gemm1_swiglu_kernel(
 #pragma unroll
     for (int d = 0; d < D; ++d) {
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) a[d][rb] = buf_load16(wr, voff + rb * 1024, d * kStepCodeBytes);
-      sa[d] = buf_load4(sr, svoff, d * kStepScaleBytes);
+      for (int rb = 0; rb < 4; ++rb) a[d][rb] = buf_load16(wr, voff + rb * 1024, d * kUnitStepStride);
+      sa[d] = buf_load4(sr, svoff, d * kUnitScaleStride);
     }
     // token of each tile row: lane n < nrows holds it, broadcast by shuffle
     const int my_tok = lane < nrows ? sorted_rows[base + t0 + lane] / k : 0;
@@ -116,13 +118,13 @@ __global__ void __launch_bounds__(256, 2) gemm1_swiglu_kernel(
         }
         const int jn = j0 + d + D;
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) a[d][rb] = buf_load16(wr, voff + rb * 1024, jn * kStepCodeBytes);
-        sa[d] = buf_load4(sr, svoff, jn * kStepScaleBytes);
+        for (int rb = 0; rb < 4; ++rb) a[d][rb] = buf_load16(wr, voff + rb * 1024, jn * kUnitStepStride);
+        sa[d] = buf_load4(sr, svoff, jn * kUnitScaleStride);
       }
       if (s0 + D != S) continue;
 
       // Unit finished: SwiGLU + requant of its 32 columns for the tile's rows.
-      gemm1_epilogue<NT>(acc, u0 + j0 / S, base + t0, nrows, I, lane, hq, hsf, acc_out);
+      gemm1_epilogue<NT>(acc, u0 + kGroupUnits * (j0 / S), base + t0, nrows, I, lane, hq, hsf, acc_out);
       zero_acc<NT>(acc);
     }
   }

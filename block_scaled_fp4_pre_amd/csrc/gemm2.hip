@@ -6,9 +6,10 @@
 // (W4A4)": title (packed FP4 x FP4) and section B "NCU Speed-of-Light" (the
 // weight stream bounds the layer at ntok=512).
 //
-// Grid: one workgroup of 4 waves per (expert, 256*upw hidden rows); wave w owns
-// upw consecutive units of 64 hidden rows, whose tiles are contiguous, and
-// streams them as one sequence of K steps, writing y at each unit's end.  The expert's requantized rows are
+// Grid: one workgroup of 4 waves per (expert, 256*upw hidden rows), i.e. upw
+// groups of 4 units of 64 hidden rows; wave w owns unit w of each group and
+// streams them as one sequence of K steps (one fixed stride in the tile order
+// of tiles.h), writing y at each unit's end.  The expert's requantized rows are
 // already contiguous (sorted order), so the B tile is a plain copy into LDS by
 // direct-to-LDS loads; weights stream through the register ring of
 // gemm_common.h.
@@ -47,9 +48,9 @@ __global__ void __launch_bounds__(256, MOE_GEMM2_MIN_BLOCKS) gemm2_kernel(
   const int base = offsets[e];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps the buffer resources in SGPRs
-  const int v0 = (g * 4 + wave) * upw;  // first of this wave's upw consecutive units
+  const int v0 = g * 4 * upw + wave;   // wave w owns unit w of each of the workgroup's upw unit groups
   const int S = I / kStepK;
-  const int total_steps = upw * S;       // the units' tiles are contiguous: one stream
+  const int total_steps = upw * S;       // the wave's upw units: one stream at stride kUnitStepStride
   const int row_bytes = I / 2, sc_bytes = I / 32;
 
   // Rows per pass: 16 for one token tile; MOE_STREAM_ROWS2 (<= 32) for two.  A
@@ -62,9 +63,9 @@ __global__ void __launch_bounds__(256, MOE_GEMM2_MIN_BLOCKS) gemm2_kernel(
   uint8_t* lds_scales = lds + ROWS * row_bytes;
 
   const __amdgpu_buffer_rsrc_t wr =
-      make_rsrc(w2c + w2_code_offset(e, v0, 0, H, I), (uint32_t)total_steps * kStepCodeBytes);
+      make_rsrc(w2c + w2_code_offset(e, v0, 0, H, I), (uint32_t)(total_steps - 1) * kUnitStepStride + kStepCodeBytes);
   const __amdgpu_buffer_rsrc_t sr =
-      make_rsrc(w2s + w2_scale_offset(e, v0, 0, H, I), (uint32_t)total_steps * kStepScaleBytes);
+      make_rsrc(w2s + w2_scale_offset(e, v0, 0, H, I), (uint32_t)(total_steps - 1) * kUnitScaleStride + kStepScaleBytes);
   const int voff = lane * 16, svoff = lane * 4;
   const int tok_lane = lane & 15, kb = lane >> 4;
 
@@ -75,8 +76,8 @@ __global__ void __launch_bounds__(256, MOE_GEMM2_MIN_BLOCKS) gemm2_kernel(
 #pragma unroll
     for (int d = 0; d < D; ++d) {
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) a[d][rb] = buf_load16(wr, voff + rb * 1024, d * kStepCodeBytes);
-      sa[d] = buf_load4(sr, svoff, d * kStepScaleBytes);
+      for (int rb = 0; rb < 4; ++rb) a[d][rb] = buf_load16(wr, voff + rb * 1024, d * kUnitStepStride);
+      sa[d] = buf_load4(sr, svoff, d * kUnitScaleStride);
     }
     __syncthreads();
     const int row0 = base + t0;
@@ -110,12 +111,12 @@ __global__ void __launch_bounds__(256, MOE_GEMM2_MIN_BLOCKS) gemm2_kernel(
         }
         const int jn = j0 + d + D;
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) a[d][rb] = buf_load16(wr, voff + rb * 1024, jn * kStepCodeBytes);
-        sa[d] = buf_load4(sr, svoff, jn * kStepScaleBytes);
+        for (int rb = 0; rb < 4; ++rb) a[d][rb] = buf_load16(wr, voff + rb * 1024, jn * kUnitStepStride);
+        sa[d] = buf_load4(sr, svoff, jn * kUnitScaleStride);
       }
       if (s0 + D == S) {
         // unit finished: its 64 hidden columns of y for the tile's rows
-        gemm2_epilogue<NT>(acc, v0 + j0 / S, base + t0, nrows, H, lane, y);
+        gemm2_epilogue<NT>(acc, v0 + kGroupUnits * (j0 / S), base + t0, nrows, H, lane, y);
         zero_acc<NT>(acc);
       }
     }

@@ -12,6 +12,8 @@
 // tile list) x (weight block of 4 units = 256 weight rows).  Wave w of the
 // 4-wave workgroup owns unit w (64 weight rows, the 16-row MFMA A side) and
 // all NT*16 token rows (the B side), so each stage feeds 4*NT MFMAs per wave.
+// A weight block is one unit group of the tile order (tiles.h): its 4 units'
+// chunks of a step are one contiguous 16 KiB.
 //
 // Per stage each wave issues its share of the DMA: its unit's 4 KiB of weight
 // codes and 256 B of weight scales (already in MFMA operand order), a quarter
@@ -180,14 +182,14 @@ __global__ void __launch_bounds__(256 * WB, WB == 1 ? MOE_LDS_BLOCKS : 1) gemm_l
     } else if (i <= 4) {
       const int rb = i - 1;
       if constexpr (WNT)
-        dma16_nt_asm(wsrc + (size_t)s * kStepCodeBytes + rb * 1024, sb + L::W_CODES + wave * kStepCodeBytes + rb * 1024);
+        dma16_nt_asm(wsrc + (size_t)s * kUnitStepStride + rb * 1024, sb + L::W_CODES + wave * kStepCodeBytes + rb * 1024);
       else
-        dma16_asm(wsrc + (size_t)s * kStepCodeBytes + rb * 1024, sb + L::W_CODES + wave * kStepCodeBytes + rb * 1024);
+        dma16_asm(wsrc + (size_t)s * kUnitStepStride + rb * 1024, sb + L::W_CODES + wave * kStepCodeBytes + rb * 1024);
     } else if (i == 5) {
       if constexpr (WNT)
-        dma4_nt_asm(ssrc + (size_t)s * kStepScaleBytes, sb + L::W_SCALES + wave * kStepScaleBytes);
+        dma4_nt_asm(ssrc + (size_t)s * kUnitScaleStride, sb + L::W_SCALES + wave * kStepScaleBytes);
       else
-        dma4_asm(ssrc + (size_t)s * kStepScaleBytes, sb + L::W_SCALES + wave * kStepScaleBytes);
+        dma4_asm(ssrc + (size_t)s * kUnitScaleStride, sb + L::W_SCALES + wave * kStepScaleBytes);
     } else {
       dma16_asm(tsrc[i - 6] + s * 64, sb + L::T_CODES + (wave * TOK_INSTS + i - 6) * 1024);
     }

@@ -25,11 +25,13 @@ __global__ void __launch_bounds__(256) prepare_w1_codes(const uint8_t* __restric
   const int lane = (int)(q & 63);
   const int64_t r1 = q >> 6;
   const int rb = (int)(r1 & 3);
-  const int64_t r2 = r1 >> 2;
-  const int s = (int)(r2 % S);
-  const int64_t r3 = r2 / S;
-  const int u = (int)(r3 % U);
-  const int e = (int)(r3 / U);
+  const int64_t r2 = r1 >> 2;                 // chunk index (tiles.h unit_chunk)
+  const int u_lo = (int)(r2 % kGroupUnits);
+  const int64_t r3 = r2 / kGroupUnits;
+  const int s = (int)(r3 % S);
+  const int64_t r4 = r3 / S;
+  const int u = (int)(r4 % (U / kGroupUnits)) * kGroupUnits + u_lo;
+  const int e = (int)(r4 / (U / kGroupUnits));
   const int row = w1_row(u, rb, lane & 15, I);
   const uint8_t* p = src + ((size_t)e * 2 * I + row) * (H / 2) + s * 64 + (lane >> 4) * 16;
   reinterpret_cast<uint4*>(dst)[q] = *reinterpret_cast<const uint4*>(p);
@@ -42,11 +44,13 @@ __global__ void __launch_bounds__(256) prepare_w1_scales(const uint8_t* __restri
   if (q >= ndwords) return;
   const int S = H / kStepK, U = I / 32;
   const int lane = (int)(q & 63);
-  const int64_t r2 = q >> 6;
-  const int s = (int)(r2 % S);
-  const int64_t r3 = r2 / S;
-  const int u = (int)(r3 % U);
-  const int e = (int)(r3 / U);
+  const int64_t r2 = q >> 6;                  // chunk index (tiles.h unit_chunk)
+  const int u_lo = (int)(r2 % kGroupUnits);
+  const int64_t r3 = r2 / kGroupUnits;
+  const int s = (int)(r3 % S);
+  const int64_t r4 = r3 / S;
+  const int u = (int)(r4 % (U / kGroupUnits)) * kGroupUnits + u_lo;
+  const int e = (int)(r4 / (U / kGroupUnits));
   uint32_t word = 0;
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
@@ -64,11 +68,13 @@ __global__ void __launch_bounds__(256) prepare_w2_codes(const uint8_t* __restric
   const int lane = (int)(q & 63);
   const int64_t r1 = q >> 6;
   const int rb = (int)(r1 & 3);
-  const int64_t r2 = r1 >> 2;
-  const int s = (int)(r2 % S);
-  const int64_t r3 = r2 / S;
-  const int v = (int)(r3 % U);
-  const int e = (int)(r3 / U);
+  const int64_t r2 = r1 >> 2;                 // chunk index (tiles.h unit_chunk)
+  const int v_lo = (int)(r2 % kGroupUnits);
+  const int64_t r3 = r2 / kGroupUnits;
+  const int s = (int)(r3 % S);
+  const int64_t r4 = r3 / S;
+  const int v = (int)(r4 % (U / kGroupUnits)) * kGroupUnits + v_lo;
+  const int e = (int)(r4 / (U / kGroupUnits));
   const int row = kUnitRows * v + 16 * rb + (lane & 15);
   const uint8_t* p = src + ((size_t)e * H + row) * (I / 2) + s * 64 + (lane >> 4) * 16;
   reinterpret_cast<uint4*>(dst)[q] = *reinterpret_cast<const uint4*>(p);
@@ -80,11 +86,13 @@ __global__ void __launch_bounds__(256) prepare_w2_scales(const uint8_t* __restri
   if (q >= ndwords) return;
   const int S = I / kStepK, U = H / kUnitRows;
   const int lane = (int)(q & 63);
-  const int64_t r2 = q >> 6;
-  const int s = (int)(r2 % S);
-  const int64_t r3 = r2 / S;
-  const int v = (int)(r3 % U);
-  const int e = (int)(r3 / U);
+  const int64_t r2 = q >> 6;                  // chunk index (tiles.h unit_chunk)
+  const int v_lo = (int)(r2 % kGroupUnits);
+  const int64_t r3 = r2 / kGroupUnits;
+  const int s = (int)(r3 % S);
+  const int64_t r4 = r3 / S;
+  const int v = (int)(r4 % (U / kGroupUnits)) * kGroupUnits + v_lo;
+  const int e = (int)(r4 / (U / kGroupUnits));
   uint32_t word = 0;
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
