@@ -45,7 +45,7 @@ class moe_w4a4_cfg(ctypes.Structure):
 class moe_w4a4_ws_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "xq", "xsf", "counts", "offsets", "sorted_rows", "pos", "hist", "hq", "hsf", "y", "tiles",
-        "num_tiles", "total")]
+        "num_tiles", "xsf_planes", "total")]
 
 
 if not os.path.exists(LIB_PATH):

@@ -80,6 +80,7 @@ moe_w4a4_ws_layout ws_layout(const moe_w4a4_cfg* c) {
   L.y = off; off = align256(off + R * H * 2);
   L.tiles = off; off = align256(off + (R / 16 + E + 1) * 8);
   L.num_tiles = off; off = align256(off + 4);
+  L.xsf_planes = off; off = align256(off + R * H / 32);
   L.total = off;
   return L;
 }
@@ -227,6 +228,8 @@ int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t n
   int32_t* hist = reinterpret_cast<int32_t*>(ws + L.hist);
   int2* tiles = reinterpret_cast<int2*>(ws + L.tiles);
   int32_t* num_tiles = reinterpret_cast<int32_t*>(ws + L.num_tiles);
+  uint8_t* xsf_planes = ws + L.xsf_planes;
+  const int hrows = cfg->max_tokens * k;   // rows of one K-step plane (routed-row capacity)
   uint8_t* hq = ws + L.hq;
   uint8_t* hsf = ws + L.hsf;
   uint16_t* y = reinterpret_cast<uint16_t*>(ws + L.y);
@@ -250,18 +253,22 @@ int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t n
     }
   }
   if (stages & MOE_STAGE_GEMM1) {
-    st = hip_status(tiled ? moe::launch_gemm1_lds(pw + P.w1c, pw + P.w1s, xq, xsf, counts, offsets, sorted_rows,
-                                                  tiles, num_tiles, max_tiles, rows_hint, H, I, k, hq, hsf,
-                                                  gemm1_acc, s)
+    if (tiled) {
+      st = hip_status(moe::launch_sorted_scales(xsf, sorted_rows, offsets, E, R, H, k, hrows, xsf_planes, s));
+      if (st != MOE_OK) return st;
+    }
+    st = hip_status(tiled ? moe::launch_gemm1_lds(pw + P.w1c, pw + P.w1s, xq, xsf_planes, counts, offsets,
+                                                  sorted_rows, tiles, num_tiles, max_tiles, rows_hint, H, I, k,
+                                                  hrows, hq, hsf, gemm1_acc, s)
                           : moe::launch_gemm1(pw + P.w1c, pw + P.w1s, xq, xsf, counts, offsets, sorted_rows,
-                                              H, I, E, k, rows_hint, hq, hsf, gemm1_acc, s));
+                                              H, I, E, k, rows_hint, hrows, hq, hsf, gemm1_acc, s));
     if (st != MOE_OK) return st;
   }
   if (stages & MOE_STAGE_GEMM2) {
     st = hip_status(tiled ? moe::launch_gemm2_lds(pw + P.w2c, pw + P.w2s, hq, hsf, counts, offsets, tiles,
-                                                  num_tiles, max_tiles, rows_hint, H, I, y, s)
+                                                  num_tiles, max_tiles, rows_hint, H, I, hrows, y, s)
                           : moe::launch_gemm2(pw + P.w2c, pw + P.w2s, hq, hsf, counts, offsets, H, I, E,
-                                              rows_hint, y, s));
+                                              rows_hint, hrows, y, s));
     if (st != MOE_OK) return st;
   }
   if (stages & MOE_STAGE_COMBINE) {

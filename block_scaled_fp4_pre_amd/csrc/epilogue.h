@@ -1,5 +1,5 @@
 // Epilogues of the two grouped GEMMs, shared by the streaming kernels
-// (gemm1.hip, gemm2.hip) and the tiled prefill kernels (gemm_tiled.hip).
+// (gemm1.hip, gemm2.hip) and the LDS-staged prefill kernels (gemm_lds.hip).
 //
 // Accumulator layout (16x16x128 MFMA, swap-AB): acc[nt][rb][i] holds weight row
 // 16*rb + 4*(lane/16) + i of the wave's 64-row unit against token column
@@ -23,8 +23,15 @@ __device__ __forceinline__ float swiglu(float g, float u) {
 // h = silu(gate) * up in fp32, requantized to MXFP4 per 32 columns: the absmax
 // over the 4 lanes of a token (xor 16, xor 32), then codes packed two per byte
 // (even column in the low nibble).  row0: sorted position of token column 0.
+//
+// hq and hsf are K-step planes for GEMM2: plane c (inter columns [128c,
+// 128c+128)) holds, for every sorted row p, its 64 code bytes at
+// (c * hrows + p) * 64 and its 4 scale bytes at (c * hrows + p) * 4, hrows
+// being the rows of a plane.  A tile of consecutive rows then reads one
+// contiguous run per K step.  Unit u is 16 code bytes and scale byte u % 4 of
+// plane u / 4.
 template <int NT>
-__device__ __forceinline__ void gemm1_epilogue(v4f (&acc)[NT][4], int u, int row0, int nrows, int I,
+__device__ __forceinline__ void gemm1_epilogue(v4f (&acc)[NT][4], int u, int row0, int nrows, int I, int hrows,
                                                int lane, uint8_t* __restrict__ hq, uint8_t* __restrict__ hsf,
                                                float* __restrict__ acc_out) {
   const int tok_lane = lane & 15, kb = lane >> 4;
@@ -51,10 +58,11 @@ __device__ __forceinline__ void gemm1_epilogue(v4f (&acc)[NT][4], int u, int row
     const uint32_t lo = e2m1_pack2<1>(e2m1_pack2<0>(0u, h[0], h[1], sc), h[2], h[3], sc);
     const uint32_t hi = e2m1_pack2<1>(e2m1_pack2<0>(0u, h[4], h[5], sc), h[6], h[7], sc);
     if (live) {
-      uint8_t* row = hq + (size_t)p * (I / 2) + u * 16;
+      const size_t pr = (size_t)(u >> 2) * hrows + p;   // row p of plane u / 4
+      uint8_t* row = hq + pr * 64 + (u & 3) * 16;
       *reinterpret_cast<uint16_t*>(row + 2 * kb) = (uint16_t)lo;
       *reinterpret_cast<uint16_t*>(row + 8 + 2 * kb) = (uint16_t)hi;
-      if (kb == 0) hsf[(size_t)p * (I / 32) + u] = (uint8_t)(ex + 127);
+      if (kb == 0) hsf[pr * 4 + (u & 3)] = (uint8_t)(ex + 127);
       if (acc_out != nullptr) {
         float* arow = acc_out + (size_t)p * (2 * I) + 32 * u + 4 * kb;
 #pragma unroll

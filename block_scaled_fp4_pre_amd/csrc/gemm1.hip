@@ -45,7 +45,7 @@ __global__ void __launch_bounds__(256, 2) gemm1_swiglu_kernel(
     const uint8_t* __restrict__ w1c, const uint8_t* __restrict__ w1s, const uint8_t* __restrict__ xq,
     const uint8_t* __restrict__ xsf, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows, int H, int I, int k,
-    int upw, uint8_t* __restrict__ hq, uint8_t* __restrict__ hsf, float* __restrict__ acc_out) {
+    int upw, int hrows, uint8_t* __restrict__ hq, uint8_t* __restrict__ hsf, float* __restrict__ acc_out) {
   const int groups = I / (128 * upw);
   const int e = blockIdx.x / groups;
   const int g = blockIdx.x - e * groups;
@@ -124,7 +124,7 @@ __global__ void __launch_bounds__(256, 2) gemm1_swiglu_kernel(
       if (s0 + D != S) continue;
 
       // Unit finished: SwiGLU + requant of its 32 columns for the tile's rows.
-      gemm1_epilogue<NT>(acc, u0 + kGroupUnits * (j0 / S), base + t0, nrows, I, lane, hq, hsf, acc_out);
+      gemm1_epilogue<NT>(acc, u0 + kGroupUnits * (j0 / S), base + t0, nrows, I, hrows, lane, hq, hsf, acc_out);
       zero_acc<NT>(acc);
     }
   }
@@ -133,7 +133,7 @@ __global__ void __launch_bounds__(256, 2) gemm1_swiglu_kernel(
 template <int NT, int D, int SWZ>
 static hipError_t launch_gemm1_t(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq,
                                  const uint8_t* xsf, const int32_t* counts, const int32_t* offsets,
-                                 const int32_t* sorted_rows, int H, int I, int E, int k, uint8_t* hq,
+                                 const int32_t* sorted_rows, int H, int I, int E, int k, int hrows, uint8_t* hq,
                                  uint8_t* hsf, float* acc_out, hipStream_t stream) {
   constexpr int ROWS = NT == 1 ? 16 : MOE_STREAM_ROWS2;
   const size_t lds = (size_t)ROWS * (H / 2) + (size_t)ROWS * (H / 32);
@@ -144,46 +144,46 @@ static hipError_t launch_gemm1_t(const uint8_t* w1c, const uint8_t* w1s, const u
     if (err != hipSuccess) return err;
   }
   hipLaunchKernelGGL(kern, dim3(E * (I / (128 * upw))), dim3(256), lds, stream, w1c, w1s, xq, xsf, counts,
-                     offsets, sorted_rows, H, I, k, upw, hq, hsf, acc_out);
+                     offsets, sorted_rows, H, I, k, upw, hrows, hq, hsf, acc_out);
   return hipGetLastError();
 }
 
 template <int NT, int D>
 static hipError_t launch_gemm1_nt(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq,
                                   const uint8_t* xsf, const int32_t* counts, const int32_t* offsets,
-                                  const int32_t* sorted_rows, int H, int I, int E, int k, uint8_t* hq,
+                                  const int32_t* sorted_rows, int H, int I, int E, int k, int hrows, uint8_t* hq,
                                   uint8_t* hsf, float* acc_out, hipStream_t stream) {
   const int chunks = H / 32;  // 16-byte chunks per token row; a multiple of 8
   if (chunks % 16 == 0)
-    return launch_gemm1_t<NT, D, 16>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hq, hsf,
+    return launch_gemm1_t<NT, D, 16>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hrows, hq, hsf,
                                      acc_out, stream);
-  return launch_gemm1_t<NT, D, 8>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hq, hsf,
+  return launch_gemm1_t<NT, D, 8>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hrows, hq, hsf,
                                   acc_out, stream);
 }
 
 template <int NT>
 static hipError_t launch_gemm1_d(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq,
                                  const uint8_t* xsf, const int32_t* counts, const int32_t* offsets,
-                                 const int32_t* sorted_rows, int H, int I, int E, int k, uint8_t* hq,
+                                 const int32_t* sorted_rows, int H, int I, int E, int k, int hrows, uint8_t* hq,
                                  uint8_t* hsf, float* acc_out, hipStream_t stream) {
   // The ring depth must divide the number of K steps H/128 (even, as H % 256 == 0).
   if ((H / kStepK) % MOE_STREAM_RING_DEPTH == 0)
-    return launch_gemm1_nt<NT, MOE_STREAM_RING_DEPTH>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hq, hsf,
+    return launch_gemm1_nt<NT, MOE_STREAM_RING_DEPTH>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hrows, hq, hsf,
                                   acc_out, stream);
-  return launch_gemm1_nt<NT, 2>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hq, hsf,
+  return launch_gemm1_nt<NT, 2>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hrows, hq, hsf,
                                 acc_out, stream);
 }
 
 hipError_t launch_gemm1(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq, const uint8_t* xsf,
                         const int32_t* counts, const int32_t* offsets, const int32_t* sorted_rows,
-                        int H, int I, int E, int k, int rows_hint, uint8_t* hq, uint8_t* hsf,
+                        int H, int I, int E, int k, int rows_hint, int hrows, uint8_t* hq, uint8_t* hsf,
                         float* acc_out, hipStream_t stream) {
   // rows_hint: mean routed rows per expert; two token tiles per pass once a
   // single 16-row tile would often overflow (and re-stream the weights).
   if (rows_hint > 8)
-    return launch_gemm1_d<2>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hq, hsf, acc_out,
+    return launch_gemm1_d<2>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hrows, hq, hsf, acc_out,
                              stream);
-  return launch_gemm1_d<1>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hq, hsf, acc_out,
+  return launch_gemm1_d<1>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hrows, hq, hsf, acc_out,
                            stream);
 }
 

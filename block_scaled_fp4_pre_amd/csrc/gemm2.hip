@@ -10,9 +10,9 @@
 // groups of 4 units of 64 hidden rows; wave w owns unit w of each group and
 // streams them as one sequence of K steps (one fixed stride in the tile order
 // of tiles.h), writing y at each unit's end.  The expert's requantized rows are
-// already contiguous (sorted order), so the B tile is a plain copy into LDS by
-// direct-to-LDS loads; weights stream through the register ring of
-// gemm_common.h.
+// consecutive in every K-step plane of hq/hsf (epilogue.h), so the B tile is
+// one contiguous run per plane, copied into LDS by direct-to-LDS loads;
+// weights stream through the register ring of gemm_common.h.
 #include "epilogue.h"
 #include "gemm_common.h"
 #include "launch.h"
@@ -39,7 +39,7 @@ template <int NT, int D, int SWZ>
 __global__ void __launch_bounds__(256, MOE_GEMM2_MIN_BLOCKS) gemm2_kernel(
     const uint8_t* __restrict__ w2c, const uint8_t* __restrict__ w2s, const uint8_t* __restrict__ hq,
     const uint8_t* __restrict__ hsf, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ offsets, int H, int I, int upw, uint16_t* __restrict__ y) {
+    const int32_t* __restrict__ offsets, int H, int I, int upw, int hrows, uint16_t* __restrict__ y) {
   const int groups = H / (256 * upw);
   const int e = blockIdx.x / groups;
   const int g = blockIdx.x - e * groups;
@@ -81,8 +81,8 @@ __global__ void __launch_bounds__(256, MOE_GEMM2_MIN_BLOCKS) gemm2_kernel(
     }
     __syncthreads();
     const int row0 = base + t0;
-    gather_tile<ROWS, SWZ>(lds_codes, lds_scales, hq, hsf, row_bytes, sc_bytes, nrows,
-                              [&](int n) { return row0 + n; }, wave, lane, 4);
+    gather_tile<ROWS, SWZ, true>(lds_codes, lds_scales, hq, hsf, row_bytes, sc_bytes, nrows,
+                                 [&](int n) { return row0 + n; }, wave, lane, 4, hrows);
     wait_vmem_all();
     __syncthreads();
 
@@ -126,7 +126,7 @@ __global__ void __launch_bounds__(256, MOE_GEMM2_MIN_BLOCKS) gemm2_kernel(
 template <int NT, int D, int SWZ>
 static hipError_t launch_gemm2_t(const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq,
                                  const uint8_t* hsf, const int32_t* counts, const int32_t* offsets,
-                                 int H, int I, int E, uint16_t* y, hipStream_t stream) {
+                                 int H, int I, int E, int hrows, uint16_t* y, hipStream_t stream) {
   constexpr int ROWS = NT == 1 ? 16 : MOE_STREAM_ROWS2;
   const size_t lds = (size_t)ROWS * (I / 2) + (size_t)ROWS * (I / 32);
   auto kern = gemm2_kernel<NT, D, SWZ>;
@@ -136,36 +136,36 @@ static hipError_t launch_gemm2_t(const uint8_t* w2c, const uint8_t* w2s, const u
     if (err != hipSuccess) return err;
   }
   hipLaunchKernelGGL(kern, dim3(E * (H / (256 * upw))), dim3(256), lds, stream, w2c, w2s, hq, hsf, counts,
-                     offsets, H, I, upw, y);
+                     offsets, H, I, upw, hrows, y);
   return hipGetLastError();
 }
 
 template <int NT, int D>
 static hipError_t launch_gemm2_nt(const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq,
                                   const uint8_t* hsf, const int32_t* counts, const int32_t* offsets,
-                                  int H, int I, int E, uint16_t* y, hipStream_t stream) {
+                                  int H, int I, int E, int hrows, uint16_t* y, hipStream_t stream) {
   const int chunks = I / 32;  // a multiple of 4
-  if (chunks % 16 == 0) return launch_gemm2_t<NT, D, 16>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, y, stream);
-  if (chunks % 8 == 0) return launch_gemm2_t<NT, D, 8>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, y, stream);
-  return launch_gemm2_t<NT, D, 4>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, y, stream);
+  if (chunks % 16 == 0) return launch_gemm2_t<NT, D, 16>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, hrows, y, stream);
+  if (chunks % 8 == 0) return launch_gemm2_t<NT, D, 8>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, hrows, y, stream);
+  return launch_gemm2_t<NT, D, 4>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, hrows, y, stream);
 }
 
 template <int NT>
 static hipError_t launch_gemm2_d(const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq,
                                  const uint8_t* hsf, const int32_t* counts, const int32_t* offsets,
-                                 int H, int I, int E, uint16_t* y, hipStream_t stream) {
+                                 int H, int I, int E, int hrows, uint16_t* y, hipStream_t stream) {
   // The ring depth must divide the number of K steps I/128.
   const int S = I / kStepK;
-  if (S % MOE_STREAM_RING_DEPTH == 0) return launch_gemm2_nt<NT, MOE_STREAM_RING_DEPTH>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, y, stream);
-  if (S % 2 == 0) return launch_gemm2_nt<NT, 2>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, y, stream);
-  return launch_gemm2_nt<NT, 1>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, y, stream);
+  if (S % MOE_STREAM_RING_DEPTH == 0) return launch_gemm2_nt<NT, MOE_STREAM_RING_DEPTH>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, hrows, y, stream);
+  if (S % 2 == 0) return launch_gemm2_nt<NT, 2>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, hrows, y, stream);
+  return launch_gemm2_nt<NT, 1>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, hrows, y, stream);
 }
 
 hipError_t launch_gemm2(const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq, const uint8_t* hsf,
                         const int32_t* counts, const int32_t* offsets, int H, int I, int E,
-                        int rows_hint, uint16_t* y, hipStream_t stream) {
-  if (rows_hint > 8) return launch_gemm2_d<2>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, y, stream);
-  return launch_gemm2_d<1>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, y, stream);
+                        int rows_hint, int hrows, uint16_t* y, hipStream_t stream) {
+  if (rows_hint > 8) return launch_gemm2_d<2>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, hrows, y, stream);
+  return launch_gemm2_d<1>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, hrows, y, stream);
 }
 
 }  // namespace moe

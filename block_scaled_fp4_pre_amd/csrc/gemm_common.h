@@ -74,14 +74,16 @@ __device__ __forceinline__ int scale_swizzle(int sc_bytes) {
   return low > 32 ? 32 : low;
 }
 
-// Copy ROWS token rows into LDS.  Row n (n < nrows) comes from global row
-// row_index(n) of `codes` (row_bytes per row) and `scales` (sc_bytes per row).
-// sc_bytes is a multiple of 4.  Lanes whose slot lies past the last row are
-// masked off, so ROWS * row_bytes need not be a multiple of 1024.
-template <int ROWS, int SWZ, class RowIndex>
+// Copy ROWS token rows into LDS.  Row n (n < nrows) is global row
+// row_index(n) of `codes` and `scales`: row-major (row_bytes and sc_bytes per
+// row) when PLANES is false; in K-step planes of hrows rows when it is true
+// (64 code bytes and one scale dword per row and plane; epilogue.h).  sc_bytes
+// is a multiple of 4.  Lanes whose slot lies past the last row are masked off,
+// so ROWS * row_bytes need not be a multiple of 1024.
+template <int ROWS, int SWZ, bool PLANES = false, class RowIndex>
 __device__ __forceinline__ void gather_tile(uint8_t* lds_codes, uint8_t* lds_scales, const uint8_t* codes,
                                             const uint8_t* scales, int row_bytes, int sc_bytes, int nrows,
-                                            RowIndex row_index, int wave, int lane, int nwaves) {
+                                            RowIndex row_index, int wave, int lane, int nwaves, int hrows = 0) {
   const int chunks = row_bytes >> 4;
   const int code_insts = (ROWS * row_bytes + 1023) >> 10;
   for (int j = wave; j < code_insts; j += nwaves) {
@@ -90,7 +92,9 @@ __device__ __forceinline__ void gather_tile(uint8_t* lds_codes, uint8_t* lds_sca
     const int src = row_index(n);            // evaluated by every lane (it may shuffle)
     if (n < nrows) {
       const int c = pos ^ (n & (SWZ - 1));
-      lds_dma16(codes + (size_t)src * row_bytes + c * 16, lds_codes + j * 1024);
+      const size_t off = PLANES ? ((size_t)(c >> 2) * hrows + src) * 64 + (c & 3) * 16
+                                : (size_t)src * row_bytes + c * 16;
+      lds_dma16(codes + off, lds_codes + j * 1024);
     }
   }
   // Scale dword d of row n sits at position d ^ (n % scale_swizzle(sc_bytes)).
@@ -101,8 +105,11 @@ __device__ __forceinline__ void gather_tile(uint8_t* lds_codes, uint8_t* lds_sca
     const int slot = j * 64 + lane;
     const int n = min(slot / dws, ROWS - 1), dpos = slot - (slot / dws) * dws;
     const int src = row_index(n);
-    if (slot < sc_total && n < nrows)
-      lds_dma4(scales + (size_t)src * sc_bytes + (dpos ^ (n & scm)) * 4, lds_scales + j * 256);
+    if (slot < sc_total && n < nrows) {
+      const int d = dpos ^ (n & scm);
+      const size_t off = PLANES ? ((size_t)d * hrows + src) * 4 : (size_t)src * sc_bytes + d * 4;
+      lds_dma4(scales + off, lds_scales + j * 256);
+    }
   }
 }
 

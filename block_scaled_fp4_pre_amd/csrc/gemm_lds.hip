@@ -112,7 +112,8 @@ __global__ void __launch_bounds__(256 * WB, WB == 1 ? MOE_LDS_BLOCKS : 1) gemm_l
     const uint8_t* __restrict__ act_sf, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows,
     const int2* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int max_tiles, int H, int I, int k,
-    uint8_t* __restrict__ hq, uint8_t* __restrict__ hsf, float* __restrict__ acc_out, uint16_t* __restrict__ y) {
+    int hrows, uint8_t* __restrict__ hq, uint8_t* __restrict__ hsf, float* __restrict__ acc_out,
+    uint16_t* __restrict__ y) {
   constexpr int WAVES = 4 * WB;
   using L = LdsStage<NT, WAVES>;
   constexpr int ROWS = L::ROWS;
@@ -149,27 +150,27 @@ __global__ void __launch_bounds__(256 * WB, WB == 1 ? MOE_LDS_BLOCKS : 1) gemm_l
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int unit = wb * WAVES + wave;
   const int S = K / kStepK;
-  const int row_bytes = K / 2, sc_row = K / 32;
+  const int row_bytes = K / 2;
 
   extern __shared__ __align__(16) uint8_t lds[];
   const uint32_t lbase = (uint32_t)(uintptr_t)lds;
 
   // DMA sources.  Rows past the tile's end re-read its last row (their
-  // results are never stored).
+  // results are never stored).  Token scales, and GEMM2's token codes, are
+  // K-step planes of sorted rows (hrows rows per plane): one contiguous run
+  // per step for the tile.  GEMM1's token codes are gathered by token from the
+  // row-major quantized x.
   const uint8_t* wsrc = wc + (G1 ? w1_code_offset(e, unit, 0, H, I) : w2_code_offset(e, unit, 0, H, I)) + lane * 16;
   const uint8_t* ssrc = wsc + (G1 ? w1_scale_offset(e, unit, 0, H, I) : w2_scale_offset(e, unit, 0, H, I)) + lane * 4;
-  auto src_row = [&](int n) -> int {
-    const int r = min(n, nrows - 1);
-    return G1 ? sorted_rows[row0 + r] / k : row0 + r;
-  };
+  const size_t code_step = G1 ? 64 : (size_t)hrows * 64, scale_step = (size_t)hrows * 4;
   const uint8_t* tsrc[TOK_INSTS];
 #pragma unroll
   for (int i = 0; i < TOK_INSTS; ++i) {
     const int slot = (wave * TOK_INSTS + i) * 64 + lane;
-    const int n = slot >> 2;
-    tsrc[i] = act + (size_t)src_row(n) * row_bytes + tok_pos(n, slot & 3) * 16;
+    const int n = slot >> 2, r = row0 + min(n, nrows - 1);
+    tsrc[i] = act + (G1 ? (size_t)(sorted_rows[r] / k) * row_bytes : (size_t)r * 64) + tok_pos(n, slot & 3) * 16;
   }
-  const uint8_t* tssrc = act_sf + (size_t)src_row(wave * SC_LANES + min(lane, SC_LANES - 1)) * sc_row;
+  const uint8_t* tssrc = act_sf + (size_t)(row0 + min(wave * SC_LANES + min(lane, SC_LANES - 1), nrows - 1)) * 4;
 
   // DMA i (0 .. DMA_PER_STAGE-1) of stage s: the token scales (the one DMA
   // that not every lane takes part in, first, so that no MFMA of the step is
@@ -178,7 +179,7 @@ __global__ void __launch_bounds__(256 * WB, WB == 1 ? MOE_LDS_BLOCKS : 1) gemm_l
   auto issue_one = [&](int s, int i) {
     const uint32_t sb = lbase + (uint32_t)((s % P) * L::BYTES);
     if (i == 0) {
-      if (lane < SC_LANES) dma4_asm(tssrc + s * 4, sb + L::T_SCALES + wave * SC_LANES * 4);
+      if (lane < SC_LANES) dma4_asm(tssrc + s * scale_step, sb + L::T_SCALES + wave * SC_LANES * 4);
     } else if (i <= 4) {
       const int rb = i - 1;
       if constexpr (WNT)
@@ -191,7 +192,7 @@ __global__ void __launch_bounds__(256 * WB, WB == 1 ? MOE_LDS_BLOCKS : 1) gemm_l
       else
         dma4_asm(ssrc + (size_t)s * kUnitScaleStride, sb + L::W_SCALES + wave * kStepScaleBytes);
     } else {
-      dma16_asm(tsrc[i - 6] + s * 64, sb + L::T_CODES + (wave * TOK_INSTS + i - 6) * 1024);
+      dma16_asm(tsrc[i - 6] + s * code_step, sb + L::T_CODES + (wave * TOK_INSTS + i - 6) * 1024);
     }
   };
   auto issue = [&](int s) {
@@ -264,7 +265,7 @@ __global__ void __launch_bounds__(256 * WB, WB == 1 ? MOE_LDS_BLOCKS : 1) gemm_l
   }
 
   if constexpr (G1)
-    gemm1_epilogue<NT>(acc, unit, row0, nrows, I, lane, hq, hsf, acc_out);
+    gemm1_epilogue<NT>(acc, unit, row0, nrows, I, hrows, lane, hq, hsf, acc_out);
   else
     gemm2_epilogue<NT>(acc, unit, row0, nrows, H, lane, y);
 }
@@ -279,8 +280,8 @@ template <bool G1, bool WNT, int WB>
 static hipError_t launch_prefill_wb(const uint8_t* wc, const uint8_t* wsc, const uint8_t* act,
                                     const uint8_t* act_sf, const int32_t* counts, const int32_t* offsets,
                                     const int32_t* sorted_rows, const int2* tiles, const int32_t* num_tiles,
-                                    int max_tiles, int H, int I, int k, uint8_t* hq, uint8_t* hsf, float* acc_out,
-                                    uint16_t* y, hipStream_t stream) {
+                                    int max_tiles, int H, int I, int k, int hrows, uint8_t* hq, uint8_t* hsf,
+                                    float* acc_out, uint16_t* y, hipStream_t stream) {
   constexpr int P = MOE_LDS_STAGES;
   auto kern = gemm_lds_kernel<G1, kLdsNT, P, WNT, WB>;
   const size_t lds = (size_t)P * LdsStage<kLdsNT, 4 * WB>::BYTES;
@@ -291,7 +292,7 @@ static hipError_t launch_prefill_wb(const uint8_t* wc, const uint8_t* wsc, const
   const int nwb = (G1 ? I / 128 : H / 256) / WB;
   const int64_t blocks = ((int64_t)max_tiles * nwb + 7) / 8 * 8;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256 * WB), lds, stream, wc, wsc, act, act_sf, counts, offsets,
-                     sorted_rows, tiles, num_tiles, max_tiles, H, I, k, hq, hsf, acc_out, y);
+                     sorted_rows, tiles, num_tiles, max_tiles, H, I, k, hrows, hq, hsf, acc_out, y);
   return hipGetLastError();
 }
 
@@ -310,10 +311,10 @@ template <bool G1>
 static hipError_t launch_prefill(const uint8_t* wc, const uint8_t* wsc, const uint8_t* act, const uint8_t* act_sf,
                                  const int32_t* counts, const int32_t* offsets, const int32_t* sorted_rows,
                                  const int2* tiles, const int32_t* num_tiles, int max_tiles, int rows_hint, int H,
-                                 int I, int k, uint8_t* hq, uint8_t* hsf, float* acc_out, uint16_t* y,
+                                 int I, int k, int hrows, uint8_t* hq, uint8_t* hsf, float* acc_out, uint16_t* y,
                                  hipStream_t stream) {
 #define MOE_PREFILL_ARGS wc, wsc, act, act_sf, counts, offsets, sorted_rows, tiles, num_tiles, max_tiles, H, I, k, \
-                         hq, hsf, acc_out, y, stream
+                         hrows, hq, hsf, acc_out, y, stream
   const bool single = rows_hint <= kLdsNT * 16;
   const int nwb = G1 ? I / 128 : H / 256;
   if (single && G1 && nwb % 2 == 0) return launch_prefill_wb<G1, true, 2>(MOE_PREFILL_ARGS);
@@ -322,20 +323,22 @@ static hipError_t launch_prefill(const uint8_t* wc, const uint8_t* wsc, const ui
 #undef MOE_PREFILL_ARGS
 }
 
-hipError_t launch_gemm1_lds(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq, const uint8_t* xsf,
+// xsf_planes: the token scales of the sorted rows in K-step planes of hrows
+// rows (launch_sorted_scales); hq/hsf: GEMM1's output planes (epilogue.h).
+hipError_t launch_gemm1_lds(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq, const uint8_t* xsf_planes,
                             const int32_t* counts, const int32_t* offsets, const int32_t* sorted_rows,
                             const int2* tiles, const int32_t* num_tiles, int max_tiles, int rows_hint, int H, int I,
-                            int k, uint8_t* hq, uint8_t* hsf, float* acc_out, hipStream_t stream) {
-  return launch_prefill<true>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, tiles, num_tiles, max_tiles, rows_hint,
-                              H, I, k, hq, hsf, acc_out, nullptr, stream);
+                            int k, int hrows, uint8_t* hq, uint8_t* hsf, float* acc_out, hipStream_t stream) {
+  return launch_prefill<true>(w1c, w1s, xq, xsf_planes, counts, offsets, sorted_rows, tiles, num_tiles, max_tiles,
+                              rows_hint, H, I, k, hrows, hq, hsf, acc_out, nullptr, stream);
 }
 
 hipError_t launch_gemm2_lds(const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq, const uint8_t* hsf,
                             const int32_t* counts, const int32_t* offsets, const int2* tiles,
-                            const int32_t* num_tiles, int max_tiles, int rows_hint, int H, int I, uint16_t* y,
-                            hipStream_t stream) {
+                            const int32_t* num_tiles, int max_tiles, int rows_hint, int H, int I, int hrows,
+                            uint16_t* y, hipStream_t stream) {
   return launch_prefill<false>(w2c, w2s, hq, hsf, counts, offsets, nullptr, tiles, num_tiles, max_tiles, rows_hint, H,
-                               I, 1, nullptr, nullptr, nullptr, y, stream);
+                               I, 1, hrows, nullptr, nullptr, nullptr, y, stream);
 }
 
 }  // namespace moe

@@ -27,27 +27,36 @@ hipError_t launch_predispatch(const uint16_t* x, int64_t ngroups, uint8_t* xq, u
 // Prefill GEMMs with both operands staged in LDS (gemm_lds.hip): tiles of
 // lds_tile_rows(mean rows per expert) routed rows; rows_hint (the mean) also
 // picks the weight load policy and the work order.
+// hrows: rows of one K-step plane of the sorted-row activations (hq/hsf and
+// the sorted token scales; epilogue.h), the workspace's routed-row capacity.
 int lds_tile_rows(int rows_hint);
 int lds_max_tiles(int R, int E, int tile_rows);
-hipError_t launch_gemm1_lds(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq, const uint8_t* xsf,
+hipError_t launch_gemm1_lds(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq, const uint8_t* xsf_planes,
                             const int32_t* counts, const int32_t* offsets, const int32_t* sorted_rows,
                             const int2* tiles, const int32_t* num_tiles, int max_tiles, int rows_hint, int H, int I,
-                            int k, uint8_t* hq, uint8_t* hsf, float* acc_out, hipStream_t stream);
+                            int k, int hrows, uint8_t* hq, uint8_t* hsf, float* acc_out, hipStream_t stream);
 hipError_t launch_gemm2_lds(const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq, const uint8_t* hsf,
                             const int32_t* counts, const int32_t* offsets, const int2* tiles,
-                            const int32_t* num_tiles, int max_tiles, int rows_hint, int H, int I, uint16_t* y,
-                            hipStream_t stream);
+                            const int32_t* num_tiles, int max_tiles, int rows_hint, int H, int I, int hrows,
+                            uint16_t* y, hipStream_t stream);
+
+// The token scales of the sorted rows [0, offsets[E]) in K-step planes:
+// plane c, row q = the 4 scale bytes of K step c of token sorted_rows[q] / k.
+// Read by the LDS-staged GEMM1, whose per-step token-scale loads then cover
+// consecutive addresses.  rows_bound >= offsets[E] sizes the grid.
+hipError_t launch_sorted_scales(const uint8_t* xsf, const int32_t* sorted_rows, const int32_t* offsets, int E,
+                                int rows_bound, int H, int k, int hrows, uint8_t* xsf_planes, hipStream_t stream);
 
 // Stage S2: grouped GEMM1 over the prepared W1 tiles + SwiGLU + MXFP4 requant.
 hipError_t launch_gemm1(const uint8_t* w1_codes, const uint8_t* w1_scales, const uint8_t* xq,
                         const uint8_t* xsf, const int32_t* counts, const int32_t* offsets,
-                        const int32_t* sorted_rows, int H, int I, int E, int k, int rows_hint,
+                        const int32_t* sorted_rows, int H, int I, int E, int k, int rows_hint, int hrows,
                         uint8_t* hq, uint8_t* hsf, float* acc_out, hipStream_t stream);
 
 // Stage S3: grouped GEMM2 over the prepared W2 tiles -> fp32 y in sorted order.
 hipError_t launch_gemm2(const uint8_t* w2_codes, const uint8_t* w2_scales, const uint8_t* hq,
                         const uint8_t* hsf, const int32_t* counts, const int32_t* offsets, int H,
-                        int I, int E, int rows_hint, uint16_t* y, hipStream_t stream);
+                        int I, int E, int rows_hint, int hrows, uint16_t* y, hipStream_t stream);
 
 // Stage S4: top-k weighted combine back to token order, bf16 output.
 hipError_t launch_combine(const uint16_t* y, const int32_t* pos, const float* w, int T, int H, int k,

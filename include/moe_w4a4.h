@@ -142,7 +142,11 @@ const char* moe_w4a4_status_string(int status);
 /* ---- inspection and stage-by-stage execution (tests, profiling) -------- */
 
 /* Byte offsets of each intermediate inside the forward workspace; every region
- * is 256-byte aligned and sized for cfg->max_tokens. */
+ * is 256-byte aligned and sized for cfg->max_tokens.  R = max_tokens*k.  The
+ * sorted-row activations of the GEMMs are stored as K-step planes, plane c
+ * holding K step c (128 elements) of every sorted row: 64 code bytes at
+ * (c*R + row)*64 and one dword of 4 scale bytes at (c*R + row)*4, so that a
+ * tile of consecutive rows reads one contiguous run per K step. */
 typedef struct moe_w4a4_ws_layout {
   uint64_t xq;           /* uint8  [max_tokens, H/2]   quantized tokens (packed)    */
   uint64_t xsf;          /* uint8  [max_tokens, H/32]  their scale bytes            */
@@ -151,11 +155,13 @@ typedef struct moe_w4a4_ws_layout {
   uint64_t sorted_rows;  /* int32  [max_tokens*k]      r = t*k+j in (expert, r) order */
   uint64_t pos;          /* int32  [max_tokens*k]      index of r in sorted_rows or -1 */
   uint64_t hist;         /* int32  [ceil(max_tokens*k/1024), E] per-block counts   */
-  uint64_t hq;           /* uint8  [max_tokens*k, I/2] requantized h (sorted order) */
-  uint64_t hsf;          /* uint8  [max_tokens*k, I/32]                             */
+  uint64_t hq;           /* uint8  [I/128, R, 64]      requantized h (sorted rows, planes) */
+  uint64_t hsf;          /* uint8  [I/128, R, 4]       its scale bytes (planes)     */
   uint64_t y;            /* bf16   [max_tokens*k, H]   GEMM2 result (sorted order)  */
   uint64_t tiles;        /* int32  [max_tokens*k/16 + E, 2] (expert, first row) work tiles */
   uint64_t num_tiles;    /* int32  [1]                 number of valid tiles        */
+  uint64_t xsf_planes;   /* uint8  [H/128, R, 4]       token scales of the sorted rows
+                                                        (planes; the tiled GEMM1's input) */
   uint64_t total;        /* == workspace_bytes                                      */
 } moe_w4a4_ws_layout;
 
@@ -165,7 +171,7 @@ int moe_w4a4_workspace_layout(const moe_w4a4_cfg* cfg, moe_w4a4_ws_layout* out);
 enum {
   MOE_STAGE_QUANT = 1,    /* x -> xq, xsf                                  */
   MOE_STAGE_ROUTE = 2,    /* topk_ids -> counts, offsets, sorted_rows, pos */
-  MOE_STAGE_GEMM1 = 4,    /* xq, route -> hq, hsf                          */
+  MOE_STAGE_GEMM1 = 4,    /* xq, xsf, route -> hq, hsf (and xsf_planes)    */
   MOE_STAGE_GEMM2 = 8,    /* hq, route -> y                                */
   MOE_STAGE_COMBINE = 16, /* y, pos, topk_weights -> out                   */
   MOE_STAGE_ALL = 31

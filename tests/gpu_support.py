@@ -59,6 +59,19 @@ def run_config(layer, cfg, tokens=None):
     return dict(x=x, ids=ids, w=w, out=host_bits(out), **workspace_host(layer, T))
 
 
+def rows_from_planes(planes, nrows):
+    """[K steps, rows, bytes] K-step planes (the workspace layout of the
+    sorted-row activations) -> [nrows, K steps * bytes] row-major on the host."""
+    a = planes[:, :nrows].cpu().numpy()
+    return np.ascontiguousarray(a.transpose(1, 0, 2)).reshape(nrows, -1)
+
+
+def planes_from_rows(rows, nplanes):
+    """Inverse of rows_from_planes for an injected [nrows, nplanes * b] array."""
+    n = rows.shape[0]
+    return np.ascontiguousarray(rows.reshape(n, nplanes, -1).transpose(1, 0, 2))
+
+
 def workspace_host(layer, T):
     H, I, E, k = layer.H, layer.I, layer.E, layer.k
     R = T * k
@@ -72,7 +85,8 @@ def workspace_host(layer, T):
         offsets=ws("offsets", (E + 1,), torch.int32).cpu().numpy(),
         sorted_rows=ws("sorted_rows", (layer.max_tokens * k,), torch.int32)[:nv].cpu().numpy(),
         pos=ws("pos", (layer.max_tokens * k,), torch.int32)[:R].cpu().numpy(),
-        hq=ws("hq", (layer.max_tokens * k, I // 2), torch.uint8)[:nv].cpu().numpy(),
-        hsf=ws("hsf", (layer.max_tokens * k, I // 32), torch.uint8)[:nv].cpu().numpy(),
+        hq=rows_from_planes(ws("hq", (I // 128, layer.max_tokens * k, 64), torch.uint8), nv),
+        hsf=rows_from_planes(ws("hsf", (I // 128, layer.max_tokens * k, 4), torch.uint8), nv),
+        xsf_planes=rows_from_planes(ws("xsf_planes", (H // 128, layer.max_tokens * k, 4), torch.uint8), nv),
         y=ws("y", (layer.max_tokens * k, H), torch.bfloat16)[:nv].float().cpu().numpy().astype(np.float64),
     )

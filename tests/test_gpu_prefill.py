@@ -47,6 +47,9 @@ def test_prefill_path_all_tokens(cfg):
     assert counts.max() > 128 and (counts % 128).max() > 0      # several tiles and a ragged one
     ref = forward(got["x"], got["ids"], got["w"], all_expert_weights(cfg), cfg.experts, cfg.inter)
     check_all_stages(got, ref, cfg.topk)
+    # the tiled GEMM1's token scales: those of sorted row q's token, bit for bit
+    nv = int(counts.sum())
+    assert np.array_equal(got["xsf_planes"], got["xsf"][got["sorted_rows"][:nv] // cfg.topk])
     # a second forward on the same workspace gives the same bits
     again = run_config(layer, cfg)
     assert np.array_equal(again["out"], got["out"]) and np.array_equal(again["hq"], got["hq"])

@@ -7,7 +7,7 @@ import torch
 from oracle import bf16, mxfp4
 from oracle.route import route
 from synth import f32_to_bf16_bits as _f32_to_bf16_bits
-from tests.gpu_support import dev, dev_bf16, host_bits, layer_for, log
+from tests.gpu_support import dev, dev_bf16, host_bits, layer_for, log, planes_from_rows
 
 
 def synth_bf16(v):
@@ -144,8 +144,8 @@ def test_gemm2_exact_on_injected_rows():
     ws = layer.ws
     ws("counts", (E,), torch.int32).copy_(torch.from_numpy(counts))
     ws("offsets", (E + 1,), torch.int32).copy_(torch.from_numpy(offsets))
-    ws("hq", (T * k, I // 2), torch.uint8)[:srt.size].copy_(torch.from_numpy(hq))
-    ws("hsf", (T * k, I // 32), torch.uint8)[:srt.size].copy_(torch.from_numpy(hsf))
+    ws("hq", (I // 128, T * k, 64), torch.uint8)[:, :srt.size].copy_(torch.from_numpy(planes_from_rows(hq, I // 128)))
+    ws("hsf", (I // 128, T * k, 4), torch.uint8)[:, :srt.size].copy_(torch.from_numpy(planes_from_rows(hsf, I // 128)))
     layer.run_stages(8, T)
     torch.cuda.synchronize()
     # the fp32 accumulators are exact here, so the stored bf16 y is the exact
