@@ -4,19 +4,23 @@
 // that packs the tokens to E2M1 with group_size=32 and hands over the top-k ids
 // and weights).
 //
-// Block 0 routes all R <= 8192 rows by itself: every thread reads its (up to 8)
-// ids once, then an LDS histogram (integer atomics only count), one block scan
-// for counts/offsets (and the tile list), then the rows in chunks of 1024 in
-// order, each placed with the in-block stable ranks of route_common.h while a
-// running base per expert carries the chunks before it.  Blocks 1.. quantize
-// one 32-element group of x per thread meanwhile.
+// Block 0 routes all R <= 8192 rows by itself.  Wave w of its 16 owns the
+// contiguous rows [w*RW, (w+1)*RW), RW a multiple of 64, and reads their ids
+// once.  Per-wave expert counts go to LDS (integer atomics only count, so the
+// result does not depend on their order); one block scan gives counts and
+// offsets (and the tile list); thread e then turns the counts of expert e into
+// the first slot of each wave's rows of e.  Each wave then places its rows 64
+// at a time, in order: the rank among the sub-chunk's rows of the same expert
+// comes from a 64-lane match (one ballot per id bit), and the lowest lane of
+// each expert advances the wave's slot for the next sub-chunk.  Blocks 1..
+// quantize one 32-element group of x per thread meanwhile.
 #include "launch.h"
 #include "quant_group.h"
 #include "route_common.h"
 
 namespace moe {
 
-constexpr int kPredispatchChunks = kPredispatchMaxRows / kRouteRows;
+constexpr int kPredispatchSubs = kPredispatchMaxRows / kRouteRows;  // 64-row sub-chunks per wave, at most
 
 __global__ void __launch_bounds__(kRouteRows) predispatch_kernel(
     const uint16_t* __restrict__ x, int64_t ngroups, uint8_t* __restrict__ xq, uint8_t* __restrict__ xsf,
@@ -30,48 +34,65 @@ __global__ void __launch_bounds__(kRouteRows) predispatch_kernel(
     return;
   }
   extern __shared__ int smem[];
-  int* base = smem;                        // [E] next free slot of expert e
-  int* wcnt = smem + E;                    // [16][E]
-  int* wave_tot = wcnt + kRouteWaves * E;  // [16]
-  int eid[kPredispatchChunks];
+  int* wslot = smem;                       // [16][E]: rows of e in wave w, then wave w's next slot of e
+  int* wave_tot = wslot + kRouteWaves * E; // [16]
+  const int lane = tid & (kWave - 1), w = tid / kWave;
+  const int nsub = (R + kRouteRows - 1) / kRouteRows;   // 64-row sub-chunks per wave (<= kPredispatchSubs)
+  const int r0 = w * nsub * kWave;
+  int eid[kPredispatchSubs];
 #pragma unroll
-  for (int c = 0; c < kPredispatchChunks; ++c) {
-    const int r = c * kRouteRows + tid;
-    eid[c] = r < R ? ids[r] : -1;
+  for (int j = 0; j < kPredispatchSubs; ++j) {
+    const int r = r0 + j * kWave + lane;
+    const int e = j < nsub && r < R ? ids[r] : -1;
+    eid[j] = e >= 0 && e < E ? e : -1;
   }
-  for (int i = tid; i < E; i += kRouteRows) base[i] = 0;
-  for (int i = tid; i < kRouteWaves * E; i += kRouteRows) wcnt[i] = 0;
+  for (int i = tid; i < kRouteWaves * E; i += kRouteRows) wslot[i] = 0;
   __syncthreads();
 #pragma unroll
-  for (int c = 0; c < kPredispatchChunks; ++c)
-    if (eid[c] >= 0 && eid[c] < E) atomicAdd(&base[eid[c]], 1);
+  for (int j = 0; j < kPredispatchSubs; ++j)
+    if (eid[j] >= 0) atomicAdd(&wslot[w * E + eid[j]], 1);
   __syncthreads();
-  const int tot = tid < E ? base[tid] : 0;
-  const int incl = block_inclusive_scan(tot, wave_tot);  // also orders the reads of base above
+  int tot = 0;
+  if (tid < E)
+    for (int ww = 0; ww < kRouteWaves; ++ww) tot += wslot[ww * E + tid];
+  const int incl = block_inclusive_scan(tot, wave_tot);   // also orders the reads above before the writes below
   if (tid < E) {
-    base[tid] = incl - tot;
     counts[tid] = tot;
     offsets[tid] = incl - tot;
     if (tid == E - 1) offsets[E] = incl;
+    int run = incl - tot;
+    for (int ww = 0; ww < kRouteWaves; ++ww) {
+      const int c = wslot[ww * E + tid];
+      wslot[ww * E + tid] = run;
+      run += c;
+    }
   }
   if (tile_rows > 0) write_tiles(tot, E, tile_rows, wave_tot, tiles, num_tiles);
   __syncthreads();
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+  int* slot = wslot + w * E;
 #pragma unroll
-  for (int c = 0; c < kPredispatchChunks; ++c) {
-    const int r0 = c * kRouteRows;
-    if (r0 >= R) break;
-    place_chunk(eid[c], R, E, nbits, r0, base, wcnt, sorted_rows, pos);
-    __syncthreads();
-    // advance the running bases past this chunk and clear the per-wave counts
-    for (int e = tid; e < E; e += kRouteRows) {
-      int cnt = 0;
-      for (int w = 0; w < kRouteWaves; ++w) {
-        cnt += wcnt[w * E + e];
-        wcnt[w * E + e] = 0;
-      }
-      base[e] += cnt;
+  for (int j = 0; j < kPredispatchSubs; ++j) {
+    if (j >= nsub) break;
+    const int r = r0 + j * kWave + lane;
+    const int e = eid[j];
+    const bool valid = e >= 0;
+    uint64_t match = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const uint64_t m1 = __ballot(valid && ((e >> bit) & 1));
+      match &= ((e >> bit) & 1) ? m1 : ~m1;
     }
-    __syncthreads();
+    const int rank = __popcll(match & below);
+    const int p = valid ? slot[e] + rank : -1;
+    // every lane has read its expert's slot before the lowest lane of each
+    // expert moves it past this sub-chunk (one wave: LDS accesses in order)
+    __builtin_amdgcn_wave_barrier();
+    if (valid && rank == 0) slot[e] += __popcll(match);
+    __builtin_amdgcn_wave_barrier();
+    if (r < R) {
+      pos[r] = p;
+      if (valid) sorted_rows[p] = r;
+    }
   }
 }
 
@@ -79,7 +100,7 @@ hipError_t launch_predispatch(const uint16_t* x, int64_t ngroups, uint8_t* xq, u
                               int R, int E, int32_t* counts, int32_t* offsets, int32_t* sorted_rows,
                               int32_t* pos, int tile_rows, int2* tiles, int32_t* num_tiles, hipStream_t stream) {
   const int64_t qblocks = (ngroups + kRouteRows - 1) / kRouteRows;
-  const size_t lds = (size_t)(E + kRouteWaves * E + kRouteWaves) * sizeof(int);
+  const size_t lds = (size_t)(kRouteWaves * E + kRouteWaves) * sizeof(int);
   hipLaunchKernelGGL(predispatch_kernel, dim3((unsigned)(1 + qblocks)), dim3(kRouteRows), lds, stream, x, ngroups,
                      xq, xsf, ids, R, E, id_bits(E), counts, offsets, sorted_rows, pos, tile_rows, tiles,
                      num_tiles);
