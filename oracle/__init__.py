@@ -7,6 +7,7 @@ from it.
 
 Plain, slow, fp64 NumPy code that follows the method step by step:
   mxfp4    E2M1 element codes and UE8M0 block scales (one per 32 elements)
+  mxfp8    E4M3 element codes with the same scales (the fp8xfp4 MMA type)
   bf16     bfloat16 encode/decode
   route    stable counting sort of routed rows by expert
   forward  quantize -> route -> GEMM1 + SwiGLU -> requantize -> GEMM2 -> combine
@@ -18,11 +19,12 @@ Pages cited in this package:
   [P3] prhub digest of sglang PR "bump sgl-deep-gemm to 0.1.7, MegaMoE uses the
        mma_type API for MXFP4" (pull 37279).
   [OCP-MX] OCP Microscaling Formats (MX) Specification v1.0: the FP4 E2M1
-       element format and the E8M0 scale format. The pages name MXFP4 and
-       UE8M0 but do not define them; the definitions come from this standard.
+       element format, the FP8 E4M3 element format and the E8M0 scale format.
+       The pages name MXFP4, FP8 and UE8M0 but do not define them; the
+       definitions come from this standard.
 
 Pins: tests/test_oracle_*.py check every function against closed forms, brute
 force and invariants. Where no pin exists a function's docstring says
 "parity unpinned".
 """
-from . import bf16, dense, forward, mxfp4, route  # noqa: F401
+from . import bf16, dense, forward, mxfp4, mxfp8, route  # noqa: F401

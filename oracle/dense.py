@@ -10,10 +10,13 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import bf16, mxfp4
+from . import bf16, mxfp4, mxfp8
 
 
-def dense_forward(x_bf16, topk_ids, topk_weights, w1_codes, w1_scales, w2_codes, w2_scales):
+def dense_forward(x_bf16, topk_ids, topk_weights, w1_codes, w1_scales, w2_codes, w2_scales,
+                  mma_type: str = "mxf4xmxf4"):
+    """mma_type "fp8xfp4" quantizes x and h to MXFP8 E4M3 instead of MXFP4."""
+    act = mxfp8 if mma_type == "fp8xfp4" else mxfp4
     x_bits = np.asarray(x_bf16, dtype=np.uint16)
     ids = np.asarray(topk_ids)
     w = np.asarray(topk_weights, dtype=np.float64)
@@ -21,16 +24,16 @@ def dense_forward(x_bf16, topk_ids, topk_weights, w1_codes, w1_scales, w2_codes,
     E, twoI, _ = np.asarray(w1_codes).shape
     I = twoI // 2
     k = ids.shape[1]
-    xq, xsf = mxfp4.quantize_packed(bf16.decode(x_bits))
-    x_hat = mxfp4.dequantize(xq, xsf)                           # [T, H]
+    xq, xsf = act.quantize_packed(bf16.decode(x_bits))
+    x_hat = act.dequantize(xq, xsf)                             # [T, H]
     W1 = mxfp4.dequantize(w1_codes, w1_scales)                  # [E, 2I, H]
     W2 = mxfp4.dequantize(w2_codes, w2_scales)                  # [E, H, I]
     acc = np.einsum("th,enh->etn", x_hat, W1)                   # [E, T, 2I]
     gate, up = acc[..., :I], acc[..., I:]
     with np.errstate(over="ignore"):
         h = gate / (1.0 + np.exp(-gate)) * up                   # [E, T, I]
-    hq, hsf = mxfp4.quantize_packed(h.astype(np.float32).astype(np.float64))
-    y = np.einsum("eti,ehi->eth", mxfp4.dequantize(hq, hsf), W2)  # [E, T, H]
+    hq, hsf = act.quantize_packed(h.astype(np.float32).astype(np.float64))
+    y = np.einsum("eti,ehi->eth", act.dequantize(hq, hsf), W2)  # [E, T, H]
     out = np.zeros((T, H))
     for t in range(T):
         for j in range(k):

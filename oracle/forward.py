@@ -20,6 +20,10 @@ MXFP4 operands on both sides):
 
 The top-k weights are applied in the combine only and are used as given.
 
+mma_type (the pages' two MMA types, [P3] "Implementation breakdown" items 1-3):
+"mxf4xmxf4" quantizes x (step 1) and h (step 4) to MXFP4; "fp8xfp4" quantizes
+both to MXFP8 E4M3 (oracle.mxfp8).  The weights are MXFP4 in both.
+
 Weight operands are passed either as arrays (w1_codes [E, 2I, H/2],
 w1_scales [E, 2I, H/32], w2_codes [E, H, I/2], w2_scales [E, H, I/32]) or as a
 callable e -> (w1_codes[e], w1_scales[e], w2_codes[e], w2_scales[e]) so that a
@@ -29,8 +33,16 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import bf16, mxfp4
+from . import bf16, mxfp4, mxfp8
 from .route import route
+
+MMA_TYPES = ("mxf4xmxf4", "fp8xfp4")
+
+
+def act_format(mma_type: str):
+    """The activation format module of an MMA type: mxfp4 or mxfp8."""
+    assert mma_type in MMA_TYPES, mma_type
+    return mxfp8 if mma_type == "fp8xfp4" else mxfp4
 
 
 def _expert_getter(weights):
@@ -52,7 +64,7 @@ def silu_mul(gate, up):
 
 
 def forward(x_bf16, topk_ids, topk_weights, weights, num_experts: int, inter: int,
-            tokens=None, keep_acc: bool = False, experts=None):
+            tokens=None, keep_acc: bool = False, experts=None, mma_type: str = "mxf4xmxf4"):
     """Run the layer.
 
     x_bf16        uint16 [T, H] bfloat16 bit patterns
@@ -67,11 +79,11 @@ def forward(x_bf16, topk_ids, topk_weights, weights, num_experts: int, inter: in
                   time a bounded slice of the layer.  None = all experts.
 
     Returns a dict with every intermediate:
-      xq, xsf          packed codes [T, H/2] and scale bytes [T, H/32] of x
+      xq, xsf          codes of x ([T, H/2] packed E2M1, or [T, H] E4M3) and scale bytes [T, H/32]
       counts, offsets, sorted_rows, pos
       acc              fp64 [n_valid, 2I] GEMM1 result (gate | up), only with keep_acc
       h                fp64 [n_valid, I] (NaN where not computed), in sorted order
-      hq, hsf          packed codes [n_valid, I/2], scale bytes [n_valid, I/32]
+      hq, hsf          codes [n_valid, I/2] (E2M1) or [n_valid, I] (E4M3), scale bytes [n_valid, I/32]
       y                fp64 [n_valid, H]
       out_f64          fp64 [T, H]
       out              uint16 [T, H] bfloat16 bits
@@ -84,9 +96,10 @@ def forward(x_bf16, topk_ids, topk_weights, weights, num_experts: int, inter: in
     E, I = int(num_experts), int(inter)
     get = _expert_getter(weights)
 
+    act = act_format(mma_type)
     xv = bf16.decode(x_bits)
-    xq, xsf = mxfp4.quantize_packed(xv)                        # step 1
-    x_hat = mxfp4.dequantize(xq, xsf)
+    xq, xsf = act.quantize_packed(xv)                          # step 1
+    x_hat = act.dequantize(xq, xsf)
 
     counts, offsets, sorted_rows, pos = route(ids, E)          # step 2
     nv = int(offsets[E])
@@ -98,7 +111,7 @@ def forward(x_bf16, topk_ids, topk_weights, weights, num_experts: int, inter: in
         want[np.asarray(list(tokens), dtype=np.int64)] = True
 
     h = np.full((nv, I), np.nan)
-    hq = np.zeros((nv, I // 2), dtype=np.uint8)
+    hq = np.zeros((nv, I if act is mxfp8 else I // 2), dtype=np.uint8)
     hsf = np.zeros((nv, I // mxfp4.GROUP), dtype=np.uint8)
     y = np.full((nv, H), np.nan)
     acc_all = np.full((nv, 2 * I), np.nan) if keep_acc else None
@@ -119,9 +132,9 @@ def forward(x_bf16, topk_ids, topk_weights, weights, num_experts: int, inter: in
         W1 = mxfp4.dequantize(w1c, w1s)                        # [2I, H]
         acc = x_hat[tok] @ W1.T                                # step 3
         h_e = silu_mul(acc[:, :I], acc[:, I:])
-        hq_e, hsf_e = mxfp4.quantize_packed(to_f32(h_e))      # step 4
+        hq_e, hsf_e = act.quantize_packed(to_f32(h_e))        # step 4
         W2 = mxfp4.dequantize(w2c, w2s)                        # [H, I]
-        y_e = mxfp4.dequantize(hq_e, hsf_e) @ W2.T             # step 5
+        y_e = act.dequantize(hq_e, hsf_e) @ W2.T               # step 5
         h[p_idx], hq[p_idx], hsf[p_idx], y[p_idx] = h_e, hq_e, hsf_e, y_e
         if keep_acc:
             acc_all[p_idx] = acc
