@@ -14,7 +14,8 @@ better): K calls of moe_w4a4_forward, bracketed by synchronizations and HIP
 events on the stream the kernels run on.  Throughput in TFLOP/s and
 algorithmic HBM GB/s ride along.  The "roofline" object is for GEMM1, the
 dominant kernel (gemm1_swiglu_kernel up to 16 routed rows per expert,
-gemm_lds_kernel above), against the HBM or the FP4 MFMA peak, whichever bounds
+gemm_lds_kernel above), against the HBM or the MFMA peak of the MMA type (MXFP4,
+or FP8 for the fp8xfp4 type), whichever bounds
 its algorithmic bytes and flops: its duration comes from K further steps of the
 same launches in which events on the same stream bracket the GEMM1 launch
 ("split_step_us" is the step time of that loop).  "cpu_baseline" times the fp64 CPU oracle on a
@@ -37,6 +38,7 @@ sys.path.insert(0, ROOT)
 METRIC = "mega-MoE layer µs + TFLOPS + HBM GB/s at ntok=512/4096, DSV4-Flash shape"
 HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E
 FP4_PEAK_TFLOPS = 10100.0         # MI355X dense MXFP4 MFMA
+FP8_PEAK_TFLOPS = 5000.0          # MI355X dense FP8 MFMA: the rate of the FP8 x FP4 mixed form
 COPY_BYTES = 256 << 20           # calibration copy size
 PAGES_US_NTOK512 = 537.6          # W4A4 mega-MoE kernel, 1 B200, 1-rank isolation, ntok=512 (context)
 
@@ -46,14 +48,16 @@ def expert_bytes(H, I):
     return 2 * I * H // 2 + 2 * I * H // 32 + H * I // 2 + H * I // 32
 
 
-def algorithmic(cfg, counts):
+def algorithmic(cfg, counts, fp8=False):
+    """fp8: the fp8xfp4 MMA type, whose x-hat and h-hat take one byte per element."""
     H, I, k, T = cfg.hidden, cfg.inter, cfg.topk, cfg.tokens
+    cb = 1 if fp8 else 2          # elements per activation code byte
     active = int((counts > 0).sum())
     R = int(counts.sum())
     layer_bytes = active * expert_bytes(H, I) + T * (2 * H + 8 * k + 2 * H)
     flops = R * (2 * H * 2 * I + 2 * I * H)
     w1 = 2 * I * H // 2 + 2 * I * H // 32
-    gemm1_bytes = active * w1 + T * (H // 2 + H // 32) + R * (I // 2 + I // 32)
+    gemm1_bytes = active * w1 + T * (H // cb + H // 32) + R * (I // cb + I // 32)
     return dict(active=active, R=R, layer_bytes=layer_bytes, flops=flops, gemm1_bytes=gemm1_bytes,
                 gemm1_flops=R * 2 * H * 2 * I)
 
@@ -98,7 +102,7 @@ def measured_traffic(workload, path):
     return int(round(fetch + write))
 
 
-def cpu_baseline(cfg, x, ids, w, n_experts_sample=40):
+def cpu_baseline(cfg, x, ids, w, n_experts_sample=40, mma_type="mxf4xmxf4"):
     """The oracle as it stands, on a slice: quantize + route of the whole batch,
     then GEMM1/SwiGLU/requant/GEMM2 for all routed rows of a few experts; the
     per-expert time is scaled to the active experts of the layer."""
@@ -121,10 +125,10 @@ def cpu_baseline(cfg, x, ids, w, n_experts_sample=40):
         w1, w2 = synth.expert_weights_f32(cfg, e)
         weights[e] = mxfp4.quantize_packed(w1) + mxfp4.quantize_packed(w2)
     t0 = time.perf_counter()
-    forward(x, ids, w, lambda e: weights[e], cfg.experts, cfg.inter, experts=[])
+    forward(x, ids, w, lambda e: weights[e], cfg.experts, cfg.inter, experts=[], mma_type=mma_type)
     t_common = time.perf_counter() - t0
     t0 = time.perf_counter()
-    forward(x, ids, w, lambda e: weights[e], cfg.experts, cfg.inter, experts=sample)
+    forward(x, ids, w, lambda e: weights[e], cfg.experts, cfg.inter, experts=sample, mma_type=mma_type)
     t_sample = time.perf_counter() - t0 - t_common
     us = (t_common + t_sample / len(sample) * len(active)) * 1e6
     rows = int(sum(counts[e] for e in sample))
@@ -142,6 +146,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="dsv4flash_t512")
+    ap.add_argument("--mma-type", default="mxf4xmxf4", choices=("mxf4xmxf4", "fp8xfp4"),
+                    help="activation format: MXFP4 (the default, W4A4) or MXFP8 E4M3 (W4A8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--threads", type=int, default=16)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -161,7 +167,9 @@ def main():
     cfg = {c.name: c for c in synth.CONFIGS}[args.workload]
     torch.cuda.set_device(0)
     t_setup = time.perf_counter()
-    layer = MoeW4A4Layer(cfg.hidden, cfg.inter, cfg.experts, cfg.topk, cfg.tokens)
+    fp8 = args.mma_type == "fp8xfp4"
+    layer = MoeW4A4Layer(cfg.hidden, cfg.inter, cfg.experts, cfg.topk, cfg.tokens,
+                         mma_type=_lib.MOE_MMA_FP8_X_MXF4 if fp8 else _lib.MOE_MMA_MXF4_X_MXF4)
     layer.load_fp32(lambda e: synth.expert_weights_f32(cfg, e), threads=args.threads)
     x_h = synth.make_tokens(cfg)
     ids_h, w_h = synth.make_routing(cfg)
@@ -231,17 +239,18 @@ def main():
         del src, dst
 
     counts = layer.ws("counts", (cfg.experts,), torch.int32).cpu().numpy()
-    alg = algorithmic(cfg, counts)
+    alg = algorithmic(cfg, counts, fp8)
     us = ms_per_step * 1e3
     tflops = alg["flops"] / (us * 1e-6) / 1e12
     gbps = alg["layer_bytes"] / (us * 1e-6) / 1e9
-    # GEMM1's roofline: HBM-bound unless its flops take longer at the FP4 MFMA
-    # peak than its algorithmic bytes at the HBM peak.
+    # GEMM1's roofline: HBM-bound unless its flops take longer at the MFMA peak
+    # of the MMA type than its algorithmic bytes at the HBM peak.
     path = gemm1_path(cfg)
     g1_kernel = GEMM1_KERNELS[path][0]
-    mfma_bound = alg["gemm1_flops"] / (FP4_PEAK_TFLOPS * 1e12) > alg["gemm1_bytes"] / (HBM_PEAK_GBPS * 1e9)
+    mfma_peak = FP8_PEAK_TFLOPS if fp8 else FP4_PEAK_TFLOPS
+    mfma_bound = alg["gemm1_flops"] / (mfma_peak * 1e12) > alg["gemm1_bytes"] / (HBM_PEAK_GBPS * 1e9)
     if mfma_bound:
-        g1_ach, g1_peak, g1_unit = alg["gemm1_flops"] / (gemm1_us * 1e-6) / 1e12, FP4_PEAK_TFLOPS, "TFLOP/s"
+        g1_ach, g1_peak, g1_unit = alg["gemm1_flops"] / (gemm1_us * 1e-6) / 1e12, mfma_peak, "TFLOP/s"
     else:
         g1_ach, g1_peak, g1_unit = alg["gemm1_bytes"] / (gemm1_us * 1e-6) / 1e9, HBM_PEAK_GBPS, "GB/s"
 
@@ -255,26 +264,27 @@ def main():
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": False,
         "scaling": "weak",
-        "vs_baseline": round(us / PAGES_US_NTOK512, 4) if cfg.name == "dsv4flash_t512" else None,
-        "dtype": "mxfp4",
+        "vs_baseline": round(us / PAGES_US_NTOK512, 4) if cfg.name == "dsv4flash_t512" and not fp8 else None,
+        "dtype": "mxfp8 x mxfp4" if fp8 else "mxfp4",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "tokens": T, "hidden": cfg.hidden, "inter": cfg.inter,
+        "config": {"workload": cfg.name, "mma_type": args.mma_type, "tokens": T, "hidden": cfg.hidden,
+                   "inter": cfg.inter,
                    "experts": cfg.experts, "topk": cfg.topk, "routing": cfg.routing,
                    "active_experts": alg["active"], "routed_rows": alg["R"]},
         "tflops": round(tflops, 2),
-        "tflops_frac": round(tflops / FP4_PEAK_TFLOPS, 4),
+        "tflops_frac": round(tflops / mfma_peak, 4),
         "hbm_gbps": round(gbps, 1),
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "split_step_us": round(split_ms * 1e3, 2),
         "roofline": {"kernel": g1_kernel, "bound": "mfma" if mfma_bound else "hbm", "achieved": round(g1_ach, 1),
                      "peak": g1_peak, "unit": g1_unit, "frac": round(g1_ach / g1_peak, 4),
-                     "traffic": measured_traffic(cfg.name, path), "avg_us": round(gemm1_us, 2),
+                     "traffic": None if fp8 else measured_traffic(cfg.name, path), "avg_us": round(gemm1_us, 2),
                      "bytes_per_launch": alg["gemm1_bytes"], "flops_per_launch": alg["gemm1_flops"]},
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle slice)", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(cfg, x_h, ids_h, w_h)
+        res["cpu_baseline"] = cpu_baseline(cfg, x_h, ids_h, w_h, mma_type=args.mma_type)
     print(json.dumps(res), flush=True)
 
 

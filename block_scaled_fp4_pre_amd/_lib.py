@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_w4a4.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ECAPACITY, MOE_EWORKSPACE, MOE_ENODEVICE, MOE_EHIP = range(7)
-MOE_MMA_MXF4_X_MXF4 = 0
+MOE_MMA_MXF4_X_MXF4, MOE_MMA_FP8_X_MXF4 = 0, 1
 MOE_ACT_SWIGLU = 0
 MOE_STAGE_QUANT, MOE_STAGE_ROUTE, MOE_STAGE_GEMM1, MOE_STAGE_GEMM2, MOE_STAGE_COMBINE = 1, 2, 4, 8, 16
 MOE_STAGE_ALL = 31

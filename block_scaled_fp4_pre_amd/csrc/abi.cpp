@@ -40,7 +40,8 @@ int check_cfg(const moe_w4a4_cfg* c) {
   if (c->hidden % 256 != 0 || c->inter % 128 != 0) return MOE_EUNSUPPORTED;
   if (c->hidden > (1 << 16) || c->inter > (1 << 16)) return MOE_EUNSUPPORTED;
   if (c->num_experts > kMaxExperts || c->topk > kMaxTopk) return MOE_EUNSUPPORTED;
-  if (c->group_size != 32 || c->mma_type != MOE_MMA_MXF4_X_MXF4 || c->activation != MOE_ACT_SWIGLU)
+  if (c->group_size != 32 || (c->mma_type != MOE_MMA_MXF4_X_MXF4 && c->mma_type != MOE_MMA_FP8_X_MXF4) ||
+      c->activation != MOE_ACT_SWIGLU)
     return MOE_EUNSUPPORTED;
   if ((int64_t)c->max_tokens * c->topk >= (int64_t)1 << 31) return MOE_EUNSUPPORTED;
   return MOE_OK;
@@ -68,14 +69,15 @@ moe_w4a4_ws_layout ws_layout(const moe_w4a4_cfg* c) {
   const uint64_t nb = (R + kRouteRows - 1) / kRouteRows;
   moe_w4a4_ws_layout L{};
   uint64_t off = 0;
-  L.xq = off; off = align256(off + M * H / 2);
+  const uint64_t ab = c->mma_type == MOE_MMA_FP8_X_MXF4 ? 2 : 1;   // activation bytes per 2 elements
+  L.xq = off; off = align256(off + M * H / 2 * ab);
   L.xsf = off; off = align256(off + M * H / 32);
   L.counts = off; off = align256(off + E * 4);
   L.offsets = off; off = align256(off + (E + 1) * 4);
   L.sorted_rows = off; off = align256(off + R * 4);
   L.pos = off; off = align256(off + R * 4);
   L.hist = off; off = align256(off + nb * E * 4);
-  L.hq = off; off = align256(off + R * I / 2);
+  L.hq = off; off = align256(off + R * I / 2 * ab);
   L.hsf = off; off = align256(off + R * I / 32);
   L.y = off; off = align256(off + R * H * 2);
   L.tiles = off; off = align256(off + (R / 16 + E + 1) * 8);
@@ -164,7 +166,7 @@ int moe_w4a4_quantize(int32_t src_dtype, const void* src, int64_t rows, int32_t 
   if (!aligned(src, 16) || !aligned(codes, 16)) return MOE_EINVAL;
   const int dv = check_device();
   if (dv != MOE_OK) return dv;
-  return hip_status(moe::launch_quantize(src_dtype == 0, src, rows * (int64_t)(cols / 32), codes, scales,
+  return hip_status(moe::launch_quantize(src_dtype == 0, false, src, rows * (int64_t)(cols / 32), codes, scales,
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -209,6 +211,7 @@ int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t n
   if (st != MOE_OK) return st;
 
   const int H = cfg->hidden, I = cfg->inter, E = cfg->num_experts, k = cfg->topk;
+  const bool fp8 = cfg->mma_type == MOE_MMA_FP8_X_MXF4;   // E4M3 activations
   const int T = num_tokens, R = T * k;
   const int rows_hint = (int)(((int64_t)R + E - 1) / E);
   // Few rows per expert: stream each expert's weights once with the whole
@@ -238,12 +241,12 @@ int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t n
 
   if ((stages & MOE_STAGE_QUANT) && (stages & MOE_STAGE_ROUTE) && R <= moe::kPredispatchMaxRows) {
     // pre-dispatch in one launch: one block routes, the others quantize
-    st = hip_status(moe::launch_predispatch(x, (int64_t)T * (H / 32), xq, xsf, topk_ids, R, E, counts, offsets,
+    st = hip_status(moe::launch_predispatch(fp8, x, (int64_t)T * (H / 32), xq, xsf, topk_ids, R, E, counts, offsets,
                                             sorted_rows, pos, tile_rows, tiles, num_tiles, s));
     if (st != MOE_OK) return st;
   } else {
     if (stages & MOE_STAGE_QUANT) {
-      st = hip_status(moe::launch_quantize(true, x, (int64_t)T * (H / 32), xq, xsf, s));
+      st = hip_status(moe::launch_quantize(true, fp8, x, (int64_t)T * (H / 32), xq, xsf, s));
       if (st != MOE_OK) return st;
     }
     if (stages & MOE_STAGE_ROUTE) {
@@ -257,17 +260,17 @@ int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t n
       st = hip_status(moe::launch_sorted_scales(xsf, sorted_rows, offsets, E, R, H, k, hrows, xsf_planes, s));
       if (st != MOE_OK) return st;
     }
-    st = hip_status(tiled ? moe::launch_gemm1_lds(pw + P.w1c, pw + P.w1s, xq, xsf_planes, counts, offsets,
+    st = hip_status(tiled ? moe::launch_gemm1_lds(fp8, pw + P.w1c, pw + P.w1s, xq, xsf_planes, counts, offsets,
                                                   sorted_rows, tiles, num_tiles, max_tiles, rows_hint, H, I, k,
                                                   hrows, hq, hsf, gemm1_acc, s)
-                          : moe::launch_gemm1(pw + P.w1c, pw + P.w1s, xq, xsf, counts, offsets, sorted_rows,
+                          : moe::launch_gemm1(fp8, pw + P.w1c, pw + P.w1s, xq, xsf, counts, offsets, sorted_rows,
                                               H, I, E, k, rows_hint, hrows, hq, hsf, gemm1_acc, s));
     if (st != MOE_OK) return st;
   }
   if (stages & MOE_STAGE_GEMM2) {
-    st = hip_status(tiled ? moe::launch_gemm2_lds(pw + P.w2c, pw + P.w2s, hq, hsf, counts, offsets, tiles,
+    st = hip_status(tiled ? moe::launch_gemm2_lds(fp8, pw + P.w2c, pw + P.w2s, hq, hsf, counts, offsets, tiles,
                                                   num_tiles, max_tiles, rows_hint, H, I, hrows, y, s)
-                          : moe::launch_gemm2(pw + P.w2c, pw + P.w2s, hq, hsf, counts, offsets, H, I, E,
+                          : moe::launch_gemm2(fp8, pw + P.w2c, pw + P.w2s, hq, hsf, counts, offsets, H, I, E,
                                               rows_hint, hrows, y, s));
     if (st != MOE_OK) return st;
   }

@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "e4m3.h"
+
 namespace moe {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -63,6 +65,20 @@ __device__ __forceinline__ v4f mfma_fp4(const uint4& a, const uint4& b, const v4
   const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
   const v8i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, OA, sa, OB, sb);
+}
+
+// The same MFMA with the token operand in FP8 E4M3 (format code 0; the fp8xfp4
+// MMA type).  Lane l supplies 32 bytes of token column l % 16: lo = K elements
+// [16g, 16g+16) and hi = K elements [64+16g, 64+16g+16), g = l / 16 -- not the
+// FP4 operand's one run [32g, 32g+32) (mapped on MI355X with a single 1.0 in
+// the FP4 operand against 128 distinct FP8 codes).  The scale byte of lane l
+// still belongs to the 32-element block g, as for FP4.
+template <int OA, int OB>
+__device__ __forceinline__ v4f mfma_fp4_fp8(const uint4& a, const uint4& blo, const uint4& bhi, const v4f& c, int sa,
+                                            int sb) {
+  const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const v8i bv = {(int)blo.x, (int)blo.y, (int)blo.z, (int)blo.w, (int)bhi.x, (int)bhi.y, (int)bhi.z, (int)bhi.w};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 0, OA, sa, OB, sb);
 }
 
 }  // namespace moe

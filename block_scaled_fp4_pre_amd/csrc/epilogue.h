@@ -24,13 +24,16 @@ __device__ __forceinline__ float swiglu(float g, float u) {
 // over the 4 lanes of a token (xor 16, xor 32), then codes packed two per byte
 // (even column in the low nibble).  row0: sorted position of token column 0.
 //
+// F8 (the fp8xfp4 MMA type): h is requantized to E4M3 instead (e4m3.h), one
+// byte per column.
+//
 // hq and hsf are K-step planes for GEMM2: plane c (inter columns [128c,
-// 128c+128)) holds, for every sorted row p, its 64 code bytes at
-// (c * hrows + p) * 64 and its 4 scale bytes at (c * hrows + p) * 4, hrows
-// being the rows of a plane.  A tile of consecutive rows then reads one
-// contiguous run per K step.  Unit u is 16 code bytes and scale byte u % 4 of
-// plane u / 4.
-template <int NT>
+// 128c+128)) holds, for every sorted row p, its PB = 64 (E4M3: 128) code
+// bytes at (c * hrows + p) * PB and its 4 scale bytes at (c * hrows + p) * 4,
+// hrows being the rows of a plane.  A tile of consecutive rows then reads one
+// contiguous run per K step.  Unit u is PB / 4 code bytes and scale byte u % 4
+// of plane u / 4.
+template <int NT, bool F8 = false>
 __device__ __forceinline__ void gemm1_epilogue(v4f (&acc)[NT][4], int u, int row0, int nrows, int I, int hrows,
                                                int lane, uint8_t* __restrict__ hq, uint8_t* __restrict__ hsf,
                                                float* __restrict__ acc_out) {
@@ -53,15 +56,23 @@ __device__ __forceinline__ void gemm1_epilogue(v4f (&acc)[NT][4], int u, int row
     for (int i = 0; i < 8; ++i) amax = max(amax, __float_as_uint(h[i]) & 0x7FFFFFFFu);
     amax = max(amax, (uint32_t)__shfl_xor((int)amax, 16, 64));
     amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32, 64));
-    const int ex = mx_scale_exp(amax);
-    const float sc = exp2_scale(ex);
-    const uint32_t lo = e2m1_pack2<1>(e2m1_pack2<0>(0u, h[0], h[1], sc), h[2], h[3], sc);
-    const uint32_t hi = e2m1_pack2<1>(e2m1_pack2<0>(0u, h[4], h[5], sc), h[6], h[7], sc);
+    const int ex = F8 ? mx8_scale_exp(amax) : mx_scale_exp(amax);
     if (live) {
       const size_t pr = (size_t)(u >> 2) * hrows + p;   // row p of plane u / 4
-      uint8_t* row = hq + pr * 64 + (u & 3) * 16;
-      *reinterpret_cast<uint16_t*>(row + 2 * kb) = (uint16_t)lo;
-      *reinterpret_cast<uint16_t*>(row + 8 + 2 * kb) = (uint16_t)hi;
+      if constexpr (F8) {
+        // columns 4kb..4kb+3 and 16+4kb..16+4kb+3 of the unit's 32 bytes
+        const float inv = e4m3_exp2(-ex);
+        uint8_t* row = hq + pr * 128 + (u & 3) * 32;
+        *reinterpret_cast<uint32_t*>(row + 4 * kb) = e4m3_pack4(h[0], h[1], h[2], h[3], inv);
+        *reinterpret_cast<uint32_t*>(row + 16 + 4 * kb) = e4m3_pack4(h[4], h[5], h[6], h[7], inv);
+      } else {
+        const float sc = exp2_scale(ex);
+        const uint32_t lo = e2m1_pack2<1>(e2m1_pack2<0>(0u, h[0], h[1], sc), h[2], h[3], sc);
+        const uint32_t hi = e2m1_pack2<1>(e2m1_pack2<0>(0u, h[4], h[5], sc), h[6], h[7], sc);
+        uint8_t* row = hq + pr * 64 + (u & 3) * 16;
+        *reinterpret_cast<uint16_t*>(row + 2 * kb) = (uint16_t)lo;
+        *reinterpret_cast<uint16_t*>(row + 8 + 2 * kb) = (uint16_t)hi;
+      }
       if (kb == 0) hsf[pr * 4 + (u & 3)] = (uint8_t)(ex + 127);
       if (acc_out != nullptr) {
         float* arow = acc_out + (size_t)p * (2 * I) + 32 * u + 4 * kb;

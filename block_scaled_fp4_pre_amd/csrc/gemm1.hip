@@ -22,6 +22,10 @@
 // then 4 MFMAs (one per 16-row block) per token tile per K step of 128.
 // Epilogue per lane: gate/up of 8 columns for one token; the 32-column absmax
 // is reduced over the 4 lanes holding that token (xor 16, xor 32).
+//
+// F8 (the fp8xfp4 MMA type, [P3] "Implementation breakdown" items 1-3): the
+// tokens are E4M3 bytes, twice the LDS per row, the B operand of each MFMA
+// takes 32 bytes (format code 0), and h is requantized to E4M3.
 #include "epilogue.h"
 #include "gemm_common.h"
 #include "launch.h"
@@ -40,7 +44,7 @@
 
 namespace moe {
 
-template <int NT, int D, int SWZ>
+template <int NT, int D, int SWZ, bool F8>
 __global__ void __launch_bounds__(256, 2) gemm1_swiglu_kernel(
     const uint8_t* __restrict__ w1c, const uint8_t* __restrict__ w1s, const uint8_t* __restrict__ xq,
     const uint8_t* __restrict__ xsf, const int32_t* __restrict__ counts,
@@ -57,7 +61,7 @@ __global__ void __launch_bounds__(256, 2) gemm1_swiglu_kernel(
   const int u0 = g * 4 * upw + wave;   // wave w owns unit w of each of the workgroup's upw unit groups
   const int S = H / kStepK;
   const int total_steps = upw * S;       // the wave's upw units: one stream at stride kUnitStepStride
-  const int row_bytes = H / 2, sc_bytes = H / 32;
+  const int row_bytes = F8 ? H : H / 2, sc_bytes = H / 32;   // token row: E4M3 bytes or packed E2M1
 
   // Rows per pass: 16 for one token tile; MOE_STREAM_ROWS2 (<= 32) for two.  A
   // cap below 32 trades a rare second pass for less LDS per workgroup; B-operand
@@ -109,12 +113,21 @@ __global__ void __launch_bounds__(256, 2) gemm1_swiglu_kernel(
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const int n = min(nt * 16 + tok_lane, ROWS - 1);
-          const uint4 b = tile_operand<SWZ>(lds_codes, row_bytes, n, s, kb);
           const int sb = tile_scale(lds_scales, sc_bytes, n, s, kb);
-          acc[nt][0] = mfma_fp4<0, 0>(a[d][0], b, acc[nt][0], (int)sa[d], sb);
-          acc[nt][1] = mfma_fp4<1, 0>(a[d][1], b, acc[nt][1], (int)sa[d], sb);
-          acc[nt][2] = mfma_fp4<2, 0>(a[d][2], b, acc[nt][2], (int)sa[d], sb);
-          acc[nt][3] = mfma_fp4<3, 0>(a[d][3], b, acc[nt][3], (int)sa[d], sb);
+          if constexpr (F8) {
+            uint4 blo, bhi;
+            tile_operand8<SWZ>(lds_codes, row_bytes, n, s, kb, blo, bhi);
+            acc[nt][0] = mfma_fp4_fp8<0, 0>(a[d][0], blo, bhi, acc[nt][0], (int)sa[d], sb);
+            acc[nt][1] = mfma_fp4_fp8<1, 0>(a[d][1], blo, bhi, acc[nt][1], (int)sa[d], sb);
+            acc[nt][2] = mfma_fp4_fp8<2, 0>(a[d][2], blo, bhi, acc[nt][2], (int)sa[d], sb);
+            acc[nt][3] = mfma_fp4_fp8<3, 0>(a[d][3], blo, bhi, acc[nt][3], (int)sa[d], sb);
+          } else {
+            const uint4 b = tile_operand<SWZ>(lds_codes, row_bytes, n, s, kb);
+            acc[nt][0] = mfma_fp4<0, 0>(a[d][0], b, acc[nt][0], (int)sa[d], sb);
+            acc[nt][1] = mfma_fp4<1, 0>(a[d][1], b, acc[nt][1], (int)sa[d], sb);
+            acc[nt][2] = mfma_fp4<2, 0>(a[d][2], b, acc[nt][2], (int)sa[d], sb);
+            acc[nt][3] = mfma_fp4<3, 0>(a[d][3], b, acc[nt][3], (int)sa[d], sb);
+          }
         }
         const int jn = j0 + d + D;
 #pragma unroll
@@ -124,20 +137,22 @@ __global__ void __launch_bounds__(256, 2) gemm1_swiglu_kernel(
       if (s0 + D != S) continue;
 
       // Unit finished: SwiGLU + requant of its 32 columns for the tile's rows.
-      gemm1_epilogue<NT>(acc, u0 + kGroupUnits * (j0 / S), base + t0, nrows, I, hrows, lane, hq, hsf, acc_out);
+      gemm1_epilogue<NT, F8>(acc, u0 + kGroupUnits * (j0 / S), base + t0, nrows, I, hrows, lane, hq, hsf, acc_out);
       zero_acc<NT>(acc);
     }
   }
 }
 
-template <int NT, int D, int SWZ>
+#define MOE_GEMM1_ARGS w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hrows, hq, hsf, acc_out, stream
+
+template <int NT, int D, int SWZ, bool F8>
 static hipError_t launch_gemm1_t(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq,
                                  const uint8_t* xsf, const int32_t* counts, const int32_t* offsets,
                                  const int32_t* sorted_rows, int H, int I, int E, int k, int hrows, uint8_t* hq,
                                  uint8_t* hsf, float* acc_out, hipStream_t stream) {
   constexpr int ROWS = NT == 1 ? 16 : MOE_STREAM_ROWS2;
-  const size_t lds = (size_t)ROWS * (H / 2) + (size_t)ROWS * (H / 32);
-  auto kern = gemm1_swiglu_kernel<NT, D, SWZ>;
+  const size_t lds = (size_t)ROWS * (F8 ? H : H / 2) + (size_t)ROWS * (H / 32);
+  auto kern = gemm1_swiglu_kernel<NT, D, SWZ, F8>;
   const int upw = units_per_wave(I / 32 / 4, MOE_GEMM1_UNITS_PER_WAVE);
   if (lds > 65536) {
     hipError_t err = raise_lds_limit(reinterpret_cast<const void*>(kern), lds);
@@ -148,43 +163,37 @@ static hipError_t launch_gemm1_t(const uint8_t* w1c, const uint8_t* w1s, const u
   return hipGetLastError();
 }
 
-template <int NT, int D>
+template <int NT, int D, bool F8>
 static hipError_t launch_gemm1_nt(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq,
                                   const uint8_t* xsf, const int32_t* counts, const int32_t* offsets,
                                   const int32_t* sorted_rows, int H, int I, int E, int k, int hrows, uint8_t* hq,
                                   uint8_t* hsf, float* acc_out, hipStream_t stream) {
-  const int chunks = H / 32;  // 16-byte chunks per token row; a multiple of 8
-  if (chunks % 16 == 0)
-    return launch_gemm1_t<NT, D, 16>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hrows, hq, hsf,
-                                     acc_out, stream);
-  return launch_gemm1_t<NT, D, 8>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hrows, hq, hsf,
-                                  acc_out, stream);
+  const int chunks = F8 ? H / 16 : H / 32;  // 16-byte chunks per token row; a multiple of 8
+  if (chunks % 16 == 0) return launch_gemm1_t<NT, D, 16, F8>(MOE_GEMM1_ARGS);
+  return launch_gemm1_t<NT, D, 8, F8>(MOE_GEMM1_ARGS);
 }
 
-template <int NT>
+template <int NT, bool F8>
 static hipError_t launch_gemm1_d(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq,
                                  const uint8_t* xsf, const int32_t* counts, const int32_t* offsets,
                                  const int32_t* sorted_rows, int H, int I, int E, int k, int hrows, uint8_t* hq,
                                  uint8_t* hsf, float* acc_out, hipStream_t stream) {
   // The ring depth must divide the number of K steps H/128 (even, as H % 256 == 0).
-  if ((H / kStepK) % MOE_STREAM_RING_DEPTH == 0)
-    return launch_gemm1_nt<NT, MOE_STREAM_RING_DEPTH>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hrows, hq, hsf,
-                                  acc_out, stream);
-  return launch_gemm1_nt<NT, 2>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hrows, hq, hsf,
-                                acc_out, stream);
+  if ((H / kStepK) % MOE_STREAM_RING_DEPTH == 0) return launch_gemm1_nt<NT, MOE_STREAM_RING_DEPTH, F8>(MOE_GEMM1_ARGS);
+  return launch_gemm1_nt<NT, 2, F8>(MOE_GEMM1_ARGS);
 }
 
-hipError_t launch_gemm1(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq, const uint8_t* xsf,
+hipError_t launch_gemm1(bool fp8, const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq, const uint8_t* xsf,
                         const int32_t* counts, const int32_t* offsets, const int32_t* sorted_rows,
                         int H, int I, int E, int k, int rows_hint, int hrows, uint8_t* hq, uint8_t* hsf,
                         float* acc_out, hipStream_t stream) {
   // rows_hint: mean routed rows per expert; two token tiles per pass once a
   // single 16-row tile would often overflow (and re-stream the weights).
   if (rows_hint > 8)
-    return launch_gemm1_d<2>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hrows, hq, hsf, acc_out,
-                             stream);
-  return launch_gemm1_d<1>(w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hrows, hq, hsf, acc_out,
-                           stream);
+    return fp8 ? launch_gemm1_d<2, true>(MOE_GEMM1_ARGS) : launch_gemm1_d<2, false>(MOE_GEMM1_ARGS);
+  return fp8 ? launch_gemm1_d<1, true>(MOE_GEMM1_ARGS) : launch_gemm1_d<1, false>(MOE_GEMM1_ARGS);
 }
+
+#undef MOE_GEMM1_ARGS
 
 }  // namespace moe

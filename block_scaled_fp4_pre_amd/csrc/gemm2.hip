@@ -12,7 +12,9 @@
 // of tiles.h), writing y at each unit's end.  The expert's requantized rows are
 // consecutive in every K-step plane of hq/hsf (epilogue.h), so the B tile is
 // one contiguous run per plane, copied into LDS by direct-to-LDS loads;
-// weights stream through the register ring of gemm_common.h.
+// weights stream through the register ring of gemm_common.h.  F8 (the
+// fp8xfp4 MMA type): h arrives as E4M3 bytes and the MFMA's B operand takes 32
+// bytes (format code 0).
 #include "epilogue.h"
 #include "gemm_common.h"
 #include "launch.h"
@@ -35,7 +37,7 @@
 
 namespace moe {
 
-template <int NT, int D, int SWZ>
+template <int NT, int D, int SWZ, bool F8>
 __global__ void __launch_bounds__(256, MOE_GEMM2_MIN_BLOCKS) gemm2_kernel(
     const uint8_t* __restrict__ w2c, const uint8_t* __restrict__ w2s, const uint8_t* __restrict__ hq,
     const uint8_t* __restrict__ hsf, const int32_t* __restrict__ counts,
@@ -51,7 +53,7 @@ __global__ void __launch_bounds__(256, MOE_GEMM2_MIN_BLOCKS) gemm2_kernel(
   const int v0 = g * 4 * upw + wave;   // wave w owns unit w of each of the workgroup's upw unit groups
   const int S = I / kStepK;
   const int total_steps = upw * S;       // the wave's upw units: one stream at stride kUnitStepStride
-  const int row_bytes = I / 2, sc_bytes = I / 32;
+  const int row_bytes = F8 ? I : I / 2, sc_bytes = I / 32;   // E4M3 bytes or packed E2M1
 
   // Rows per pass: 16 for one token tile; MOE_STREAM_ROWS2 (<= 32) for two.  A
   // cap below 32 trades a rare second pass for less LDS per workgroup; B-operand
@@ -81,8 +83,8 @@ __global__ void __launch_bounds__(256, MOE_GEMM2_MIN_BLOCKS) gemm2_kernel(
     }
     __syncthreads();
     const int row0 = base + t0;
-    gather_tile<ROWS, SWZ, true>(lds_codes, lds_scales, hq, hsf, row_bytes, sc_bytes, nrows,
-                                 [&](int n) { return row0 + n; }, wave, lane, 4, hrows);
+    gather_tile<ROWS, SWZ, true, F8 ? 128 : 64>(lds_codes, lds_scales, hq, hsf, row_bytes, sc_bytes, nrows,
+                                                [&](int n) { return row0 + n; }, wave, lane, 4, hrows);
     wait_vmem_all();
     __syncthreads();
 
@@ -102,12 +104,21 @@ __global__ void __launch_bounds__(256, MOE_GEMM2_MIN_BLOCKS) gemm2_kernel(
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const int n = min(nt * 16 + tok_lane, ROWS - 1);
-          const uint4 b = tile_operand<SWZ>(lds_codes, row_bytes, n, s, kb);
           const int sb = tile_scale(lds_scales, sc_bytes, n, s, kb);
-          acc[nt][0] = mfma_fp4<0, 0>(a[d][0], b, acc[nt][0], (int)sa[d], sb);
-          acc[nt][1] = mfma_fp4<1, 0>(a[d][1], b, acc[nt][1], (int)sa[d], sb);
-          acc[nt][2] = mfma_fp4<2, 0>(a[d][2], b, acc[nt][2], (int)sa[d], sb);
-          acc[nt][3] = mfma_fp4<3, 0>(a[d][3], b, acc[nt][3], (int)sa[d], sb);
+          if constexpr (F8) {
+            uint4 blo, bhi;
+            tile_operand8<SWZ>(lds_codes, row_bytes, n, s, kb, blo, bhi);
+            acc[nt][0] = mfma_fp4_fp8<0, 0>(a[d][0], blo, bhi, acc[nt][0], (int)sa[d], sb);
+            acc[nt][1] = mfma_fp4_fp8<1, 0>(a[d][1], blo, bhi, acc[nt][1], (int)sa[d], sb);
+            acc[nt][2] = mfma_fp4_fp8<2, 0>(a[d][2], blo, bhi, acc[nt][2], (int)sa[d], sb);
+            acc[nt][3] = mfma_fp4_fp8<3, 0>(a[d][3], blo, bhi, acc[nt][3], (int)sa[d], sb);
+          } else {
+            const uint4 b = tile_operand<SWZ>(lds_codes, row_bytes, n, s, kb);
+            acc[nt][0] = mfma_fp4<0, 0>(a[d][0], b, acc[nt][0], (int)sa[d], sb);
+            acc[nt][1] = mfma_fp4<1, 0>(a[d][1], b, acc[nt][1], (int)sa[d], sb);
+            acc[nt][2] = mfma_fp4<2, 0>(a[d][2], b, acc[nt][2], (int)sa[d], sb);
+            acc[nt][3] = mfma_fp4<3, 0>(a[d][3], b, acc[nt][3], (int)sa[d], sb);
+          }
         }
         const int jn = j0 + d + D;
 #pragma unroll
@@ -123,13 +134,15 @@ __global__ void __launch_bounds__(256, MOE_GEMM2_MIN_BLOCKS) gemm2_kernel(
   }
 }
 
-template <int NT, int D, int SWZ>
+#define MOE_GEMM2_ARGS w2c, w2s, hq, hsf, counts, offsets, H, I, E, hrows, y, stream
+
+template <int NT, int D, int SWZ, bool F8>
 static hipError_t launch_gemm2_t(const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq,
                                  const uint8_t* hsf, const int32_t* counts, const int32_t* offsets,
                                  int H, int I, int E, int hrows, uint16_t* y, hipStream_t stream) {
   constexpr int ROWS = NT == 1 ? 16 : MOE_STREAM_ROWS2;
-  const size_t lds = (size_t)ROWS * (I / 2) + (size_t)ROWS * (I / 32);
-  auto kern = gemm2_kernel<NT, D, SWZ>;
+  const size_t lds = (size_t)ROWS * (F8 ? I : I / 2) + (size_t)ROWS * (I / 32);
+  auto kern = gemm2_kernel<NT, D, SWZ, F8>;
   const int upw = units_per_wave(H / kUnitRows / 4, MOE_GEMM2_UNITS_PER_WAVE);
   if (lds > 65536) {
     hipError_t err = raise_lds_limit(reinterpret_cast<const void*>(kern), lds);
@@ -140,32 +153,34 @@ static hipError_t launch_gemm2_t(const uint8_t* w2c, const uint8_t* w2s, const u
   return hipGetLastError();
 }
 
-template <int NT, int D>
+template <int NT, int D, bool F8>
 static hipError_t launch_gemm2_nt(const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq,
                                   const uint8_t* hsf, const int32_t* counts, const int32_t* offsets,
                                   int H, int I, int E, int hrows, uint16_t* y, hipStream_t stream) {
-  const int chunks = I / 32;  // a multiple of 4
-  if (chunks % 16 == 0) return launch_gemm2_t<NT, D, 16>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, hrows, y, stream);
-  if (chunks % 8 == 0) return launch_gemm2_t<NT, D, 8>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, hrows, y, stream);
-  return launch_gemm2_t<NT, D, 4>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, hrows, y, stream);
+  const int chunks = F8 ? I / 16 : I / 32;  // 16-byte chunks per token row; a multiple of 4
+  if (chunks % 16 == 0) return launch_gemm2_t<NT, D, 16, F8>(MOE_GEMM2_ARGS);
+  if (chunks % 8 == 0) return launch_gemm2_t<NT, D, 8, F8>(MOE_GEMM2_ARGS);
+  return launch_gemm2_t<NT, D, 4, F8>(MOE_GEMM2_ARGS);
 }
 
-template <int NT>
+template <int NT, bool F8>
 static hipError_t launch_gemm2_d(const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq,
                                  const uint8_t* hsf, const int32_t* counts, const int32_t* offsets,
                                  int H, int I, int E, int hrows, uint16_t* y, hipStream_t stream) {
   // The ring depth must divide the number of K steps I/128.
   const int S = I / kStepK;
-  if (S % MOE_STREAM_RING_DEPTH == 0) return launch_gemm2_nt<NT, MOE_STREAM_RING_DEPTH>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, hrows, y, stream);
-  if (S % 2 == 0) return launch_gemm2_nt<NT, 2>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, hrows, y, stream);
-  return launch_gemm2_nt<NT, 1>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, hrows, y, stream);
+  if (S % MOE_STREAM_RING_DEPTH == 0) return launch_gemm2_nt<NT, MOE_STREAM_RING_DEPTH, F8>(MOE_GEMM2_ARGS);
+  if (S % 2 == 0) return launch_gemm2_nt<NT, 2, F8>(MOE_GEMM2_ARGS);
+  return launch_gemm2_nt<NT, 1, F8>(MOE_GEMM2_ARGS);
 }
 
-hipError_t launch_gemm2(const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq, const uint8_t* hsf,
+hipError_t launch_gemm2(bool fp8, const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq, const uint8_t* hsf,
                         const int32_t* counts, const int32_t* offsets, int H, int I, int E,
                         int rows_hint, int hrows, uint16_t* y, hipStream_t stream) {
-  if (rows_hint > 8) return launch_gemm2_d<2>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, hrows, y, stream);
-  return launch_gemm2_d<1>(w2c, w2s, hq, hsf, counts, offsets, H, I, E, hrows, y, stream);
+  if (rows_hint > 8) return fp8 ? launch_gemm2_d<2, true>(MOE_GEMM2_ARGS) : launch_gemm2_d<2, false>(MOE_GEMM2_ARGS);
+  return fp8 ? launch_gemm2_d<1, true>(MOE_GEMM2_ARGS) : launch_gemm2_d<1, false>(MOE_GEMM2_ARGS);
 }
+
+#undef MOE_GEMM2_ARGS
 
 }  // namespace moe

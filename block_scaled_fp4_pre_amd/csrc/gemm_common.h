@@ -77,10 +77,11 @@ __device__ __forceinline__ int scale_swizzle(int sc_bytes) {
 // Copy ROWS token rows into LDS.  Row n (n < nrows) is global row
 // row_index(n) of `codes` and `scales`: row-major (row_bytes and sc_bytes per
 // row) when PLANES is false; in K-step planes of hrows rows when it is true
-// (64 code bytes and one scale dword per row and plane; epilogue.h).  sc_bytes
-// is a multiple of 4.  Lanes whose slot lies past the last row are masked off,
-// so ROWS * row_bytes need not be a multiple of 1024.
-template <int ROWS, int SWZ, bool PLANES = false, class RowIndex>
+// (PB code bytes -- 64 for E2M1, 128 for E4M3 -- and one scale dword per row
+// and plane; epilogue.h).  sc_bytes is a multiple of 4.  Lanes whose slot lies
+// past the last row are masked off, so ROWS * row_bytes need not be a
+// multiple of 1024.
+template <int ROWS, int SWZ, bool PLANES = false, int PB = 64, class RowIndex>
 __device__ __forceinline__ void gather_tile(uint8_t* lds_codes, uint8_t* lds_scales, const uint8_t* codes,
                                             const uint8_t* scales, int row_bytes, int sc_bytes, int nrows,
                                             RowIndex row_index, int wave, int lane, int nwaves, int hrows = 0) {
@@ -92,7 +93,8 @@ __device__ __forceinline__ void gather_tile(uint8_t* lds_codes, uint8_t* lds_sca
     const int src = row_index(n);            // evaluated by every lane (it may shuffle)
     if (n < nrows) {
       const int c = pos ^ (n & (SWZ - 1));
-      const size_t off = PLANES ? ((size_t)(c >> 2) * hrows + src) * 64 + (c & 3) * 16
+      constexpr int CPP = PB / 16;           // 16-byte chunks per plane row
+      const size_t off = PLANES ? ((size_t)(c / CPP) * hrows + src) * PB + (c % CPP) * 16
                                 : (size_t)src * row_bytes + c * 16;
       lds_dma16(codes + off, lds_codes + j * 1024);
     }
@@ -124,6 +126,17 @@ template <int SWZ>
 __device__ __forceinline__ uint4 tile_operand(const uint8_t* lds_codes, int row_bytes, int n, int s, int kb) {
   const int pos = (s * 4 + kb) ^ (n & (SWZ - 1));
   return *reinterpret_cast<const uint4*>(lds_codes + n * row_bytes + pos * 16);
+}
+
+// The same for E4M3 codes (one byte per element): lane group kb takes the
+// 16-element chunks kb and kb + 4 of step s (the FP8 operand layout,
+// device_common.h).
+template <int SWZ>
+__device__ __forceinline__ void tile_operand8(const uint8_t* lds_codes, int row_bytes, int n, int s, int kb,
+                                              uint4& lo, uint4& hi) {
+  const int c = s * 8 + kb;
+  lo = *reinterpret_cast<const uint4*>(lds_codes + n * row_bytes + (c ^ (n & (SWZ - 1))) * 16);
+  hi = *reinterpret_cast<const uint4*>(lds_codes + n * row_bytes + ((c + 4) ^ (n & (SWZ - 1))) * 16);
 }
 
 }  // namespace moe

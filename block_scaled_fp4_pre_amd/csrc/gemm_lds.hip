@@ -15,6 +15,9 @@
 // A weight block is one unit group of the tile order (tiles.h): its 4 units'
 // chunks of a step are one contiguous 16 KiB.
 //
+// F8 (the fp8xfp4 MMA type): the token codes are E4M3 bytes, 128 per row and
+// K step instead of 64, and each MFMA's B operand is two 16-byte pieces.
+//
 // Per stage each wave issues its share of the DMA: its unit's 4 KiB of weight
 // codes and 256 B of weight scales (already in MFMA operand order), a quarter
 // of the token rows' 64-byte code pieces (gathered by row index; 16-byte piece
@@ -45,14 +48,15 @@
 
 namespace moe {
 
-// One stage of the ring for WAVES waves (one weight unit each) and NT*16 token rows.
-template <int NT, int WAVES>
+// One stage of the ring for WAVES waves (one weight unit each) and NT*16 token
+// rows of TB code bytes per K step (64: E2M1; 128: E4M3, the fp8xfp4 MMA type).
+template <int NT, int WAVES, int TB>
 struct LdsStage {
   static constexpr int ROWS = NT * 16;
   static constexpr int W_CODES = 0;                          // WAVES units x 4 KiB
   static constexpr int W_SCALES = WAVES * kStepCodeBytes;    // WAVES units x 256 B
-  static constexpr int T_CODES = W_SCALES + WAVES * kStepScaleBytes;  // ROWS x 64 B
-  static constexpr int T_SCALES = T_CODES + ROWS * 64;       // ROWS x 4 B
+  static constexpr int T_CODES = W_SCALES + WAVES * kStepScaleBytes;  // ROWS x TB
+  static constexpr int T_SCALES = T_CODES + ROWS * TB;       // ROWS x 4 B
   static constexpr int BYTES = T_SCALES + ROWS * 4;
 };
 
@@ -61,8 +65,11 @@ struct BoolConst {
   static constexpr bool value = B;
 };
 
-// Position of 16-byte piece c (0..3) of staged token row n.
-__device__ __forceinline__ int tok_pos(int n, int c) { return c ^ ((n >> 2) & 3); }
+// Position of 16-byte piece c of staged token row n: 4 pieces per row (E2M1)
+// or 8 (E4M3).  The 16 rows one MFMA operand read touches then fall on 16
+// different 16-byte bank groups.
+template <bool F8>
+__device__ __forceinline__ int tok_pos(int n, int c) { return F8 ? c ^ ((n >> 1) & 7) : c ^ ((n >> 2) & 3); }
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -106,7 +113,7 @@ __device__ __forceinline__ void stage_barrier() { asm volatile("s_waitcnt lgkmcn
 // WNT: weight DMA with the non-temporal hint (each weight byte is read by one
 // tile only).  WB: weight blocks per workgroup (4*WB waves, one unit each), so
 // each staged token piece feeds WB weight blocks.
-template <bool G1, int NT, int P, bool WNT, int WB>
+template <bool G1, int NT, int P, bool WNT, int WB, bool F8>
 __global__ void __launch_bounds__(256 * WB, WB == 1 ? MOE_LDS_BLOCKS : 1) gemm_lds_kernel(
     const uint8_t* __restrict__ wc, const uint8_t* __restrict__ wsc, const uint8_t* __restrict__ act,
     const uint8_t* __restrict__ act_sf, const int32_t* __restrict__ counts,
@@ -115,14 +122,16 @@ __global__ void __launch_bounds__(256 * WB, WB == 1 ? MOE_LDS_BLOCKS : 1) gemm_l
     int hrows, uint8_t* __restrict__ hq, uint8_t* __restrict__ hsf, float* __restrict__ acc_out,
     uint16_t* __restrict__ y) {
   constexpr int WAVES = 4 * WB;
-  using L = LdsStage<NT, WAVES>;
+  constexpr int TB = F8 ? 128 : 64;                    // token code bytes per row and K step
+  constexpr int PPR = TB / 16;                         // 16-byte pieces per row
+  using L = LdsStage<NT, WAVES, TB>;
   constexpr int ROWS = L::ROWS;
-  constexpr int TOK_INSTS = NT / WAVES;                // token-code DMAs (1 KiB each) per wave per stage
+  constexpr int TOK_INSTS = ROWS * TB / 1024 / WAVES;  // token-code DMAs (1 KiB each) per wave per stage
   constexpr int SC_LANES = ROWS / WAVES;               // token-scale dwords per wave per stage
   constexpr int DMA_PER_STAGE = 4 + 1 + TOK_INSTS + 1;
   // The waves' token DMAs tile the stage's token region exactly: ROWS rows x
-  // 64 B of codes, ROWS x 4 B of scales.
-  static_assert(TOK_INSTS >= 1 && TOK_INSTS * WAVES * 1024 == ROWS * 64, "token code DMAs");
+  // TB bytes of codes, ROWS x 4 B of scales.
+  static_assert(TOK_INSTS >= 1 && TOK_INSTS * WAVES * 1024 == ROWS * TB, "token code DMAs");
   static_assert(SC_LANES * WAVES == ROWS && SC_LANES <= 64, "token scale DMAs");
   static_assert(DMA_PER_STAGE * (P - 2) <= 63, "vmcnt range");
 
@@ -150,7 +159,7 @@ __global__ void __launch_bounds__(256 * WB, WB == 1 ? MOE_LDS_BLOCKS : 1) gemm_l
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int unit = wb * WAVES + wave;
   const int S = K / kStepK;
-  const int row_bytes = K / 2;
+  const int row_bytes = F8 ? K : K / 2;
 
   extern __shared__ __align__(16) uint8_t lds[];
   const uint32_t lbase = (uint32_t)(uintptr_t)lds;
@@ -162,13 +171,13 @@ __global__ void __launch_bounds__(256 * WB, WB == 1 ? MOE_LDS_BLOCKS : 1) gemm_l
   // row-major quantized x.
   const uint8_t* wsrc = wc + (G1 ? w1_code_offset(e, unit, 0, H, I) : w2_code_offset(e, unit, 0, H, I)) + lane * 16;
   const uint8_t* ssrc = wsc + (G1 ? w1_scale_offset(e, unit, 0, H, I) : w2_scale_offset(e, unit, 0, H, I)) + lane * 4;
-  const size_t code_step = G1 ? 64 : (size_t)hrows * 64, scale_step = (size_t)hrows * 4;
+  const size_t code_step = G1 ? TB : (size_t)hrows * TB, scale_step = (size_t)hrows * 4;
   const uint8_t* tsrc[TOK_INSTS];
 #pragma unroll
   for (int i = 0; i < TOK_INSTS; ++i) {
     const int slot = (wave * TOK_INSTS + i) * 64 + lane;
-    const int n = slot >> 2, r = row0 + min(n, nrows - 1);
-    tsrc[i] = act + (G1 ? (size_t)(sorted_rows[r] / k) * row_bytes : (size_t)r * 64) + tok_pos(n, slot & 3) * 16;
+    const int n = slot / PPR, r = row0 + min(n, nrows - 1);
+    tsrc[i] = act + (G1 ? (size_t)(sorted_rows[r] / k) * row_bytes : (size_t)r * TB) + tok_pos<F8>(n, slot % PPR) * 16;
   }
   const uint8_t* tssrc = act_sf + (size_t)(row0 + min(wave * SC_LANES + min(lane, SC_LANES - 1), nrows - 1)) * 4;
 
@@ -216,7 +225,7 @@ __global__ void __launch_bounds__(256 * WB, WB == 1 ? MOE_LDS_BLOCKS : 1) gemm_l
     if constexpr (WITH_DMA) issue(s + P - 1);
 #endif
     const uint8_t* st = lds + (s % P) * L::BYTES;
-    uint4 a[4], b[NT];
+    uint4 a[4], b[NT], b2[F8 ? NT : 1];
     int sbv[NT];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
@@ -225,7 +234,12 @@ __global__ void __launch_bounds__(256 * WB, WB == 1 ? MOE_LDS_BLOCKS : 1) gemm_l
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int n = nt * 16 + tok_lane;
-      b[nt] = *reinterpret_cast<const uint4*>(st + L::T_CODES + n * 64 + tok_pos(n, kb) * 16);
+      if constexpr (F8) {   // pieces kb and kb + 4 (the FP8 operand layout, device_common.h)
+        b[nt] = *reinterpret_cast<const uint4*>(st + L::T_CODES + n * TB + tok_pos<true>(n, kb) * 16);
+        b2[nt] = *reinterpret_cast<const uint4*>(st + L::T_CODES + n * TB + tok_pos<true>(n, kb + 4) * 16);
+      } else {
+        b[nt] = *reinterpret_cast<const uint4*>(st + L::T_CODES + n * TB + tok_pos<false>(n, kb) * 16);
+      }
       sbv[nt] = (int)(*reinterpret_cast<const uint32_t*>(st + L::T_SCALES + n * 4) >> (8 * kb));
     }
 #pragma unroll
@@ -237,10 +251,17 @@ __global__ void __launch_bounds__(256 * WB, WB == 1 ? MOE_LDS_BLOCKS : 1) gemm_l
           if (i * NT / DMA_PER_STAGE == nt) issue_one(s + P - 1, i);
       }
 #endif
-      acc[nt][0] = mfma_fp4<0, 0>(a[0], b[nt], acc[nt][0], sa, sbv[nt]);
-      acc[nt][1] = mfma_fp4<1, 0>(a[1], b[nt], acc[nt][1], sa, sbv[nt]);
-      acc[nt][2] = mfma_fp4<2, 0>(a[2], b[nt], acc[nt][2], sa, sbv[nt]);
-      acc[nt][3] = mfma_fp4<3, 0>(a[3], b[nt], acc[nt][3], sa, sbv[nt]);
+      if constexpr (F8) {
+        acc[nt][0] = mfma_fp4_fp8<0, 0>(a[0], b[nt], b2[nt], acc[nt][0], sa, sbv[nt]);
+        acc[nt][1] = mfma_fp4_fp8<1, 0>(a[1], b[nt], b2[nt], acc[nt][1], sa, sbv[nt]);
+        acc[nt][2] = mfma_fp4_fp8<2, 0>(a[2], b[nt], b2[nt], acc[nt][2], sa, sbv[nt]);
+        acc[nt][3] = mfma_fp4_fp8<3, 0>(a[3], b[nt], b2[nt], acc[nt][3], sa, sbv[nt]);
+      } else {
+        acc[nt][0] = mfma_fp4<0, 0>(a[0], b[nt], acc[nt][0], sa, sbv[nt]);
+        acc[nt][1] = mfma_fp4<1, 0>(a[1], b[nt], acc[nt][1], sa, sbv[nt]);
+        acc[nt][2] = mfma_fp4<2, 0>(a[2], b[nt], acc[nt][2], sa, sbv[nt]);
+        acc[nt][3] = mfma_fp4<3, 0>(a[3], b[nt], acc[nt][3], sa, sbv[nt]);
+      }
 #if MOE_LDS_INTERLEAVE
       __builtin_amdgcn_sched_barrier(0);
 #endif
@@ -265,7 +286,7 @@ __global__ void __launch_bounds__(256 * WB, WB == 1 ? MOE_LDS_BLOCKS : 1) gemm_l
   }
 
   if constexpr (G1)
-    gemm1_epilogue<NT>(acc, unit, row0, nrows, I, hrows, lane, hq, hsf, acc_out);
+    gemm1_epilogue<NT, F8>(acc, unit, row0, nrows, I, hrows, lane, hq, hsf, acc_out);
   else
     gemm2_epilogue<NT>(acc, unit, row0, nrows, H, lane, y);
 }
@@ -276,15 +297,15 @@ __global__ void __launch_bounds__(256 * WB, WB == 1 ? MOE_LDS_BLOCKS : 1) gemm_l
 
 constexpr int kLdsNT = 8;     // token tiles of 16 rows per wave: 128-row work tiles
 
-template <bool G1, bool WNT, int WB>
+template <bool G1, bool WNT, int WB, bool F8>
 static hipError_t launch_prefill_wb(const uint8_t* wc, const uint8_t* wsc, const uint8_t* act,
                                     const uint8_t* act_sf, const int32_t* counts, const int32_t* offsets,
                                     const int32_t* sorted_rows, const int2* tiles, const int32_t* num_tiles,
                                     int max_tiles, int H, int I, int k, int hrows, uint8_t* hq, uint8_t* hsf,
                                     float* acc_out, uint16_t* y, hipStream_t stream) {
   constexpr int P = MOE_LDS_STAGES;
-  auto kern = gemm_lds_kernel<G1, kLdsNT, P, WNT, WB>;
-  const size_t lds = (size_t)P * LdsStage<kLdsNT, 4 * WB>::BYTES;
+  auto kern = gemm_lds_kernel<G1, kLdsNT, P, WNT, WB, F8>;
+  const size_t lds = (size_t)P * LdsStage<kLdsNT, 4 * WB, F8 ? 128 : 64>::BYTES;
   if (lds > 65536) {
     hipError_t err = raise_lds_limit(reinterpret_cast<const void*>(kern), lds);
     if (err != hipSuccess) return err;
@@ -307,7 +328,7 @@ int lds_max_tiles(int R, int E, int tile_rows) { return (R + tile_rows - 1) / ti
 // expert).  More rows: the tiles of an expert share each weight block through
 // L2, loads keep the default policy, and single-block workgroups (two per CU,
 // each with its own barrier) keep the MFMAs busier.
-template <bool G1>
+template <bool G1, bool F8>
 static hipError_t launch_prefill(const uint8_t* wc, const uint8_t* wsc, const uint8_t* act, const uint8_t* act_sf,
                                  const int32_t* counts, const int32_t* offsets, const int32_t* sorted_rows,
                                  const int2* tiles, const int32_t* num_tiles, int max_tiles, int rows_hint, int H,
@@ -317,28 +338,31 @@ static hipError_t launch_prefill(const uint8_t* wc, const uint8_t* wsc, const ui
                          hrows, hq, hsf, acc_out, y, stream
   const bool single = rows_hint <= kLdsNT * 16;
   const int nwb = G1 ? I / 128 : H / 256;
-  if (single && G1 && nwb % 2 == 0) return launch_prefill_wb<G1, true, 2>(MOE_PREFILL_ARGS);
-  if (single) return launch_prefill_wb<G1, true, 1>(MOE_PREFILL_ARGS);
-  return launch_prefill_wb<G1, false, 1>(MOE_PREFILL_ARGS);
+  if (single && G1 && nwb % 2 == 0) return launch_prefill_wb<G1, true, 2, F8>(MOE_PREFILL_ARGS);
+  if (single) return launch_prefill_wb<G1, true, 1, F8>(MOE_PREFILL_ARGS);
+  return launch_prefill_wb<G1, false, 1, F8>(MOE_PREFILL_ARGS);
 #undef MOE_PREFILL_ARGS
 }
 
 // xsf_planes: the token scales of the sorted rows in K-step planes of hrows
 // rows (launch_sorted_scales); hq/hsf: GEMM1's output planes (epilogue.h).
-hipError_t launch_gemm1_lds(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq, const uint8_t* xsf_planes,
-                            const int32_t* counts, const int32_t* offsets, const int32_t* sorted_rows,
-                            const int2* tiles, const int32_t* num_tiles, int max_tiles, int rows_hint, int H, int I,
-                            int k, int hrows, uint8_t* hq, uint8_t* hsf, float* acc_out, hipStream_t stream) {
-  return launch_prefill<true>(w1c, w1s, xq, xsf_planes, counts, offsets, sorted_rows, tiles, num_tiles, max_tiles,
-                              rows_hint, H, I, k, hrows, hq, hsf, acc_out, nullptr, stream);
+hipError_t launch_gemm1_lds(bool fp8, const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq,
+                            const uint8_t* xsf_planes, const int32_t* counts, const int32_t* offsets,
+                            const int32_t* sorted_rows, const int2* tiles, const int32_t* num_tiles, int max_tiles,
+                            int rows_hint, int H, int I, int k, int hrows, uint8_t* hq, uint8_t* hsf, float* acc_out,
+                            hipStream_t stream) {
+  auto launch = fp8 ? launch_prefill<true, true> : launch_prefill<true, false>;
+  return launch(w1c, w1s, xq, xsf_planes, counts, offsets, sorted_rows, tiles, num_tiles, max_tiles, rows_hint, H, I,
+                k, hrows, hq, hsf, acc_out, nullptr, stream);
 }
 
-hipError_t launch_gemm2_lds(const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq, const uint8_t* hsf,
+hipError_t launch_gemm2_lds(bool fp8, const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq, const uint8_t* hsf,
                             const int32_t* counts, const int32_t* offsets, const int2* tiles,
                             const int32_t* num_tiles, int max_tiles, int rows_hint, int H, int I, int hrows,
                             uint16_t* y, hipStream_t stream) {
-  return launch_prefill<false>(w2c, w2s, hq, hsf, counts, offsets, nullptr, tiles, num_tiles, max_tiles, rows_hint, H,
-                               I, 1, hrows, nullptr, nullptr, nullptr, y, stream);
+  auto launch = fp8 ? launch_prefill<false, true> : launch_prefill<false, false>;
+  return launch(w2c, w2s, hq, hsf, counts, offsets, nullptr, tiles, num_tiles, max_tiles, rows_hint, H, I, 1, hrows,
+                nullptr, nullptr, nullptr, y, stream);
 }
 
 }  // namespace moe

@@ -6,8 +6,9 @@
 
 namespace moe {
 
-// Stage S1a: MXFP4 quantization of rows of bf16 (src_is_bf16) or fp32 values.
-hipError_t launch_quantize(bool src_is_bf16, const void* src, int64_t ngroups,
+// Stage S1a: MXFP4 quantization of rows of bf16 (src_is_bf16) or fp32 values;
+// fp8: MXFP8 E4M3 codes instead (the fp8xfp4 MMA type's activations, bf16 only).
+hipError_t launch_quantize(bool src_is_bf16, bool fp8, const void* src, int64_t ngroups,
                            uint8_t* codes, uint8_t* scales, hipStream_t stream);
 
 // Stage S1b: stable counting sort of R routed rows over E experts.  With
@@ -20,9 +21,10 @@ hipError_t launch_route(const int32_t* ids, int R, int E, int32_t* hist, int32_t
 // Stages S1a + S1b in one launch: block 0 routes all R <= kPredispatchMaxRows
 // rows, the other blocks quantize the bf16 tokens.
 constexpr int kPredispatchMaxRows = 8192;
-hipError_t launch_predispatch(const uint16_t* x, int64_t ngroups, uint8_t* xq, uint8_t* xsf, const int32_t* ids,
-                              int R, int E, int32_t* counts, int32_t* offsets, int32_t* sorted_rows,
-                              int32_t* pos, int tile_rows, int2* tiles, int32_t* num_tiles, hipStream_t stream);
+hipError_t launch_predispatch(bool fp8, const uint16_t* x, int64_t ngroups, uint8_t* xq, uint8_t* xsf,
+                              const int32_t* ids, int R, int E, int32_t* counts, int32_t* offsets,
+                              int32_t* sorted_rows, int32_t* pos, int tile_rows, int2* tiles, int32_t* num_tiles,
+                              hipStream_t stream);
 
 // Prefill GEMMs with both operands staged in LDS (gemm_lds.hip): tiles of
 // lds_tile_rows(mean rows per expert) routed rows; rows_hint (the mean) also
@@ -31,11 +33,13 @@ hipError_t launch_predispatch(const uint16_t* x, int64_t ngroups, uint8_t* xq, u
 // the sorted token scales; epilogue.h), the workspace's routed-row capacity.
 int lds_tile_rows(int rows_hint);
 int lds_max_tiles(int R, int E, int tile_rows);
-hipError_t launch_gemm1_lds(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq, const uint8_t* xsf_planes,
-                            const int32_t* counts, const int32_t* offsets, const int32_t* sorted_rows,
-                            const int2* tiles, const int32_t* num_tiles, int max_tiles, int rows_hint, int H, int I,
-                            int k, int hrows, uint8_t* hq, uint8_t* hsf, float* acc_out, hipStream_t stream);
-hipError_t launch_gemm2_lds(const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq, const uint8_t* hsf,
+// fp8: the activations are E4M3 (the fp8xfp4 MMA type) instead of E2M1.
+hipError_t launch_gemm1_lds(bool fp8, const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq,
+                            const uint8_t* xsf_planes, const int32_t* counts, const int32_t* offsets,
+                            const int32_t* sorted_rows, const int2* tiles, const int32_t* num_tiles, int max_tiles,
+                            int rows_hint, int H, int I, int k, int hrows, uint8_t* hq, uint8_t* hsf, float* acc_out,
+                            hipStream_t stream);
+hipError_t launch_gemm2_lds(bool fp8, const uint8_t* w2c, const uint8_t* w2s, const uint8_t* hq, const uint8_t* hsf,
                             const int32_t* counts, const int32_t* offsets, const int2* tiles,
                             const int32_t* num_tiles, int max_tiles, int rows_hint, int H, int I, int hrows,
                             uint16_t* y, hipStream_t stream);
@@ -47,14 +51,16 @@ hipError_t launch_gemm2_lds(const uint8_t* w2c, const uint8_t* w2s, const uint8_
 hipError_t launch_sorted_scales(const uint8_t* xsf, const int32_t* sorted_rows, const int32_t* offsets, int E,
                                 int rows_bound, int H, int k, int hrows, uint8_t* xsf_planes, hipStream_t stream);
 
-// Stage S2: grouped GEMM1 over the prepared W1 tiles + SwiGLU + MXFP4 requant.
-hipError_t launch_gemm1(const uint8_t* w1_codes, const uint8_t* w1_scales, const uint8_t* xq,
+// Stage S2: grouped GEMM1 over the prepared W1 tiles + SwiGLU + MXFP4 requant
+// (fp8: E4M3 activations and requant, the fp8xfp4 MMA type).
+hipError_t launch_gemm1(bool fp8, const uint8_t* w1_codes, const uint8_t* w1_scales, const uint8_t* xq,
                         const uint8_t* xsf, const int32_t* counts, const int32_t* offsets,
                         const int32_t* sorted_rows, int H, int I, int E, int k, int rows_hint, int hrows,
                         uint8_t* hq, uint8_t* hsf, float* acc_out, hipStream_t stream);
 
-// Stage S3: grouped GEMM2 over the prepared W2 tiles -> fp32 y in sorted order.
-hipError_t launch_gemm2(const uint8_t* w2_codes, const uint8_t* w2_scales, const uint8_t* hq,
+// Stage S3: grouped GEMM2 over the prepared W2 tiles -> bf16 y in sorted order
+// (fp8: E4M3 activations).
+hipError_t launch_gemm2(bool fp8, const uint8_t* w2_codes, const uint8_t* w2_scales, const uint8_t* hq,
                         const uint8_t* hsf, const int32_t* counts, const int32_t* offsets, int H,
                         int I, int E, int rows_hint, int hrows, uint16_t* y, hipStream_t stream);
 

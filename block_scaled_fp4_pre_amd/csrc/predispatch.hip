@@ -13,7 +13,8 @@
 // at a time, in order: the rank among the sub-chunk's rows of the same expert
 // comes from a 64-lane match (one ballot per id bit), and the lowest lane of
 // each expert advances the wave's slot for the next sub-chunk.  Blocks 1..
-// quantize one 32-element group of x per thread meanwhile.
+// quantize one 32-element group of x per thread meanwhile (E2M1, or E4M3 for
+// the fp8xfp4 MMA type).
 #include "launch.h"
 #include "quant_group.h"
 #include "route_common.h"
@@ -22,6 +23,7 @@ namespace moe {
 
 constexpr int kPredispatchSubs = kPredispatchMaxRows / kRouteRows;  // 64-row sub-chunks per wave, at most
 
+template <bool F8>
 __global__ void __launch_bounds__(kRouteRows) predispatch_kernel(
     const uint16_t* __restrict__ x, int64_t ngroups, uint8_t* __restrict__ xq, uint8_t* __restrict__ xsf,
     const int32_t* __restrict__ ids, int R, int E, int nbits, int32_t* __restrict__ counts,
@@ -30,7 +32,7 @@ __global__ void __launch_bounds__(kRouteRows) predispatch_kernel(
   const int tid = threadIdx.x;
   if (blockIdx.x > 0) {
     const int64_t g = (int64_t)(blockIdx.x - 1) * kRouteRows + tid;
-    if (g < ngroups) quantize_group<true>(x, g, xq, xsf);
+    if (g < ngroups) quantize_group<true, F8>(x, g, xq, xsf);
     return;
   }
   extern __shared__ int smem[];
@@ -96,14 +98,15 @@ __global__ void __launch_bounds__(kRouteRows) predispatch_kernel(
   }
 }
 
-hipError_t launch_predispatch(const uint16_t* x, int64_t ngroups, uint8_t* xq, uint8_t* xsf, const int32_t* ids,
-                              int R, int E, int32_t* counts, int32_t* offsets, int32_t* sorted_rows,
-                              int32_t* pos, int tile_rows, int2* tiles, int32_t* num_tiles, hipStream_t stream) {
+hipError_t launch_predispatch(bool fp8, const uint16_t* x, int64_t ngroups, uint8_t* xq, uint8_t* xsf,
+                              const int32_t* ids, int R, int E, int32_t* counts, int32_t* offsets,
+                              int32_t* sorted_rows, int32_t* pos, int tile_rows, int2* tiles, int32_t* num_tiles,
+                              hipStream_t stream) {
   const int64_t qblocks = (ngroups + kRouteRows - 1) / kRouteRows;
   const size_t lds = (size_t)(kRouteWaves * E + kRouteWaves) * sizeof(int);
-  hipLaunchKernelGGL(predispatch_kernel, dim3((unsigned)(1 + qblocks)), dim3(kRouteRows), lds, stream, x, ngroups,
-                     xq, xsf, ids, R, E, id_bits(E), counts, offsets, sorted_rows, pos, tile_rows, tiles,
-                     num_tiles);
+  auto kern = fp8 ? predispatch_kernel<true> : predispatch_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(1 + qblocks)), dim3(kRouteRows), lds, stream, x, ngroups, xq, xsf, ids, R,
+                     E, id_bits(E), counts, offsets, sorted_rows, pos, tile_rows, tiles, num_tiles);
   return hipGetLastError();
 }
 

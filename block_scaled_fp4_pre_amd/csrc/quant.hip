@@ -1,5 +1,6 @@
 // Stage S1a (pre-dispatch quantization): every 32-element group of a row becomes
-// 16 bytes of packed E2M1 codes and one UE8M0 scale byte.
+// 16 bytes of packed E2M1 codes (the fp8xfp4 MMA type: 32 bytes of E4M3 codes)
+// and one UE8M0 scale byte.
 // [P3] prhub digest of sglang PR "bump sgl-deep-gemm to 0.1.7, MegaMoE uses the
 // mma_type API for MXFP4", "Key source snippets": the mxf4xmxf4 pre_dispatch
 // packs E2M1 with group_size=32.  Formats per [OCP-MX] (OCP MX v1.0).
@@ -12,22 +13,26 @@
 
 namespace moe {
 
-template <bool BF16>
+template <bool BF16, bool F8>
 __global__ void __launch_bounds__(256) quantize_kernel(const void* __restrict__ src, int64_t ngroups,
                                                        uint8_t* __restrict__ codes,
                                                        uint8_t* __restrict__ scales) {
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (g < ngroups) quantize_group<BF16>(src, g, codes, scales);
+  if (g < ngroups) quantize_group<BF16, F8>(src, g, codes, scales);
 }
 
-hipError_t launch_quantize(bool src_is_bf16, const void* src, int64_t ngroups, uint8_t* codes,
+hipError_t launch_quantize(bool src_is_bf16, bool fp8, const void* src, int64_t ngroups, uint8_t* codes,
                            uint8_t* scales, hipStream_t stream) {
   if (ngroups <= 0) return hipSuccess;
   const dim3 grid((unsigned)((ngroups + 255) / 256));
-  if (src_is_bf16)
-    hipLaunchKernelGGL(quantize_kernel<true>, grid, dim3(256), 0, stream, src, ngroups, codes, scales);
+  if (fp8 && src_is_bf16)
+    hipLaunchKernelGGL((quantize_kernel<true, true>), grid, dim3(256), 0, stream, src, ngroups, codes, scales);
+  else if (fp8)
+    return hipErrorInvalidValue;                // E4M3 is an activation format: bf16 input only
+  else if (src_is_bf16)
+    hipLaunchKernelGGL((quantize_kernel<true, false>), grid, dim3(256), 0, stream, src, ngroups, codes, scales);
   else
-    hipLaunchKernelGGL(quantize_kernel<false>, grid, dim3(256), 0, stream, src, ngroups, codes, scales);
+    hipLaunchKernelGGL((quantize_kernel<false, false>), grid, dim3(256), 0, stream, src, ngroups, codes, scales);
   return hipGetLastError();
 }
 

@@ -10,9 +10,10 @@
 namespace moe {
 
 // Group g of a row-major source (32 consecutive values) -> 16 bytes of packed
-// codes at codes + 16g and one scale byte at scales[g].  64 B (bf16) or 128 B
-// (fp32) in as 16-byte loads.
-template <bool BF16>
+// E2M1 codes at codes + 16g (F8: 32 bytes of E4M3 codes at codes + 32g, the
+// fp8xfp4 MMA type's activations, e4m3.h) and one scale byte at scales[g].
+// 64 B (bf16) or 128 B (fp32) in as 16-byte loads.
+template <bool BF16, bool F8 = false>
 __device__ __forceinline__ void quantize_group(const void* __restrict__ src, int64_t g,
                                                uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
   float v[32];
@@ -39,6 +40,18 @@ __device__ __forceinline__ void quantize_group(const void* __restrict__ src, int
   uint32_t amax = 0;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = max(amax, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+  if constexpr (F8) {
+    const int e = mx8_scale_exp(amax);
+    const float inv = e4m3_exp2(-e);
+    uint32_t w[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) w[q] = e4m3_pack4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3], inv);
+    uint4* out = reinterpret_cast<uint4*>(codes) + 2 * g;
+    out[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    out[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    scales[g] = (uint8_t)(e + 127);
+    return;
+  }
   const int e = mx_scale_exp(amax);
   const float sc = exp2_scale(e);
   uint32_t packed[4];

@@ -16,10 +16,13 @@ from . import _lib
 
 class MoeW4A4Layer:
     def __init__(self, hidden: int, inter: int, num_experts: int, topk: int, max_tokens: int,
-                 device: str | torch.device = "cuda"):
+                 device: str | torch.device = "cuda", mma_type: int = _lib.MOE_MMA_MXF4_X_MXF4):
+        """mma_type: MOE_MMA_MXF4_X_MXF4 (MXFP4 activations) or MOE_MMA_FP8_X_MXF4
+        (MXFP8 E4M3 activations); the weights are MXFP4 in both."""
         self.H, self.I, self.E, self.k, self.max_tokens = hidden, inter, num_experts, topk, max_tokens
+        self.mma_type = mma_type
         self.device = torch.device(device)
-        self.cfg = _lib.make_cfg(hidden, inter, num_experts, topk, max_tokens)
+        self.cfg = _lib.make_cfg(hidden, inter, num_experts, topk, max_tokens, mma_type=mma_type)
         pb, wb = _lib.moe_w4a4_query(self.cfg)
         self.prepared = torch.empty(pb, dtype=torch.uint8, device=self.device)
         self.workspace = torch.empty(wb, dtype=torch.uint8, device=self.device)

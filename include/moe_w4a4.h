@@ -62,15 +62,20 @@ enum {
   MOE_EHIP = 6           /* a HIP runtime call or kernel launch failed            */
 };
 
-/* mma_type: the pairing of activation and weight formats.  Only MXFP4 x MXFP4
- * ("mxf4xmxf4" in [P3]) is implemented; the FP8-activation pairing is not. */
-enum { MOE_MMA_MXF4_X_MXF4 = 0 };
+/* mma_type: the pairing of activation and weight formats ([P3] "Implementation
+ * breakdown" items 1-3: the mma_type that replaced the env-var switches).
+ *   MOE_MMA_MXF4_X_MXF4 ("mxf4xmxf4"): x and h are MXFP4 E2M1, two codes a byte.
+ *   MOE_MMA_FP8_X_MXF4  ("fp8xfp4"):  x and h are MXFP8 E4M3 ([OCP-MX]), one
+ *     code a byte, with the same UE8M0 scale per 32 (scale 2^e: the smallest
+ *     with amax <= 448 * 2^e); ties to the even mantissa, sign kept.
+ * The weights are MXFP4 in both. */
+enum { MOE_MMA_MXF4_X_MXF4 = 0, MOE_MMA_FP8_X_MXF4 = 1 };
 /* activation: SwiGLU, silu(gate) * up, with no clamp or bias ([P3]). */
 enum { MOE_ACT_SWIGLU = 0 };
 
 /* Layer configuration.  Supported: hidden % 256 == 0, inter % 128 == 0,
  * 1 <= num_experts <= 512, 1 <= topk <= 16, 0 <= max_tokens and
- * max_tokens * topk < 2^31, group_size == 32, mma_type == MOE_MMA_MXF4_X_MXF4,
+ * max_tokens * topk < 2^31, group_size == 32, mma_type one of the two above,
  * activation == MOE_ACT_SWIGLU.  max_tokens is the capacity the workspace is
  * sized for (num_max_tokens_per_rank in [P3]); each forward passes the live
  * token count. */
@@ -81,7 +86,7 @@ typedef struct moe_w4a4_cfg {
   int32_t topk;         /* k */
   int32_t max_tokens;   /* capacity */
   int32_t group_size;   /* must be 32 */
-  int32_t mma_type;     /* MOE_MMA_MXF4_X_MXF4 */
+  int32_t mma_type;     /* MOE_MMA_MXF4_X_MXF4 or MOE_MMA_FP8_X_MXF4 */
   int32_t activation;   /* MOE_ACT_SWIGLU */
 } moe_w4a4_cfg;
 
@@ -114,7 +119,8 @@ int moe_w4a4_prepare_weights(const moe_w4a4_cfg* cfg,
                              void* prepared, size_t prepared_bytes, void* stream);
 
 /* One forward of the layer for num_tokens (0 <= num_tokens <= cfg->max_tokens):
- *   1. pre-dispatch: each token row of x quantized once to MXFP4;
+ *   1. pre-dispatch: each token row of x quantized once to MXFP4 (MXFP8 E4M3
+ *      for MOE_MMA_FP8_X_MXF4; so is h in step 3);
  *   2. route: stable counting sort of the routed rows r = t*k + j by expert
  *      (ids outside [0, E) are skipped; duplicates are separate rows);
  *   3. GEMM1 per expert with fp32 accumulation, SwiGLU, requantization of h to
@@ -148,14 +154,16 @@ const char* moe_w4a4_status_string(int status);
  * (c*R + row)*64 and one dword of 4 scale bytes at (c*R + row)*4, so that a
  * tile of consecutive rows reads one contiguous run per K step. */
 typedef struct moe_w4a4_ws_layout {
-  uint64_t xq;           /* uint8  [max_tokens, H/2]   quantized tokens (packed)    */
+  uint64_t xq;           /* uint8  [max_tokens, H/2]   quantized tokens (packed E2M1;
+                                                        E4M3: [max_tokens, H])      */
   uint64_t xsf;          /* uint8  [max_tokens, H/32]  their scale bytes            */
   uint64_t counts;       /* int32  [E]                 routed rows per expert       */
   uint64_t offsets;      /* int32  [E+1]               exclusive prefix of counts   */
   uint64_t sorted_rows;  /* int32  [max_tokens*k]      r = t*k+j in (expert, r) order */
   uint64_t pos;          /* int32  [max_tokens*k]      index of r in sorted_rows or -1 */
   uint64_t hist;         /* int32  [ceil(max_tokens*k/1024), E] per-block counts   */
-  uint64_t hq;           /* uint8  [I/128, R, 64]      requantized h (sorted rows, planes) */
+  uint64_t hq;           /* uint8  [I/128, R, 64]      requantized h (sorted rows, planes;
+                                                        E4M3: [I/128, R, 128])      */
   uint64_t hsf;          /* uint8  [I/128, R, 4]       its scale bytes (planes)     */
   uint64_t y;            /* bf16   [max_tokens*k, H]   GEMM2 result (sorted order)  */
   uint64_t tiles;        /* int32  [max_tokens*k/16 + E, 2] (expert, first row) work tiles */

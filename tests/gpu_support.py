@@ -31,9 +31,9 @@ def dev(a, dtype=None) -> torch.Tensor:
     return t.cuda()
 
 
-def layer_for(H, I, E, k, max_tokens):
+def layer_for(H, I, E, k, max_tokens, mma_type=0):
     from block_scaled_fp4_pre_amd.layer import MoeW4A4Layer
-    return MoeW4A4Layer(H, I, E, k, max_tokens)
+    return MoeW4A4Layer(H, I, E, k, max_tokens, mma_type=mma_type)
 
 
 @functools.lru_cache(maxsize=2)
@@ -46,6 +46,17 @@ def synth_layer(weight_set_cfg_index: int, max_tokens: int):
     layer.load_fp32(lambda e: synth.expert_weights_f32(cfg, e))
     torch.cuda.synchronize()
     log("[gpu_support] layer ready")
+    return layer
+
+
+@functools.lru_cache(maxsize=1)
+def synth_layer_fp8(weight_set_cfg_index: int, max_tokens: int):
+    """The same layer with the fp8xfp4 MMA type.  The prepared weights (MXFP4
+    for both MMA types) are shared with synth_layer's."""
+    from block_scaled_fp4_pre_amd.layer import MoeW4A4Layer
+    base = synth_layer(weight_set_cfg_index, max_tokens)
+    layer = MoeW4A4Layer(base.H, base.I, base.E, base.k, max_tokens, mma_type=1)
+    layer.prepared = base.prepared
     return layer
 
 
@@ -76,16 +87,17 @@ def workspace_host(layer, T):
     H, I, E, k = layer.H, layer.I, layer.E, layer.k
     R = T * k
     ws = layer.ws
+    f8 = layer.mma_type == 1             # E4M3 activations: one byte per element
     counts = ws("counts", (E,), torch.int32).cpu().numpy()
     nv = int(counts.sum())
     return dict(
-        xq=ws("xq", (layer.max_tokens, H // 2), torch.uint8)[:T].cpu().numpy(),
+        xq=ws("xq", (layer.max_tokens, H if f8 else H // 2), torch.uint8)[:T].cpu().numpy(),
         xsf=ws("xsf", (layer.max_tokens, H // 32), torch.uint8)[:T].cpu().numpy(),
         counts=counts,
         offsets=ws("offsets", (E + 1,), torch.int32).cpu().numpy(),
         sorted_rows=ws("sorted_rows", (layer.max_tokens * k,), torch.int32)[:nv].cpu().numpy(),
         pos=ws("pos", (layer.max_tokens * k,), torch.int32)[:R].cpu().numpy(),
-        hq=rows_from_planes(ws("hq", (I // 128, layer.max_tokens * k, 64), torch.uint8), nv),
+        hq=rows_from_planes(ws("hq", (I // 128, layer.max_tokens * k, 128 if f8 else 64), torch.uint8), nv),
         hsf=rows_from_planes(ws("hsf", (I // 128, layer.max_tokens * k, 4), torch.uint8), nv),
         xsf_planes=rows_from_planes(ws("xsf_planes", (H // 128, layer.max_tokens * k, 4), torch.uint8), nv),
         y=ws("y", (layer.max_tokens * k, H), torch.bfloat16)[:nv].float().cpu().numpy().astype(np.float64),

@@ -35,7 +35,7 @@ def test_query_sizes_dsv4():
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("hidden", 4000, 2), ("inter", 100, 2), ("group_size", 16, 2), ("mma_type", 1, 2),
+    ("hidden", 4000, 2), ("inter", 100, 2), ("group_size", 16, 2), ("mma_type", 2, 2),
     ("activation", 3, 2), ("num_experts", 0, 1), ("num_experts", 513, 2), ("topk", 0, 1),
     ("topk", 17, 2), ("max_tokens", -1, 1)])
 def test_query_rejects_bad_config(field, value, status):
@@ -87,3 +87,16 @@ def test_forward_validation_before_any_hip_call():
     assert L.moe_w4a4_quantize(0, fake, -1, 64, fake, fake, None) == _lib.MOE_EINVAL
     assert L.moe_w4a4_quantize(0, fake, 0, 64, fake, fake, None) == _lib.MOE_OK
     assert _lib.status_string(_lib.MOE_ECAPACITY).startswith("num_tokens")
+
+
+def test_fp8_activations_double_the_token_regions():
+    """mma_type fp8xfp4: x and h take one E4M3 byte per element instead of half."""
+    from block_scaled_fp4_pre_amd import _lib
+    c4 = _lib.make_cfg(4096, 2048, 256, 6, 512)
+    c8 = _lib.make_cfg(4096, 2048, 256, 6, 512)
+    c8.mma_type = _lib.MOE_MMA_FP8_X_MXF4
+    l4, l8 = _lib.moe_w4a4_workspace_layout(c4), _lib.moe_w4a4_workspace_layout(c8)
+    size = lambda lay, a, b: lay[b] - lay[a]
+    assert size(l8, "xq", "xsf") == 2 * size(l4, "xq", "xsf") == 512 * 4096
+    assert size(l8, "hq", "hsf") == 2 * size(l4, "hq", "hsf") == 512 * 6 * 2048
+    assert _lib.moe_w4a4_query(c8)[0] == _lib.moe_w4a4_query(c4)[0]      # same MXFP4 weights

@@ -1,0 +1,107 @@
+"""GPU tier for the fp8xfp4 MMA type (MXFP8 E4M3 activations, MXFP4 weights):
+the same kernels with the token operand in FP8, compared with the oracle run
+with mma_type="fp8xfp4".
+
+  quantize        every bfloat16 pattern as a lone value in a group, through
+                  the pre-dispatch quantization stage: codes and scales exact
+  tiny / stream   the streaming path on every token (16- and 32-row passes,
+                  2 units per wave in GEMM1)
+  prefill         the LDS-staged path on every token: the per-XCD work order
+                  with several tiles per expert, and the single-tile form
+                  (non-temporal weights, two weight blocks per GEMM1 workgroup)
+  full size       DeepSeek-V4-Flash shape at 512 and 4096 tokens: quantized
+                  tokens and routing in full, the rest on sampled tokens"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from block_scaled_fp4_pre_amd import _lib
+from oracle import bf16, mxfp8
+from oracle.forward import forward
+from oracle.route import route
+from tests.gpu_support import dev_bf16, layer_for, log, run_config, synth_layer_fp8
+from tests.oracle_inputs import all_expert_weights, lazy_expert_weights
+from tests.parity import (OUT_REL_L2, check_y, compare_requant, fp8_bound_for, fp8_requant_sampled, rel_l2,
+                          same_h_rows)
+from tests.test_gpu_layer import check_all_stages
+
+pytestmark = pytest.mark.gpu
+FP8 = _lib.MOE_MMA_FP8_X_MXF4
+
+
+def test_fp8_quantize_every_bf16_pattern():
+    log("[test] fp8 quantize: every bf16 pattern")
+    H = 256
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    finite = np.isfinite((bits << 16).view(np.float32))
+    vals = bits[finite].astype(np.uint16)
+    T = -(-vals.size // (H // 32))
+    x = np.zeros((T * (H // 32), 32), dtype=np.uint16)
+    x[:vals.size, 9] = vals                    # one value per 32-group, the rest +0
+    x = x.reshape(T, H)
+    layer = layer_for(H, 128, 4, 1, T, mma_type=FP8)
+    layer.run_stages(_lib.MOE_STAGE_QUANT, T, x=dev_bf16(x))
+    torch.cuda.synchronize()
+    xq = layer.ws("xq", (T, H), torch.uint8).cpu().numpy()
+    xsf = layer.ws("xsf", (T, H // 32), torch.uint8).cpu().numpy()
+    rq, rs = mxfp8.quantize(bf16.decode(x))
+    assert np.array_equal(xsf, rs)
+    assert np.array_equal(xq, rq)
+
+
+SHAPES = [
+    synth.CONFIGS[0],
+    synth.LayerConfig(120, "fp8_stream_h1024_i512_e16_k2_t100", 100, 1024, 512, 16, 2, "uniform", 120),
+    synth.LayerConfig(121, "fp8_prefill_h2048_i1024_e8_k2_t1500_zipf", 1500, 2048, 1024, 8, 2, "zipf", 121, 1.1),
+    synth.LayerConfig(122, "fp8_prefill_h512_i512_e16_k2_t1000", 1000, 512, 512, 16, 2, "uniform", 122),
+]
+
+
+@pytest.mark.parametrize("cfg", SHAPES, ids=lambda c: c.name)
+def test_fp8_all_tokens(cfg):
+    log(f"[test] fp8 {cfg.name}")
+    layer = layer_for(cfg.hidden, cfg.inter, cfg.experts, cfg.topk, cfg.tokens, mma_type=FP8)
+    layer.load_fp32(lambda e: synth.expert_weights_f32(cfg, e), threads=4)
+    got = run_config(layer, cfg)
+    log(f"    rows per expert {got['counts'].tolist()[:16]}")
+    W = all_expert_weights(cfg)
+    ref = forward(got["x"], got["ids"], got["w"], W, cfg.experts, cfg.inter, mma_type="fp8xfp4", keep_acc=True)
+    check_all_stages(got, ref, cfg.topk, weights=lambda e: (W[0][e], W[1][e], W[2][e], W[3][e]))
+    if cfg.tokens * cfg.topk > 16 * cfg.experts:     # the LDS-staged path: its GEMM1 scale planes
+        nv = int(got["counts"].sum())
+        assert np.array_equal(got["xsf_planes"], got["xsf"][got["sorted_rows"][:nv] // cfg.topk])
+    again = run_config(layer, cfg)
+    assert np.array_equal(again["out"], got["out"]) and np.array_equal(again["hq"], got["hq"])
+
+
+_oracle_weights = lazy_expert_weights(synth.CONFIGS[1])
+
+
+@pytest.mark.parametrize("cfg", [synth.CONFIGS[2], synth.CONFIGS[3]], ids=lambda c: c.name)
+def test_fp8_full_size_sampled(cfg):
+    layer = synth_layer_fp8(1, 16384)
+    log(f"[test] fp8 full size {cfg.name}: forward")
+    got = run_config(layer, cfg)
+    x, ids, w = got["x"], got["ids"], got["w"]
+    rq, rs = mxfp8.quantize(bf16.decode(x))
+    assert np.array_equal(got["xq"], rq) and np.array_equal(got["xsf"], rs)
+    counts, offsets, srt, pos = route(ids, cfg.experts)
+    assert np.array_equal(got["sorted_rows"], srt) and np.array_equal(got["pos"], pos)
+    rng = np.random.default_rng(100 + cfg.index)
+    toks = sorted(rng.choice(cfg.tokens, 2, replace=False).tolist())
+    log(f"    oracle on tokens {toks}")
+    ref = forward(x, ids, w, _oracle_weights, cfg.experts, cfg.inter, tokens=toks, mma_type="fp8xfp4",
+                  keep_acc=True)
+    rows = np.array([pos[t * cfg.topk + j] for t in toks for j in range(cfg.topk) if pos[t * cfg.topk + j] >= 0])
+    stats = compare_requant(got["hq"][rows], got["hsf"][rows], ref["hq"][rows], ref["hsf"][rows], ref["h"][rows],
+                            fp8=True)
+    stats.update(fp8_requant_sampled(rows, got["hq"][rows], got["hsf"][rows], ref, cfg.topk,
+                                     lambda e: _oracle_weights(e)[:2]))
+    exact = same_h_rows(got["hq"][rows], got["hsf"][rows], ref["hq"][rows], ref["hsf"][rows])
+    fb = fp8_bound_for(rows[exact], offsets, ref["hq"][rows[exact]], ref["hsf"][rows[exact]],
+                       lambda e: _oracle_weights(e)[2:])
+    y_err, y_same = check_y(got["y"][rows], ref["y"][rows], exact, fp8_bound=fb)
+    o_err = rel_l2(bf16.decode(got["out"][toks]), ref["out_f64"][toks])
+    log(f"    requant {stats} y rel-L2 {y_err:.2e} (bf16-equal {y_same:.4f}) out rel-L2 {o_err:.2e}")
+    assert o_err <= OUT_REL_L2

@@ -13,7 +13,7 @@ from oracle.forward import forward
 from oracle.route import route
 from tests.gpu_support import log, run_config, synth_layer
 from tests.oracle_inputs import lazy_expert_weights
-from tests.parity import OUT_REL_L2, check_y, compare_requant, rel_l2
+from tests.parity import OUT_REL_L2, check_y, compare_requant, rel_l2, same_h_rows
 
 pytestmark = pytest.mark.gpu
 DSV4 = [c for c in synth.CONFIGS if c.weight_set == 1]
@@ -41,7 +41,8 @@ def test_full_size_sampled(cfg):
     ref = forward(x, ids, w, _oracle_weights, cfg.experts, cfg.inter, tokens=toks)
     rows = np.array([pos[t * cfg.topk + j] for t in toks for j in range(cfg.topk) if pos[t * cfg.topk + j] >= 0])
     stats = compare_requant(got["hq"][rows], got["hsf"][rows], ref["hq"][rows], ref["hsf"][rows], ref["h"][rows])
-    y_err, y_same = check_y(got["y"][rows], ref["y"][rows])
+    y_err, y_same = check_y(got["y"][rows], ref["y"][rows],
+                            same_h_rows(got["hq"][rows], got["hsf"][rows], ref["hq"][rows], ref["hsf"][rows]))
     o_err = rel_l2(bf16.decode(got["out"][toks]), ref["out_f64"][toks])
     log(f"    requant {stats} y rel-L2 {y_err:.2e} (bf16-equal {y_same:.4f}) out rel-L2 {o_err:.2e}")
     assert o_err <= OUT_REL_L2

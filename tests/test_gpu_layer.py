@@ -10,22 +10,36 @@ import synth
 from oracle.forward import forward
 from tests.gpu_support import dev, dev_bf16, host_bits, layer_for, log, run_config, synth_layer, workspace_host
 from tests.oracle_inputs import all_expert_weights
-from tests.parity import OUT_REL_L2, check_y, compare_requant, rel_l2
+from tests.parity import (OUT_REL_L2, check_y, compare_requant, fp8_bound_for, fp8_requant_sampled, rel_l2,
+                          same_h_rows, sample_rows)
 
 pytestmark = pytest.mark.gpu
 TINY = synth.CONFIGS[0]
 
 
-def check_all_stages(got, ref, k):
+def check_all_stages(got, ref, k, weights=None):
+    """weights: for the fp8xfp4 MMA type (E4M3 codes for x and h), e -> the
+    oracle's (W1 codes, W1 scales, W2 codes, W2 scales) of expert e, which the
+    error bounds need; ref then comes from forward(..., keep_acc=True)."""
     from oracle import bf16
+    fp8 = weights is not None
     assert np.array_equal(got["xq"], ref["xq"]) and np.array_equal(got["xsf"], ref["xsf"])
     for key in ("counts", "offsets", "sorted_rows", "pos"):
         assert np.array_equal(got[key], ref[key]), key
-    stats = compare_requant(got["hq"], got["hsf"], ref["hq"], ref["hsf"], ref["h"])
-    y_err, y_same = check_y(got["y"], ref["y"])
+    stats = compare_requant(got["hq"], got["hsf"], ref["hq"], ref["hsf"], ref["h"], fp8=fp8)
+    exact = same_h_rows(got["hq"], got["hsf"], ref["hq"], ref["hsf"])
+    fb = None
+    if fp8:
+        rows = sample_rows(~exact)
+        stats.update(fp8_requant_sampled(rows, got["hq"][rows], got["hsf"][rows], ref, k,
+                                         lambda e: weights(e)[:2]))
+        idx = np.nonzero(exact)[0]
+        fb = fp8_bound_for(idx, ref["offsets"], ref["hq"][idx], ref["hsf"][idx], lambda e: weights(e)[2:])
+    y_err, y_same = check_y(got["y"], ref["y"], exact, fp8_bound=fb)
     o_err = rel_l2(bf16.decode(got["out"]), ref["out_f64"])
     same = float(np.mean(got["out"] == ref["out"])) if got["out"].size else 1.0
-    log(f"    requant {stats}  y rel-L2 {y_err:.2e} (bf16-equal {y_same:.4f})  out rel-L2 {o_err:.2e}  "
+    log(f"    requant {stats}  rows with identical h {int(exact.sum())}/{exact.size}  "
+        f"y rel-L2 {y_err:.2e} (bf16-equal {y_same:.4f})  out rel-L2 {o_err:.2e}  "
         f"out bit-identical {same:.4f}")
     assert o_err <= OUT_REL_L2
     return o_err
