@@ -106,6 +106,12 @@ __device__ __forceinline__ void stage_barrier() { asm volatile("s_waitcnt lgkmcn
 #ifndef MOE_LDS_INTERLEAVE
 #define MOE_LDS_INTERLEAVE 1    // 1: a stage's DMAs are issued between the MFMA groups of the step
 #endif
+#ifndef MOE_LDS_PAIR_G2_F8
+#define MOE_LDS_PAIR_G2_F8 1    // fp8xfp4, one tile per expert: GEMM2 pairs weight blocks as GEMM1 does
+#endif
+#ifndef MOE_LDS_PAIR_MULTI_F8
+#define MOE_LDS_PAIR_MULTI_F8 1 // fp8xfp4, several tiles per expert: both GEMMs pair weight blocks
+#endif
 #ifndef MOE_LDS_BLOCKS
 #define MOE_LDS_BLOCKS 2        // workgroups per CU the launch bound asks for
 #endif
@@ -327,7 +333,10 @@ int lds_max_tiles(int R, int E, int tile_rows) { return (R + tile_rows - 1) / ti
 // both (half the token traffic; measured 6% faster GEMM1 at 96 rows per
 // expert).  More rows: the tiles of an expert share each weight block through
 // L2, loads keep the default policy, and single-block workgroups (two per CU,
-// each with its own barrier) keep the MFMAs busier.
+// each with its own barrier) keep the MFMAs busier.  With E4M3 tokens a stage
+// holds twice the token bytes, three stages no longer fit two workgroups per
+// CU, and pairing wins everywhere (GEMM2 at 96 rows per expert: 914 -> 897 us
+// per layer; Zipf tiles at 16384 tokens: 3066 -> 2748 us).
 template <bool G1, bool F8>
 static hipError_t launch_prefill(const uint8_t* wc, const uint8_t* wsc, const uint8_t* act, const uint8_t* act_sf,
                                  const int32_t* counts, const int32_t* offsets, const int32_t* sorted_rows,
@@ -338,8 +347,10 @@ static hipError_t launch_prefill(const uint8_t* wc, const uint8_t* wsc, const ui
                          hrows, hq, hsf, acc_out, y, stream
   const bool single = rows_hint <= kLdsNT * 16;
   const int nwb = G1 ? I / 128 : H / 256;
-  if (single && G1 && nwb % 2 == 0) return launch_prefill_wb<G1, true, 2, F8>(MOE_PREFILL_ARGS);
+  const bool pair = nwb % 2 == 0 && (single ? (G1 || (F8 && MOE_LDS_PAIR_G2_F8)) : (F8 && MOE_LDS_PAIR_MULTI_F8));
+  if (single && pair) return launch_prefill_wb<G1, true, 2, F8>(MOE_PREFILL_ARGS);
   if (single) return launch_prefill_wb<G1, true, 1, F8>(MOE_PREFILL_ARGS);
+  if (pair) return launch_prefill_wb<G1, false, 2, F8>(MOE_PREFILL_ARGS);
   return launch_prefill_wb<G1, false, 1, F8>(MOE_PREFILL_ARGS);
 #undef MOE_PREFILL_ARGS
 }
