@@ -8,7 +8,9 @@ seconds:
   h512_i256_e8    16-row token tiles (about 6 rows per expert; the hot
                   expert's 19 take two passes)
   e4_k1_zipf      a hot expert with more rows than one pass holds (24): the
-                  weights are streamed once per pass"""
+                  weights are streamed once per pass
+  h1024_i512_e4_k1_zipf  the same with the 4-slot weight ring of the DSV4
+                  shape's K loops (H and I multiples of 512)"""
 import numpy as np
 import pytest
 
@@ -24,6 +26,7 @@ SHAPES = [
     synth.LayerConfig(110, "stream_h1024_i512_e16_k2_t100", 100, 1024, 512, 16, 2, "uniform", 110),
     synth.LayerConfig(111, "stream_h512_i256_e8_k2_t24", 24, 512, 256, 8, 2, "zipf", 111, 1.1),
     synth.LayerConfig(112, "stream_h512_i256_e4_k1_t60_zipf", 60, 512, 256, 4, 1, "zipf", 112, 1.5),
+    synth.LayerConfig(113, "stream_h1024_i512_e4_k1_t60_zipf", 60, 1024, 512, 4, 1, "zipf", 113, 1.5),
 ]
 
 
@@ -40,3 +43,4 @@ def test_stream_path_all_tokens(cfg):
         assert counts.max() > 24                                # a second pass over the weights
     ref = forward(got["x"], got["ids"], got["w"], all_expert_weights(cfg), cfg.experts, cfg.inter)
     check_all_stages(got, ref, cfg.topk)
+
