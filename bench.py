@@ -78,13 +78,14 @@ def gemm1_path(cfg):
     return "stream" if rows_hint <= STREAM_MAX_ROWS else "prefill"
 
 
-def measured_traffic(workload, path):
+def measured_traffic(workload, path, fp8=False):
     """HBM bytes per GEMM1 launch from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE runs, each scaled by the same counter on a copy of known size;
-    None if there are none for this workload or the kernel changed since."""
+    None if there are none for this workload and MMA type or the kernel
+    changed since."""
     import hashlib
     kernel, sources = GEMM1_KERNELS[path]
-    path = COUNTERS_FILE.format(kernel, workload)
+    path = COUNTERS_FILE.format(kernel, workload + ("_fp8xfp4" if fp8 else ""))
     if not os.path.exists(path):
         return None
     kv = {}
@@ -281,7 +282,7 @@ def main():
         "split_step_us": round(split_ms * 1e3, 2),
         "roofline": {"kernel": g1_kernel, "bound": "mfma" if mfma_bound else "hbm", "achieved": round(g1_ach, 1),
                      "peak": g1_peak, "unit": g1_unit, "frac": round(g1_ach / g1_peak, 4),
-                     "traffic": None if fp8 else measured_traffic(cfg.name, path), "avg_us": round(gemm1_us, 2),
+                     "traffic": measured_traffic(cfg.name, path, fp8), "avg_us": round(gemm1_us, 2),
                      "bytes_per_launch": alg["gemm1_bytes"], "flops_per_launch": alg["gemm1_flops"]},
         "wall_s": round(wall, 3),
     }

@@ -36,7 +36,10 @@
 // XCDs, so each XCD gets a contiguous range of L: the tiles that share a
 // weight block run on one XCD at about the same time and fetch it from HBM
 // once into that XCD's L2.  (Tile-major order, which keeps a tile's tokens in
-// L2 instead, measured 30% slower at 96 rows per expert.)
+// L2 instead, measured 30% slower at 96 rows per expert.)  Exception: GEMM2
+// with one tile per expert, where no weight block is shared: XCD x owns whole
+// tiles, so each tile's rows of h reach one L2 only (E4M3 h at 96 rows per
+// expert: 889 -> 866 us per layer; E2M1 about even; GEMM1 measured slower so).
 //
 // Occupancy: two workgroups per CU (3 stages x 26 KiB of LDS each, 176 VGPRs
 // including the accumulators) measured faster than one workgroup with a
@@ -103,6 +106,9 @@ __device__ __forceinline__ void stage_barrier() { asm volatile("s_waitcnt lgkmcn
 #ifndef MOE_LDS_PAIRED
 #define MOE_LDS_PAIRED 1        // 1: per-XCD weight blocks, tile-major inside an XCD
 #endif
+#ifndef MOE_LDS_XCD_TILES
+#define MOE_LDS_XCD_TILES 1     // GEMM2, one tile per expert: XCDs own whole tiles (else weight blocks)
+#endif
 #ifndef MOE_LDS_INTERLEAVE
 #define MOE_LDS_INTERLEAVE 1    // 1: a stage's DMAs are issued between the MFMA groups of the step
 #endif
@@ -144,8 +150,16 @@ __global__ void __launch_bounds__(256 * WB, WB == 1 ? MOE_LDS_BLOCKS : 1) gemm_l
   const int K = G1 ? H : I;
   const int nwb = (G1 ? I / 128 : H / 256) / WB;      // weight-block groups per expert
   const int G = gridDim.x;
+  constexpr bool XCD_TILES = WNT && !G1 && MOE_LDS_XCD_TILES;
   int wb, ti;
-  if (MOE_LDS_PAIRED && nwb % 8 == 0) {
+  if (XCD_TILES) {
+    // GEMM2, one tile per expert: XCD x owns tiles x, x+8, ... and runs all
+    // weight blocks of each before the next, so a tile's rows of h are fetched
+    // into one L2 only (the launch covers ceil(max_tiles/8)*8 tiles).
+    const int j = blockIdx.x >> 3, tq = j / nwb;
+    ti = tq * 8 + (blockIdx.x & 7);
+    wb = j - tq * nwb;
+  } else if (MOE_LDS_PAIRED && nwb % 8 == 0) {
     // XCD x owns weight blocks [x*q, x*q+q); its workgroups run tile-major
     // over them, so the q workgroups of a tile share its token lines in L2.
     const int q = nwb >> 3, j = blockIdx.x >> 3;
@@ -317,7 +331,8 @@ static hipError_t launch_prefill_wb(const uint8_t* wc, const uint8_t* wsc, const
     if (err != hipSuccess) return err;
   }
   const int nwb = (G1 ? I / 128 : H / 256) / WB;
-  const int64_t blocks = ((int64_t)max_tiles * nwb + 7) / 8 * 8;
+  const int64_t blocks = WNT && !G1 && MOE_LDS_XCD_TILES ? (int64_t)((max_tiles + 7) / 8) * nwb * 8
+                                                  : ((int64_t)max_tiles * nwb + 7) / 8 * 8;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256 * WB), lds, stream, wc, wsc, act, act_sf, counts, offsets,
                      sorted_rows, tiles, num_tiles, max_tiles, H, I, k, hrows, hq, hsf, acc_out, y);
   return hipGetLastError();
