@@ -13,8 +13,8 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # The GPU tier runs on the GPU machine; here (no GPU) those tests are skipped
-    # unless they were deselected with -m "not gpu" already.
+    # The GPU tier needs an MI355X; on a machine without a GPU those tests are
+    # skipped unless they were deselected with -m "not gpu" already.
     try:
         import torch
         have_gpu = torch.cuda.is_available()
