@@ -41,9 +41,10 @@
 // tiles, so each tile's rows of h reach one L2 only (E4M3 h at 96 rows per
 // expert: 889 -> 866 us per layer; E2M1 about even; GEMM1 measured slower so).
 //
-// Occupancy: two workgroups per CU (3 stages x 26 KiB of LDS each, 176 VGPRs
-// including the accumulators) measured faster than one workgroup with a
-// deeper ring; the second workgroup's MFMAs cover the first one's waits.
+// Occupancy: two workgroups per CU (3 stages x 26 KiB of LDS each; about 210
+// VGPRs per lane with the accumulators, 245 with E4M3 tokens) measured faster
+// than one workgroup with a deeper ring; the second workgroup's MFMAs cover
+// the first one's waits.
 #include "epilogue.h"
 #include "gemm_common.h"
 #include "launch.h"
