@@ -100,3 +100,35 @@ def test_fp8_activations_double_the_token_regions():
     assert size(l8, "xq", "xsf") == 2 * size(l4, "xq", "xsf") == 512 * 4096
     assert size(l8, "hq", "hsf") == 2 * size(l4, "hq", "hsf") == 512 * 6 * 2048
     assert _lib.moe_w4a4_query(c8)[0] == _lib.moe_w4a4_query(c4)[0]      # same MXFP4 weights
+
+
+def test_prepare_weights_validation():
+    from block_scaled_fp4_pre_amd import _lib
+    L = _lib.lib()
+    cfg = _lib.make_cfg(256, 128, 8, 2, 16)
+    prepared, _ = _lib.moe_w4a4_query(cfg)
+    P = ctypes.c_void_p
+    fake = P(1 << 20)
+    st = L.moe_w4a4_prepare_weights(ctypes.byref(cfg), None, fake, fake, fake, fake, prepared, None)
+    assert st == _lib.MOE_EINVAL
+    st = L.moe_w4a4_prepare_weights(ctypes.byref(cfg), fake, fake, fake, fake, P((1 << 20) + 64), prepared, None)
+    assert st == _lib.MOE_EINVAL                       # prepared must be 256-byte aligned
+    st = L.moe_w4a4_prepare_weights(ctypes.byref(cfg), fake, fake, fake, fake, fake, prepared - 1, None)
+    assert st == _lib.MOE_EWORKSPACE
+    bad = _lib.make_cfg(256, 128, 8, 2, 16)
+    bad.mma_type = 7
+    st = L.moe_w4a4_prepare_weights(ctypes.byref(bad), fake, fake, fake, fake, fake, prepared, None)
+    assert st == _lib.MOE_EUNSUPPORTED
+
+
+def test_valid_call_without_a_gfx950_reports_no_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: the call would run")
+    from block_scaled_fp4_pre_amd import _lib
+    L = _lib.lib()
+    cfg = _lib.make_cfg(256, 128, 8, 2, 16)
+    _, ws = _lib.moe_w4a4_query(cfg)
+    fake = ctypes.c_void_p(1 << 20)                    # aligned, never dereferenced
+    st = L.moe_w4a4_forward(ctypes.byref(cfg), fake, 4, fake, fake, fake, fake, fake, ws, None)
+    assert st == _lib.MOE_ENODEVICE
