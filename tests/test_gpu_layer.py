@@ -134,3 +134,29 @@ def test_zero_tokens_is_a_no_op(tiny_layer):
                           device="cuda"), torch.zeros((0, 2), device="cuda"), out, tiny_layer.workspace)
     torch.cuda.synchronize()
     assert torch.all(out == 7.0)
+
+
+@pytest.mark.parametrize("E,k,T", [(5, 2, 37), (7, 3, 1000), (512, 8, 300), (512, 16, 2000)],
+                         ids=["E5_k2_T37", "E7_k3_T1000", "E512_k8_T300", "E512_k16_T2000"])
+def test_expert_count_extremes(E, k, T):
+    """Odd expert counts and the largest E and k the ABI takes, on every token:
+    the streaming path (E5, E512_k8), the LDS-staged path (E7), and 32000
+    routed rows, past the one-block pre-dispatch limit, so quantization and
+    routing run as separate kernels (E512_k16)."""
+    from oracle import mxfp4
+    log(f"[test] E={E} k={k} T={T}")
+    H, I = 256, 128
+    rng = np.random.default_rng(1000 * E + k)
+    W1 = (rng.standard_normal((E, 2 * I, H)) * 0.05).astype(np.float32)
+    W2 = (rng.standard_normal((E, H, I)) * 0.05).astype(np.float32)
+    layer = layer_for(H, I, E, k, T)
+    layer.load_fp32(lambda e: (W1[e], W2[e]), threads=4)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    w /= w.sum(axis=1, keepdims=True)
+    got = _run_custom(layer, x, ids, w)
+    c1, s1 = mxfp4.quantize_packed(W1)
+    c2, s2 = mxfp4.quantize_packed(W2)
+    ref = forward(x, ids, w, (c1, s1, c2, s2), E, I)
+    check_all_stages(got, ref, k)
