@@ -136,20 +136,28 @@ def test_zero_tokens_is_a_no_op(tiny_layer):
     assert torch.all(out == 7.0)
 
 
-@pytest.mark.parametrize("E,k,T", [(5, 2, 37), (7, 3, 1000), (512, 8, 300), (512, 16, 2000)],
-                         ids=["E5_k2_T37", "E7_k3_T1000", "E512_k8_T300", "E512_k16_T2000"])
-def test_expert_count_extremes(E, k, T):
+EXTREMES = [  # (E, k, T, H, I, mma_type)
+    (5, 2, 37, 256, 128, 0), (7, 3, 1000, 256, 128, 0), (512, 8, 300, 256, 128, 0), (512, 16, 2000, 256, 128, 0),
+    (6, 2, 40, 768, 384, 0), (6, 2, 600, 768, 384, 0), (6, 2, 40, 768, 384, 1), (6, 2, 600, 768, 384, 1),
+]
+
+
+@pytest.mark.parametrize("E,k,T,H,I,mma", EXTREMES,
+                         ids=[f"E{e}_k{k}_T{t}_H{h}_I{i}_{'fp8' if m else 'fp4'}" for e, k, t, h, i, m in EXTREMES])
+def test_expert_count_extremes(E, k, T, H, I, mma):
     """Odd expert counts and the largest E and k the ABI takes, on every token:
     the streaming path (E5, E512_k8), the LDS-staged path (E7), and 32000
     routed rows, past the one-block pre-dispatch limit, so quantization and
-    routing run as separate kernels (E512_k16)."""
+    routing run as separate kernels (E512_k16).  Then H = 768, I = 384 (6 and
+    3 K steps: the 2- and 1-slot weight rings and the 8- and 4-chunk token
+    swizzles of the streaming GEMMs), streaming and LDS-staged, for both MMA
+    types."""
     from oracle import mxfp4
-    log(f"[test] E={E} k={k} T={T}")
-    H, I = 256, 128
-    rng = np.random.default_rng(1000 * E + k)
+    log(f"[test] E={E} k={k} T={T} H={H} I={I} mma_type={mma}")
+    rng = np.random.default_rng(1000 * E + k + 7 * H + T)
     W1 = (rng.standard_normal((E, 2 * I, H)) * 0.05).astype(np.float32)
     W2 = (rng.standard_normal((E, H, I)) * 0.05).astype(np.float32)
-    layer = layer_for(H, I, E, k, T)
+    layer = layer_for(H, I, E, k, T, mma_type=mma)
     layer.load_fp32(lambda e: (W1[e], W2[e]), threads=4)
     x = synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
     ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
@@ -158,5 +166,7 @@ def test_expert_count_extremes(E, k, T):
     got = _run_custom(layer, x, ids, w)
     c1, s1 = mxfp4.quantize_packed(W1)
     c2, s2 = mxfp4.quantize_packed(W2)
-    ref = forward(x, ids, w, (c1, s1, c2, s2), E, I)
-    check_all_stages(got, ref, k)
+    ref = forward(x, ids, w, (c1, s1, c2, s2), E, I, mma_type="fp8xfp4" if mma else "mxf4xmxf4",
+                  keep_acc=bool(mma))
+    weights = (lambda e: (c1[e], s1[e], c2[e], s2[e])) if mma else None
+    check_all_stages(got, ref, k, weights=weights)
