@@ -3,8 +3,9 @@
  *
  * The layer is the fused "mega-MoE" W4A4 layer of a DeepSeek-V4-Flash-shaped
  * model (hidden 4096, inter 2048, 256 experts, top-6): tokens and expert
- * weights are both MXFP4 (E2M1 codes, one UE8M0 scale per 32 elements), the
- * expert MLP is SwiGLU.  Sources:
+ * weights are both MXFP4 (E2M1 codes, one UE8M0 scale per 32 elements), or,
+ * with the fp8xfp4 mma_type below, the tokens are MXFP8 E4M3; the expert MLP
+ * is SwiGLU.  Sources:
  *   [P1] sglang PR "[deepseek-v4] Bump sgl-deep-gemm for packed FP4xFP4
  *        mega-MoE (W4A4)": title (packed FP4 x FP4 operands), Appendix
  *        "measured data" (the layer shape).
