@@ -110,6 +110,9 @@ __device__ __forceinline__ void stage_barrier() { asm volatile("s_waitcnt lgkmcn
 #ifndef MOE_LDS_XCD_TILES
 #define MOE_LDS_XCD_TILES 1     // GEMM2, one tile per expert: XCDs own whole tiles (else weight blocks)
 #endif
+#ifndef MOE_LDS_MFMA_PRIO
+#define MOE_LDS_MFMA_PRIO 1     // several tiles per expert: raised wave priority over each MFMA block
+#endif
 #ifndef MOE_LDS_INTERLEAVE
 #define MOE_LDS_INTERLEAVE 1    // 1: a stage's DMAs are issued between the MFMA groups of the step
 #endif
@@ -263,6 +266,10 @@ __global__ void __launch_bounds__(256 * WB, WB == 1 ? MOE_LDS_BLOCKS : 1) gemm_l
       }
       sbv[nt] = (int)(*reinterpret_cast<const uint32_t*>(st + L::T_SCALES + n * 4) >> (8 * kb));
     }
+    // Several tiles per expert (the MFMA-bound regime): the wave keeps a
+    // raised issue priority over its MFMA block, so the SIMD's other wave
+    // (between its own steps) does not interleave its instructions into it.
+    if constexpr (!WNT && MOE_LDS_MFMA_PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
 #if MOE_LDS_INTERLEAVE
@@ -287,6 +294,7 @@ __global__ void __launch_bounds__(256 * WB, WB == 1 ? MOE_LDS_BLOCKS : 1) gemm_l
       __builtin_amdgcn_sched_barrier(0);
 #endif
     }
+    if constexpr (!WNT && MOE_LDS_MFMA_PRIO) __builtin_amdgcn_s_setprio(0);
   };
   // Before step s a wave waits until only the DMAs of the P-2 stages after s
   // that it issued are in flight; the barrier then makes stage s whole and
