@@ -1,0 +1,43 @@
+"""bench.py's command-line contract: more than one GPU is refused with a
+message (CPU tier), and one short run prints exactly one JSON line with the
+fields and types the benchmark record needs (GPU tier)."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+BENCH = os.path.join(ROOT, "bench.py")
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, BENCH, "--gpus", "2"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("mma", ["mxf4xmxf4", "fp8xfp4"])
+def test_one_json_line_with_the_record_fields(mma):
+    r = subprocess.run([sys.executable, BENCH, "--steps", "3", "--warmup", "1", "--no-cpu-baseline",
+                        "--mma-type", mma], capture_output=True, text=True, timeout=600, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stdout.splitlines() if ln.strip()]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    for key, typ in (("metric", str), ("value", float), ("unit", str), ("n_gpus", int), ("steps", int),
+                     ("warmup", int), ("ms_per_step", float), ("higher_is_better", bool), ("scaling", str),
+                     ("dtype", str), ("data", str), ("config", dict), ("roofline", dict)):
+        assert isinstance(d[key], typ), key
+    assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1 and d["unit"] == "us"
+    assert d["higher_is_better"] is False and d["data"] == "synthetic"
+    assert d["config"]["workload"] == "dsv4flash_t512" and d["config"]["mma_type"] == mma
+    assert abs(d["value"] - 1e3 * d["ms_per_step"]) <= 0.01 * d["value"]
+    assert isinstance(d["vs_baseline"], float)                  # the pages quote this workload for both types
+    roof = d["roofline"]
+    assert roof["bound"] in ("hbm", "mfma") and roof["unit"] in ("GB/s", "TFLOP/s")
+    assert 0 < roof["achieved"] and roof["peak"] > 0 and abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
+    assert roof["traffic"] is None or roof["traffic"] > 0
+    assert "cpu_baseline" not in d
