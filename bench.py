@@ -67,7 +67,8 @@ def algorithmic(cfg, counts, fp8=False):
 STREAM_MAX_ROWS = 16              # mean routed rows per expert up to which GEMM1 is the streaming kernel
 # GEMM1 kernel of each path, with the sources its code comes from.
 GEMM1_KERNELS = {
-    "stream": ("gemm1_swiglu_kernel", ("gemm1.hip", "gemm_common.h", "epilogue.h", "device_common.h", "tiles.h")),
+    "stream": ("gemm1_swiglu_kernel", ("gemm1.hip", "stream_ring.h", "gemm_common.h", "epilogue.h", "device_common.h",
+                                       "tiles.h")),
     "prefill": ("gemm_lds_kernel", ("gemm_lds.hip", "gemm_common.h", "epilogue.h", "device_common.h", "tiles.h")),
 }
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "{}_{}_hbm_counters.txt")

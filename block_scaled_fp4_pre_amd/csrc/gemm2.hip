@@ -18,6 +18,7 @@
 #include "epilogue.h"
 #include "gemm_common.h"
 #include "launch.h"
+#include "stream_ring.h"
 #include "tiles.h"
 
 #ifndef MOE_STREAM_RING_DEPTH
@@ -29,6 +30,10 @@
 
 #ifndef MOE_GEMM2_MIN_BLOCKS
 #define MOE_GEMM2_MIN_BLOCKS 2    // launch bound: workgroups per CU the register budget must allow
+#endif
+
+#ifndef MOE_STREAM_EARLY
+#define MOE_STREAM_EARLY 1        // two-tile form: first weight loads before the row count is read
 #endif
 
 #ifndef MOE_GEMM2_UNITS_PER_WAVE
@@ -45,9 +50,6 @@ __global__ void __launch_bounds__(256, MOE_GEMM2_MIN_BLOCKS) gemm2_kernel(
   const int groups = H / (256 * upw);
   const int e = blockIdx.x / groups;
   const int g = blockIdx.x - e * groups;
-  const int n_e = counts[e];
-  if (n_e == 0) return;
-  const int base = offsets[e];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps the buffer resources in SGPRs
   const int v0 = g * 4 * upw + wave;   // wave w owns unit w of each of the workgroup's upw unit groups
@@ -71,16 +73,28 @@ __global__ void __launch_bounds__(256, MOE_GEMM2_MIN_BLOCKS) gemm2_kernel(
   const int voff = lane * 16, svoff = lane * 4;
   const int tok_lane = lane & 15, kb = lane >> 4;
 
+  // With two token tiles (many rows per expert) an empty expert is rare, so
+  // the first pass's weight loads go out before the expert's row count is
+  // known; an empty expert's workgroup waits for them and exits.  The empty
+  // asm statement may, as far as the compiler knows, write the weights, so the
+  // loads cannot be sunk below the branch.
+  constexpr bool kEarly = NT == 2 && MOE_STREAM_EARLY;
+  uint4 a[D][4];
+  uint32_t sa[D];
+  if constexpr (kEarly) {
+    fill_weight_ring<D>(a, sa, wr, sr, voff, svoff, kUnitStepStride, kUnitScaleStride);
+    asm volatile("" ::"s"(w2c), "s"(w2s) : "memory");
+  }
+  const int n_e = counts[e];
+  if (n_e == 0) {
+    if constexpr (kEarly) wait_vmem_all();
+    return;
+  }
+  const int base = offsets[e];
+
   for (int t0 = 0; t0 < n_e; t0 += ROWS) {
     const int nrows = min(ROWS, n_e - t0);
-    uint4 a[D][4];
-    uint32_t sa[D];
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) a[d][rb] = buf_load16(wr, voff + rb * 1024, d * kUnitStepStride);
-      sa[d] = buf_load4(sr, svoff, d * kUnitScaleStride);
-    }
+    if (!kEarly || t0 > 0) fill_weight_ring<D>(a, sa, wr, sr, voff, svoff, kUnitStepStride, kUnitScaleStride);
     __syncthreads();
     const int row0 = base + t0;
     gather_tile<ROWS, SWZ, true, F8 ? 128 : 64>(lds_codes, lds_scales, hq, hsf, row_bytes, sc_bytes, nrows,

@@ -1,0 +1,22 @@
+// Weight ring of the streaming GEMMs (gemm1.hip, gemm2.hip): each wave keeps
+// its next D K steps of weights in VGPRs, one step being four 1 KiB code loads
+// (16 bytes per lane each) and one scale dword per lane.
+#pragma once
+#include "gemm_common.h"
+
+namespace moe {
+
+// Fill the ring with the wave's first D K steps.
+template <int D>
+__device__ __forceinline__ void fill_weight_ring(uint4 (&a)[D][4], uint32_t (&sa)[D], __amdgpu_buffer_rsrc_t wr,
+                                                 __amdgpu_buffer_rsrc_t sr, int voff, int svoff, int step_stride,
+                                                 int scale_stride) {
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) a[d][rb] = buf_load16(wr, voff + rb * 1024, d * step_stride);
+    sa[d] = buf_load4(sr, svoff, d * scale_stride);
+  }
+}
+
+}  // namespace moe
