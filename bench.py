@@ -1,7 +1,7 @@
 """Benchmark of the W4A4 MoE layer forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--mma-type {mxf4xmxf4,fp8xfp4}]
-                    [--no-cpu-baseline]
+                    [--no-cpu-baseline] [--no-ceiling]
 
 A step is one whole forward of the layer (pre-dispatch quantization, routing,
 GEMM1 + SwiGLU + requant, GEMM2, combine) on one batch of synthetic tokens whose
@@ -19,7 +19,13 @@ gemm_lds_kernel above), against the HBM or the MFMA peak of the MMA type (MXFP4,
 or FP8 for the fp8xfp4 type), whichever bounds
 its algorithmic bytes and flops: its duration comes from K further steps of the
 same launches in which events on the same stream bracket the GEMM1 launch
-("split_step_us" is the step time of that loop).  "cpu_baseline" times the fp64 CPU oracle on a
+("split_step_us" is the step time of that loop).  "forward_us" gives the
+median, minimum and maximum of K more forwards, each bracketed by its own
+events.  "ceiling" holds this GPU's measured ceilings (libmoe_ceiling.so): the
+streaming-read rate of a 2 GiB buffer with non-temporal and with default loads
+(best over 2 to 16 workgroups per CU),
+the rate of back-to-back FP4 MFMAs, and GEMM1's achieved rate as a fraction of
+the ceiling that bounds it.  "cpu_baseline" times the fp64 CPU oracle on a
 bounded slice of the same workload (a few experts with all their routed rows)
 and scales it to one layer.
 """
@@ -153,6 +159,8 @@ def main():
     ap.add_argument("--mma-type", default="mxf4xmxf4", choices=("mxf4xmxf4", "fp8xfp4"),
                     help="activation format: MXFP4 (the default, W4A4) or MXFP8 E4M3 (W4A8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-read and FP4 MFMA probes (libmoe_ceiling.so)")
     ap.add_argument("--threads", type=int, default=16)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a 256 MiB device-to-device copy (reference for HBM counters)")
@@ -232,6 +240,15 @@ def main():
     gemm1_us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
     split_ms = split_s.elapsed_time(split_e) / args.steps
 
+    # Per-forward spread: K more forwards, each bracketed by its own events.
+    fwd = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in fwd:
+        a.record()
+        layer.forward(x, ids, w, out)
+        b.record()
+    torch.cuda.synchronize()
+    fwd_us = np.array([a.elapsed_time(b) for a, b in fwd]) * 1e3
+
     if args.calibrate_copy:
         # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE per dispatch
         # calibrate the counters read for the layer's kernels.
@@ -281,12 +298,22 @@ def main():
         "hbm_gbps": round(gbps, 1),
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "split_step_us": round(split_ms * 1e3, 2),
+        "forward_us": {"median": round(float(np.median(fwd_us)), 2), "min": round(float(fwd_us.min()), 2),
+                       "max": round(float(fwd_us.max()), 2)},
         "roofline": {"kernel": g1_kernel, "bound": "mfma" if mfma_bound else "hbm", "achieved": round(g1_ach, 1),
                      "peak": g1_peak, "unit": g1_unit, "frac": round(g1_ach / g1_peak, 4),
                      "traffic": measured_traffic(cfg.name, path, fp8), "avg_us": round(gemm1_us, 2),
                      "bytes_per_launch": alg["gemm1_bytes"], "flops_per_launch": alg["gemm1_flops"]},
         "wall_s": round(wall, 3),
     }
+    if not args.no_ceiling:
+        # Measured ceilings of this GPU, beside the published peaks the
+        # roofline fraction uses.
+        from block_scaled_fp4_pre_amd import ceiling
+        ceil = ceiling.measure()
+        ref = ceil["mfma_fp4_TFLOPs"] if mfma_bound else ceil["read_nt_GBps"]
+        ceil["gemm1_frac"] = round(g1_ach / ref, 4)
+        res["ceiling"] = ceil
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle slice)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg, x_h, ids_h, w_h, mma_type=args.mma_type)

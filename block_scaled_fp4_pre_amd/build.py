@@ -2,8 +2,10 @@
 
     python block_scaled_fp4_pre_amd/build.py      (or __graft_entry__.build())
 
-Each source under csrc/ is compiled to an object in _build/ and the objects are
-linked into block_scaled_fp4_pre_amd/libmoe_w4a4.so next to the binding.
+Each source of the layer under csrc/ is compiled to an object in _build/ and the
+objects are linked into block_scaled_fp4_pre_amd/libmoe_w4a4.so next to the
+binding.  The measurement probes (csrc/ceiling.hip) become a library of their
+own, libmoe_ceiling.so, so that the layer's library holds the layer only.
 """
 from __future__ import annotations
 
@@ -18,6 +20,11 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe_w4a4.so")
+PROBE_LIB = os.path.join(HERE, "libmoe_ceiling.so")
+PROBE_SOURCES = ("ceiling.hip",)
+# The MFMA probe keeps its accumulators in VGPRs: in AGPRs the compiler
+# rotated them through copies on every loop iteration.
+SOURCE_FLAGS = {"ceiling.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 DEVICE_SOURCES = ("quant.hip", "route.hip", "predispatch.hip", "gemm1.hip", "gemm2.hip", "gemm_lds.hip",
@@ -50,23 +57,24 @@ def _compile(args):
 def build(verbose: bool = False) -> str:
     hipcc = _hipcc()
     os.makedirs(BUILD, exist_ok=True)
-    jobs, objs = [], []
-    for src in DEVICE_SOURCES + HOST_SOURCES:
+    jobs, objs, probe_objs = [], [], []
+    for src in DEVICE_SOURCES + HOST_SOURCES + PROBE_SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        flags = COMMON + (DEVICE_FLAGS if src.endswith(".hip") else HOST_FLAGS)
+        flags = COMMON + (DEVICE_FLAGS if src.endswith(".hip") else HOST_FLAGS) + SOURCE_FLAGS.get(src, [])
         jobs.append(([hipcc, *flags, "-c", os.path.join(CSRC, src), "-o", obj], src))
-        objs.append(obj)
+        (probe_objs if src in PROBE_SOURCES else objs).append(obj)
     workers = min(len(jobs), max(1, (os.cpu_count() or 4)))
     with concurrent.futures.ThreadPoolExecutor(workers) as ex:
         for out in ex.map(_compile, jobs):
             if verbose and out.strip():
                 print(out)
-    tmp = LIB + ".tmp"
-    link = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
-    r = subprocess.run(link, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"linking failed:\n{' '.join(link)}\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    for lib, lib_objs in ((LIB, objs), (PROBE_LIB, probe_objs)):
+        tmp = lib + ".tmp"
+        link = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *lib_objs]
+        r = subprocess.run(link, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"linking failed:\n{' '.join(link)}\n{r.stdout}{r.stderr}")
+        os.replace(tmp, lib)
     return LIB
 
 

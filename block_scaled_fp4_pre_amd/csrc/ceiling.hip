@@ -1,0 +1,99 @@
+// Measurement probes (libmoe_ceiling.so, include/moe_ceiling.h): the practical
+// HBM streaming-read rate and the practical FP4 block-scaled MFMA rate of the
+// GPU, the two ceilings the layer's kernels run against.  Not on the layer's
+// path; the layer's library does not contain them.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_ceiling.h"
+
+namespace {
+
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+constexpr int kThreads = 256;
+constexpr int kRing = 8;                       // 16-byte loads in flight per lane
+constexpr uint32_t kRound = kThreads * 16;     // bytes one workgroup reads per load round
+constexpr int kPolicyNT = 2;                   // non-temporal
+constexpr int kChains = 8;                     // independent MFMA accumulators per wave
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Workgroup g streams its chunk through a ring of kRing loads per lane: each
+// step folds the oldest load into the XOR and issues the load kRing rounds
+// ahead.  Loads past the chunk fall outside the buffer range and return zeros
+// (no memory access), which leave the XOR unchanged.
+template <int CP>
+__global__ void __launch_bounds__(kThreads) stream_read_kernel(const uint8_t* __restrict__ src, uint32_t chunk,
+                                                               uint32_t* __restrict__ digest) {
+  const __amdgpu_buffer_rsrc_t r = chunk_rsrc(src + (size_t)blockIdx.x * chunk, chunk);
+  const uint32_t lane_off = threadIdx.x * 16;
+  v4u v[kRing];
+#pragma unroll
+  for (int i = 0; i < kRing; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(lane_off + i * kRound), 0, CP);
+  uint32_t x = 0;
+  for (uint32_t base = 0; base < chunk; base += kRing * kRound) {
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) {
+      x ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+      const uint32_t next = base + (kRing + i) * kRound + lane_off;
+      v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)min(next, chunk), 0, CP);
+    }
+  }
+  for (int m = 32; m >= 1; m >>= 1) x ^= __shfl_xor(x, m, 64);
+  __shared__ uint32_t part[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) digest[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+}
+
+// code_word carries eight E2M1 codes (one per nibble) and scale the UE8M0
+// byte of both operands; both come from the host, so the compiler cannot fold
+// the products.
+__global__ void __launch_bounds__(kThreads) mfma_fp4_kernel(uint32_t code_word, int scale, int iterations,
+                                                            float* __restrict__ out) {
+  const int w = (int)code_word;
+  const v8i a = {w, w, w, w, 0, 0, 0, 0};
+  v4f acc[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) acc[c] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iterations; ++it) {
+#pragma unroll
+    for (int c = 0; c < kChains; ++c)
+      acc[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, a, acc[c], 4, 4, 0, scale, 0, scale);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) s += acc[c][0];
+  if ((threadIdx.x & 63) == 0) out[blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)] = s;
+}
+
+}  // namespace
+
+extern "C" int moe_ceiling_stream_read(const void* src, uint64_t bytes, uint32_t workgroups, int non_temporal,
+                                       uint32_t* digest, hipStream_t stream) {
+  if (src == nullptr || digest == nullptr || workgroups == 0 || bytes == 0) return MOE_CEILING_EINVAL;
+  if (reinterpret_cast<uintptr_t>(src) % 16 != 0 || bytes % (16ull * workgroups) != 0) return MOE_CEILING_EINVAL;
+  const uint64_t chunk = bytes / workgroups;
+  if (chunk >= (1ull << 31)) return MOE_CEILING_EINVAL;
+  const uint8_t* s = static_cast<const uint8_t*>(src);
+  if (non_temporal)
+    hipLaunchKernelGGL(stream_read_kernel<kPolicyNT>, dim3(workgroups), dim3(kThreads), 0, stream, s,
+                       (uint32_t)chunk, digest);
+  else
+    hipLaunchKernelGGL(stream_read_kernel<0>, dim3(workgroups), dim3(kThreads), 0, stream, s, (uint32_t)chunk,
+                       digest);
+  return hipGetLastError() == hipSuccess ? MOE_CEILING_OK : MOE_CEILING_EHIP;
+}
+
+extern "C" int moe_ceiling_mfma_fp4(uint32_t workgroups, int32_t iterations, float* out, hipStream_t stream) {
+  if (out == nullptr || workgroups == 0 || iterations < 1 || iterations > 16384) return MOE_CEILING_EINVAL;
+  // 0x2 is the E2M1 code of 1.0; 127 the UE8M0 byte of 2^0.
+  hipLaunchKernelGGL(mfma_fp4_kernel, dim3(workgroups), dim3(kThreads), 0, stream, 0x22222222u, 127, (int)iterations,
+                     out);
+  return hipGetLastError() == hipSuccess ? MOE_CEILING_OK : MOE_CEILING_EHIP;
+}
