@@ -24,7 +24,7 @@ median, minimum and maximum of K more forwards, each bracketed by its own
 events.  "ceiling" holds this GPU's measured ceilings (libmoe_ceiling.so): the
 streaming-read rate of a 2 GiB buffer with non-temporal and with default loads
 (best over 2 to 16 workgroups per CU),
-the rate of back-to-back FP4 MFMAs, and GEMM1's achieved rate as a fraction of
+the rate of back-to-back MFMAs of each MMA type, and GEMM1's achieved rate as a fraction of
 the ceiling that bounds it.  "cpu_baseline" times the fp64 CPU oracle on a
 bounded slice of the same workload (a few experts with all their routed rows)
 and scales it to one layer.
@@ -311,7 +311,7 @@ def main():
         # roofline fraction uses.
         from block_scaled_fp4_pre_amd import ceiling
         ceil = ceiling.measure()
-        ref = ceil["mfma_fp4_TFLOPs"] if mfma_bound else ceil["read_nt_GBps"]
+        ref = ceil["mfma_fp8xfp4_TFLOPs" if fp8 else "mfma_fp4_TFLOPs"] if mfma_bound else ceil["read_nt_GBps"]
         ceil["gemm1_frac"] = round(g1_ach / ref, 4)
         res["ceiling"] = ceil
     if not args.no_cpu_baseline:

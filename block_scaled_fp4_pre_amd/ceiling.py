@@ -20,6 +20,8 @@ _lib.moe_ceiling_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctype
 _lib.moe_ceiling_stream_read.restype = ctypes.c_int
 _lib.moe_ceiling_mfma_fp4.argtypes = [ctypes.c_uint32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
 _lib.moe_ceiling_mfma_fp4.restype = ctypes.c_int
+_lib.moe_ceiling_mfma_fp8xfp4.argtypes = _lib.moe_ceiling_mfma_fp4.argtypes
+_lib.moe_ceiling_mfma_fp8xfp4.restype = ctypes.c_int
 
 MOE_CEILING_OK, MOE_CEILING_EINVAL, MOE_CEILING_EHIP = 0, 1, 2
 FLOPS_PER_MFMA = 2 * 16 * 16 * 128
@@ -46,6 +48,12 @@ def moe_ceiling_mfma_fp4(workgroups: int, iterations: int, out: torch.Tensor) ->
     _check(_lib.moe_ceiling_mfma_fp4(workgroups, iterations, out.data_ptr(), _stream()), "moe_ceiling_mfma_fp4")
 
 
+def moe_ceiling_mfma_fp8xfp4(workgroups: int, iterations: int, out: torch.Tensor) -> None:
+    assert out.is_cuda and out.dtype == torch.float32 and out.numel() >= 4 * workgroups
+    _check(_lib.moe_ceiling_mfma_fp8xfp4(workgroups, iterations, out.data_ptr(), _stream()),
+           "moe_ceiling_mfma_fp8xfp4")
+
+
 def _timed_ms(fn, reps: int) -> list[float]:
     times = []
     for _ in range(reps):
@@ -63,8 +71,8 @@ def measure(read_bytes: int = 2 << 30, workgroups=(512, 1024, 2048, 4096), reps:
     """Best-of-`reps` rates of the two probes on cuda:0: a streaming read of a
     `read_bytes` random buffer, each workgroup reading one contiguous chunk,
     with non-temporal and with default loads, best over the `workgroups`
-    counts (2 to 16 per CU); and `mfma_workgroups` x 4 waves of back-to-back FP4
-    MFMAs.  Each result is checked: the read's per-workgroup XOR against the
+    counts (2 to 16 per CU); and `mfma_workgroups` x 4 waves of back-to-back
+    MFMAs of each MMA type (E2M1 x E2M1, E2M1 x E4M3).  Each result is checked: the read's per-workgroup XOR against the
     same XOR taken by torch, the MFMA sums against their exact value."""
     src = torch.randint(-2**31, 2**31 - 1, (read_bytes // 4,), dtype=torch.int32, device="cuda")
     res = {"read_bytes": read_bytes}
@@ -84,13 +92,15 @@ def measure(read_bytes: int = 2 << 30, workgroups=(512, 1024, 2048, 4096), reps:
         del digest, expect
     del src
     out = torch.zeros(4 * mfma_workgroups, dtype=torch.float32, device="cuda")
-    moe_ceiling_mfma_fp4(mfma_workgroups, mfma_iterations, out)
-    torch.cuda.synchronize()
-    if not bool((out == float(CHAINS * 128 * mfma_iterations)).all()):
-        raise RuntimeError("MFMA probe: sums differ from 8*128*iterations")
-    ms = min(_timed_ms(lambda: moe_ceiling_mfma_fp4(mfma_workgroups, mfma_iterations, out), reps))
     flops = 4 * mfma_workgroups * mfma_iterations * CHAINS * FLOPS_PER_MFMA
-    res["mfma_fp4_TFLOPs"] = round(flops / (ms * 1e-3) / 1e12, 1)
+    for name, fn in (("mfma_fp4_TFLOPs", moe_ceiling_mfma_fp4), ("mfma_fp8xfp4_TFLOPs", moe_ceiling_mfma_fp8xfp4)):
+        out.fill_(-1.0)
+        fn(mfma_workgroups, mfma_iterations, out)
+        torch.cuda.synchronize()
+        if not bool((out == float(CHAINS * 128 * mfma_iterations)).all()):
+            raise RuntimeError(f"MFMA probe ({name}): sums differ from 8*128*iterations")
+        ms = min(_timed_ms(lambda: fn(mfma_workgroups, mfma_iterations, out), reps))
+        res[name] = round(flops / (ms * 1e-3) / 1e12, 1)
     return res
 
 

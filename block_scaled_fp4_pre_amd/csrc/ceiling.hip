@@ -1,7 +1,7 @@
 // Measurement probes (libmoe_ceiling.so, include/moe_ceiling.h): the practical
-// HBM streaming-read rate and the practical FP4 block-scaled MFMA rate of the
-// GPU, the two ceilings the layer's kernels run against.  Not on the layer's
-// path; the layer's library does not contain them.
+// HBM streaming-read rate and the practical block-scaled MFMA rate of the GPU
+// for both MMA types, the ceilings the layer's kernels run against.  Not on the
+// layer's path; the layer's library does not contain them.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -51,20 +51,24 @@ __global__ void __launch_bounds__(kThreads) stream_read_kernel(const uint8_t* __
   if (threadIdx.x == 0) digest[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
 }
 
-// code_word carries eight E2M1 codes (one per nibble) and scale the UE8M0
-// byte of both operands; both come from the host, so the compiler cannot fold
-// the products.
-__global__ void __launch_bounds__(kThreads) mfma_fp4_kernel(uint32_t code_word, int scale, int iterations,
-                                                            float* __restrict__ out) {
-  const int w = (int)code_word;
+// a_word carries eight E2M1 codes (one per nibble) of the A operand, b_word
+// four E4M3 codes (F8) or eight E2M1 codes of the B operand, and scale the
+// UE8M0 byte of both; all come from the host, so the compiler cannot fold the
+// products.  F8 is the fp8xfp4 form: E2M1 A (format 4), E4M3 B (format 0, 32
+// bytes per lane).
+template <bool F8>
+__global__ void __launch_bounds__(kThreads) mfma_kernel(uint32_t a_word, uint32_t b_word, int scale, int iterations,
+                                                        float* __restrict__ out) {
+  const int w = (int)a_word, x = (int)b_word;
   const v8i a = {w, w, w, w, 0, 0, 0, 0};
+  const v8i b = F8 ? v8i{x, x, x, x, x, x, x, x} : v8i{x, x, x, x, 0, 0, 0, 0};
   v4f acc[kChains];
 #pragma unroll
   for (int c = 0; c < kChains; ++c) acc[c] = v4f{0.f, 0.f, 0.f, 0.f};
   for (int it = 0; it < iterations; ++it) {
 #pragma unroll
     for (int c = 0; c < kChains; ++c)
-      acc[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, a, acc[c], 4, 4, 0, scale, 0, scale);
+      acc[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[c], 4, F8 ? 0 : 4, 0, scale, 0, scale);
   }
   float s = 0.f;
 #pragma unroll
@@ -90,10 +94,17 @@ extern "C" int moe_ceiling_stream_read(const void* src, uint64_t bytes, uint32_t
   return hipGetLastError() == hipSuccess ? MOE_CEILING_OK : MOE_CEILING_EHIP;
 }
 
+// 0x2 is the E2M1 code of 1.0, 0x38 the E4M3 code of 1.0, 127 the UE8M0 byte of 2^0.
 extern "C" int moe_ceiling_mfma_fp4(uint32_t workgroups, int32_t iterations, float* out, hipStream_t stream) {
   if (out == nullptr || workgroups == 0 || iterations < 1 || iterations > 16384) return MOE_CEILING_EINVAL;
-  // 0x2 is the E2M1 code of 1.0; 127 the UE8M0 byte of 2^0.
-  hipLaunchKernelGGL(mfma_fp4_kernel, dim3(workgroups), dim3(kThreads), 0, stream, 0x22222222u, 127, (int)iterations,
-                     out);
+  hipLaunchKernelGGL(mfma_kernel<false>, dim3(workgroups), dim3(kThreads), 0, stream, 0x22222222u, 0x22222222u, 127,
+                     (int)iterations, out);
+  return hipGetLastError() == hipSuccess ? MOE_CEILING_OK : MOE_CEILING_EHIP;
+}
+
+extern "C" int moe_ceiling_mfma_fp8xfp4(uint32_t workgroups, int32_t iterations, float* out, hipStream_t stream) {
+  if (out == nullptr || workgroups == 0 || iterations < 1 || iterations > 16384) return MOE_CEILING_EINVAL;
+  hipLaunchKernelGGL(mfma_kernel<true>, dim3(workgroups), dim3(kThreads), 0, stream, 0x22222222u, 0x38383838u, 127,
+                     (int)iterations, out);
   return hipGetLastError() == hipSuccess ? MOE_CEILING_OK : MOE_CEILING_EHIP;
 }

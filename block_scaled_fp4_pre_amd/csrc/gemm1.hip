@@ -16,9 +16,10 @@
 // each group.  In the tile order of tiles.h those units' chunks follow each
 // other at one fixed stride, so the wave streams them as one sequence of K
 // steps, and the 4 waves read one contiguous 16 KiB per step.  A workgroup whose
-// expert has no rows exits at once.  Per pass it takes up to NT*16 of the
-// expert's rows: their quantized tokens are gathered into LDS (B operand) by
-// direct-to-LDS loads while the wave's weight ring (gemm_common.h) fills;
+// expert has no rows exits (with two token tiles, once the first ring loads it
+// issued ahead of the row count have landed).  Per pass it takes up to NT*16 of
+// the expert's rows: their quantized tokens are gathered into LDS (B operand)
+// by direct-to-LDS loads while the wave's weight ring (stream_ring.h) fills;
 // then 4 MFMAs (one per 16-row block) per token tile per K step of 128.
 // Epilogue per lane: gate/up of 8 columns for one token; the 32-column absmax
 // is reduced over the 4 lanes holding that token (xor 16, xor 32).

@@ -12,7 +12,8 @@
 // of tiles.h), writing y at each unit's end.  The expert's requantized rows are
 // consecutive in every K-step plane of hq/hsf (epilogue.h), so the B tile is
 // one contiguous run per plane, copied into LDS by direct-to-LDS loads;
-// weights stream through the register ring of gemm_common.h.  F8 (the
+// weights stream through the register ring of stream_ring.h; a workgroup
+// whose expert has no rows exits as in gemm1.hip.  F8 (the
 // fp8xfp4 MMA type): h arrives as E4M3 bytes and the MFMA's B operand takes 32
 // bytes (format code 0).
 #include "epilogue.h"

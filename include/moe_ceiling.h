@@ -7,9 +7,10 @@
  *     read, with the access pattern of the layer's weight streams (each
  *     workgroup reads one contiguous chunk with 16-byte buffer loads, several
  *     in flight per lane);
- *   - moe_ceiling_mfma_fp4: the practical rate of the block-scaled FP4 MFMA
- *     (V_MFMA_SCALE_F32_16X16X128_F8F6F4 with both operands E2M1), issued back
- *     to back from register operands.
+ *   - moe_ceiling_mfma_fp4 / moe_ceiling_mfma_fp8xfp4: the practical rate of
+ *     the block-scaled MFMA (V_MFMA_SCALE_F32_16X16X128_F8F6F4) with both
+ *     operands E2M1, or with E2M1 weights and E4M3 tokens (the layer's two MMA
+ *     types), issued back to back from register operands.
  * Each probe writes a result the caller can check exactly, so that a probe
  * that skipped work would be caught.
  *
@@ -52,6 +53,10 @@ int moe_ceiling_stream_read(const void* src, uint64_t bytes, uint32_t workgroups
  * 1 <= iterations <= 16384 (the sums stay exact in fp32); out holds
  * 4 * workgroups floats. */
 int moe_ceiling_mfma_fp4(uint32_t workgroups, int32_t iterations, float* out, hipStream_t stream);
+
+/* The same with E4M3 B operands (every element 1.0): the fp8xfp4 MMA type's
+ * instruction form.  Same result, requirements and flops per MFMA. */
+int moe_ceiling_mfma_fp8xfp4(uint32_t workgroups, int32_t iterations, float* out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

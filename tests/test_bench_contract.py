@@ -1,6 +1,7 @@
 """bench.py's command-line contract: more than one GPU is refused with a
 message (CPU tier), and one short run prints exactly one JSON line with the
-fields and types the benchmark record needs (GPU tier)."""
+fields and types the benchmark record needs, plus the per-forward spread and
+the measured ceilings (GPU tier)."""
 import json
 import os
 import subprocess
@@ -41,3 +42,10 @@ def test_one_json_line_with_the_record_fields(mma):
     assert 0 < roof["achieved"] and roof["peak"] > 0 and abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
     assert roof["traffic"] is None or roof["traffic"] > 0
     assert "cpu_baseline" not in d
+    fw = d["forward_us"]
+    assert 0 < fw["min"] <= fw["median"] <= fw["max"]
+    ceil = d["ceiling"]                                         # measured ceilings beside the published peaks
+    assert 0 < ceil["read_GBps"] and 0 < ceil["read_nt_GBps"] and 0 < ceil["mfma_fp4_TFLOPs"]
+    ref = (ceil["read_nt_GBps"] if roof["bound"] == "hbm"
+           else ceil["mfma_fp8xfp4_TFLOPs" if mma == "fp8xfp4" else "mfma_fp4_TFLOPs"])
+    assert abs(ceil["gemm1_frac"] - roof["achieved"] / ref) < 1e-3
