@@ -5,7 +5,8 @@ with mma_type="fp8xfp4".
   quantize        every bfloat16 pattern as a lone value in a group, through
                   the pre-dispatch quantization stage: codes and scales exact
   tiny / stream   the streaming path on every token (16- and 32-row passes,
-                  2 units per wave in GEMM1)
+                  2 units per wave in GEMM1; a two-tile launch in which 5 of
+                  16 experts get no rows and the hot expert takes 5 passes)
   prefill         the LDS-staged path on every token: the per-XCD work order
                   with several tiles per expert, and the single-tile form
                   (non-temporal weights, two weight blocks per GEMM1 workgroup)
@@ -55,6 +56,7 @@ def test_fp8_quantize_every_bf16_pattern():
 SHAPES = [
     synth.CONFIGS[0],
     synth.LayerConfig(120, "fp8_stream_h1024_i512_e16_k2_t100", 100, 1024, 512, 16, 2, "uniform", 120),
+    synth.LayerConfig(114, "fp8_stream_h1024_i512_e16_k1_t160_empty_zipf", 160, 1024, 512, 16, 1, "zipf", 114, 2.0),
     synth.LayerConfig(121, "fp8_prefill_h2048_i1024_e8_k2_t1500_zipf", 1500, 2048, 1024, 8, 2, "zipf", 121, 1.1),
     synth.LayerConfig(122, "fp8_prefill_h512_i512_e16_k2_t1000", 1000, 512, 512, 16, 2, "uniform", 122),
 ]
