@@ -101,6 +101,45 @@ def _ptr(t) -> int | None:
     return t.data_ptr()
 
 
+_BF16_LIKE = ("bfloat16", "int16", "uint16")   # bf16 values or their bit patterns
+
+
+def _expect(t, name: str, dtypes, shape=None, min_rows=None) -> None:
+    """Raise ValueError unless tensor t (if given) has one of the dtypes (by
+    name), the exact shape (None entries match any size) or at least min_rows
+    rows, and lives on the current device.  The library sees only pointers:
+    a wrong dtype or a short buffer would be read or written out of bounds
+    by the kernels, so it is refused here."""
+    if t is None or isinstance(t, int):
+        return
+    dt = str(t.dtype).replace("torch.", "")
+    if dt not in dtypes:
+        raise ValueError(f"{name}: dtype {dt}, expected {' or '.join(dtypes)}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(w is not None and w != g for g, w in zip(t.shape, shape)):
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected "
+                             f"({', '.join('*' if w is None else str(w) for w in shape)})")
+        if min_rows is not None and t.shape[0] < min_rows:
+            raise ValueError(f"{name}: {t.shape[0]} rows, at least {min_rows} needed")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: expected a device tensor, got one on {t.device}")
+    import torch
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name}: on {t.device}, but the current device is cuda:{torch.cuda.current_device()}")
+
+
+def _check_forward_tensors(cfg, num_tokens, x, topk_ids, topk_weights, out, workspace, prepared,
+                           gemm1_acc=None) -> None:
+    T, H, k, I = int(num_tokens), cfg.hidden, cfg.topk, cfg.inter
+    _expect(x, "x", _BF16_LIKE, (None, H), T)
+    _expect(topk_ids, "topk_ids", ("int32",), (None, k), T)
+    _expect(topk_weights, "topk_weights", ("float32",), (None, k), T)
+    _expect(out, "out", _BF16_LIKE, (None, H), T)
+    _expect(workspace, "workspace", ("uint8",))
+    _expect(prepared, "prepared", ("uint8",))
+    _expect(gemm1_acc, "gemm1_acc", ("float32",), (None, 2 * I), T * k)
+
+
 def _stream(stream) -> int | None:
     if stream is not None:
         return int(stream)
@@ -128,7 +167,8 @@ def moe_w4a4_workspace_layout(cfg: moe_w4a4_cfg) -> dict:
 
 
 def moe_w4a4_quantize(src, codes, scales, stream=None) -> None:
-    """src: device bf16 (or uint16 bit patterns) / float32 [rows, cols]."""
+    """src: device bf16 (or uint16 bit patterns) / float32 [rows, cols];
+    codes uint8 [rows, cols/2]; scales uint8 [rows, cols/32]."""
     import torch
     if src.dtype in (torch.bfloat16, torch.uint16, torch.int16):
         dt = 0
@@ -136,12 +176,23 @@ def moe_w4a4_quantize(src, codes, scales, stream=None) -> None:
         dt = 1
     else:
         raise ValueError(f"unsupported dtype {src.dtype}")
+    if src.dim() != 2:
+        raise ValueError(f"src: expected [rows, cols], got shape {tuple(src.shape)}")
     rows, cols = src.shape
+    _expect(src, "src", ("bfloat16", "int16", "uint16", "float32"))
+    _expect(codes, "codes", ("uint8",), (rows, cols // 2))
+    _expect(scales, "scales", ("uint8",), (rows, cols // 32))
     _check(_lib.moe_w4a4_quantize(dt, _ptr(src), rows, cols, _ptr(codes), _ptr(scales), _stream(stream)),
            "moe_w4a4_quantize")
 
 
 def moe_w4a4_prepare_weights(cfg, w1_codes, w1_scales, w2_codes, w2_scales, prepared, stream=None) -> None:
+    E, H, I = cfg.num_experts, cfg.hidden, cfg.inter
+    _expect(w1_codes, "w1_codes", ("uint8",), (E, 2 * I, H // 2))
+    _expect(w1_scales, "w1_scales", ("uint8",), (E, 2 * I, H // 32))
+    _expect(w2_codes, "w2_codes", ("uint8",), (E, H, I // 2))
+    _expect(w2_scales, "w2_scales", ("uint8",), (E, H, I // 32))
+    _expect(prepared, "prepared", ("uint8",))
     _check(_lib.moe_w4a4_prepare_weights(ctypes.byref(cfg), _ptr(w1_codes), _ptr(w1_scales), _ptr(w2_codes),
                                          _ptr(w2_scales), _ptr(prepared), prepared.numel() * prepared.element_size(),
                                          _stream(stream)), "moe_w4a4_prepare_weights")
@@ -149,6 +200,9 @@ def moe_w4a4_prepare_weights(cfg, w1_codes, w1_scales, w2_codes, w2_scales, prep
 
 def moe_w4a4_forward(cfg, prepared, num_tokens: int, x, topk_ids, topk_weights, out, workspace,
                      stream=None) -> None:
+    """x bf16 [>= T, H], topk_ids int32 [>= T, k], topk_weights float32
+    [>= T, k], out bf16 [>= T, H], all on the current device; T = num_tokens."""
+    _check_forward_tensors(cfg, num_tokens, x, topk_ids, topk_weights, out, workspace, prepared)
     _check(_lib.moe_w4a4_forward(ctypes.byref(cfg), _ptr(prepared), int(num_tokens), _ptr(x), _ptr(topk_ids),
                                  _ptr(topk_weights), _ptr(out), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream)),
@@ -157,6 +211,7 @@ def moe_w4a4_forward(cfg, prepared, num_tokens: int, x, topk_ids, topk_weights, 
 
 def moe_w4a4_run_stages(cfg, prepared, num_tokens: int, x, topk_ids, topk_weights, out, workspace,
                         stages: int, gemm1_acc=None, stream=None) -> None:
+    _check_forward_tensors(cfg, num_tokens, x, topk_ids, topk_weights, out, workspace, prepared, gemm1_acc)
     _check(_lib.moe_w4a4_run_stages(ctypes.byref(cfg), _ptr(prepared), int(num_tokens), _ptr(x), _ptr(topk_ids),
                                     _ptr(topk_weights), _ptr(out), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), int(stages), _ptr(gemm1_acc),

@@ -30,11 +30,11 @@ ARCH = "gfx950"
 DEVICE_SOURCES = ("quant.hip", "route.hip", "predispatch.hip", "gemm1.hip", "gemm2.hip", "gemm_lds.hip",
                   "combine.hip",
                   "prepare.hip")
-HOST_SOURCES = ("abi.cpp",)
+HOST_SOURCES = ("abi.cpp", "validate.cpp")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include")]
 # Packed fp32 VALU ops are kept out of the device code.
 DEVICE_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-# abi.cpp holds host code only: plain C++ against the HIP runtime headers.
+# abi.cpp and validate.cpp hold host code only: plain C++ (abi.cpp against the HIP runtime headers).
 HOST_FLAGS = ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "include")]
 
 

@@ -16,76 +16,17 @@
 
 #include "moe_w4a4.h"
 #include "launch.h"
+#include "validate.h"
 
 namespace {
 
 constexpr int kMaxDevices = 64;
-constexpr int kMaxExperts = 512;
-constexpr int kMaxTopk = 16;
-constexpr int kRouteRows = 1024;
 #ifndef MOE_STREAM_MAX_ROWS
 #define MOE_STREAM_MAX_ROWS 16   // mean routed rows per expert up to which the VGPR-streaming GEMMs run
 #endif
 constexpr int kStreamMaxRows = MOE_STREAM_MAX_ROWS;
 
 std::atomic<int> g_is_gfx950[kMaxDevices];  // 0 unknown, 1 yes, 2 no
-
-inline uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
-inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
-
-int check_cfg(const moe_w4a4_cfg* c) {
-  if (c == nullptr) return MOE_EINVAL;
-  if (c->hidden <= 0 || c->inter <= 0 || c->num_experts <= 0 || c->topk <= 0 || c->max_tokens < 0)
-    return MOE_EINVAL;
-  if (c->hidden % 256 != 0 || c->inter % 128 != 0) return MOE_EUNSUPPORTED;
-  if (c->hidden > (1 << 16) || c->inter > (1 << 16)) return MOE_EUNSUPPORTED;
-  if (c->num_experts > kMaxExperts || c->topk > kMaxTopk) return MOE_EUNSUPPORTED;
-  if (c->group_size != 32 || (c->mma_type != MOE_MMA_MXF4_X_MXF4 && c->mma_type != MOE_MMA_FP8_X_MXF4) ||
-      c->activation != MOE_ACT_SWIGLU)
-    return MOE_EUNSUPPORTED;
-  if ((int64_t)c->max_tokens * c->topk >= (int64_t)1 << 31) return MOE_EUNSUPPORTED;
-  return MOE_OK;
-}
-
-struct Prepared {
-  uint64_t w1c, w1s, w2c, w2s, total;
-};
-
-Prepared prepared_layout(const moe_w4a4_cfg* c) {
-  const uint64_t H = c->hidden, I = c->inter, E = c->num_experts;
-  Prepared p{};
-  uint64_t off = 0;
-  p.w1c = off; off = align256(off + E * 2 * I * H / 2);
-  p.w1s = off; off = align256(off + E * 2 * I * H / 32);
-  p.w2c = off; off = align256(off + E * H * I / 2);
-  p.w2s = off; off = align256(off + E * H * I / 32);
-  p.total = off;
-  return p;
-}
-
-moe_w4a4_ws_layout ws_layout(const moe_w4a4_cfg* c) {
-  const uint64_t H = c->hidden, I = c->inter, E = c->num_experts, M = c->max_tokens;
-  const uint64_t R = M * c->topk;
-  const uint64_t nb = (R + kRouteRows - 1) / kRouteRows;
-  moe_w4a4_ws_layout L{};
-  uint64_t off = 0;
-  const uint64_t ab = c->mma_type == MOE_MMA_FP8_X_MXF4 ? 2 : 1;   // activation bytes per 2 elements
-  L.xq = off; off = align256(off + M * H / 2 * ab);
-  L.xsf = off; off = align256(off + M * H / 32);
-  L.counts = off; off = align256(off + E * 4);
-  L.offsets = off; off = align256(off + (E + 1) * 4);
-  L.sorted_rows = off; off = align256(off + R * 4);
-  L.pos = off; off = align256(off + R * 4);
-  L.hist = off; off = align256(off + nb * E * 4);
-  L.hq = off; off = align256(off + R * I / 2 * ab);
-  L.hsf = off; off = align256(off + R * I / 32);
-  L.y = off; off = align256(off + R * H * 2);
-  L.tiles = off; off = align256(off + (R / 16 + E + 1) * 8);
-  L.num_tiles = off; off = align256(off + 4);
-  L.xsf_planes = off; off = align256(off + R * H / 32);
-  L.total = off;
-  return L;
-}
 
 int check_device() {
   int dev = -1;
@@ -141,29 +82,26 @@ const char* moe_w4a4_status_string(int status) {
 }
 
 int moe_w4a4_query(const moe_w4a4_cfg* cfg, size_t* prepared_bytes, size_t* workspace_bytes) {
-  const int st = check_cfg(cfg);
+  const int st = moe::check_cfg(cfg);
   if (st != MOE_OK) return st;
-  if (prepared_bytes) *prepared_bytes = (size_t)prepared_layout(cfg).total;
-  if (workspace_bytes) *workspace_bytes = (size_t)ws_layout(cfg).total;
+  if (prepared_bytes) *prepared_bytes = (size_t)moe::prepared_layout(cfg).total;
+  if (workspace_bytes) *workspace_bytes = (size_t)moe::ws_layout(cfg).total;
   return MOE_OK;
 }
 
 int moe_w4a4_workspace_layout(const moe_w4a4_cfg* cfg, moe_w4a4_ws_layout* out) {
-  const int st = check_cfg(cfg);
+  const int st = moe::check_cfg(cfg);
   if (st != MOE_OK) return st;
   if (out == nullptr) return MOE_EINVAL;
-  *out = ws_layout(cfg);
+  *out = moe::ws_layout(cfg);
   return MOE_OK;
 }
 
 int moe_w4a4_quantize(int32_t src_dtype, const void* src, int64_t rows, int32_t cols, uint8_t* codes,
                       uint8_t* scales, void* stream) {
-  if (src_dtype != 0 && src_dtype != 1) return MOE_EUNSUPPORTED;
-  if (rows < 0 || cols <= 0) return MOE_EINVAL;
-  if (cols % 32 != 0) return MOE_EUNSUPPORTED;
-  if (rows == 0) return MOE_OK;
-  if (src == nullptr || codes == nullptr || scales == nullptr) return MOE_EINVAL;
-  if (!aligned(src, 16) || !aligned(codes, 16)) return MOE_EINVAL;
+  bool noop = false;
+  const int st = moe::check_quantize_args(src_dtype, src, rows, cols, codes, scales, &noop);
+  if (st != MOE_OK || noop) return st;
   const int dv = check_device();
   if (dv != MOE_OK) return dv;
   return hip_status(moe::launch_quantize(src_dtype == 0, false, src, rows * (int64_t)(cols / 32), codes, scales,
@@ -173,14 +111,11 @@ int moe_w4a4_quantize(int32_t src_dtype, const void* src, int64_t rows, int32_t 
 int moe_w4a4_prepare_weights(const moe_w4a4_cfg* cfg, const uint8_t* w1_codes, const uint8_t* w1_scales,
                              const uint8_t* w2_codes, const uint8_t* w2_scales, void* prepared,
                              size_t prepared_bytes, void* stream) {
-  int st = check_cfg(cfg);
+  int st = moe::check_prepare_args(cfg, w1_codes, w1_scales, w2_codes, w2_scales, prepared, prepared_bytes);
   if (st != MOE_OK) return st;
-  if (!w1_codes || !w1_scales || !w2_codes || !w2_scales || !prepared) return MOE_EINVAL;
-  if (!aligned(w1_codes, 16) || !aligned(w2_codes, 16) || !aligned(prepared, 256)) return MOE_EINVAL;
-  const Prepared P = prepared_layout(cfg);
-  if (prepared_bytes < P.total) return MOE_EWORKSPACE;
   st = check_device();
   if (st != MOE_OK) return st;
+  const moe::PreparedLayout P = moe::prepared_layout(cfg);
   uint8_t* base = static_cast<uint8_t*>(prepared);
   return hip_status(moe::launch_prepare(w1_codes, w1_scales, w2_codes, w2_scales, cfg->hidden, cfg->inter,
                                         cfg->num_experts, base + P.w1c, base + P.w1s, base + P.w2c,
@@ -190,25 +125,13 @@ int moe_w4a4_prepare_weights(const moe_w4a4_cfg* cfg, const uint8_t* w1_codes, c
 int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t num_tokens, const uint16_t* x,
                         const int32_t* topk_ids, const float* topk_weights, uint16_t* out, void* workspace,
                         size_t workspace_bytes, uint32_t stages, float* gemm1_acc, void* stream) {
-  int st = check_cfg(cfg);
-  if (st != MOE_OK) return st;
-  if (num_tokens < 0) return MOE_EINVAL;
-  if (num_tokens > cfg->max_tokens) return MOE_ECAPACITY;
-  if ((stages & ~uint32_t(MOE_STAGE_ALL)) != 0) return MOE_EINVAL;
-  if (num_tokens == 0 || stages == 0) return MOE_OK;   // nothing to do; empty tensors may be NULL
-  if (workspace == nullptr || !aligned(workspace, 256)) return MOE_EINVAL;
-  const moe_w4a4_ws_layout L = ws_layout(cfg);
-  if (workspace_bytes < L.total) return MOE_EWORKSPACE;
-  if ((stages & MOE_STAGE_QUANT) && (x == nullptr || !aligned(x, 16))) return MOE_EINVAL;
-  if ((stages & MOE_STAGE_ROUTE) && (topk_ids == nullptr || !aligned(topk_ids, 4))) return MOE_EINVAL;
-  if ((stages & (MOE_STAGE_GEMM1 | MOE_STAGE_GEMM2)) && (prepared == nullptr || !aligned(prepared, 256)))
-    return MOE_EINVAL;
-  if ((stages & MOE_STAGE_COMBINE) &&
-      (topk_weights == nullptr || out == nullptr || !aligned(topk_weights, 4) || !aligned(out, 16)))
-    return MOE_EINVAL;
-  if (gemm1_acc != nullptr && !aligned(gemm1_acc, 16)) return MOE_EINVAL;
+  bool noop = false;
+  int st = moe::check_stage_args(cfg, prepared, num_tokens, x, topk_ids, topk_weights, out, workspace,
+                                 workspace_bytes, stages, gemm1_acc, &noop);
+  if (st != MOE_OK || noop) return st;
   st = check_device();
   if (st != MOE_OK) return st;
+  const moe_w4a4_ws_layout L = moe::ws_layout(cfg);
 
   const int H = cfg->hidden, I = cfg->inter, E = cfg->num_experts, k = cfg->topk;
   const bool fp8 = cfg->mma_type == MOE_MMA_FP8_X_MXF4;   // E4M3 activations
@@ -236,7 +159,7 @@ int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t n
   uint8_t* hq = ws + L.hq;
   uint8_t* hsf = ws + L.hsf;
   uint16_t* y = reinterpret_cast<uint16_t*>(ws + L.y);
-  const Prepared P = prepared_layout(cfg);
+  const moe::PreparedLayout P = moe::prepared_layout(cfg);
   const uint8_t* pw = static_cast<const uint8_t*>(prepared);
 
   if ((stages & MOE_STAGE_QUANT) && (stages & MOE_STAGE_ROUTE) && R <= moe::kPredispatchMaxRows) {
@@ -255,11 +178,12 @@ int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t n
       if (st != MOE_OK) return st;
     }
   }
+  if ((stages & MOE_STAGE_ROUTE) && tiled) {
+    // the tiled GEMM1's token scales, in the sorted order the route just fixed
+    st = hip_status(moe::launch_sorted_scales(xsf, sorted_rows, offsets, E, R, H, k, hrows, xsf_planes, s));
+    if (st != MOE_OK) return st;
+  }
   if (stages & MOE_STAGE_GEMM1) {
-    if (tiled) {
-      st = hip_status(moe::launch_sorted_scales(xsf, sorted_rows, offsets, E, R, H, k, hrows, xsf_planes, s));
-      if (st != MOE_OK) return st;
-    }
     st = hip_status(tiled ? moe::launch_gemm1_lds(fp8, pw + P.w1c, pw + P.w1s, xq, xsf_planes, counts, offsets,
                                                   sorted_rows, tiles, num_tiles, max_tiles, rows_hint, H, I, k,
                                                   hrows, hq, hsf, gemm1_acc, s)

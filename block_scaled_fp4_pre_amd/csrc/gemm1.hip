@@ -118,8 +118,10 @@ __global__ void __launch_bounds__(256, 2) gemm1_swiglu_kernel(
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) acc[nt][rb] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // Steady state without branches: D divides S, and the loads issued past
-    // the wave's last step fall outside the buffer range and return zeros.
+    // Steady state without branches: D divides S.  The D steps of loads
+    // issued past the wave's last step are never consumed; they read the
+    // bytes after its stream (the next unit's, or the prepared buffer's tail,
+    // kPreparedTailBytes), or zeros where the buffer range check drops them.
     for (int j0 = 0; j0 < total_steps; j0 += D) {
       const int s0 = j0 % S;
 #pragma unroll

@@ -3,14 +3,19 @@
 // (16 bytes per lane each) and one scale dword per lane.
 #pragma once
 #include "gemm_common.h"
+#include "tiles.h"
+#include "validate.h"
 
 namespace moe {
 
 // Fill the ring with the wave's first D K steps.
+// The ring's refills run up to D steps past a wave's last one (gemm1.hip,
+// gemm2.hip); the prepared buffer's tail covers them after its last region.
 template <int D>
 __device__ __forceinline__ void fill_weight_ring(uint4 (&a)[D][4], uint32_t (&sa)[D], __amdgpu_buffer_rsrc_t wr,
                                                  __amdgpu_buffer_rsrc_t sr, int voff, int svoff, int step_stride,
                                                  int scale_stride) {
+  static_assert(D * kUnitStepStride <= kPreparedTailBytes, "weight read-ahead past the prepared tail");
 #pragma unroll
   for (int d = 0; d < D; ++d) {
 #pragma unroll

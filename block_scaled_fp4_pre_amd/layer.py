@@ -16,17 +16,33 @@ from . import _lib
 
 class MoeW4A4Layer:
     def __init__(self, hidden: int, inter: int, num_experts: int, topk: int, max_tokens: int,
-                 device: str | torch.device = "cuda", mma_type: int = _lib.MOE_MMA_MXF4_X_MXF4):
+                 device: str | torch.device = "cuda", mma_type: int = _lib.MOE_MMA_MXF4_X_MXF4,
+                 prepared: torch.Tensor | None = None):
         """mma_type: MOE_MMA_MXF4_X_MXF4 (MXFP4 activations) or MOE_MMA_FP8_X_MXF4
-        (MXFP8 E4M3 activations); the weights are MXFP4 in both."""
+        (MXFP8 E4M3 activations); the weights are MXFP4 in both.  prepared: an
+        existing prepared-weights buffer of the same shape to share (see
+        with_capacity), else a new one is allocated."""
         self.H, self.I, self.E, self.k, self.max_tokens = hidden, inter, num_experts, topk, max_tokens
         self.mma_type = mma_type
         self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
         self.cfg = _lib.make_cfg(hidden, inter, num_experts, topk, max_tokens, mma_type=mma_type)
         pb, wb = _lib.moe_w4a4_query(self.cfg)
-        self.prepared = torch.empty(pb, dtype=torch.uint8, device=self.device)
+        if prepared is None:
+            prepared = torch.empty(pb, dtype=torch.uint8, device=self.device)
+        elif prepared.numel() * prepared.element_size() < pb or prepared.device != self.device:
+            raise ValueError("shared prepared buffer is too small or on another device")
+        self.prepared = prepared
         self.workspace = torch.empty(wb, dtype=torch.uint8, device=self.device)
         self.layout = _lib.moe_w4a4_workspace_layout(self.cfg)
+
+    def with_capacity(self, max_tokens: int, mma_type: int | None = None) -> "MoeW4A4Layer":
+        """A layer over the same prepared weights (shared, not copied) with its
+        own workspace for max_tokens tokens; mma_type may differ, since both
+        types use the same MXFP4 weights."""
+        return MoeW4A4Layer(self.H, self.I, self.E, self.k, max_tokens, self.device,
+                            self.mma_type if mma_type is None else mma_type, prepared=self.prepared)
 
     # ---- weights ------------------------------------------------------------
     def canonical_buffers(self):
@@ -68,17 +84,23 @@ class MoeW4A4Layer:
 
     # ---- forward ------------------------------------------------------------
     def forward(self, x, topk_ids, topk_weights, out=None, stream=None):
+        """x bf16 [T, H]; topk_ids int32 [T, k] (ids outside [0, E) are skipped);
+        topk_weights float32 [T, k]; out bf16 [T, H] or None.  Every tensor must
+        be on the layer's device; anything else raises ValueError before a
+        kernel is launched."""
         T = x.shape[0]
         if out is None:
             out = torch.empty((T, self.H), dtype=torch.bfloat16, device=self.device)
-        _lib.moe_w4a4_forward(self.cfg, self.prepared, T, x, topk_ids, topk_weights, out, self.workspace,
-                              stream=stream)
+        with torch.cuda.device(self.device):
+            _lib.moe_w4a4_forward(self.cfg, self.prepared, T, x, topk_ids, topk_weights, out, self.workspace,
+                                  stream=stream)
         return out
 
     def run_stages(self, stages, num_tokens, x=None, topk_ids=None, topk_weights=None, out=None,
                    gemm1_acc=None, stream=None):
-        _lib.moe_w4a4_run_stages(self.cfg, self.prepared, num_tokens, x, topk_ids, topk_weights, out,
-                                 self.workspace, stages, gemm1_acc=gemm1_acc, stream=stream)
+        with torch.cuda.device(self.device):
+            _lib.moe_w4a4_run_stages(self.cfg, self.prepared, num_tokens, x, topk_ids, topk_weights, out,
+                                     self.workspace, stages, gemm1_acc=gemm1_acc, stream=stream)
 
     def ws(self, name: str, shape, dtype) -> torch.Tensor:
         """A view of one intermediate region of the workspace (see moe_w4a4_ws_layout)."""

@@ -92,7 +92,15 @@ typedef struct moe_w4a4_cfg {
 } moe_w4a4_cfg;
 
 /* Sizes in bytes of the prepared-weights buffer and of the forward workspace
- * for `cfg`.  Either output pointer may be NULL.  Pure host function. */
+ * for `cfg`.  This is the sizing half of the pages' buffer factory ([P3]
+ * "Key source snippets", _get_mega_moe_symm_buffer: one buffer per
+ * (num_max_tokens_per_rank, experts, topk, hidden, intermediate_hidden,
+ * mma_type, activation), reused by every forward); here the caller allocates
+ * what these sizes say.  The prepared size is the four weight regions plus a
+ * 64 KiB tail that the weight streams' read-ahead may touch.  Either output
+ * pointer may be NULL.  Pure host function: returns MOE_EINVAL or
+ * MOE_EUNSUPPORTED for a configuration moe_w4a4_cfg does not allow, with the
+ * outputs untouched. */
 int moe_w4a4_query(const moe_w4a4_cfg* cfg, size_t* prepared_bytes, size_t* workspace_bytes);
 
 /* Quantize `rows` rows of `cols` values to MXFP4 along each row.
@@ -119,7 +127,11 @@ int moe_w4a4_prepare_weights(const moe_w4a4_cfg* cfg,
                              const uint8_t* w2_codes, const uint8_t* w2_scales,
                              void* prepared, size_t prepared_bytes, void* stream);
 
-/* One forward of the layer for num_tokens (0 <= num_tokens <= cfg->max_tokens):
+/* One forward of the layer for num_tokens (0 <= num_tokens <= cfg->max_tokens).
+ * It is the routed branch of the pages' MoE runner ([P3] "Key source snippets",
+ * _run_mega_routed: pre_dispatch of the bf16 hidden states with topk_ids and
+ * topk_weights into the buffer for the live num_tokens, group_size=32, then
+ * the fused mega-MoE kernel over the prepared L1/L2 weights), as one call:
  *   1. pre-dispatch: each token row of x quantized once to MXFP4 (MXFP8 E4M3
  *      for MOE_MMA_FP8_X_MXF4; so is h in step 3);
  *   2. route: stable counting sort of the routed rows r = t*k + j by expert
@@ -137,7 +149,12 @@ int moe_w4a4_prepare_weights(const moe_w4a4_cfg* cfg,
  * workspace:    device buffer of at least query()'s workspace_bytes, 256-byte
  *               aligned; holds the intermediates (layout: moe_w4a4_workspace_layout)
  * num_tokens == 0 returns MOE_OK and enqueues nothing, without looking at
- * any pointer (empty tensors may have NULL data).
+ * any pointer (empty tensors may have NULL data).  Errors, before anything is
+ * enqueued: MOE_EINVAL (a null or misaligned pointer, num_tokens < 0),
+ * MOE_ECAPACITY (num_tokens > max_tokens), MOE_EWORKSPACE (workspace_bytes
+ * too small), MOE_EUNSUPPORTED (cfg), MOE_ENODEVICE (current device not a
+ * gfx950); MOE_EHIP if a launch fails.  The shapes behind the pointers are
+ * the caller's promise: the library cannot see them.
  * The result is deterministic: no floating-point atomics, stable sort. */
 int moe_w4a4_forward(const moe_w4a4_cfg* cfg, const void* prepared, int32_t num_tokens,
                      const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
@@ -179,8 +196,11 @@ int moe_w4a4_workspace_layout(const moe_w4a4_cfg* cfg, moe_w4a4_ws_layout* out);
 /* Stage bits for moe_w4a4_run_stages. */
 enum {
   MOE_STAGE_QUANT = 1,    /* x -> xq, xsf                                  */
-  MOE_STAGE_ROUTE = 2,    /* topk_ids -> counts, offsets, sorted_rows, pos */
-  MOE_STAGE_GEMM1 = 4,    /* xq, xsf, route -> hq, hsf (and xsf_planes)    */
+  MOE_STAGE_ROUTE = 2,    /* topk_ids -> counts, offsets, sorted_rows, pos;
+                             with more than 16 routed rows per expert on
+                             average also the tile list, and xsf ->
+                             xsf_planes (the token scales in sorted order) */
+  MOE_STAGE_GEMM1 = 4,    /* xq, xsf (or xsf_planes), route -> hq, hsf     */
   MOE_STAGE_GEMM2 = 8,    /* hq, route -> y                                */
   MOE_STAGE_COMBINE = 16, /* y, pos, topk_weights -> out                   */
   MOE_STAGE_ALL = 31

@@ -27,7 +27,8 @@ def test_query_sizes_dsv4():
     from block_scaled_fp4_pre_amd import _lib
     cfg = _lib.make_cfg(4096, 2048, 256, 6, 512)
     prepared, ws = _lib.moe_w4a4_query(cfg)
-    assert prepared == 256 * 13369344          # all experts' MXFP4 codes + scales
+    # all experts' MXFP4 codes + scales, then the 64 KiB tail the weight streams' read-ahead may touch
+    assert prepared == 256 * 13369344 + 65536
     lay = _lib.moe_w4a4_workspace_layout(cfg)
     assert lay["total"] == ws
     assert all(v % 256 == 0 for v in lay.values())
@@ -132,3 +133,74 @@ def test_valid_call_without_a_gfx950_reports_no_device():
     fake = ctypes.c_void_p(1 << 20)                    # aligned, never dereferenced
     st = L.moe_w4a4_forward(ctypes.byref(cfg), fake, 4, fake, fake, fake, fake, fake, ws, None)
     assert st == _lib.MOE_ENODEVICE
+
+
+def test_prepared_buffer_has_the_read_ahead_tail():
+    """The streaming GEMMs read up to 4 K steps (4 x 16 KiB of codes) past a
+    unit's last step without consuming them; for the last expert those reads
+    run past the four weight regions, into a 64 KiB tail of the buffer."""
+    from block_scaled_fp4_pre_amd import _lib
+    for H, I, E in ((256, 128, 8), (4096, 2048, 256), (768, 384, 5)):
+        cfg = _lib.make_cfg(H, I, E, 2, 16)
+        prepared, _ = _lib.moe_w4a4_query(cfg)
+        regions = 0
+        for nbytes in (E * 2 * I * H // 2, E * 2 * I * H // 32, E * H * I // 2, E * H * I // 32):
+            regions = -(-(regions + nbytes) // 256) * 256
+        assert prepared - regions == 65536, (H, I, E)
+
+
+def _t(shape, dtype):
+    import torch
+    return torch.zeros(shape, dtype=dtype)
+
+
+@pytest.mark.parametrize("case", ["ids_int64", "weights_bf16", "x_fp32", "x_narrow", "ids_short", "out_short",
+                                  "out_narrow", "ids_wrong_k", "x_1d", "cpu_tensors"])
+def test_binding_rejects_bad_tensors_before_the_library(case):
+    """The binding hands the library raw pointers only, so it checks dtype,
+    shape and device itself: topk_ids straight from torch.topk (int64) would
+    otherwise be read as int32 pairs, and a short x or out would be read or
+    written past its end by the kernels."""
+    import torch
+    from block_scaled_fp4_pre_amd import _lib
+    T, H, k = 8, 256, 2
+    cfg = _lib.make_cfg(H, 128, 8, k, 16)
+    a = dict(x=_t((T, H), torch.bfloat16), topk_ids=_t((T, k), torch.int32), topk_weights=_t((T, k), torch.float32),
+             out=_t((T, H), torch.bfloat16))
+    bad = {"ids_int64": ("topk_ids", _t((T, k), torch.int64)),
+           "weights_bf16": ("topk_weights", _t((T, k), torch.bfloat16)),
+           "x_fp32": ("x", _t((T, H), torch.float32)),
+           "x_narrow": ("x", _t((T, H // 2), torch.bfloat16)),
+           "ids_short": ("topk_ids", _t((T - 1, k), torch.int32)),
+           "out_short": ("out", _t((T - 1, H), torch.bfloat16)),
+           "out_narrow": ("out", _t((T, H - 32), torch.bfloat16)),
+           "ids_wrong_k": ("topk_ids", _t((T, k + 1), torch.int32)),
+           "x_1d": ("x", _t((T * H,), torch.bfloat16)),
+           "cpu_tensors": (None, None)}[case]
+    if bad[0] is not None:
+        a[bad[0]] = bad[1]
+    ws = _t((1 << 20,), torch.uint8)
+    prep = _t((1 << 20,), torch.uint8)
+    with pytest.raises(ValueError):
+        _lib.moe_w4a4_forward(cfg, prep, T, a["x"], a["topk_ids"], a["topk_weights"], a["out"], ws)
+    with pytest.raises(ValueError):
+        _lib.moe_w4a4_run_stages(cfg, prep, T, a["x"], a["topk_ids"], a["topk_weights"], a["out"], ws,
+                                 _lib.MOE_STAGE_ALL)
+
+
+def test_binding_rejects_bad_weight_and_quantize_buffers():
+    import torch
+    from block_scaled_fp4_pre_amd import _lib
+    cfg = _lib.make_cfg(256, 128, 8, 2, 16)
+    E, H, I = 8, 256, 128
+    ok = [_t((E, 2 * I, H // 2), torch.uint8), _t((E, 2 * I, H // 32), torch.uint8),
+          _t((E, H, I // 2), torch.uint8), _t((E, H, I // 32), torch.uint8)]
+    for i in range(4):
+        w = list(ok)
+        w[i] = _t(tuple(w[i].shape[:-1]) + (w[i].shape[-1] - 1,), torch.uint8)
+        with pytest.raises(ValueError):
+            _lib.moe_w4a4_prepare_weights(cfg, *w, _t((1 << 20,), torch.uint8))
+    with pytest.raises(ValueError):
+        _lib.moe_w4a4_quantize(_t((4, 64), torch.float32), _t((4, 31), torch.uint8), _t((4, 2), torch.uint8))
+    with pytest.raises(ValueError):
+        _lib.moe_w4a4_quantize(_t((4, 64), torch.float64), _t((4, 32), torch.uint8), _t((4, 2), torch.uint8))
