@@ -1,7 +1,7 @@
 """Benchmark of the W4A4 MoE layer forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--mma-type {mxf4xmxf4,fp8xfp4}]
-                    [--no-cpu-baseline] [--no-ceiling]
+                    [--no-cpu-baseline] [--no-ceiling] [--no-prefill]
 
 A step is one whole forward of the layer (pre-dispatch quantization, routing,
 GEMM1 + SwiGLU + requant, GEMM2, combine) on one batch of synthetic tokens whose
@@ -13,21 +13,24 @@ weights resident.
 Prints ONE JSON line.  `value` is the time of one layer forward in us (lower is
 better): K calls of moe_w4a4_forward, bracketed by synchronizations and HIP
 events on the stream the kernels run on.  Throughput in TFLOP/s and
-algorithmic HBM GB/s ride along.  The "roofline" object is for GEMM1, the
-dominant kernel (gemm1_swiglu_kernel up to 16 routed rows per expert,
-gemm_lds_kernel above), against the HBM or the MFMA peak of the MMA type (MXFP4,
-or FP8 for the fp8xfp4 type), whichever bounds
-its algorithmic bytes and flops: its duration comes from K further steps of the
-same launches in which events on the same stream bracket the GEMM1 launch
+algorithmic HBM GB/s ride along.  "roofline" is GEMM1's, the dominant kernel
+(gemm1_swiglu_kernel up to 16 routed rows per expert, gemm_lds_kernel above),
+and "roofline_gemm2" GEMM2's, each against the HBM or the MFMA peak of the MMA
+type (MXFP4, or FP8 for the fp8xfp4 type), whichever bounds its algorithmic
+bytes and flops.  Their durations come from K further steps of the same
+launches in which events on the same stream bracket each GEMM launch
 ("split_step_us" is the step time of that loop).  "forward_us" gives the
 median, minimum and maximum of K more forwards, each bracketed by its own
-events.  "ceiling" holds this GPU's measured ceilings (libmoe_ceiling.so): the
+events.  With the default workload the metric's second operating point,
+ntok = 4096, rides along as the object "dsv4flash_t4096_prefill" (same
+weights, same measurements).  "context" holds the pages' own figure for
+ntok = 512 (another machine: not a baseline, so "vs_baseline" is null).
+"ceiling" holds this GPU's measured ceilings (libmoe_ceiling.so): the
 streaming-read rate of a 2 GiB buffer with non-temporal and with default loads
-(best over 2 to 16 workgroups per CU),
-the rate of back-to-back MFMAs of each MMA type, and GEMM1's achieved rate as a fraction of
-the ceiling that bounds it.  "cpu_baseline" times the fp64 CPU oracle on a
-bounded slice of the same workload (a few experts with all their routed rows)
-and scales it to one layer.
+(best over 2 to 16 workgroups per CU), the rate of back-to-back MFMAs of each
+MMA type, and GEMM1's achieved rate as a fraction of the ceiling that bounds
+it.  "cpu_baseline" times the fp64 CPU oracle over one whole forward of the
+same workload, with the BLAS it runs on.
 """
 from __future__ import annotations
 
@@ -66,33 +69,42 @@ def algorithmic(cfg, counts, fp8=False):
     flops = R * (2 * H * 2 * I + 2 * I * H)
     w1 = 2 * I * H // 2 + 2 * I * H // 32
     gemm1_bytes = active * w1 + T * (H // cb + H // 32) + R * (I // cb + I // 32)
+    w2 = H * I // 2 + H * I // 32
+    gemm2_bytes = active * w2 + R * (I // cb + I // 32) + R * 2 * H     # W2, h-hat in, y out (bf16)
     return dict(active=active, R=R, layer_bytes=layer_bytes, flops=flops, gemm1_bytes=gemm1_bytes,
-                gemm1_flops=R * 2 * H * 2 * I)
+                gemm1_flops=R * 2 * H * 2 * I, gemm2_bytes=gemm2_bytes, gemm2_flops=R * 2 * I * H)
 
 
-STREAM_MAX_ROWS = 16              # mean routed rows per expert up to which GEMM1 is the streaming kernel
-# GEMM1 kernel of each path, with the sources its code comes from.
-GEMM1_KERNELS = {
-    "stream": ("gemm1_swiglu_kernel", ("gemm1.hip", "stream_ring.h", "gemm_common.h", "epilogue.h", "device_common.h",
-                                       "tiles.h")),
-    "prefill": ("gemm_lds_kernel", ("gemm_lds.hip", "gemm_common.h", "epilogue.h", "device_common.h", "tiles.h")),
+STREAM_MAX_ROWS = 16              # mean routed rows per expert up to which the GEMMs are the streaming kernels
+# Each GEMM's kernel on each path, with the sources its code comes from.  The
+# label names the committed HBM-counter file of that kernel
+# (profiles/<label>_<workload>[_fp8xfp4]_hbm_counters.txt).
+KERNELS = {
+    ("gemm1", "stream"): ("gemm1_swiglu_kernel", "gemm1_swiglu_kernel",
+                          ("gemm1.hip", "stream_ring.h", "gemm_common.h", "epilogue.h", "device_common.h", "tiles.h")),
+    ("gemm2", "stream"): ("gemm2_kernel", "gemm2_kernel",
+                          ("gemm2.hip", "stream_ring.h", "gemm_common.h", "epilogue.h", "device_common.h", "tiles.h")),
+    ("gemm1", "prefill"): ("gemm_lds_kernel", "gemm_lds_kernel",
+                           ("gemm_lds.hip", "gemm_common.h", "epilogue.h", "device_common.h", "tiles.h")),
+    ("gemm2", "prefill"): ("gemm_lds_kernel", "gemm_lds_kernel_gemm2",
+                           ("gemm_lds.hip", "gemm_common.h", "epilogue.h", "device_common.h", "tiles.h")),
 }
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "{}_{}_hbm_counters.txt")
 
 
-def gemm1_path(cfg):
+def gemm_path(cfg):
     rows_hint = -(-cfg.tokens * cfg.topk // cfg.experts)
     return "stream" if rows_hint <= STREAM_MAX_ROWS else "prefill"
 
 
-def measured_traffic(workload, path, fp8=False):
-    """HBM bytes per GEMM1 launch from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE runs, each scaled by the same counter on a copy of known size;
-    None if there are none for this workload and MMA type or the kernel
-    changed since."""
+def measured_traffic(workload, gemm, path, fp8=False):
+    """HBM bytes per launch of one GEMM kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs, each scaled by the same counter on a copy of
+    known size; None if there are none for this workload and MMA type or the
+    kernel's sources changed since."""
     import hashlib
-    kernel, sources = GEMM1_KERNELS[path]
-    path = COUNTERS_FILE.format(kernel, workload + ("_fp8xfp4" if fp8 else ""))
+    _, label, sources = KERNELS[(gemm, path)]
+    path = COUNTERS_FILE.format(label, workload + ("_fp8xfp4" if fp8 else ""))
     if not os.path.exists(path):
         return None
     kv = {}
@@ -112,42 +124,167 @@ def measured_traffic(workload, path, fp8=False):
     return int(round(fetch + write))
 
 
-def cpu_baseline(cfg, x, ids, w, n_experts_sample=40, mma_type="mxf4xmxf4"):
-    """The oracle as it stands, on a slice: quantize + route of the whole batch,
-    then GEMM1/SwiGLU/requant/GEMM2 for all routed rows of a few experts; the
-    per-expert time is scaled to the active experts of the layer."""
+def blas_info():
+    """(threads, vendor string) of the BLAS that numpy uses for the oracle's products."""
     try:
         import threadpoolctl
-        blas = threadpoolctl.threadpool_info()
-        cores = max([b.get("num_threads", 1) for b in blas] + [1])
+        blas = [b for b in threadpoolctl.threadpool_info() if b.get("user_api") == "blas"]
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+        blas = []
+    if not blas:
+        return os.cpu_count() or 1, "unknown"
+    b = blas[0]
+    return int(b.get("num_threads", 1)), f"{b.get('internal_api', '?')} {b.get('version', '?')} " \
+                                         f"({b.get('architecture', '?')} kernels, {b.get('threading_layer', '?')})"
+
+
+def cpu_baseline(cfg, x, ids, w, mma_type="mxf4xmxf4", weight_pool=2):
+    """The oracle as it stands, timed over one whole forward of the workload:
+    quantization of all tokens, the route, GEMM1/SwiGLU/requant/GEMM2 of
+    every routed row of every active expert, and the combine.  Expert weights
+    are load-time work and are not timed; the oracle quantizes weight_pool
+    experts' weights and every expert uses one of them in turn (its arithmetic
+    and cost do not depend on the weight values, and quantizing all 256
+    experts' 3.4 GB with the oracle's brute-force quantizer would take tens of
+    CPU-minutes)."""
     import synth
     from oracle import mxfp4
     from oracle.forward import forward
     from oracle.route import route
 
+    threads, vendor = blas_info()
     counts = route(ids, cfg.experts)[0]
-    active = [e for e in range(cfg.experts) if counts[e] > 0]
-    sample = active[:n_experts_sample]
-    weights = {}
-    for e in sample:                       # weight quantization is load-time work: not timed
+    active = int((counts > 0).sum())
+    pool = []
+    for e in range(weight_pool):
         w1, w2 = synth.expert_weights_f32(cfg, e)
-        weights[e] = mxfp4.quantize_packed(w1) + mxfp4.quantize_packed(w2)
+        pool.append(mxfp4.quantize_packed(w1) + mxfp4.quantize_packed(w2))
     t0 = time.perf_counter()
-    forward(x, ids, w, lambda e: weights[e], cfg.experts, cfg.inter, experts=[], mma_type=mma_type)
-    t_common = time.perf_counter() - t0
+    forward(x, ids, w, lambda e: pool[e % weight_pool], cfg.experts, cfg.inter, mma_type=mma_type)
+    secs = time.perf_counter() - t0
+    return {"value": round(secs * 1e6, 1), "unit": "us", "cores": threads, "kind": "oracle", "blas": vendor,
+            "sample": f"one whole forward of the {cfg.name} workload ({cfg.tokens} tokens, {int(counts.sum())} "
+                      f"routed rows over {active} active experts, combine included), measured, not scaled; the "
+                      f"experts use {weight_pool} experts' oracle-quantized weights in turn",
+            "measured_s": round(secs, 2)}
+
+
+def roofline(kernel, nbytes, flops, us, fp8, traffic):
+    """Roofline object of one kernel: HBM-bound unless its flops take longer
+    at the MFMA peak of the MMA type than its algorithmic bytes at the HBM peak."""
+    mfma_peak = FP8_PEAK_TFLOPS if fp8 else FP4_PEAK_TFLOPS
+    mfma_bound = flops / (mfma_peak * 1e12) > nbytes / (HBM_PEAK_GBPS * 1e9)
+    if mfma_bound:
+        ach, peak, unit = flops / (us * 1e-6) / 1e12, mfma_peak, "TFLOP/s"
+    else:
+        ach, peak, unit = nbytes / (us * 1e-6) / 1e9, HBM_PEAK_GBPS, "GB/s"
+    return {"kernel": kernel, "bound": "mfma" if mfma_bound else "hbm", "achieved": round(ach, 1), "peak": peak,
+            "unit": unit, "frac": round(ach / peak, 4), "traffic": traffic, "avg_us": round(us, 2),
+            "bytes_per_launch": int(nbytes), "flops_per_launch": int(flops)}
+
+
+def measure(layer, cfg, x, ids, w, out, steps, warmup):
+    """Times the forward: K forwards through the single entry point (the
+    timed region), K more split into the stage groups so that events on the
+    kernels' stream bracket GEMM1 and GEMM2, and K more each bracketed by its
+    own events."""
+    import torch
+
+    from block_scaled_fp4_pre_amd import _lib
+    T = cfg.tokens
+    S_A = _lib.MOE_STAGE_QUANT | _lib.MOE_STAGE_ROUTE
+
+    def split_step(ev=None):
+        # The launches of moe_w4a4_forward, in three calls, with events
+        # between them on the same stream.
+        layer.run_stages(S_A, T, x=x, topk_ids=ids)
+        if ev is not None:
+            ev[0].record()
+        layer.run_stages(_lib.MOE_STAGE_GEMM1, T)
+        if ev is not None:
+            ev[1].record()
+        layer.run_stages(_lib.MOE_STAGE_GEMM2, T)
+        if ev is not None:
+            ev[2].record()
+        layer.run_stages(_lib.MOE_STAGE_COMBINE, T, topk_weights=w, out=out)
+
+    ev_t = lambda: torch.cuda.Event(enable_timing=True)
+    for _ in range(warmup):
+        layer.forward(x, ids, w, out)
+    torch.cuda.synchronize()
+    start, end = ev_t(), ev_t()
     t0 = time.perf_counter()
-    forward(x, ids, w, lambda e: weights[e], cfg.experts, cfg.inter, experts=sample, mma_type=mma_type)
-    t_sample = time.perf_counter() - t0 - t_common
-    us = (t_common + t_sample / len(sample) * len(active)) * 1e6
-    rows = int(sum(counts[e] for e in sample))
-    return {"value": round(us, 1), "unit": "us", "cores": int(cores), "kind": "oracle",
-            "sample": f"quantize+route of all {cfg.tokens} tokens, then the {len(sample)} lowest-numbered "
-                      f"active experts ({sample[0]}..{sample[-1]}) "
-                      f"({rows} routed rows) through GEMM1/SwiGLU/requant/GEMM2; expert time scaled "
-                      f"to {len(active)} active experts",
-            "measured_s": round(t_common + t_sample, 2)}
+    start.record()
+    for _ in range(steps):
+        layer.forward(x, ids, w, out)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us = start.elapsed_time(end) / steps * 1e3
+
+    # Kernel attribution.  The event packets add a few us of idle time around
+    # each bracketed launch, so these averages are upper bounds on the
+    # kernels' durations (the kernel traces in profiles/ agree).
+    for _ in range(2):
+        split_step()
+    evs = [(ev_t(), ev_t(), ev_t()) for _ in range(steps)]
+    split_s, split_e = ev_t(), ev_t()
+    torch.cuda.synchronize()
+    split_s.record()
+    for i in range(steps):
+        split_step(evs[i])
+    split_e.record()
+    torch.cuda.synchronize()
+    gemm1_us = float(np.mean([a.elapsed_time(b) for a, b, _ in evs])) * 1e3
+    gemm2_us = float(np.mean([b.elapsed_time(c) for _, b, c in evs])) * 1e3
+    split_us = split_s.elapsed_time(split_e) / steps * 1e3
+
+    fwd = [(ev_t(), ev_t()) for _ in range(steps)]
+    for a, b in fwd:
+        a.record()
+        layer.forward(x, ids, w, out)
+        b.record()
+    torch.cuda.synchronize()
+    fwd_us = np.array([a.elapsed_time(b) for a, b in fwd]) * 1e3
+    return dict(us=us, wall=wall, gemm1_us=gemm1_us, gemm2_us=gemm2_us, split_us=split_us, fwd_us=fwd_us)
+
+
+def workload_record(layer, cfg, steps, warmup, fp8):
+    """Times one workload on `layer` and returns (its record, its inputs)."""
+    import torch
+
+    import synth
+    x_h = synth.make_tokens(cfg)
+    ids_h, w_h = synth.make_routing(cfg)
+    x = torch.from_numpy(x_h.view(np.int16)).cuda().view(torch.bfloat16)
+    ids = torch.from_numpy(ids_h).cuda()
+    w = torch.from_numpy(w_h).cuda()
+    out = torch.empty((cfg.tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    m = measure(layer, cfg, x, ids, w, out, steps, warmup)
+    counts = layer.ws("counts", (cfg.experts,), torch.int32).cpu().numpy()
+    alg = algorithmic(cfg, counts, fp8)
+    us = m["us"]
+    mfma_peak = FP8_PEAK_TFLOPS if fp8 else FP4_PEAK_TFLOPS
+    tflops = alg["flops"] / (us * 1e-6) / 1e12
+    gbps = alg["layer_bytes"] / (us * 1e-6) / 1e9
+    path = gemm_path(cfg)
+    rec = {
+        "value": round(us, 2),
+        "tflops": round(tflops, 2),
+        "tflops_frac": round(tflops / mfma_peak, 4),
+        "hbm_gbps": round(gbps, 1),
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "split_step_us": round(m["split_us"], 2),
+        "forward_us": {"median": round(float(np.median(m["fwd_us"])), 2), "min": round(float(m["fwd_us"].min()), 2),
+                       "max": round(float(m["fwd_us"].max()), 2)},
+        "roofline": roofline(KERNELS[("gemm1", path)][0], alg["gemm1_bytes"], alg["gemm1_flops"], m["gemm1_us"], fp8,
+                             measured_traffic(cfg.name, "gemm1", path, fp8)),
+        "roofline_gemm2": roofline(KERNELS[("gemm2", path)][0], alg["gemm2_bytes"], alg["gemm2_flops"],
+                                   m["gemm2_us"], fp8, measured_traffic(cfg.name, "gemm2", path, fp8)),
+        "wall_s": round(m["wall"], 3),
+    }
+    return rec, alg, (x_h, ids_h, w_h)
 
 
 def main():
@@ -161,6 +298,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the streaming-read and FP4 MFMA probes (libmoe_ceiling.so)")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the ntok=4096 prefill record that rides along with the ntok=512 headline")
     ap.add_argument("--threads", type=int, default=16)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a 256 MiB device-to-device copy (reference for HBM counters)")
@@ -176,79 +315,58 @@ def main():
     from block_scaled_fp4_pre_amd import _lib
     from block_scaled_fp4_pre_amd.layer import MoeW4A4Layer
 
-    cfg = {c.name: c for c in synth.CONFIGS}[args.workload]
+    configs = {c.name: c for c in synth.CONFIGS}
+    cfg = configs[args.workload]
     torch.cuda.set_device(0)
     t_setup = time.perf_counter()
     fp8 = args.mma_type == "fp8xfp4"
     layer = MoeW4A4Layer(cfg.hidden, cfg.inter, cfg.experts, cfg.topk, cfg.tokens,
                          mma_type=_lib.MOE_MMA_FP8_X_MXF4 if fp8 else _lib.MOE_MMA_MXF4_X_MXF4)
     layer.load_fp32(lambda e: synth.expert_weights_f32(cfg, e), threads=args.threads)
-    x_h = synth.make_tokens(cfg)
-    ids_h, w_h = synth.make_routing(cfg)
-    x = torch.from_numpy(x_h.view(np.int16)).cuda().view(torch.bfloat16)
-    ids = torch.from_numpy(ids_h).cuda()
-    w = torch.from_numpy(w_h).cuda()
-    out = torch.empty((cfg.tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda")
     torch.cuda.synchronize()
     print(f"[bench] setup {time.perf_counter() - t_setup:.1f}s workload={cfg.name}", file=sys.stderr, flush=True)
 
-    T = cfg.tokens
-    S_A = _lib.MOE_STAGE_QUANT | _lib.MOE_STAGE_ROUTE
-    S_B = _lib.MOE_STAGE_GEMM1
-    S_C = _lib.MOE_STAGE_GEMM2 | _lib.MOE_STAGE_COMBINE
-
-    def step(ev=None):
-        # The same launches as moe_w4a4_forward, split in three calls so that
-        # GEMM1 can be bracketed by events on the stream it runs on.
-        layer.run_stages(S_A, T, x=x, topk_ids=ids)
-        if ev is not None:
-            ev[0].record()
-        layer.run_stages(S_B, T)
-        if ev is not None:
-            ev[1].record()
-        layer.run_stages(S_C, T, topk_weights=w, out=out)
-
-    # Timed region: K forwards through the single entry point, bracketed by
-    # synchronizations and events on the stream the kernels run on.
-    for _ in range(args.warmup):
-        layer.forward(x, ids, w, out)
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    start.record()
-    for _ in range(args.steps):
-        layer.forward(x, ids, w, out)
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = start.elapsed_time(end) / args.steps
-
-    # GEMM1 attribution: K more steps of the same launches, split in three calls
-    # so that events on the same stream bracket the GEMM1 launch.  The event
-    # packets add a few us of idle time around it, so this average is an upper
-    # bound on the kernel's duration (the kernel trace in profiles/ agrees).
-    for _ in range(2):
-        step()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    split_s, split_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    split_s.record()
-    for i in range(args.steps):
-        step(evs[i])
-    split_e.record()
-    torch.cuda.synchronize()
-    gemm1_us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
-    split_ms = split_s.elapsed_time(split_e) / args.steps
-
-    # Per-forward spread: K more forwards, each bracketed by its own events.
-    fwd = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for a, b in fwd:
-        a.record()
-        layer.forward(x, ids, w, out)
-        b.record()
-    torch.cuda.synchronize()
-    fwd_us = np.array([a.elapsed_time(b) for a, b in fwd]) * 1e3
-
+    rec, alg, (x_h, ids_h, w_h) = workload_record(layer, cfg, args.steps, args.warmup, fp8)
+    print(f"[bench] {cfg.name}: {rec['value']} us", file=sys.stderr, flush=True)
+    us = rec["value"]
+    pages_us = PAGES_US_NTOK512_W4A8 if fp8 else PAGES_US_NTOK512
+    res = {
+        "metric": METRIC,
+        "value": us,
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        # The pages' figure was measured on another machine (one B200): it is
+        # context, not the baseline (see "context" and "cpu_baseline").
+        "vs_baseline": None,
+        "dtype": "mxfp8 x mxfp4" if fp8 else "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "mma_type": args.mma_type, "tokens": cfg.tokens, "hidden": cfg.hidden,
+                   "inter": cfg.inter, "experts": cfg.experts, "topk": cfg.topk, "routing": cfg.routing,
+                   "active_experts": alg["active"], "routed_rows": alg["R"]},
+    }
+    res.update({k: v for k, v in rec.items() if k != "value"})
+    if cfg.name == "dsv4flash_t512":
+        res["context"] = {"pages_us": pages_us, "pages_hardware": "1x B200, 1-rank isolation",
+                          "value_over_pages": round(us / pages_us, 4)}
+    if not args.no_prefill and cfg.name == "dsv4flash_t512":
+        # The metric's second operating point, ntok=4096 (uniform routing, about
+        # 96 rows per expert: the LDS-staged GEMMs), on the same prepared
+        # weights with a workspace for 4096 tokens.
+        pcfg = configs["dsv4flash_t4096_prefill"]
+        player = layer.with_capacity(pcfg.tokens)
+        prec, palg, _ = workload_record(player, pcfg, args.steps, args.warmup, fp8)
+        prec = {("value_us" if k == "value" else k): v for k, v in prec.items()}
+        prec["config"] = {"tokens": pcfg.tokens, "routing": pcfg.routing, "active_experts": palg["active"],
+                          "routed_rows": palg["R"]}
+        res[pcfg.name] = prec
+        print(f"[bench] {pcfg.name}: {prec['value_us']} us", file=sys.stderr, flush=True)
+        del player
+        torch.cuda.synchronize()
     if args.calibrate_copy:
         # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE per dispatch
         # calibrate the counters read for the layer's kernels.
@@ -258,64 +376,18 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-
-    counts = layer.ws("counts", (cfg.experts,), torch.int32).cpu().numpy()
-    alg = algorithmic(cfg, counts, fp8)
-    us = ms_per_step * 1e3
-    tflops = alg["flops"] / (us * 1e-6) / 1e12
-    gbps = alg["layer_bytes"] / (us * 1e-6) / 1e9
-    # GEMM1's roofline: HBM-bound unless its flops take longer at the MFMA peak
-    # of the MMA type than its algorithmic bytes at the HBM peak.
-    path = gemm1_path(cfg)
-    g1_kernel = GEMM1_KERNELS[path][0]
-    mfma_peak = FP8_PEAK_TFLOPS if fp8 else FP4_PEAK_TFLOPS
-    mfma_bound = alg["gemm1_flops"] / (mfma_peak * 1e12) > alg["gemm1_bytes"] / (HBM_PEAK_GBPS * 1e9)
-    if mfma_bound:
-        g1_ach, g1_peak, g1_unit = alg["gemm1_flops"] / (gemm1_us * 1e-6) / 1e12, mfma_peak, "TFLOP/s"
-    else:
-        g1_ach, g1_peak, g1_unit = alg["gemm1_bytes"] / (gemm1_us * 1e-6) / 1e9, HBM_PEAK_GBPS, "GB/s"
-
-    res = {
-        "metric": METRIC,
-        "value": round(us, 2),
-        "unit": "us",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": False,
-        "scaling": "weak",
-        "vs_baseline": (round(us / (PAGES_US_NTOK512_W4A8 if fp8 else PAGES_US_NTOK512), 4)
-                        if cfg.name == "dsv4flash_t512" else None),
-        "dtype": "mxfp8 x mxfp4" if fp8 else "mxfp4",
-        "data": "synthetic",
-        "config": {"workload": cfg.name, "mma_type": args.mma_type, "tokens": T, "hidden": cfg.hidden,
-                   "inter": cfg.inter,
-                   "experts": cfg.experts, "topk": cfg.topk, "routing": cfg.routing,
-                   "active_experts": alg["active"], "routed_rows": alg["R"]},
-        "tflops": round(tflops, 2),
-        "tflops_frac": round(tflops / mfma_peak, 4),
-        "hbm_gbps": round(gbps, 1),
-        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
-        "split_step_us": round(split_ms * 1e3, 2),
-        "forward_us": {"median": round(float(np.median(fwd_us)), 2), "min": round(float(fwd_us.min()), 2),
-                       "max": round(float(fwd_us.max()), 2)},
-        "roofline": {"kernel": g1_kernel, "bound": "mfma" if mfma_bound else "hbm", "achieved": round(g1_ach, 1),
-                     "peak": g1_peak, "unit": g1_unit, "frac": round(g1_ach / g1_peak, 4),
-                     "traffic": measured_traffic(cfg.name, path, fp8), "avg_us": round(gemm1_us, 2),
-                     "bytes_per_launch": alg["gemm1_bytes"], "flops_per_launch": alg["gemm1_flops"]},
-        "wall_s": round(wall, 3),
-    }
     if not args.no_ceiling:
         # Measured ceilings of this GPU, beside the published peaks the
         # roofline fraction uses.
         from block_scaled_fp4_pre_amd import ceiling
         ceil = ceiling.measure()
-        ref = ceil["mfma_fp8xfp4_TFLOPs" if fp8 else "mfma_fp4_TFLOPs"] if mfma_bound else ceil["read_nt_GBps"]
-        ceil["gemm1_frac"] = round(g1_ach / ref, 4)
+        roof = res["roofline"]
+        ref = (ceil["mfma_fp8xfp4_TFLOPs" if fp8 else "mfma_fp4_TFLOPs"] if roof["bound"] == "mfma"
+               else ceil["read_nt_GBps"])
+        ceil["gemm1_frac"] = round(roof["achieved"] / ref, 4)
         res["ceiling"] = ceil
     if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle slice)", file=sys.stderr, flush=True)
+        print("[bench] cpu baseline (the oracle, one whole forward)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg, x_h, ids_h, w_h, mma_type=args.mma_type)
     print(json.dumps(res), flush=True)
 

@@ -28,6 +28,12 @@ constexpr int kStreamMaxRows = MOE_STREAM_MAX_ROWS;
 
 std::atomic<int> g_is_gfx950[kMaxDevices];  // 0 unknown, 1 yes, 2 no
 
+inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+}  // namespace
+
+namespace moe {
+
 int check_device() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOE_ENODEVICE;
@@ -41,12 +47,6 @@ int check_device() {
   if (dev < kMaxDevices) g_is_gfx950[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
   return ok ? MOE_OK : MOE_ENODEVICE;
 }
-
-inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
-
-}  // namespace
-
-namespace moe {
 
 hipError_t raise_lds_limit(const void* kernel, size_t bytes) {
   struct Entry { const void* kernel; int device; size_t bytes; };
@@ -102,7 +102,7 @@ int moe_w4a4_quantize(int32_t src_dtype, const void* src, int64_t rows, int32_t 
   bool noop = false;
   const int st = moe::check_quantize_args(src_dtype, src, rows, cols, codes, scales, &noop);
   if (st != MOE_OK || noop) return st;
-  const int dv = check_device();
+  const int dv = moe::check_device();
   if (dv != MOE_OK) return dv;
   return hip_status(moe::launch_quantize(src_dtype == 0, false, src, rows * (int64_t)(cols / 32), codes, scales,
                                          static_cast<hipStream_t>(stream)));
@@ -113,7 +113,7 @@ int moe_w4a4_prepare_weights(const moe_w4a4_cfg* cfg, const uint8_t* w1_codes, c
                              size_t prepared_bytes, void* stream) {
   int st = moe::check_prepare_args(cfg, w1_codes, w1_scales, w2_codes, w2_scales, prepared, prepared_bytes);
   if (st != MOE_OK) return st;
-  st = check_device();
+  st = moe::check_device();
   if (st != MOE_OK) return st;
   const moe::PreparedLayout P = moe::prepared_layout(cfg);
   uint8_t* base = static_cast<uint8_t*>(prepared);
@@ -129,7 +129,7 @@ int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t n
   int st = moe::check_stage_args(cfg, prepared, num_tokens, x, topk_ids, topk_weights, out, workspace,
                                  workspace_bytes, stages, gemm1_acc, &noop);
   if (st != MOE_OK || noop) return st;
-  st = check_device();
+  st = moe::check_device();
   if (st != MOE_OK) return st;
   const moe_w4a4_ws_layout L = moe::ws_layout(cfg);
 

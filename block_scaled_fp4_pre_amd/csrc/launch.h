@@ -6,6 +6,9 @@
 
 namespace moe {
 
+// MOE_OK if the current HIP device is a gfx950, else MOE_ENODEVICE (cached per device).
+int check_device();
+
 // Stage S1a: MXFP4 quantization of rows of bf16 (src_is_bf16) or fp32 values;
 // fp8: MXFP8 E4M3 codes instead (the fp8xfp4 MMA type's activations, bf16 only).
 hipError_t launch_quantize(bool src_is_bf16, bool fp8, const void* src, int64_t ngroups,

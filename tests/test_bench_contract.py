@@ -1,7 +1,9 @@
 """bench.py's command-line contract: more than one GPU is refused with a
 message (CPU tier), and one short run prints exactly one JSON line with the
-fields and types the benchmark record needs, plus the per-forward spread and
-the measured ceilings (GPU tier)."""
+fields and types the benchmark record needs, plus the per-forward spread,
+both GEMMs' rooflines, the ntok=4096 record and the measured ceilings (GPU
+tier); the CPU baseline is the oracle over one whole forward (CPU tier, at the
+tiny size)."""
 import json
 import os
 import subprocess
@@ -36,11 +38,17 @@ def test_one_json_line_with_the_record_fields(mma):
     assert d["higher_is_better"] is False and d["data"] == "synthetic"
     assert d["config"]["workload"] == "dsv4flash_t512" and d["config"]["mma_type"] == mma
     assert abs(d["value"] - 1e3 * d["ms_per_step"]) <= 0.01 * d["value"]
-    assert isinstance(d["vs_baseline"], float)                  # the pages quote this workload for both types
+    assert d["vs_baseline"] is None                 # the pages' figure is another machine's: context only
+    assert d["context"]["pages_us"] in (537.6, 753.2)
+    for roof in (d["roofline"], d["roofline_gemm2"]):
+        assert roof["bound"] in ("hbm", "mfma") and roof["unit"] in ("GB/s", "TFLOP/s")
+        assert 0 < roof["achieved"] and roof["peak"] > 0
+        assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
+        assert roof["traffic"] is None or roof["traffic"] > 0
     roof = d["roofline"]
-    assert roof["bound"] in ("hbm", "mfma") and roof["unit"] in ("GB/s", "TFLOP/s")
-    assert 0 < roof["achieved"] and roof["peak"] > 0 and abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
-    assert roof["traffic"] is None or roof["traffic"] > 0
+    pre = d["dsv4flash_t4096_prefill"]                # the metric's second operating point
+    assert pre["config"]["tokens"] == 4096 and pre["value_us"] > 0
+    assert pre["roofline"]["kernel"] == "gemm_lds_kernel" and pre["roofline_gemm2"]["avg_us"] > 0
     assert "cpu_baseline" not in d
     fw = d["forward_us"]
     assert 0 < fw["min"] <= fw["median"] <= fw["max"]
@@ -49,3 +57,15 @@ def test_one_json_line_with_the_record_fields(mma):
     ref = (ceil["read_nt_GBps"] if roof["bound"] == "hbm"
            else ceil["mfma_fp8xfp4_TFLOPs" if mma == "fp8xfp4" else "mfma_fp4_TFLOPs"])
     assert abs(ceil["gemm1_frac"] - roof["achieved"] / ref) < 1e-3
+
+
+def test_cpu_baseline_times_one_whole_forward():
+    import synth
+    sys.path.insert(0, ROOT)
+    import bench
+    cfg = synth.CONFIGS[0]
+    x = synth.make_tokens(cfg)
+    ids, w = synth.make_routing(cfg)
+    cb = bench.cpu_baseline(cfg, x, ids, w)
+    assert cb["kind"] == "oracle" and cb["unit"] == "us" and cb["value"] > 0 and cb["cores"] >= 1
+    assert "whole forward" in cb["sample"] and "blas" in cb
