@@ -13,7 +13,8 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_w4a4.so")
 
-MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ECAPACITY, MOE_EWORKSPACE, MOE_ENODEVICE, MOE_EHIP = range(7)
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ECAPACITY, MOE_EWORKSPACE, MOE_ENODEVICE, MOE_EHIP, MOE_ESCRATCH = range(8)
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 MOE_MMA_MXF4_X_MXF4, MOE_MMA_FP8_X_MXF4 = 0, 1
 MOE_ACT_SWIGLU = 0
 MOE_STAGE_QUANT, MOE_STAGE_ROUTE, MOE_STAGE_GEMM1, MOE_STAGE_GEMM2, MOE_STAGE_COMBINE = 1, 2, 4, 8, 16
@@ -25,6 +26,7 @@ EXPORTED = (
     "moe_w4a4_quantize",
     "moe_w4a4_prepare_weights",
     "moe_w4a4_forward",
+    "moe_w4a4_forward_noalloc",
     "moe_w4a4_status_string",
     "moe_w4a4_workspace_layout",
     "moe_w4a4_run_stages",
@@ -66,6 +68,7 @@ _lib.moe_w4a4_query.argtypes = [_CFG, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]
 _lib.moe_w4a4_quantize.argtypes = [_i32, _P, ctypes.c_int64, _i32, _P, _P, _P]
 _lib.moe_w4a4_prepare_weights.argtypes = [_CFG, _P, _P, _P, _P, _P, _sz, _P]
 _lib.moe_w4a4_forward.argtypes = [_CFG, _P, _i32, _P, _P, _P, _P, _P, _sz, _P]
+_lib.moe_w4a4_forward_noalloc.argtypes = [_CFG, _P, _i32, _P, _P, _P, _P, _P]
 _lib.moe_w4a4_status_string.argtypes = [ctypes.c_int]
 _lib.moe_w4a4_status_string.restype = ctypes.c_char_p
 _lib.moe_w4a4_workspace_layout.argtypes = [_CFG, ctypes.POINTER(moe_w4a4_ws_layout)]
@@ -207,6 +210,15 @@ def moe_w4a4_forward(cfg, prepared, num_tokens: int, x, topk_ids, topk_weights, 
                                  _ptr(topk_weights), _ptr(out), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream)),
            "moe_w4a4_forward")
+
+
+def moe_w4a4_forward_noalloc(cfg, prepared, num_tokens: int, x, topk_ids, topk_weights, out,
+                             stream=None) -> None:
+    """The forward on the library's static scratch instead of a workspace."""
+    _check_forward_tensors(cfg, num_tokens, x, topk_ids, topk_weights, out, None, prepared)
+    _check(_lib.moe_w4a4_forward_noalloc(ctypes.byref(cfg), _ptr(prepared), int(num_tokens), _ptr(x),
+                                         _ptr(topk_ids), _ptr(topk_weights), _ptr(out), _stream(stream)),
+           "moe_w4a4_forward_noalloc")
 
 
 def moe_w4a4_run_stages(cfg, prepared, num_tokens: int, x, topk_ids, topk_weights, out, workspace,

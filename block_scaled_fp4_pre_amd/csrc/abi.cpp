@@ -77,6 +77,9 @@ const char* moe_w4a4_status_string(int status) {
     case MOE_EWORKSPACE: return "buffer smaller than moe_w4a4_query requires";
     case MOE_ENODEVICE: return "current HIP device is not a gfx950";
     case MOE_EHIP: return "HIP runtime call or kernel launch failed";
+    case MOE_ESCRATCH:
+      return "the forward needs more workspace than the library's static scratch; "
+             "use moe_w4a4_forward with a caller-owned workspace";
     default: return "unknown status";
   }
 }

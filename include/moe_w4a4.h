@@ -60,7 +60,8 @@ enum {
   MOE_ECAPACITY = 3,     /* num_tokens > cfg->max_tokens                          */
   MOE_EWORKSPACE = 4,    /* a buffer is smaller than moe_w4a4_query() requires    */
   MOE_ENODEVICE = 5,     /* the current HIP device is not a gfx950                */
-  MOE_EHIP = 6           /* a HIP runtime call or kernel launch failed            */
+  MOE_EHIP = 6,          /* a HIP runtime call or kernel launch failed            */
+  MOE_ESCRATCH = 7       /* moe_w4a4_forward_noalloc: more than its static scratch */
 };
 
 /* mma_type: the pairing of activation and weight formats ([P3] "Implementation
@@ -159,6 +160,22 @@ int moe_w4a4_prepare_weights(const moe_w4a4_cfg* cfg,
 int moe_w4a4_forward(const moe_w4a4_cfg* cfg, const void* prepared, int32_t num_tokens,
                      const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
                      uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The same forward with no workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The intermediates live in a static
+ * device array of the library, MOE_NOALLOC_SCRATCH_BYTES per GPU, which each
+ * GPU the library runs on holds until the process ends; its layout is
+ * moe_w4a4_workspace_layout of cfg with max_tokens = num_tokens.  Nothing is
+ * allocated or freed.  Returns MOE_ESCRATCH, enqueuing nothing, when that
+ * layout exceeds the scratch (about 1,100 tokens at hidden 4096, inter 2048,
+ * top-6).  Every call on a GPU uses that GPU's one array: calls that overlap on
+ * one GPU (other streams, other threads) race and must be serialized by the
+ * caller.  Other arguments, results and errors as for moe_w4a4_forward. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_w4a4_forward_noalloc(const moe_w4a4_cfg* cfg, const void* prepared, int32_t num_tokens,
+                             const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
+                             uint16_t* out, void* stream);
 
 /* Human-readable text of a status code (static storage). */
 const char* moe_w4a4_status_string(int status);
