@@ -37,37 +37,60 @@ def layer_for(H, I, E, k, max_tokens, mma_type=0):
 
 
 @functools.lru_cache(maxsize=2)
-def synth_layer(weight_set_cfg_index: int, max_tokens: int):
-    """A layer holding the synthetic weights of the config's weight set."""
+def _weights_layer(weight_set_cfg_index: int):
+    """A layer holding the synthetic weights of the config's weight set (and
+    a workspace for one token); the layers of synth_layer share its weights."""
     cfg = synth.CONFIGS[weight_set_cfg_index]
-    log(f"[gpu_support] building layer weight_set={cfg.weight_set} H={cfg.hidden} I={cfg.inter} "
-        f"E={cfg.experts} k={cfg.topk} max_tokens={max_tokens}")
-    layer = layer_for(cfg.hidden, cfg.inter, cfg.experts, cfg.topk, max_tokens)
+    log(f"[gpu_support] loading weight_set={cfg.weight_set} H={cfg.hidden} I={cfg.inter} E={cfg.experts} "
+        f"k={cfg.topk}")
+    layer = layer_for(cfg.hidden, cfg.inter, cfg.experts, cfg.topk, 1)
     layer.load_fp32(lambda e: synth.expert_weights_f32(cfg, e))
     torch.cuda.synchronize()
-    log("[gpu_support] layer ready")
+    log("[gpu_support] weights ready")
     return layer
 
 
-@functools.lru_cache(maxsize=1)
-def synth_layer_fp8(weight_set_cfg_index: int, max_tokens: int):
-    """The same layer with the fp8xfp4 MMA type.  The prepared weights (MXFP4
-    for both MMA types) are shared with synth_layer's."""
-    from block_scaled_fp4_pre_amd.layer import MoeW4A4Layer
-    base = synth_layer(weight_set_cfg_index, max_tokens)
-    layer = MoeW4A4Layer(base.H, base.I, base.E, base.k, max_tokens, mma_type=1)
-    layer.prepared = base.prepared
-    return layer
+@functools.lru_cache(maxsize=8)
+def synth_layer(weight_set_cfg_index: int, max_tokens: int, mma_type: int = 0):
+    """A layer over the synthetic weights of the config's weight set with a
+    workspace for max_tokens tokens; both MMA types use the same MXFP4
+    weights, so every such layer shares one prepared buffer."""
+    return _weights_layer(weight_set_cfg_index).with_capacity(max_tokens, mma_type=mma_type)
 
 
-def run_config(layer, cfg, tokens=None):
+def run_inputs(layer, x, ids, w, acc=False, acc_rows=None):
+    """Forward of host inputs on `layer`; returns host copies of every
+    intermediate.  acc: run the same launches through moe_w4a4_run_stages
+    with GEMM1's raw accumulators captured as "acc" (sorted-row order; only
+    the rows acc_rows, default all, are copied back)."""
+    from block_scaled_fp4_pre_amd import _lib
+    T = x.shape[0]
+    xd, idd, wd = dev_bf16(x), dev(ids), dev(w)
+    res = {}
+    if acc:
+        out = torch.empty((T, layer.H), dtype=torch.bfloat16, device="cuda")
+        buf = torch.full((T * layer.k, 2 * layer.I), float("nan"), device="cuda")
+        layer.run_stages(_lib.MOE_STAGE_ALL, T, x=xd, topk_ids=idd, topk_weights=wd, out=out, gemm1_acc=buf)
+        torch.cuda.synchronize()
+        rows = slice(None) if acc_rows is None else torch.from_numpy(np.asarray(acc_rows, np.int64)).cuda()
+        a = buf[rows].cpu().numpy()
+        if acc_rows is not None:
+            full = np.full((T * layer.k, 2 * layer.I), np.nan, np.float32)
+            full[np.asarray(acc_rows)] = a
+            a = full
+        res["acc"] = a
+        del buf
+    else:
+        out = layer.forward(xd, idd, wd)
+    torch.cuda.synchronize()
+    return dict(x=x, ids=ids, w=w, out=host_bits(out), **res, **workspace_host(layer, T))
+
+
+def run_config(layer, cfg, tokens=None, acc=False, acc_rows=None):
     """Forward of config cfg on `layer`; returns host copies of every intermediate."""
     x = synth.make_tokens(cfg, tokens)
     ids, w = synth.make_routing(cfg, tokens)
-    T = x.shape[0]
-    out = layer.forward(dev_bf16(x), dev(ids), dev(w))
-    torch.cuda.synchronize()
-    return dict(x=x, ids=ids, w=w, out=host_bits(out), **workspace_host(layer, T))
+    return run_inputs(layer, x, ids, w, acc=acc, acc_rows=acc_rows)
 
 
 def rows_from_planes(planes, nrows):

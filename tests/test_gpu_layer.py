@@ -8,10 +8,9 @@ import torch
 
 import synth
 from oracle.forward import forward
-from tests.gpu_support import dev, dev_bf16, host_bits, layer_for, log, run_config, synth_layer, workspace_host
+from tests.gpu_support import dev, dev_bf16, host_bits, layer_for, log, run_config, run_inputs
 from tests.oracle_inputs import all_expert_weights
-from tests.parity import (OUT_REL_L2, check_y, compare_requant, fp8_bound_for, fp8_requant_sampled, rel_l2,
-                          same_h_rows, sample_rows)
+from tests.parity import OUT_REL_L2, check_y, compare_requant, fp8_model_checks, rel_l2, same_h_rows
 
 pytestmark = pytest.mark.gpu
 TINY = synth.CONFIGS[0]
@@ -20,7 +19,8 @@ TINY = synth.CONFIGS[0]
 def check_all_stages(got, ref, k, weights=None):
     """weights: for the fp8xfp4 MMA type (E4M3 codes for x and h), e -> the
     oracle's (W1 codes, W1 scales, W2 codes, W2 scales) of expert e, which the
-    error bounds need; ref then comes from forward(..., keep_acc=True)."""
+    MFMA model's element rules need (on every row; with got["acc"], GEMM1's
+    captured accumulators, checked bit for bit too)."""
     from oracle import bf16
     fp8 = weights is not None
     assert np.array_equal(got["xq"], ref["xq"]) and np.array_equal(got["xsf"], ref["xsf"])
@@ -28,14 +28,9 @@ def check_all_stages(got, ref, k, weights=None):
         assert np.array_equal(got[key], ref[key]), key
     stats = compare_requant(got["hq"], got["hsf"], ref["hq"], ref["hsf"], ref["h"], fp8=fp8)
     exact = same_h_rows(got["hq"], got["hsf"], ref["hq"], ref["hsf"])
-    fb = None
     if fp8:
-        rows = sample_rows(~exact)
-        stats.update(fp8_requant_sampled(rows, got["hq"][rows], got["hsf"][rows], ref, k,
-                                         lambda e: weights(e)[:2]))
-        idx = np.nonzero(exact)[0]
-        fb = fp8_bound_for(idx, ref["offsets"], ref["hq"][idx], ref["hsf"][idx], lambda e: weights(e)[2:])
-    y_err, y_same = check_y(got["y"], ref["y"], exact, fp8_bound=fb)
+        stats.update(fp8_model_checks(got, ref, k, weights))
+    y_err, y_same = check_y(got["y"], ref["y"], exact, bf16_rule=not fp8)
     o_err = rel_l2(bf16.decode(got["out"]), ref["out_f64"])
     same = float(np.mean(got["out"] == ref["out"])) if got["out"].size else 1.0
     log(f"    requant {stats}  rows with identical h {int(exact.sum())}/{exact.size}  "
@@ -64,10 +59,8 @@ def test_tiny_config_end_to_end(tiny_layer, tiny_weights):
     check_all_stages(got, ref, TINY.topk)
 
 
-def _run_custom(layer, x, ids, w):
-    out = layer.forward(dev_bf16(x), dev(ids), dev(w))
-    torch.cuda.synchronize()
-    return dict(out=host_bits(out), **workspace_host(layer, x.shape[0]))
+def _run_custom(layer, x, ids, w, acc=False):
+    return run_inputs(layer, x, ids, w, acc=acc)
 
 
 @pytest.mark.parametrize("case", ["T1", "T3", "T129", "T1000", "one_expert", "masked_dups", "zero_x"])
@@ -163,7 +156,7 @@ def test_expert_count_extremes(E, k, T, H, I, mma):
     ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
     w = rng.random((T, k)).astype(np.float32)
     w /= w.sum(axis=1, keepdims=True)
-    got = _run_custom(layer, x, ids, w)
+    got = _run_custom(layer, x, ids, w, acc=bool(mma))
     c1, s1 = mxfp4.quantize_packed(W1)
     c2, s2 = mxfp4.quantize_packed(W2)
     ref = forward(x, ids, w, (c1, s1, c2, s2), E, I, mma_type="fp8xfp4" if mma else "mxf4xmxf4",

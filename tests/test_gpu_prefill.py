@@ -11,6 +11,11 @@ every intermediate, at shapes the oracle finishes in seconds:
               workgroup; some experts spill into a second tile
   t600_e8     about 150 rows per expert: several tiles per expert, default
               load policy
+  h1024_i512_e16_k2_t1000  about 125 rows per expert (the single-tile form)
+              with one expert spilling into a second tile
+  h512_i1024_e32_k4_t800_zipf0.7  Zipf(0.7) over 32 experts at about 100
+              rows per expert: the single-tile form with several tiles on
+              the hot experts
 
 Zipf routing gives hot experts with several full 128-row tiles and a ragged
 last tile, and cold experts with a single short tile."""
@@ -32,6 +37,8 @@ SHAPES = [
     synth.LayerConfig(102, "prefill_h256_i128_e8_k2_t2000", 2000, 256, 128, 8, 2, "uniform", 102),
     synth.LayerConfig(103, "prefill_h512_i512_e16_k2_t1000", 1000, 512, 512, 16, 2, "uniform", 103),
     synth.LayerConfig(104, "prefill_h512_i512_e8_k2_t600", 600, 512, 512, 8, 2, "uniform", 104),
+    synth.LayerConfig(105, "prefill_h1024_i512_e16_k2_t1000", 1000, 1024, 512, 16, 2, "uniform", 105),
+    synth.LayerConfig(106, "prefill_h512_i1024_e32_k4_t800_zipf0.7", 800, 512, 1024, 32, 4, "zipf", 106, 0.7),
 ]
 
 
