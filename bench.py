@@ -28,9 +28,11 @@ ntok = 512 (another machine: not a baseline, so "vs_baseline" is null).
 "ceiling" holds this GPU's measured ceilings (libmoe_ceiling.so): the
 streaming-read rate of a 2 GiB buffer with non-temporal and with default loads
 (best over 2 to 16 workgroups per CU), the rate of back-to-back MFMAs of each
-MMA type, and GEMM1's achieved rate as a fraction of the ceiling that bounds
-it.  "cpu_baseline" times the fp64 CPU oracle over one whole forward of the
-same workload, with the BLAS it runs on.
+MMA type and of dense bf16.  Each roofline object then carries
+"ceiling_frac", its achieved rate over the measured ceiling of its bound (the
+read, or the MFMA rate of its MMA type), and "gemm1_frac" repeats the
+headline GEMM1's.  "cpu_baseline" times the fp64 CPU oracle over one whole
+forward of the same workload, with the BLAS it runs on.
 """
 from __future__ import annotations
 
@@ -75,6 +77,7 @@ def algorithmic(cfg, counts, fp8=False):
                 gemm1_flops=R * 2 * H * 2 * I, gemm2_bytes=gemm2_bytes, gemm2_flops=R * 2 * I * H)
 
 
+PREFILL = "dsv4flash_t4096_prefill"   # the metric's second operating point
 STREAM_MAX_ROWS = 16              # mean routed rows per expert up to which the GEMMs are the streaming kernels
 # Each GEMM's kernel on each path, with the sources its code comes from.  The
 # label names the committed HBM-counter file of that kernel
@@ -357,7 +360,7 @@ def main():
         # The metric's second operating point, ntok=4096 (uniform routing, about
         # 96 rows per expert: the LDS-staged GEMMs), on the same prepared
         # weights with a workspace for 4096 tokens.
-        pcfg = configs["dsv4flash_t4096_prefill"]
+        pcfg = configs[PREFILL]
         player = layer.with_capacity(pcfg.tokens)
         prec, palg, _ = workload_record(player, pcfg, args.steps, args.warmup, fp8)
         prec = {("value_us" if k == "value" else k): v for k, v in prec.items()}
@@ -381,10 +384,15 @@ def main():
         # roofline fraction uses.
         from block_scaled_fp4_pre_amd import ceiling
         ceil = ceiling.measure()
-        roof = res["roofline"]
-        ref = (ceil["mfma_fp8xfp4_TFLOPs" if fp8 else "mfma_fp4_TFLOPs"] if roof["bound"] == "mfma"
-               else ceil["read_nt_GBps"])
-        ceil["gemm1_frac"] = round(roof["achieved"] / ref, 4)
+        mfma_ref = ceil["mfma_fp8xfp4_TFLOPs" if fp8 else "mfma_fp4_TFLOPs"]
+        for r in [res] + ([res[PREFILL]] if PREFILL in res else []):
+            # both GEMMs against the read ceiling or the MFMA rate (GEMM2
+            # also writes y, which the read ceiling does not include)
+            for key in ("roofline", "roofline_gemm2"):
+                roof = r[key]
+                ref = mfma_ref if roof["bound"] == "mfma" else ceil["read_nt_GBps"]
+                roof["ceiling_frac"] = round(roof["achieved"] / ref, 4)
+        ceil["gemm1_frac"] = res["roofline"]["ceiling_frac"]
         res["ceiling"] = ceil
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (the oracle, one whole forward)", file=sys.stderr, flush=True)

@@ -22,9 +22,12 @@ _lib.moe_ceiling_mfma_fp4.argtypes = [ctypes.c_uint32, ctypes.c_int32, ctypes.c_
 _lib.moe_ceiling_mfma_fp4.restype = ctypes.c_int
 _lib.moe_ceiling_mfma_fp8xfp4.argtypes = _lib.moe_ceiling_mfma_fp4.argtypes
 _lib.moe_ceiling_mfma_fp8xfp4.restype = ctypes.c_int
+_lib.moe_ceiling_mfma_bf16.argtypes = _lib.moe_ceiling_mfma_fp4.argtypes
+_lib.moe_ceiling_mfma_bf16.restype = ctypes.c_int
 
 MOE_CEILING_OK, MOE_CEILING_EINVAL, MOE_CEILING_EHIP = 0, 1, 2
 FLOPS_PER_MFMA = 2 * 16 * 16 * 128
+FLOPS_PER_MFMA_BF16 = 2 * 16 * 16 * 32
 CHAINS = 8
 
 
@@ -41,6 +44,11 @@ def moe_ceiling_stream_read(src: torch.Tensor, workgroups: int, non_temporal: bo
     assert src.is_cuda and digest.is_cuda and digest.dtype == torch.int32 and digest.numel() >= workgroups
     _check(_lib.moe_ceiling_stream_read(src.data_ptr(), src.numel() * src.element_size(), workgroups,
                                         int(non_temporal), digest.data_ptr(), _stream()), "moe_ceiling_stream_read")
+
+
+def moe_ceiling_mfma_bf16(workgroups: int, iterations: int, out: torch.Tensor) -> None:
+    assert out.is_cuda and out.dtype == torch.float32 and out.numel() >= 4 * workgroups
+    _check(_lib.moe_ceiling_mfma_bf16(workgroups, iterations, out.data_ptr(), _stream()), "moe_ceiling_mfma_bf16")
 
 
 def moe_ceiling_mfma_fp4(workgroups: int, iterations: int, out: torch.Tensor) -> None:
@@ -72,8 +80,9 @@ def measure(read_bytes: int = 2 << 30, workgroups=(512, 1024, 2048, 4096), reps:
     `read_bytes` random buffer, each workgroup reading one contiguous chunk,
     with non-temporal and with default loads, best over the `workgroups`
     counts (2 to 16 per CU); and `mfma_workgroups` x 4 waves of back-to-back
-    MFMAs of each MMA type (E2M1 x E2M1, E2M1 x E4M3).  Each result is checked: the read's per-workgroup XOR against the
-    same XOR taken by torch, the MFMA sums against their exact value."""
+    MFMAs of each MMA type (E2M1 x E2M1, E2M1 x E4M3) and of dense bf16.
+    Each result is checked: the read's per-workgroup XOR against the same
+    XOR taken by torch, the MFMA sums against their exact value."""
     src = torch.randint(-2**31, 2**31 - 1, (read_bytes // 4,), dtype=torch.int32, device="cuda")
     res = {"read_bytes": read_bytes}
     for wgs in workgroups:
@@ -101,6 +110,14 @@ def measure(read_bytes: int = 2 << 30, workgroups=(512, 1024, 2048, 4096), reps:
             raise RuntimeError(f"MFMA probe ({name}): sums differ from 8*128*iterations")
         ms = min(_timed_ms(lambda: fn(mfma_workgroups, mfma_iterations, out), reps))
         res[name] = round(flops / (ms * 1e-3) / 1e12, 1)
+    out.fill_(-1.0)
+    moe_ceiling_mfma_bf16(mfma_workgroups, mfma_iterations, out)
+    torch.cuda.synchronize()
+    if not bool((out == float(CHAINS * 32 * mfma_iterations)).all()):
+        raise RuntimeError("MFMA probe (bf16): sums differ from 8*32*iterations")
+    ms = min(_timed_ms(lambda: moe_ceiling_mfma_bf16(mfma_workgroups, mfma_iterations, out), reps))
+    res["mfma_bf16_TFLOPs"] = round(4 * mfma_workgroups * mfma_iterations * CHAINS * FLOPS_PER_MFMA_BF16 /
+                                    (ms * 1e-3) / 1e12, 1)
     return res
 
 

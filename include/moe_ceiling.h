@@ -10,7 +10,10 @@
  *   - moe_ceiling_mfma_fp4 / moe_ceiling_mfma_fp8xfp4: the practical rate of
  *     the block-scaled MFMA (V_MFMA_SCALE_F32_16X16X128_F8F6F4) with both
  *     operands E2M1, or with E2M1 weights and E4M3 tokens (the layer's two MMA
- *     types), issued back to back from register operands.
+ *     types), issued back to back from register operands;
+ *   - moe_ceiling_mfma_bf16: the practical dense bf16 MFMA rate
+ *     (V_MFMA_F32_16X16X32_BF16), the rate a block-scaled format whose scales
+ *     the f8f6f4 MFMA cannot take (E4M3 block scales, NVFP4) would run at.
  * Each probe writes a result the caller can check exactly, so that a probe
  * that skipped work would be caught.
  *
@@ -57,6 +60,13 @@ int moe_ceiling_mfma_fp4(uint32_t workgroups, int32_t iterations, float* out, hi
 /* The same with E4M3 B operands (every element 1.0): the fp8xfp4 MMA type's
  * instruction form.  Same result, requirements and flops per MFMA. */
 int moe_ceiling_mfma_fp8xfp4(uint32_t workgroups, int32_t iterations, float* out, hipStream_t stream);
+
+/* `workgroups` workgroups of 4 waves; each wave runs `iterations` rounds of 8
+ * independent 16x16x32 bf16 MFMAs (2*16*16*32 flops each) on operands whose
+ * every element is 1.0, then writes to out[wave] the sum of element 0 of its
+ * 8 accumulators: exactly 8 * 32 * iterations.  Requires 1 <= iterations <=
+ * 16384; out holds 4 * workgroups floats. */
+int moe_ceiling_mfma_bf16(uint32_t workgroups, int32_t iterations, float* out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

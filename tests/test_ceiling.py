@@ -3,7 +3,7 @@
 CPU: the library exports every declared symbol and rejects bad arguments
 before any HIP call.  GPU: the streaming read visits every byte of every chunk
 exactly once (its per-workgroup XOR equals numpy's, also for chunks that end
-inside a ring round), and both MFMA loops run every MFMA (exact sums)."""
+inside a ring round), and the three MFMA loops run every MFMA (exact sums)."""
 import ctypes
 import os
 import re
@@ -22,7 +22,8 @@ def _declared():
 def test_probe_library_exports_every_declared_symbol():
     from block_scaled_fp4_pre_amd import ceiling
     names = _declared()
-    assert names == ["moe_ceiling_mfma_fp4", "moe_ceiling_mfma_fp8xfp4", "moe_ceiling_stream_read"]
+    assert names == ["moe_ceiling_mfma_bf16", "moe_ceiling_mfma_fp4", "moe_ceiling_mfma_fp8xfp4",
+                     "moe_ceiling_stream_read"]
     for n in names:
         assert hasattr(ceiling._lib, n), n
 
@@ -44,6 +45,9 @@ def test_probe_arguments_checked_before_any_hip_call():
     assert lib.moe_ceiling_mfma_fp4(4, 10, None, None) == EINVAL
     assert lib.moe_ceiling_mfma_fp8xfp4(4, 0, fake, None) == EINVAL
     assert lib.moe_ceiling_mfma_fp8xfp4(4, 10, None, None) == EINVAL
+    assert lib.moe_ceiling_mfma_bf16(4, 0, fake, None) == EINVAL
+    assert lib.moe_ceiling_mfma_bf16(4, 16385, fake, None) == EINVAL
+    assert lib.moe_ceiling_mfma_bf16(4, 10, None, None) == EINVAL
 
 
 @pytest.mark.gpu
@@ -66,8 +70,8 @@ def test_stream_read_xors_every_word(chunk, non_temporal):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("form", ["fp4", "fp8xfp4"])
-def test_mfma_probe_sums_are_exact(form):
+@pytest.mark.parametrize("form,k", [("fp4", 128), ("fp8xfp4", 128), ("bf16", 32)])
+def test_mfma_probe_sums_are_exact(form, k):
     import torch
     from block_scaled_fp4_pre_amd import ceiling
     from tests.gpu_support import log
@@ -75,7 +79,7 @@ def test_mfma_probe_sums_are_exact(form):
     out = torch.full((160,), -1.0, dtype=torch.float32, device="cuda")
     getattr(ceiling, f"moe_ceiling_mfma_{form}")(40, 1000, out)
     torch.cuda.synchronize()
-    assert bool((out == 8 * 128 * 1000).all())
+    assert bool((out == 8 * k * 1000).all())
 
 
 @pytest.mark.gpu
@@ -87,4 +91,4 @@ def test_measure_reports_checked_rates():
                           mfma_iterations=256)
     log(f"    {res}")
     assert res["read_nt_GBps"] > 0 and res["read_GBps"] > 0
-    assert res["mfma_fp4_TFLOPs"] > 0 and res["mfma_fp8xfp4_TFLOPs"] > 0
+    assert res["mfma_fp4_TFLOPs"] > 0 and res["mfma_fp8xfp4_TFLOPs"] > 0 and res["mfma_bf16_TFLOPs"] > 0
