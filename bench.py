@@ -198,7 +198,7 @@ def measure(layer, cfg, x, ids, w, out, steps, warmup):
     S_A = _lib.MOE_STAGE_QUANT | _lib.MOE_STAGE_ROUTE
 
     def split_step(ev=None):
-        # The launches of moe_w4a4_forward, in three calls, with events
+        # The launches of moe_w4a4_forward, in four calls, with events
         # between them on the same stream.
         layer.run_stages(S_A, T, x=x, topk_ids=ids)
         if ev is not None:
