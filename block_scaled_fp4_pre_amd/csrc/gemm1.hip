@@ -26,7 +26,9 @@
 //
 // F8 (the fp8xfp4 MMA type, [P3] "Implementation breakdown" items 1-3): the
 // tokens are E4M3 bytes, twice the LDS per row, the B operand of each MFMA
-// takes 32 bytes (format code 0), and h is requantized to E4M3.
+// takes 32 bytes (format code 0), and h is requantized to E4M3.  With two
+// token tiles its workgroups have 8 waves: waves 4q..4q+3 own the q-th run of
+// upw unit groups, and all 8 share the token tile.
 #include "epilogue.h"
 #include "gemm_common.h"
 #include "launch.h"
@@ -44,24 +46,29 @@
 #define MOE_STREAM_EARLY 1        // two-tile form: first weight loads before the row count is read
 #endif
 
+#ifndef MOE_G1_F8_WAVES
+#define MOE_G1_F8_WAVES 8         // waves per workgroup, E4M3 tokens with two tiles (4 or 8)
+#endif
 #ifndef MOE_GEMM1_UNITS_PER_WAVE
 #define MOE_GEMM1_UNITS_PER_WAVE 2
 #endif
 
 namespace moe {
 
-template <int NT, int D, int SWZ, bool F8>
-__global__ void __launch_bounds__(256, 2) gemm1_swiglu_kernel(
+template <int NT, int D, int SWZ, bool F8, int WAVES = 4>
+__global__ void __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) gemm1_swiglu_kernel(
     const uint8_t* __restrict__ w1c, const uint8_t* __restrict__ w1s, const uint8_t* __restrict__ xq,
     const uint8_t* __restrict__ xsf, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_rows, int H, int I, int k,
     int upw, int hrows, uint8_t* __restrict__ hq, uint8_t* __restrict__ hsf, float* __restrict__ acc_out) {
-  const int groups = I / (128 * upw);
+  const int groups = I / (32 * WAVES * upw);   // unit blocks (WAVES * upw units) per expert
   const int e = blockIdx.x / groups;
   const int g = blockIdx.x - e * groups;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps the buffer resources in SGPRs
-  const int u0 = g * 4 * upw + wave;   // wave w owns unit w of each of the workgroup's upw unit groups
+  // wave w owns unit w % 4 of each of its upw unit groups; waves 4q..4q+3
+  // take the q-th run of upw groups of the workgroup's block
+  const int u0 = (g * (WAVES / 4) + wave / 4) * 4 * upw + (wave & 3);
   const int S = H / kStepK;
   const int total_steps = upw * S;       // the wave's upw units: one stream at stride kUnitStepStride
   const int row_bytes = F8 ? H : H / 2, sc_bytes = H / 32;   // token row: E4M3 bytes or packed E2M1
@@ -108,7 +115,7 @@ __global__ void __launch_bounds__(256, 2) gemm1_swiglu_kernel(
     const int my_tok = lane < nrows ? sorted_rows[base + t0 + lane] / k : 0;
     __syncthreads();  // the previous pass has finished reading LDS
     gather_tile<ROWS, SWZ>(lds_codes, lds_scales, xq, xsf, row_bytes, sc_bytes, nrows,
-                              [&](int n) { return __shfl(my_tok, n, 64); }, wave, lane, 4);
+                              [&](int n) { return __shfl(my_tok, n, 64); }, wave, lane, WAVES);
     wait_vmem_all();
     __syncthreads();
 
@@ -169,20 +176,20 @@ __global__ void __launch_bounds__(256, 2) gemm1_swiglu_kernel(
 
 #define MOE_GEMM1_ARGS w1c, w1s, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hrows, hq, hsf, acc_out, stream
 
-template <int NT, int D, int SWZ, bool F8>
+template <int NT, int D, int SWZ, bool F8, int WAVES = 4>
 static hipError_t launch_gemm1_t(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* xq,
                                  const uint8_t* xsf, const int32_t* counts, const int32_t* offsets,
                                  const int32_t* sorted_rows, int H, int I, int E, int k, int hrows, uint8_t* hq,
                                  uint8_t* hsf, float* acc_out, hipStream_t stream) {
   constexpr int ROWS = NT == 1 ? 16 : MOE_STREAM_ROWS2;
   const size_t lds = (size_t)ROWS * (F8 ? H : H / 2) + (size_t)ROWS * (H / 32);
-  auto kern = gemm1_swiglu_kernel<NT, D, SWZ, F8>;
-  const int upw = units_per_wave(I / 32 / 4, MOE_GEMM1_UNITS_PER_WAVE);
+  auto kern = gemm1_swiglu_kernel<NT, D, SWZ, F8, WAVES>;
+  const int upw = units_per_wave(I / 32 / WAVES, MOE_GEMM1_UNITS_PER_WAVE);
   if (lds > 65536) {
     hipError_t err = raise_lds_limit(reinterpret_cast<const void*>(kern), lds);
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(kern, dim3(E * (I / (128 * upw))), dim3(256), lds, stream, w1c, w1s, xq, xsf, counts,
+  hipLaunchKernelGGL(kern, dim3(E * (I / (32 * WAVES * upw))), dim3(64 * WAVES), lds, stream, w1c, w1s, xq, xsf, counts,
                      offsets, sorted_rows, H, I, k, upw, hrows, hq, hsf, acc_out);
   return hipGetLastError();
 }
@@ -193,8 +200,16 @@ static hipError_t launch_gemm1_nt(const uint8_t* w1c, const uint8_t* w1s, const 
                                   const int32_t* sorted_rows, int H, int I, int E, int k, int hrows, uint8_t* hq,
                                   uint8_t* hsf, float* acc_out, hipStream_t stream) {
   const int chunks = F8 ? H / 16 : H / 32;  // 16-byte chunks per token row; a multiple of 8
-  if (chunks % 16 == 0) return launch_gemm1_t<NT, D, 16, F8>(MOE_GEMM1_ARGS);
-  return launch_gemm1_t<NT, D, 8, F8>(MOE_GEMM1_ARGS);
+  // E4M3 tokens with two tiles: the token tile (101 KiB at H = 4096) fits
+  // one workgroup per CU, so 8 waves (two unit groups) share it: at 512
+  // tokens GEMM1 343 against 345 us with 4 waves.
+  constexpr int W = F8 && NT == 2 ? MOE_G1_F8_WAVES : 4;
+  if (W != 4 && (I / 32) % W != 0) {
+    if (chunks % 16 == 0) return launch_gemm1_t<NT, D, 16, F8>(MOE_GEMM1_ARGS);
+    return launch_gemm1_t<NT, D, 8, F8>(MOE_GEMM1_ARGS);
+  }
+  if (chunks % 16 == 0) return launch_gemm1_t<NT, D, 16, F8, W>(MOE_GEMM1_ARGS);
+  return launch_gemm1_t<NT, D, 8, F8, W>(MOE_GEMM1_ARGS);
 }
 
 template <int NT, bool F8>
