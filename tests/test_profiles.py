@@ -54,3 +54,26 @@ def test_gemm1_kernel_row_agrees_with_its_split_loop_average(path):
     split_us = float(re.search(r"GEMM1 kernel-trace average over the \d+ split-loop dispatches that the events "
                                r"bracket: ([\d.]+) us", text).group(1))
     assert abs(all_us - split_us) / split_us <= 0.05, (all_us, split_us)
+
+
+COUNTERS = sorted(glob.glob(os.path.join(ROOT, "profiles", "*_hbm_counters.txt")))
+
+
+@pytest.mark.parametrize("path", COUNTERS, ids=os.path.basename)
+def test_hbm_counters_match_the_current_kernel_sources(path):
+    """bench.py reports a kernel's HBM traffic from these files only while
+    their source hash matches: a kernel changed without retaking its
+    counters would silently drop the bench line's "traffic"."""
+    import bench
+    kv = dict(l.split("=", 1) for l in open(path) if "=" in l and not l.lstrip().startswith("#"))
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    name = os.path.basename(path)[:-len("_hbm_counters.txt")]
+    matches = [(g, p) for (g, p), (_, label, _) in bench.KERNELS.items() if name.startswith(label + "_dsv4flash")
+               and (label != "gemm_lds_kernel" or not name.startswith("gemm_lds_kernel_gemm2"))]
+    assert len(matches) == 1, (name, matches)
+    gemm, kpath = matches[0]
+    workload = name[len(bench.KERNELS[matches[0]][1]) + 1:]
+    fp8 = workload.endswith("_fp8xfp4")
+    traffic = bench.measured_traffic(workload[:-len("_fp8xfp4")] if fp8 else workload, gemm, kpath, fp8)
+    assert traffic is not None, f"{name}: kernel sources changed since the counters were taken"
+    assert traffic > 0
