@@ -63,6 +63,34 @@ def silu_mul(gate, up):
         return gate / (1.0 + np.exp(-gate)) * up
 
 
+def expert_gemm2(hq, hsf, w2_codes, w2_scales, act=mxfp4):
+    """Step 5 for one expert's rows: y = h_hat . W2_hat^T in fp64, h_hat the
+    dequantized requantized h (act: the activation format, oracle.mxfp4 or
+    oracle.mxfp8) and W2_hat the dequantized MXFP4 W2 [H, I]."""
+    return act.dequantize(hq, hsf) @ mxfp4.dequantize(w2_codes, w2_scales).T
+
+
+def combine(y, pos, topk_weights, want=None):
+    """Step 6: out[t] = sum over the valid slots j (pos >= 0), in slot order and
+    starting from +0, of w[t, j] * y[pos[t * k + j]], in fp64; a token with no
+    valid slot gives +0.  Rows of tokens outside `want` (a boolean mask) are
+    NaN.  Rounding to bfloat16 is the caller's."""
+    w = np.asarray(topk_weights, dtype=np.float64)
+    T, k = w.shape
+    H = y.shape[1]
+    out = np.full((T, H), np.nan)
+    for t in range(T):
+        if want is not None and not want[t]:
+            continue
+        acc = np.zeros(H)
+        for j in range(k):
+            p = pos[t * k + j]
+            if p >= 0:
+                acc = acc + w[t, j] * y[p]
+        out[t] = acc
+    return out
+
+
 def forward(x_bf16, topk_ids, topk_weights, weights, num_experts: int, inter: int,
             tokens=None, keep_acc: bool = False, experts=None, mma_type: str = "mxf4xmxf4"):
     """Run the layer.
@@ -133,22 +161,15 @@ def forward(x_bf16, topk_ids, topk_weights, weights, num_experts: int, inter: in
         acc = x_hat[tok] @ W1.T                                # step 3
         h_e = silu_mul(acc[:, :I], acc[:, I:])
         hq_e, hsf_e = act.quantize_packed(to_f32(h_e))        # step 4
-        W2 = mxfp4.dequantize(w2c, w2s)                        # [H, I]
-        y_e = act.dequantize(hq_e, hsf_e) @ W2.T               # step 5
+        y_e = expert_gemm2(hq_e, hsf_e, w2c, w2s, act)         # step 5
         h[p_idx], hq[p_idx], hsf[p_idx], y[p_idx] = h_e, hq_e, hsf_e, y_e
         if keep_acc:
             acc_all[p_idx] = acc
 
-    out = np.full((T, H), np.nan)                              # step 6
-    for t in range(T):
-        if not want[t] or experts is not None:
-            continue
-        acc = np.zeros(H)
-        for j in range(k):
-            p = pos[t * k + j]
-            if p >= 0:
-                acc = acc + w[t, j] * y[p]
-        out[t] = acc
+    if experts is None:                                        # step 6
+        out = combine(y, pos, w, want)
+    else:
+        out = np.full((T, H), np.nan)
     out_bits = np.zeros((T, H), dtype=np.uint16)
     if experts is None:
         out_bits[want] = bf16.encode(out[want])

@@ -5,6 +5,7 @@ import pytest
 import torch
 
 from oracle import bf16, mxfp4
+from oracle.forward import combine, expert_gemm2
 from oracle.route import route
 from synth import f32_to_bf16_bits as _f32_to_bf16_bits
 from tests.gpu_support import dev, dev_bf16, host_bits, layer_for, log, planes_from_rows
@@ -151,11 +152,9 @@ def test_gemm2_exact_on_injected_rows():
     # the fp32 accumulators are exact here, so the stored bf16 y is the exact
     # product rounded once to bf16 (nearest even)
     y = host_bits(ws("y", (T * k, H), torch.bfloat16)[:srt.size])
-    W2hat = mxfp4.dequantize(W[2], W[3])
-    hhat = mxfp4.dequantize(hq, hsf)
     for e in range(E):
         lo, hi = offsets[e], offsets[e + 1]
-        assert np.array_equal(y[lo:hi], bf16.encode(hhat[lo:hi] @ W2hat[e].T))
+        assert np.array_equal(y[lo:hi], bf16.encode(expert_gemm2(hq[lo:hi], hsf[lo:hi], W[2][e], W[3][e])))
 
 
 def test_combine_exact_cases():
@@ -179,11 +178,7 @@ def test_combine_exact_cases():
             layer.run_stages(16, T, topk_weights=dev(w * np.float32(scale)), out=out)
             torch.cuda.synchronize()
             outs.append(host_bits(out).copy())
-        ref = np.zeros((T, H))
-        for t in range(T):
-            for j in range(k):
-                if pos[t * k + j] >= 0:
-                    ref[t] = ref[t] + np.float64(w[t, j]) * y[pos[t * k + j]]
+        ref = combine(y, pos, w)
         if k == 1:
             assert np.array_equal(outs[0], bf16.encode(ref))   # out = bf16(y) exactly
         else:
