@@ -27,9 +27,12 @@
  *   - Arguments are validated on the host before any HIP call; a failed check
  *     returns a status code and enqueues nothing.
  *   - Faults while kernels execute surface at the caller's next synchronization.
- *   - The library is stateless apart from a per-device cache of "is this a
- *     gfx950"; calls on different streams with distinct workspaces may run
- *     concurrently.
+ *   - The library keeps only per-device caches (whether the device is a
+ *     gfx950, the dynamic-LDS limits it raised for its large-tile kernels,
+ *     the address of moe_w4a4_forward_noalloc's static scratch), each behind
+ *     a lock or an atomic; calls on different streams with distinct
+ *     workspaces may run concurrently (moe_w4a4_forward_noalloc calls share
+ *     their GPU's scratch and may not).
  *
  * MXFP4 encoding used throughout ([OCP-MX]; the scale rule is the reading
  * taken where the pages are silent):
