@@ -141,9 +141,11 @@ int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t n
   const int T = num_tokens, R = T * k;
   const int rows_hint = (int)(((int64_t)R + E - 1) / E);
   // Few rows per expert: stream each expert's weights once with the whole
-  // token tile in LDS.  Many rows: tiled GEMMs over a device-built tile list,
-  // both operands staged through LDS.
-  const bool tiled = rows_hint > kStreamMaxRows;
+  // token tile in LDS.  Many rows, or a K too long for that tile to fit a
+  // CU's LDS: tiled GEMMs over a device-built tile list, both operands staged
+  // through LDS one K step at a time.
+  const bool tiled = rows_hint > kStreamMaxRows || moe::stream_tile_lds(fp8, H, rows_hint) > moe::kCuLdsBytes ||
+                     moe::stream_tile_lds(fp8, I, rows_hint) > moe::kCuLdsBytes;
   const int tile_rows = tiled ? moe::lds_tile_rows(rows_hint) : 0;
   const int max_tiles = tiled ? moe::lds_max_tiles(R, E, tile_rows) : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -4,7 +4,21 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#ifndef MOE_STREAM_ROWS2
+#define MOE_STREAM_ROWS2 24   // token rows per pass of the streaming GEMMs' two-tile form (17..32)
+#endif
+
 namespace moe {
+
+constexpr size_t kCuLdsBytes = 160 * 1024;   // LDS of one gfx950 CU
+
+// LDS of a streaming GEMM's token tile, which spans all of K (H for GEMM1, I
+// for GEMM2): 16 rows, or MOE_STREAM_ROWS2 with two tiles (mean rows per
+// expert above 8), each K/2 code bytes (E4M3: K) plus K/32 scale bytes.
+inline size_t stream_tile_lds(bool fp8, int K, int rows_hint) {
+  const size_t rows = rows_hint > 8 ? MOE_STREAM_ROWS2 : 16;
+  return rows * ((size_t)(fp8 ? K : K / 2) + (size_t)K / 32);
+}
 
 // MOE_OK if the current HIP device is a gfx950, else MOE_ENODEVICE (cached per device).
 int check_device();

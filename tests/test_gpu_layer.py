@@ -132,6 +132,7 @@ def test_zero_tokens_is_a_no_op(tiny_layer):
 EXTREMES = [  # (E, k, T, H, I, mma_type)
     (5, 2, 37, 256, 128, 0), (7, 3, 1000, 256, 128, 0), (512, 8, 300, 256, 128, 0), (512, 16, 2000, 256, 128, 0),
     (6, 2, 40, 768, 384, 0), (6, 2, 600, 768, 384, 0), (6, 2, 40, 768, 384, 1), (6, 2, 600, 768, 384, 1),
+    (4, 1, 40, 16384, 256, 0), (4, 1, 40, 8192, 256, 1), (4, 1, 40, 256, 8192, 1),
 ]
 
 
@@ -144,7 +145,9 @@ def test_expert_count_extremes(E, k, T, H, I, mma):
     routing run as separate kernels (E512_k16).  Then H = 768, I = 384 (6 and
     3 K steps: the 2- and 1-slot weight rings and the 8- and 4-chunk token
     swizzles of the streaming GEMMs), streaming and LDS-staged, for both MMA
-    types."""
+    types.  Last, K too long for a streaming GEMM's token tile to fit a CU's
+    LDS at 10 rows per expert (H = 16384 with MXFP4 tokens; H = 8192 and
+    I = 8192 with E4M3): those run on the LDS-staged path."""
     from oracle import mxfp4
     log(f"[test] E={E} k={k} T={T} H={H} I={I} mma_type={mma}")
     rng = np.random.default_rng(1000 * E + k + 7 * H + T)
