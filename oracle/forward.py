@@ -20,9 +20,14 @@ MXFP4 operands on both sides):
 
 The top-k weights are applied in the combine only and are used as given.
 
-mma_type (the pages' two MMA types, [P3] "Implementation breakdown" items 1-3):
-"mxf4xmxf4" quantizes x (step 1) and h (step 4) to MXFP4; "fp8xfp4" quantizes
-both to MXFP8 E4M3 (oracle.mxfp8).  The weights are MXFP4 in both.
+mma_type (the pages' two MMA types, [P3] "Implementation breakdown" items 1-3,
+and the NVFP4 variant its "Motivation" names): "mxf4xmxf4" quantizes x
+(step 1) and h (step 4) to MXFP4; "fp8xfp4" quantizes both to MXFP8 E4M3
+(oracle.mxfp8); the weights are MXFP4 in both.  "nvf4xnvf4" makes x, h and the
+weights NVFP4 (oracle.nvfp4: E4M3 scales per 16 elements and an fp32 tensor
+scale), with the tensor scales passed as `tensor_scales` = (g_x, g_h,
+g_w1 [E], g_w2 [E]); the weight scale arrays then hold one byte per 16
+elements.
 
 Weight operands are passed either as arrays (w1_codes [E, 2I, H/2],
 w1_scales [E, 2I, H/32], w2_codes [E, H, I/2], w2_scales [E, H, I/32]) or as a
@@ -33,16 +38,30 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import bf16, mxfp4, mxfp8
+from . import bf16, mxfp4, mxfp8, nvfp4
 from .route import route
 
-MMA_TYPES = ("mxf4xmxf4", "fp8xfp4")
+MMA_TYPES = ("mxf4xmxf4", "fp8xfp4", "nvf4xnvf4")
 
 
 def act_format(mma_type: str):
-    """The activation format module of an MMA type: mxfp4 or mxfp8."""
-    assert mma_type in MMA_TYPES, mma_type
+    """The activation format module of an MX MMA type: mxfp4 or mxfp8."""
+    assert mma_type in MMA_TYPES[:2], mma_type
     return mxfp8 if mma_type == "fp8xfp4" else mxfp4
+
+
+class NvTensor:
+    """The NVFP4 codec of one tensor (oracle.nvfp4) with its tensor scale g,
+    with the quantize_packed / dequantize interface of the MX format modules."""
+
+    def __init__(self, g):
+        self.g = np.float32(g)
+
+    def quantize_packed(self, v):
+        return nvfp4.quantize_packed(v, self.g)
+
+    def dequantize(self, packed, scales):
+        return nvfp4.dequantize(packed, scales, self.g)
 
 
 def _expert_getter(weights):
@@ -63,11 +82,12 @@ def silu_mul(gate, up):
         return gate / (1.0 + np.exp(-gate)) * up
 
 
-def expert_gemm2(hq, hsf, w2_codes, w2_scales, act=mxfp4):
+def expert_gemm2(hq, hsf, w2_codes, w2_scales, act=mxfp4, wfmt=mxfp4):
     """Step 5 for one expert's rows: y = h_hat . W2_hat^T in fp64, h_hat the
-    dequantized requantized h (act: the activation format, oracle.mxfp4 or
-    oracle.mxfp8) and W2_hat the dequantized MXFP4 W2 [H, I]."""
-    return act.dequantize(hq, hsf) @ mxfp4.dequantize(w2_codes, w2_scales).T
+    dequantized requantized h (act: the activation format, oracle.mxfp4,
+    oracle.mxfp8 or an NvTensor) and W2_hat the dequantized W2 [H, I] (wfmt:
+    oracle.mxfp4, or the expert's NvTensor)."""
+    return act.dequantize(hq, hsf) @ wfmt.dequantize(w2_codes, w2_scales).T
 
 
 def combine(y, pos, topk_weights, want=None):
@@ -92,7 +112,8 @@ def combine(y, pos, topk_weights, want=None):
 
 
 def forward(x_bf16, topk_ids, topk_weights, weights, num_experts: int, inter: int,
-            tokens=None, keep_acc: bool = False, experts=None, mma_type: str = "mxf4xmxf4"):
+            tokens=None, keep_acc: bool = False, experts=None, mma_type: str = "mxf4xmxf4",
+            tensor_scales=None):
     """Run the layer.
 
     x_bf16        uint16 [T, H] bfloat16 bit patterns
@@ -105,9 +126,11 @@ def forward(x_bf16, topk_ids, topk_weights, weights, num_experts: int, inter: in
     experts       optional iterable of expert indices: run steps 3-5 only for
                   these experts' rows and skip step 6 (out stays NaN); used to
                   time a bounded slice of the layer.  None = all experts.
+    tensor_scales (g_x, g_h, g_w1 [E], g_w2 [E]) for mma_type "nvf4xnvf4"
 
     Returns a dict with every intermediate:
-      xq, xsf          codes of x ([T, H/2] packed E2M1, or [T, H] E4M3) and scale bytes [T, H/32]
+      xq, xsf          codes of x ([T, H/2] packed E2M1, or [T, H] E4M3) and scale bytes
+                       [T, H/32] (NVFP4: [T, H/16])
       counts, offsets, sorted_rows, pos
       acc              fp64 [n_valid, 2I] GEMM1 result (gate | up), only with keep_acc
       h                fp64 [n_valid, I] (NaN where not computed), in sorted order
@@ -124,10 +147,20 @@ def forward(x_bf16, topk_ids, topk_weights, weights, num_experts: int, inter: in
     E, I = int(num_experts), int(inter)
     get = _expert_getter(weights)
 
-    act = act_format(mma_type)
+    if mma_type == "nvf4xnvf4":
+        g_x, g_h, g_w1, g_w2 = tensor_scales
+        act_x, act = NvTensor(g_x), NvTensor(g_h)
+        w1fmt = lambda e: NvTensor(np.asarray(g_w1, dtype=np.float32)[e])   # noqa: E731
+        w2fmt = lambda e: NvTensor(np.asarray(g_w2, dtype=np.float32)[e])   # noqa: E731
+        group = nvfp4.GROUP
+    else:
+        assert tensor_scales is None
+        act_x = act = act_format(mma_type)
+        w1fmt = w2fmt = lambda e: mxfp4                                     # noqa: E731
+        group = mxfp4.GROUP
     xv = bf16.decode(x_bits)
-    xq, xsf = act.quantize_packed(xv)                          # step 1
-    x_hat = act.dequantize(xq, xsf)
+    xq, xsf = act_x.quantize_packed(xv)                        # step 1
+    x_hat = act_x.dequantize(xq, xsf)
 
     counts, offsets, sorted_rows, pos = route(ids, E)          # step 2
     nv = int(offsets[E])
@@ -140,7 +173,7 @@ def forward(x_bf16, topk_ids, topk_weights, weights, num_experts: int, inter: in
 
     h = np.full((nv, I), np.nan)
     hq = np.zeros((nv, I if act is mxfp8 else I // 2), dtype=np.uint8)
-    hsf = np.zeros((nv, I // mxfp4.GROUP), dtype=np.uint8)
+    hsf = np.zeros((nv, I // group), dtype=np.uint8)
     y = np.full((nv, H), np.nan)
     acc_all = np.full((nv, 2 * I), np.nan) if keep_acc else None
 
@@ -157,11 +190,11 @@ def forward(x_bf16, topk_ids, topk_weights, weights, num_experts: int, inter: in
             continue
         p_idx, tok = p_idx[sel], tok[sel]
         w1c, w1s, w2c, w2s = get(e)
-        W1 = mxfp4.dequantize(w1c, w1s)                        # [2I, H]
+        W1 = w1fmt(e).dequantize(w1c, w1s)                     # [2I, H]
         acc = x_hat[tok] @ W1.T                                # step 3
         h_e = silu_mul(acc[:, :I], acc[:, I:])
         hq_e, hsf_e = act.quantize_packed(to_f32(h_e))        # step 4
-        y_e = expert_gemm2(hq_e, hsf_e, w2c, w2s, act)         # step 5
+        y_e = expert_gemm2(hq_e, hsf_e, w2c, w2s, act, w2fmt(e))   # step 5
         h[p_idx], hq[p_idx], hsf[p_idx], y[p_idx] = h_e, hq_e, hsf_e, y_e
         if keep_acc:
             acc_all[p_idx] = acc

@@ -1,11 +1,12 @@
 """Test-side assembly of oracle inputs: synthetic fp32 weights quantized by the
-oracle's own MXFP4 quantizer (never by the device path)."""
+oracle's own MXFP4 or NVFP4 quantizer (never by the device path), and the
+NVFP4 tensor scales the tests use."""
 import functools
 
 import numpy as np
 
 import synth
-from oracle import mxfp4
+from oracle import mxfp4, nvfp4
 
 
 def quantize_expert(cfg, e):
@@ -40,3 +41,32 @@ def all_experts_parallel(cfg, workers=8):
     with concurrent.futures.ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
         parts = list(ex.map(_quantize_expert_job, [(cfg, e) for e in range(cfg.experts)], chunksize=4))
     return lambda e: parts[e]
+
+
+def quantize_expert_nv(cfg, e):
+    """Expert e's NVFP4 weights, each matrix with the tensor scale of its own
+    absolute maximum: ((w1c, w1s, w2c, w2s), g_w1, g_w2)."""
+    w1, w2 = synth.expert_weights_f32(cfg, e)
+    g1, g2 = nvfp4.tensor_scale(np.abs(w1).max()), nvfp4.tensor_scale(np.abs(w2).max())
+    w1c, w1s = nvfp4.quantize_packed(w1, g1)
+    w2c, w2s = nvfp4.quantize_packed(w2, g2)
+    return (w1c, w1s, w2c, w2s), g1, g2
+
+
+def all_expert_weights_nv(cfg):
+    """(stacked (w1c, w1s, w2c, w2s), g_w1 fp32 [E], g_w2 fp32 [E])."""
+    parts = [quantize_expert_nv(cfg, e) for e in range(cfg.experts)]
+    W = tuple(np.stack([p[0][i] for p in parts]) for i in range(4))
+    return W, np.array([p[1] for p in parts], np.float32), np.array([p[2] for p in parts], np.float32)
+
+
+# Calibration bound of |h| per layer shape (hidden size): above the largest
+# |silu(gate) * up| of the synthetic layers, so no block of h saturates.
+H_AMAX = {256: 2.0, 4096: 64.0}
+
+
+def nv_act_scales(cfg, x_bits):
+    """(g_x, g_h): x's tensor scale from its absolute maximum, h's from the
+    shape's calibration bound."""
+    return (nvfp4.tensor_scale(np.abs(synth.bf16_bits_to_f32(x_bits)).max()),
+            nvfp4.tensor_scale(H_AMAX[cfg.hidden]))
