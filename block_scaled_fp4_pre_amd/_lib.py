@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_w4a4.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ECAPACITY, MOE_EWORKSPACE, MOE_ENODEVICE, MOE_EHIP, MOE_ESCRATCH = range(8)
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
-MOE_MMA_MXF4_X_MXF4, MOE_MMA_FP8_X_MXF4 = 0, 1
+MOE_MMA_MXF4_X_MXF4, MOE_MMA_FP8_X_MXF4, MOE_MMA_NVF4_X_NVF4 = 0, 1, 2
 MOE_ACT_SWIGLU = 0
 MOE_STAGE_QUANT, MOE_STAGE_ROUTE, MOE_STAGE_GEMM1, MOE_STAGE_GEMM2, MOE_STAGE_COMBINE = 1, 2, 4, 8, 16
 MOE_STAGE_ALL = 31
@@ -24,7 +24,9 @@ MOE_STAGE_ALL = 31
 EXPORTED = (
     "moe_w4a4_query",
     "moe_w4a4_quantize",
+    "moe_w4a4_quantize_nvfp4",
     "moe_w4a4_prepare_weights",
+    "moe_w4a4_prepare_weights_nvfp4",
     "moe_w4a4_forward",
     "moe_w4a4_forward_noalloc",
     "moe_w4a4_status_string",
@@ -66,7 +68,10 @@ _i32 = ctypes.c_int32
 _CFG = ctypes.POINTER(moe_w4a4_cfg)
 _lib.moe_w4a4_query.argtypes = [_CFG, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]
 _lib.moe_w4a4_quantize.argtypes = [_i32, _P, ctypes.c_int64, _i32, _P, _P, _P]
+_lib.moe_w4a4_quantize_nvfp4.argtypes = [_i32, _P, ctypes.c_int64, _i32, ctypes.c_float, _P, _P, _P]
 _lib.moe_w4a4_prepare_weights.argtypes = [_CFG, _P, _P, _P, _P, _P, _sz, _P]
+_lib.moe_w4a4_prepare_weights_nvfp4.argtypes = [_CFG, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_float, _P,
+                                                _sz, _P]
 _lib.moe_w4a4_forward.argtypes = [_CFG, _P, _i32, _P, _P, _P, _P, _P, _sz, _P]
 _lib.moe_w4a4_forward_noalloc.argtypes = [_CFG, _P, _i32, _P, _P, _P, _P, _P]
 _lib.moe_w4a4_status_string.argtypes = [ctypes.c_int]
@@ -151,9 +156,17 @@ def _stream(stream) -> int | None:
 
 
 def make_cfg(hidden: int, inter: int, num_experts: int, topk: int, max_tokens: int,
-             group_size: int = 32, mma_type: int = MOE_MMA_MXF4_X_MXF4,
+             group_size: int | None = None, mma_type: int = MOE_MMA_MXF4_X_MXF4,
              activation: int = MOE_ACT_SWIGLU) -> moe_w4a4_cfg:
+    """group_size None: the MMA type's own (16 for NVFP4, else 32)."""
+    if group_size is None:
+        group_size = 16 if mma_type == MOE_MMA_NVF4_X_NVF4 else 32
     return moe_w4a4_cfg(hidden, inter, num_experts, topk, max_tokens, group_size, mma_type, activation)
+
+
+def scale_group(cfg) -> int:
+    """Elements per scale byte of cfg's MMA type."""
+    return 16 if cfg.mma_type == MOE_MMA_NVF4_X_NVF4 else 32
 
 
 def moe_w4a4_query(cfg: moe_w4a4_cfg):
@@ -187,6 +200,43 @@ def moe_w4a4_quantize(src, codes, scales, stream=None) -> None:
     _expect(scales, "scales", ("uint8",), (rows, cols // 32))
     _check(_lib.moe_w4a4_quantize(dt, _ptr(src), rows, cols, _ptr(codes), _ptr(scales), _stream(stream)),
            "moe_w4a4_quantize")
+
+
+def moe_w4a4_quantize_nvfp4(src, g: float, codes, scales, stream=None) -> None:
+    """NVFP4 with tensor scale g: src device bf16 (or uint16 bit patterns) /
+    float32 [rows, cols]; codes uint8 [rows, cols/2]; scales uint8 [rows, cols/16]."""
+    import torch
+    if src.dtype in (torch.bfloat16, torch.uint16, torch.int16):
+        dt = 0
+    elif src.dtype == torch.float32:
+        dt = 1
+    else:
+        raise ValueError(f"unsupported dtype {src.dtype}")
+    if src.dim() != 2:
+        raise ValueError(f"src: expected [rows, cols], got shape {tuple(src.shape)}")
+    rows, cols = src.shape
+    _expect(src, "src", ("bfloat16", "int16", "uint16", "float32"))
+    _expect(codes, "codes", ("uint8",), (rows, cols // 2))
+    _expect(scales, "scales", ("uint8",), (rows, cols // 16))
+    _check(_lib.moe_w4a4_quantize_nvfp4(dt, _ptr(src), rows, cols, float(g), _ptr(codes), _ptr(scales),
+                                        _stream(stream)), "moe_w4a4_quantize_nvfp4")
+
+
+def moe_w4a4_prepare_weights_nvfp4(cfg, w1_codes, w1_scales, w1_tensor_scales, w2_codes, w2_scales,
+                                   w2_tensor_scales, x_tensor_scale: float, h_tensor_scale: float, prepared,
+                                   stream=None) -> None:
+    E, H, I = cfg.num_experts, cfg.hidden, cfg.inter
+    _expect(w1_codes, "w1_codes", ("uint8",), (E, 2 * I, H // 2))
+    _expect(w1_scales, "w1_scales", ("uint8",), (E, 2 * I, H // 16))
+    _expect(w1_tensor_scales, "w1_tensor_scales", ("float32",), (E,))
+    _expect(w2_codes, "w2_codes", ("uint8",), (E, H, I // 2))
+    _expect(w2_scales, "w2_scales", ("uint8",), (E, H, I // 16))
+    _expect(w2_tensor_scales, "w2_tensor_scales", ("float32",), (E,))
+    _expect(prepared, "prepared", ("uint8",))
+    _check(_lib.moe_w4a4_prepare_weights_nvfp4(
+        ctypes.byref(cfg), _ptr(w1_codes), _ptr(w1_scales), _ptr(w1_tensor_scales), _ptr(w2_codes), _ptr(w2_scales),
+        _ptr(w2_tensor_scales), float(x_tensor_scale), float(h_tensor_scale), _ptr(prepared),
+        prepared.numel() * prepared.element_size(), _stream(stream)), "moe_w4a4_prepare_weights_nvfp4")
 
 
 def moe_w4a4_prepare_weights(cfg, w1_codes, w1_scales, w2_codes, w2_scales, prepared, stream=None) -> None:

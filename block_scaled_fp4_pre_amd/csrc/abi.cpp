@@ -111,6 +111,36 @@ int moe_w4a4_quantize(int32_t src_dtype, const void* src, int64_t rows, int32_t 
                                          static_cast<hipStream_t>(stream)));
 }
 
+int moe_w4a4_quantize_nvfp4(int32_t src_dtype, const void* src, int64_t rows, int32_t cols, float g,
+                            uint8_t* codes, uint8_t* scales, void* stream) {
+  bool noop = false;
+  const int st = moe::check_quantize_args(src_dtype, src, rows, cols, codes, scales, &noop);
+  if (st != MOE_OK) return st;
+  if (!moe::nv_scale_ok(g)) return MOE_EINVAL;
+  if (noop) return MOE_OK;
+  const int dv = moe::check_device();
+  if (dv != MOE_OK) return dv;
+  return hip_status(moe::launch_quantize_nv(src_dtype == 0, src, rows * (int64_t)(cols / 32), g, nullptr, codes,
+                                            scales, static_cast<hipStream_t>(stream)));
+}
+
+int moe_w4a4_prepare_weights_nvfp4(const moe_w4a4_cfg* cfg, const uint8_t* w1_codes, const uint8_t* w1_scales,
+                                   const float* w1_tensor_scales, const uint8_t* w2_codes, const uint8_t* w2_scales,
+                                   const float* w2_tensor_scales, float x_tensor_scale, float h_tensor_scale,
+                                   void* prepared, size_t prepared_bytes, void* stream) {
+  int st = moe::check_prepare_nv_args(cfg, w1_codes, w1_scales, w1_tensor_scales, w2_codes, w2_scales,
+                                      w2_tensor_scales, x_tensor_scale, h_tensor_scale, prepared, prepared_bytes);
+  if (st != MOE_OK) return st;
+  st = moe::check_device();
+  if (st != MOE_OK) return st;
+  const moe::PreparedLayout P = moe::prepared_layout(cfg);
+  uint8_t* base = static_cast<uint8_t*>(prepared);
+  return hip_status(moe::launch_prepare_nv(w1_codes, w1_scales, w1_tensor_scales, w2_codes, w2_scales,
+                                           w2_tensor_scales, x_tensor_scale, h_tensor_scale, cfg->hidden, cfg->inter,
+                                           cfg->num_experts, base + P.w1c, base + P.w1s, base + P.w2c, base + P.w2s,
+                                           reinterpret_cast<float*>(base + P.gsc), static_cast<hipStream_t>(stream)));
+}
+
 int moe_w4a4_prepare_weights(const moe_w4a4_cfg* cfg, const uint8_t* w1_codes, const uint8_t* w1_scales,
                              const uint8_t* w2_codes, const uint8_t* w2_scales, void* prepared,
                              size_t prepared_bytes, void* stream) {
@@ -138,14 +168,17 @@ int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t n
 
   const int H = cfg->hidden, I = cfg->inter, E = cfg->num_experts, k = cfg->topk;
   const bool fp8 = cfg->mma_type == MOE_MMA_FP8_X_MXF4;   // E4M3 activations
+  const bool nv = cfg->mma_type == MOE_MMA_NVF4_X_NVF4;   // NVFP4 activations and weights
+  const int act = nv ? 2 : fp8 ? 1 : 0;
   const int T = num_tokens, R = T * k;
   const int rows_hint = (int)(((int64_t)R + E - 1) / E);
   // Few rows per expert: stream each expert's weights once with the whole
   // token tile in LDS.  Many rows, or a K too long for that tile to fit a
   // CU's LDS: tiled GEMMs over a device-built tile list, both operands staged
-  // through LDS one K step at a time.
-  const bool tiled = rows_hint > kStreamMaxRows || moe::stream_tile_lds(fp8, H, rows_hint) > moe::kCuLdsBytes ||
-                     moe::stream_tile_lds(fp8, I, rows_hint) > moe::kCuLdsBytes;
+  // through LDS one K step at a time.  NVFP4 has the streaming GEMMs only
+  // (several passes over the weights for many rows; check_cfg bounds K).
+  const bool tiled = !nv && (rows_hint > kStreamMaxRows || moe::stream_tile_lds(fp8, H, rows_hint) > moe::kCuLdsBytes ||
+                             moe::stream_tile_lds(fp8, I, rows_hint) > moe::kCuLdsBytes);
   const int tile_rows = tiled ? moe::lds_tile_rows(rows_hint) : 0;
   const int max_tiles = tiled ? moe::lds_max_tiles(R, E, tile_rows) : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -166,15 +199,20 @@ int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t n
   uint16_t* y = reinterpret_cast<uint16_t*>(ws + L.y);
   const moe::PreparedLayout P = moe::prepared_layout(cfg);
   const uint8_t* pw = static_cast<const uint8_t*>(prepared);
+  // NVFP4 tensor scales [g_w1[E], g_w2[E], g_x, g_h] (check_stage_args: prepared
+  // is given whenever a stage that reads them runs)
+  const float* gsc = nv && pw != nullptr ? reinterpret_cast<const float*>(pw + P.gsc) : nullptr;
+  const float* gx = gsc != nullptr ? gsc + 2 * E : nullptr;
 
   if ((stages & MOE_STAGE_QUANT) && (stages & MOE_STAGE_ROUTE) && R <= moe::kPredispatchMaxRows) {
     // pre-dispatch in one launch: one block routes, the others quantize
-    st = hip_status(moe::launch_predispatch(fp8, x, (int64_t)T * (H / 32), xq, xsf, topk_ids, R, E, counts, offsets,
-                                            sorted_rows, pos, tile_rows, tiles, num_tiles, s));
+    st = hip_status(moe::launch_predispatch(act, x, (int64_t)T * (H / 32), gx, xq, xsf, topk_ids, R, E, counts,
+                                            offsets, sorted_rows, pos, tile_rows, tiles, num_tiles, s));
     if (st != MOE_OK) return st;
   } else {
     if (stages & MOE_STAGE_QUANT) {
-      st = hip_status(moe::launch_quantize(true, fp8, x, (int64_t)T * (H / 32), xq, xsf, s));
+      st = hip_status(nv ? moe::launch_quantize_nv(true, x, (int64_t)T * (H / 32), 0.0f, gx, xq, xsf, s)
+                         : moe::launch_quantize(true, fp8, x, (int64_t)T * (H / 32), xq, xsf, s));
       if (st != MOE_OK) return st;
     }
     if (stages & MOE_STAGE_ROUTE) {
@@ -188,7 +226,11 @@ int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t n
     st = hip_status(moe::launch_sorted_scales(xsf, sorted_rows, offsets, E, R, H, k, hrows, xsf_planes, s));
     if (st != MOE_OK) return st;
   }
-  if (stages & MOE_STAGE_GEMM1) {
+  if ((stages & MOE_STAGE_GEMM1) && nv) {
+    st = hip_status(moe::launch_gemm1_nv(pw + P.w1c, pw + P.w1s, gsc, xq, xsf, counts, offsets, sorted_rows, H, I, E,
+                                         k, rows_hint, hrows, hq, hsf, gemm1_acc, s));
+    if (st != MOE_OK) return st;
+  } else if (stages & MOE_STAGE_GEMM1) {
     st = hip_status(tiled ? moe::launch_gemm1_lds(fp8, pw + P.w1c, pw + P.w1s, xq, xsf_planes, counts, offsets,
                                                   sorted_rows, tiles, num_tiles, max_tiles, rows_hint, H, I, k,
                                                   hrows, hq, hsf, gemm1_acc, s)
@@ -196,7 +238,11 @@ int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t n
                                               H, I, E, k, rows_hint, hrows, hq, hsf, gemm1_acc, s));
     if (st != MOE_OK) return st;
   }
-  if (stages & MOE_STAGE_GEMM2) {
+  if ((stages & MOE_STAGE_GEMM2) && nv) {
+    st = hip_status(moe::launch_gemm2_nv(pw + P.w2c, pw + P.w2s, gsc, hq, hsf, counts, offsets, H, I, E, rows_hint,
+                                         hrows, y, s));
+    if (st != MOE_OK) return st;
+  } else if (stages & MOE_STAGE_GEMM2) {
     st = hip_status(tiled ? moe::launch_gemm2_lds(fp8, pw + P.w2c, pw + P.w2s, hq, hsf, counts, offsets, tiles,
                                                   num_tiles, max_tiles, rows_hint, H, I, hrows, y, s)
                           : moe::launch_gemm2(fp8, pw + P.w2c, pw + P.w2s, hq, hsf, counts, offsets, H, I, E,

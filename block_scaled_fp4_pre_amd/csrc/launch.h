@@ -27,6 +27,10 @@ int check_device();
 // fp8: MXFP8 E4M3 codes instead (the fp8xfp4 MMA type's activations, bf16 only).
 hipError_t launch_quantize(bool src_is_bf16, bool fp8, const void* src, int64_t ngroups,
                            uint8_t* codes, uint8_t* scales, hipStream_t stream);
+// NVFP4 under tensor scale gs (or *gsp, a device address, when gsp is not
+// null): per 32-element group 16 code bytes and 2 scale bytes.
+hipError_t launch_quantize_nv(bool src_is_bf16, const void* src, int64_t ngroups, float gs, const float* gsp,
+                              uint8_t* codes, uint8_t* scales, hipStream_t stream);
 
 // Stage S1b: stable counting sort of R routed rows over E experts.  With
 // tile_rows > 0 it also lists the (expert, first row) tiles of tile_rows rows
@@ -36,10 +40,11 @@ hipError_t launch_route(const int32_t* ids, int R, int E, int32_t* hist, int32_t
                         int32_t* num_tiles, hipStream_t stream);
 
 // Stages S1a + S1b in one launch: block 0 routes all R <= kPredispatchMaxRows
-// rows, the other blocks quantize the bf16 tokens.
+// rows, the other blocks quantize the bf16 tokens (act: 0 MXFP4, 1 MXFP8
+// E4M3, 2 NVFP4 under the tensor scale at device address gx).
 constexpr int kPredispatchMaxRows = 8192;
-hipError_t launch_predispatch(bool fp8, const uint16_t* x, int64_t ngroups, uint8_t* xq, uint8_t* xsf,
-                              const int32_t* ids, int R, int E, int32_t* counts, int32_t* offsets,
+hipError_t launch_predispatch(int act, const uint16_t* x, int64_t ngroups, const float* gx, uint8_t* xq,
+                              uint8_t* xsf, const int32_t* ids, int R, int E, int32_t* counts, int32_t* offsets,
                               int32_t* sorted_rows, int32_t* pos, int tile_rows, int2* tiles, int32_t* num_tiles,
                               hipStream_t stream);
 
@@ -81,6 +86,20 @@ hipError_t launch_gemm2(bool fp8, const uint8_t* w2_codes, const uint8_t* w2_sca
                         const uint8_t* hsf, const int32_t* counts, const int32_t* offsets, int H,
                         int I, int E, int rows_hint, int hrows, uint16_t* y, hipStream_t stream);
 
+// Stages S2 and S3 of the NVFP4 type (gemm_nv.hip): the weight-streaming
+// GEMMs on the dense bf16 MFMA, any rows per expert (passes of 16 rows, or of
+// kNvStreamRows with two token tiles).  gsc: the prepared tensor scales
+// [g_w1[E], g_w2[E], g_x, g_h] on the device.  hsf holds the scale bytes of h
+// in dword planes: unit u's two bytes of sorted row p at ((u/2) * hrows + p)
+// * 4 + (u%2) * 2.
+hipError_t launch_gemm1_nv(const uint8_t* w1_codes, const uint8_t* w1_scales, const float* gsc, const uint8_t* xq,
+                           const uint8_t* xsf, const int32_t* counts, const int32_t* offsets,
+                           const int32_t* sorted_rows, int H, int I, int E, int k, int rows_hint, int hrows,
+                           uint8_t* hq, uint8_t* hsf, float* acc_out, hipStream_t stream);
+hipError_t launch_gemm2_nv(const uint8_t* w2_codes, const uint8_t* w2_scales, const float* gsc, const uint8_t* hq,
+                           const uint8_t* hsf, const int32_t* counts, const int32_t* offsets, int H, int I, int E,
+                           int rows_hint, int hrows, uint16_t* y, hipStream_t stream);
+
 // Stage S4: top-k weighted combine back to token order, bf16 output.
 hipError_t launch_combine(const uint16_t* y, const int32_t* pos, const float* w, int T, int H, int k,
                           uint16_t* out, hipStream_t stream);
@@ -89,5 +108,11 @@ hipError_t launch_combine(const uint16_t* y, const int32_t* pos, const float* w,
 hipError_t launch_prepare(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* w2c,
                           const uint8_t* w2s, int H, int I, int E, uint8_t* p_w1c, uint8_t* p_w1s,
                           uint8_t* p_w2c, uint8_t* p_w2s, hipStream_t stream);
+// The same for NVFP4 weights (scale bytes per 16, nvfp4.h), and the tensor
+// scales into gsc = [g_w1[E], g_w2[E], g_x, g_h].
+hipError_t launch_prepare_nv(const uint8_t* w1c, const uint8_t* w1s, const float* gw1, const uint8_t* w2c,
+                             const uint8_t* w2s, const float* gw2, float gx, float gh, int H, int I, int E,
+                             uint8_t* p_w1c, uint8_t* p_w1s, uint8_t* p_w2c, uint8_t* p_w2s, float* gsc,
+                             hipStream_t stream);
 
 }  // namespace moe

@@ -13,8 +13,8 @@
 // at a time, in order: the rank among the sub-chunk's rows of the same expert
 // comes from a 64-lane match (one ballot per id bit), and the lowest lane of
 // each expert advances the wave's slot for the next sub-chunk.  Blocks 1..
-// quantize one 32-element group of x per thread meanwhile (E2M1, or E4M3 for
-// the fp8xfp4 MMA type).
+// quantize one 32-element group of x per thread meanwhile (E2M1, E4M3 for the
+// fp8xfp4 MMA type, or NVFP4 under the layer's tensor scale g_x).
 #include "launch.h"
 #include "quant_group.h"
 #include "route_common.h"
@@ -23,16 +23,23 @@ namespace moe {
 
 constexpr int kPredispatchSubs = kPredispatchMaxRows / kRouteRows;  // 64-row sub-chunks per wave, at most
 
-template <bool F8>
+// ACT: the activation format, 0 = MXFP4, 1 = MXFP8 E4M3, 2 = NVFP4 with the
+// tensor scale *gx.
+template <int ACT>
 __global__ void __launch_bounds__(kRouteRows) predispatch_kernel(
-    const uint16_t* __restrict__ x, int64_t ngroups, uint8_t* __restrict__ xq, uint8_t* __restrict__ xsf,
-    const int32_t* __restrict__ ids, int R, int E, int nbits, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_rows, int32_t* __restrict__ pos, int tile_rows,
-    int2* __restrict__ tiles, int32_t* __restrict__ num_tiles) {
+    const uint16_t* __restrict__ x, int64_t ngroups, const float* __restrict__ gx, uint8_t* __restrict__ xq,
+    uint8_t* __restrict__ xsf, const int32_t* __restrict__ ids, int R, int E, int nbits,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_rows,
+    int32_t* __restrict__ pos, int tile_rows, int2* __restrict__ tiles, int32_t* __restrict__ num_tiles) {
   const int tid = threadIdx.x;
   if (blockIdx.x > 0) {
     const int64_t g = (int64_t)(blockIdx.x - 1) * kRouteRows + tid;
-    if (g < ngroups) quantize_group<true, F8>(x, g, xq, xsf);
+    if (g < ngroups) {
+      if constexpr (ACT == 2)
+        quantize_group_nv<true>(x, g, xq, xsf, *gx);
+      else
+        quantize_group<true, ACT == 1>(x, g, xq, xsf);
+    }
     return;
   }
   extern __shared__ int smem[];
@@ -98,15 +105,15 @@ __global__ void __launch_bounds__(kRouteRows) predispatch_kernel(
   }
 }
 
-hipError_t launch_predispatch(bool fp8, const uint16_t* x, int64_t ngroups, uint8_t* xq, uint8_t* xsf,
-                              const int32_t* ids, int R, int E, int32_t* counts, int32_t* offsets,
+hipError_t launch_predispatch(int act, const uint16_t* x, int64_t ngroups, const float* gx, uint8_t* xq,
+                              uint8_t* xsf, const int32_t* ids, int R, int E, int32_t* counts, int32_t* offsets,
                               int32_t* sorted_rows, int32_t* pos, int tile_rows, int2* tiles, int32_t* num_tiles,
                               hipStream_t stream) {
   const int64_t qblocks = (ngroups + kRouteRows - 1) / kRouteRows;
   const size_t lds = (size_t)(kRouteWaves * E + kRouteWaves) * sizeof(int);
-  auto kern = fp8 ? predispatch_kernel<true> : predispatch_kernel<false>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(1 + qblocks)), dim3(kRouteRows), lds, stream, x, ngroups, xq, xsf, ids, R,
-                     E, id_bits(E), counts, offsets, sorted_rows, pos, tile_rows, tiles, num_tiles);
+  auto kern = act == 2 ? predispatch_kernel<2> : act == 1 ? predispatch_kernel<1> : predispatch_kernel<0>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(1 + qblocks)), dim3(kRouteRows), lds, stream, x, ngroups, gx, xq, xsf,
+                     ids, R, E, id_bits(E), counts, offsets, sorted_rows, pos, tile_rows, tiles, num_tiles);
   return hipGetLastError();
 }
 

@@ -6,6 +6,7 @@
 // device_common.h.
 #pragma once
 #include "device_common.h"
+#include "nvfp4.h"
 
 namespace moe {
 
@@ -13,10 +14,8 @@ namespace moe {
 // E2M1 codes at codes + 16g (F8: 32 bytes of E4M3 codes at codes + 32g, the
 // fp8xfp4 MMA type's activations, e4m3.h) and one scale byte at scales[g].
 // 64 B (bf16) or 128 B (fp32) in as 16-byte loads.
-template <bool BF16, bool F8 = false>
-__device__ __forceinline__ void quantize_group(const void* __restrict__ src, int64_t g,
-                                               uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
-  float v[32];
+template <bool BF16>
+__device__ __forceinline__ void load_group(const void* __restrict__ src, int64_t g, float (&v)[32]) {
   if (BF16) {
     const uint4* p = reinterpret_cast<const uint4*>(src) + g * 4;
 #pragma unroll
@@ -37,6 +36,13 @@ __device__ __forceinline__ void quantize_group(const void* __restrict__ src, int
       v[4 * q] = w.x; v[4 * q + 1] = w.y; v[4 * q + 2] = w.z; v[4 * q + 3] = w.w;
     }
   }
+}
+
+template <bool BF16, bool F8 = false>
+__device__ __forceinline__ void quantize_group(const void* __restrict__ src, int64_t g,
+                                               uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  float v[32];
+  load_group<BF16>(src, g, v);
   uint32_t amax = 0;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = max(amax, __float_as_uint(v[i]) & 0x7FFFFFFFu);
@@ -64,6 +70,37 @@ __device__ __forceinline__ void quantize_group(const void* __restrict__ src, int
   }
   reinterpret_cast<uint4*>(codes)[g] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
   scales[g] = (uint8_t)(e + 127);
+}
+
+// NVFP4 (nvfp4.h): group g of 32 values -> 16 bytes of packed E2M1 codes at
+// codes + 16g and the E4M3 scale bytes of its two 16-element blocks at
+// scales + 2g (the first block's in the low byte), under tensor scale gs.
+template <bool BF16>
+__device__ __forceinline__ void quantize_group_nv(const void* __restrict__ src, int64_t g,
+                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                  float gs) {
+  float v[32];
+  load_group<BF16>(src, g, v);
+  uint32_t packed[4];
+  uint32_t sc[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[16 * b + i]));
+    sc[b] = nv_scale_code(amax, gs);
+    const float inv = nv_inv(sc[b], gs);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const float* p = v + 16 * b + 8 * q;
+      uint32_t w = nv_pack2<0>(0u, p[0], p[1], inv);
+      w = nv_pack2<1>(w, p[2], p[3], inv);
+      w = nv_pack2<2>(w, p[4], p[5], inv);
+      packed[2 * b + q] = nv_pack2<3>(w, p[6], p[7], inv);
+    }
+  }
+  reinterpret_cast<uint4*>(codes)[g] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  reinterpret_cast<uint16_t*>(scales)[g] = (uint16_t)(sc[0] | (sc[1] << 8));
 }
 
 }  // namespace moe

@@ -16,6 +16,15 @@ constexpr int kMaxExperts = 512;
 constexpr int kMaxTopk = 16;
 constexpr int kRouteRowsPerBlock = 1024;   // rows per block of the multi-block route (per-block histograms)
 
+// NVFP4 (MOE_MMA_NVF4_X_NVF4): token rows per pass of its streaming GEMMs
+// with two token tiles, and the longest K (hidden or inter) whose token tile
+// (rows * (K/2 code bytes + K/16 scale bytes)) fits a CU's 160 KiB of LDS.
+constexpr int kNvStreamRows = 24;
+constexpr int kNvMaxK = 12032;
+// Range of an NVFP4 tensor scale: every fp32 step of the encoding stays finite.
+constexpr float kNvScaleMin = 0x1p-100f;
+constexpr float kNvScaleMax = 0x1p100f;
+
 // Bytes after the last region of the prepared weights.  The streaming GEMMs
 // keep a ring of up to 4 K steps of weight loads in flight per wave and issue
 // the ring's refills past a unit's last step without a branch; for the last
@@ -23,10 +32,15 @@ constexpr int kRouteRowsPerBlock = 1024;   // rows per block of the multi-block 
 // 16 KiB past the end of the codes, into the following regions and this tail.
 constexpr uint64_t kPreparedTailBytes = 64 * 1024;
 
-// Region offsets of the prepared weights (256-byte aligned), tail included in total.
+// Region offsets of the prepared weights (256-byte aligned), tail included in
+// total.  gsc: the NVFP4 tensor scales, fp32 [g_w1[E], g_w2[E], g_x, g_h]
+// (empty for the MX types).
 struct PreparedLayout {
-  uint64_t w1c, w1s, w2c, w2s, total;
+  uint64_t w1c, w1s, w2c, w2s, gsc, total;
 };
+
+// Elements per scale byte of cfg's MMA type: 16 for NVFP4, else 32.
+inline int scale_group(const moe_w4a4_cfg* c) { return c->mma_type == MOE_MMA_NVF4_X_NVF4 ? 16 : 32; }
 
 int check_cfg(const moe_w4a4_cfg* c);
 PreparedLayout prepared_layout(const moe_w4a4_cfg* c);      // c must pass check_cfg
@@ -37,9 +51,18 @@ moe_w4a4_ws_layout ws_layout(const moe_w4a4_cfg* c);        // c must pass check
 int check_quantize_args(int32_t src_dtype, const void* src, int64_t rows, int32_t cols, const void* codes,
                         const void* scales, bool* noop);
 
-// Arguments of moe_w4a4_prepare_weights.
+// An NVFP4 tensor scale passed by value: finite and in [kNvScaleMin, kNvScaleMax].
+bool nv_scale_ok(float g);
+
+// Arguments of moe_w4a4_prepare_weights (MX types only).
 int check_prepare_args(const moe_w4a4_cfg* cfg, const void* w1_codes, const void* w1_scales,
                        const void* w2_codes, const void* w2_scales, const void* prepared, size_t prepared_bytes);
+
+// Arguments of moe_w4a4_prepare_weights_nvfp4 (NVFP4 configurations only).
+int check_prepare_nv_args(const moe_w4a4_cfg* cfg, const void* w1_codes, const void* w1_scales,
+                          const void* w1_tensor_scales, const void* w2_codes, const void* w2_scales,
+                          const void* w2_tensor_scales, float x_tensor_scale, float h_tensor_scale,
+                          const void* prepared, size_t prepared_bytes);
 
 // Arguments of moe_w4a4_run_stages (and so of moe_w4a4_forward, which runs
 // every stage).  *noop is set when there is nothing to enqueue (no tokens or

@@ -18,6 +18,9 @@
  *        load time for the chosen mma_type).
  *   [OCP-MX] OCP Microscaling Formats (MX) v1.0: E2M1 element and E8M0 scale
  *        encodings.
+ *   [P3] "Motivation" names an NVFP4 mega-MoE as well; MOE_MMA_NVF4_X_NVF4
+ *        below is that variant in the public NVFP4 format (E2M1 elements, an
+ *        E4M3 scale per 16 elements, an fp32 scale per tensor).
  *
  * Conventions for every entry point
  *   - Device pointers are allocated and owned by the caller; the library never
@@ -73,15 +76,27 @@ enum {
  *   MOE_MMA_FP8_X_MXF4  ("fp8xfp4"):  x and h are MXFP8 E4M3 ([OCP-MX]), one
  *     code a byte, with the same UE8M0 scale per 32 (scale 2^e: the smallest
  *     with amax <= 448 * 2^e); ties to the even mantissa, sign kept.
- * The weights are MXFP4 in both. */
-enum { MOE_MMA_MXF4_X_MXF4 = 0, MOE_MMA_FP8_X_MXF4 = 1 };
+ * The weights are MXFP4 in both.
+ *   MOE_MMA_NVF4_X_NVF4 ("nvf4xnvf4", group_size 16): x, h and the weights are
+ *     NVFP4: E2M1 codes (two a byte, as above), one E4M3 scale byte per 16
+ *     elements along K (sign bit clear) and one fp32 tensor scale g per
+ *     tensor (x and h per layer, W1 and W2 per expert), value = e2m1 * e4m3
+ *     * g.  A block with absolute maximum a gets the E4M3 code nearest to
+ *     min(f32(a / f32(6*g)), 448) (ties to even); its codes are the E2M1
+ *     codes nearest to f32(v * inv) clamped to [-6, 6], inv = 0 for a zero
+ *     scale, else f32(1 / f32(e4m3 * g)) (ties to even, sign kept).  The
+ *     GEMMs run the 16-bit MFMA on the exact products e2m1 * e4m3 in
+ *     bfloat16 and apply the tensor scales to the fp32 sums.  hidden and
+ *     inter are limited to 12032 (the token tile of the weight-streaming
+ *     GEMMs, the only ones built for this type, must fit a CU's LDS). */
+enum { MOE_MMA_MXF4_X_MXF4 = 0, MOE_MMA_FP8_X_MXF4 = 1, MOE_MMA_NVF4_X_NVF4 = 2 };
 /* activation: SwiGLU, silu(gate) * up, with no clamp or bias ([P3]). */
 enum { MOE_ACT_SWIGLU = 0 };
 
 /* Layer configuration.  Supported: hidden % 256 == 0, inter % 128 == 0,
  * 1 <= num_experts <= 512, 1 <= topk <= 16, 0 <= max_tokens and
- * max_tokens * topk < 2^31, group_size == 32, mma_type one of the two above,
- * activation == MOE_ACT_SWIGLU.  max_tokens is the capacity the workspace is
+ * max_tokens * topk < 2^31, group_size == 32 for the two MX types and 16 for
+ * NVFP4, mma_type one of the three above, activation == MOE_ACT_SWIGLU.  max_tokens is the capacity the workspace is
  * sized for (num_max_tokens_per_rank in [P3]); each forward passes the live
  * token count. */
 typedef struct moe_w4a4_cfg {
@@ -90,8 +105,8 @@ typedef struct moe_w4a4_cfg {
   int32_t num_experts;  /* E */
   int32_t topk;         /* k */
   int32_t max_tokens;   /* capacity */
-  int32_t group_size;   /* must be 32 */
-  int32_t mma_type;     /* MOE_MMA_MXF4_X_MXF4 or MOE_MMA_FP8_X_MXF4 */
+  int32_t group_size;   /* 32 (MX types) or 16 (NVFP4) */
+  int32_t mma_type;     /* MOE_MMA_MXF4_X_MXF4, MOE_MMA_FP8_X_MXF4 or MOE_MMA_NVF4_X_NVF4 */
   int32_t activation;   /* MOE_ACT_SWIGLU */
 } moe_w4a4_cfg;
 
@@ -100,8 +115,9 @@ typedef struct moe_w4a4_cfg {
  * "Key source snippets", _get_mega_moe_symm_buffer: one buffer per
  * (num_max_tokens_per_rank, experts, topk, hidden, intermediate_hidden,
  * mma_type, activation), reused by every forward); here the caller allocates
- * what these sizes say.  The prepared size is the four weight regions plus a
- * 64 KiB tail that the weight streams' read-ahead may touch.  Either output
+ * what these sizes say.  The prepared size is the four weight regions (with
+ * NVFP4 also its tensor scales) plus a 64 KiB tail that the weight streams'
+ * read-ahead may touch.  Either output
  * pointer may be NULL.  Pure host function: returns MOE_EINVAL or
  * MOE_EUNSUPPORTED for a configuration moe_w4a4_cfg does not allow, with the
  * outputs untouched. */
@@ -117,6 +133,18 @@ int moe_w4a4_query(const moe_w4a4_cfg* cfg, size_t* prepared_bytes, size_t* work
 int moe_w4a4_quantize(int32_t src_dtype, const void* src, int64_t rows, int32_t cols,
                       uint8_t* codes, uint8_t* scales, void* stream);
 
+/* NVFP4 quantization of `rows` rows of `cols` values along each row with the
+ * tensor scale g (the rule under MOE_MMA_NVF4_X_NVF4 above): codes uint8
+ * [rows, cols/2] (packed, 16-byte aligned), scales uint8 [rows, cols/16] (E4M3
+ * bytes).  src_dtype, src, rows and cols as for moe_w4a4_quantize (cols % 32
+ * == 0).  g must be finite and in [2^-100, 2^100] (else MOE_EINVAL).  The
+ * pre-dispatch step of the NVFP4 type uses the same rule for x with the
+ * layer's g_x; callers use it to quantize fp32 expert weights at load time.
+ * Source: [P3] "Motivation" (the NVFP4 variant) and "Key source snippets"
+ * (pre_dispatch quantizes the tokens once, group by group). */
+int moe_w4a4_quantize_nvfp4(int32_t src_dtype, const void* src, int64_t rows, int32_t cols, float g,
+                            uint8_t* codes, uint8_t* scales, void* stream);
+
 /* Re-lay canonical MXFP4 expert weights into the device tile order used by the
  * forward ([P3] "Implementation breakdown" item 4: a one-off weight transform at
  * load time).  A pure byte permutation.
@@ -125,11 +153,31 @@ int moe_w4a4_quantize(int32_t src_dtype, const void* src, int64_t rows, int32_t 
  *   w2_codes  [E, H, I/2],  w2_scales [E, H, I/32].
  * All device pointers; codes 16-byte aligned.  prepared: device buffer of at
  * least moe_w4a4_query()'s prepared_bytes, 256-byte aligned; owned by the
- * caller and read by every later forward. */
+ * caller and read by every later forward.  An NVFP4 cfg returns
+ * MOE_EUNSUPPORTED (it takes moe_w4a4_prepare_weights_nvfp4). */
 int moe_w4a4_prepare_weights(const moe_w4a4_cfg* cfg,
                              const uint8_t* w1_codes, const uint8_t* w1_scales,
                              const uint8_t* w2_codes, const uint8_t* w2_scales,
                              void* prepared, size_t prepared_bytes, void* stream);
+
+/* The same for NVFP4 weights ([P3] "Motivation"; the one-off weight transform
+ * of "Implementation breakdown" item 4), for a cfg with MOE_MMA_NVF4_X_NVF4
+ * (else MOE_EUNSUPPORTED):
+ *   w1_codes [E, 2I, H/2], w1_scales [E, 2I, H/16] (E4M3 bytes),
+ *   w1_tensor_scales fp32 [E]; w2_codes [E, H, I/2], w2_scales [E, H, I/16],
+ *   w2_tensor_scales fp32 [E] -- device pointers; each tensor scale in
+ *   [2^-100, 2^100] (the library cannot read device values on the host: out
+ *   of range gives unspecified numbers, never a fault);
+ *   x_tensor_scale, h_tensor_scale: g of the layer's activations x and of the
+ *   intermediate h (calibration constants: every forward quantizes x and
+ *   requantizes h with them), by value, in [2^-100, 2^100] (else MOE_EINVAL).
+ * All tensor scales are copied into `prepared`, which the forward then reads
+ * on the device. */
+int moe_w4a4_prepare_weights_nvfp4(const moe_w4a4_cfg* cfg,
+                                   const uint8_t* w1_codes, const uint8_t* w1_scales, const float* w1_tensor_scales,
+                                   const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_tensor_scales,
+                                   float x_tensor_scale, float h_tensor_scale,
+                                   void* prepared, size_t prepared_bytes, void* stream);
 
 /* One forward of the layer for num_tokens (0 <= num_tokens <= cfg->max_tokens).
  * It is the routed branch of the pages' MoE runner ([P3] "Key source snippets",
@@ -137,13 +185,14 @@ int moe_w4a4_prepare_weights(const moe_w4a4_cfg* cfg,
  * topk_weights into the buffer for the live num_tokens, group_size=32, then
  * the fused mega-MoE kernel over the prepared L1/L2 weights), as one call:
  *   1. pre-dispatch: each token row of x quantized once to MXFP4 (MXFP8 E4M3
- *      for MOE_MMA_FP8_X_MXF4; so is h in step 3);
+ *      for MOE_MMA_FP8_X_MXF4, NVFP4 with g_x for MOE_MMA_NVF4_X_NVF4; so is
+ *      h in step 3, NVFP4 with g_h);
  *   2. route: stable counting sort of the routed rows r = t*k + j by expert
  *      (ids outside [0, E) are skipped; duplicates are separate rows);
  *   3. GEMM1 per expert with fp32 accumulation, SwiGLU, requantization of h to
- *      MXFP4 along I;
+ *      MXFP4 along I (NVFP4: the sums times g_x * g_w1[e] before SwiGLU);
  *   4. GEMM2 per expert with fp32 accumulation, the result per routed row
- *      rounded to bfloat16;
+ *      rounded to bfloat16 (NVFP4: the sums times g_h * g_w2[e] first);
  *   5. combine: out[t] = sum over valid slots j (in slot order, fp32, from +0)
  *      of topk_weights[t, j] * y[row (t, j)], rounded to bfloat16.
  * x:            device bfloat16 [num_tokens, H], 16-byte aligned
@@ -190,7 +239,9 @@ const char* moe_w4a4_status_string(int status);
  * sorted-row activations of the GEMMs are stored as K-step planes, plane c
  * holding K step c (128 elements) of every sorted row: 64 code bytes at
  * (c*R + row)*64 and one dword of 4 scale bytes at (c*R + row)*4, so that a
- * tile of consecutive rows reads one contiguous run per K step. */
+ * tile of consecutive rows reads one contiguous run per K step.  With NVFP4
+ * every scale region holds one byte per 16 elements: xsf [max_tokens, H/16],
+ * hsf planes of 8 bytes per row ([I/128, R, 8]), xsf_planes unused. */
 typedef struct moe_w4a4_ws_layout {
   uint64_t xq;           /* uint8  [max_tokens, H/2]   quantized tokens (packed E2M1;
                                                         E4M3: [max_tokens, H])      */
@@ -232,7 +283,8 @@ enum {
  * moe_w4a4_forward; a pointer only some stages read may be NULL when those
  * stages are not selected.  gemm1_acc: NULL, or a device float buffer
  * [max_tokens*k, 2I] into which GEMM1 also writes its raw fp32 accumulators
- * (gate in columns [0, I), up in [I, 2I)), in sorted-row order. */
+ * (gate in columns [0, I), up in [I, 2I)), in sorted-row order; with NVFP4
+ * after the tensor scales g_x * g_w1[e] are applied. */
 int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t num_tokens,
                         const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
                         uint16_t* out, void* workspace, size_t workspace_bytes,

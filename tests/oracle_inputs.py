@@ -43,11 +43,15 @@ def all_experts_parallel(cfg, workers=8):
     return lambda e: parts[e]
 
 
-def quantize_expert_nv(cfg, e):
+def quantize_expert_nv(cfg, e, scales=None):
     """Expert e's NVFP4 weights, each matrix with the tensor scale of its own
-    absolute maximum: ((w1c, w1s, w2c, w2s), g_w1, g_w2)."""
+    absolute maximum, or with scales = (g_w1, g_w2) when given:
+    ((w1c, w1s, w2c, w2s), g_w1, g_w2)."""
     w1, w2 = synth.expert_weights_f32(cfg, e)
-    g1, g2 = nvfp4.tensor_scale(np.abs(w1).max()), nvfp4.tensor_scale(np.abs(w2).max())
+    if scales is None:
+        g1, g2 = nvfp4.tensor_scale(np.abs(w1).max()), nvfp4.tensor_scale(np.abs(w2).max())
+    else:
+        g1, g2 = np.float32(scales[0]), np.float32(scales[1])
     w1c, w1s = nvfp4.quantize_packed(w1, g1)
     w2c, w2s = nvfp4.quantize_packed(w2, g2)
     return (w1c, w1s, w2c, w2s), g1, g2
@@ -60,9 +64,19 @@ def all_expert_weights_nv(cfg):
     return W, np.array([p[1] for p in parts], np.float32), np.array([p[2] for p in parts], np.float32)
 
 
+def lazy_expert_weights_nv(cfg, scales):
+    """e -> expert e's NVFP4 weights (w1c, w1s, w2c, w2s) under the fixed tensor
+    scales (g_w1, g_w2), quantized on first use."""
+    return functools.lru_cache(maxsize=None)(lambda e: quantize_expert_nv(cfg, e, scales)[0])
+
+
 # Calibration bound of |h| per layer shape (hidden size): above the largest
 # |silu(gate) * up| of the synthetic layers, so no block of h saturates.
-H_AMAX = {256: 2.0, 4096: 64.0}
+H_AMAX = {256: 2.0, 512: 4.0, 1024: 8.0, 4096: 64.0}
+
+# Tensor scales of the DSV4-shaped synthetic weights (N(0, 0.02^2): every
+# |w| is far below 6 * 448 * g), the same constants for every expert.
+NV_WEIGHT_SCALES = (np.float32(6.1e-5), np.float32(5.3e-5))
 
 
 def nv_act_scales(cfg, x_bits):

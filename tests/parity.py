@@ -18,6 +18,11 @@
       nearly every y value.)
   final bf16 output ........................ relative L2 error <= 5e-3
 
+The NVFP4 type (nvf4xnvf4) takes the MXFP4 rules with its own block of 16
+and E4M3 scale byte (nv_compare_requant): the GEMMs multiply exact bf16
+products e2m1 * e4m3 and sum them in fp32, as the MXFP4 MFMA does with its
+exact E2M1 products, so the same element and y rules apply.
+
 The fp8xfp4 rules follow from how the MI355X scaled MFMA adds E2M1 x E4M3
 products (tests/fp8_mfma_model.py, pinned bit for bit on the device by
 tests/test_gpu_fp8_mfma.py; the bound fp8_dot_bound covers the model's error
@@ -80,6 +85,40 @@ def compare_requant(g_hq, g_hsf, r_hq, r_hsf, r_h, fp8=False, element_rules=None
         amax = np.abs(h32.reshape(*h32.shape[:-1], -1, 32)).max(axis=-1)[~same]
         nearest = top * 2.0 ** np.round(np.log2(np.maximum(amax, 1e-300) / top))
         rel = np.abs(amax / nearest - 1.0)
+        assert np.all(rel <= 1e-4), (stats, rel.max())
+    return stats
+
+
+def nv_compare_requant(g_hq, g_hsf, r_hq, r_hsf, r_h, g_h):
+    """The requantized h of the NVFP4 MMA type (scale bytes per 16 elements):
+    on blocks whose E4M3 scale bytes agree, >= 99.9 % of the codes identical
+    and every difference at most one step on the signed E2M1 grid; a block
+    whose scale byte differs must differ by one E4M3 code and have the
+    oracle's f32(amax / f32(6 g_h)) within 1e-4 (relative) of the midpoint
+    between two E4M3 values, where fp32 sums in another order can round the
+    other way.  Returns statistics."""
+    gc, rc = mxfp4.unpack(g_hq), mxfp4.unpack(r_hq)
+    gs, rs = np.asarray(g_hsf), np.asarray(r_hsf)
+    same = gs == rs
+    mask = np.repeat(same, 16, axis=-1)
+    d = np.abs(grid_index(gc) - grid_index(rc))
+    n = int(mask.sum())
+    ident = int(((d == 0) & mask).sum())
+    stats = dict(elements=n, identical=ident, max_step=int(d[mask].max()) if n else 0,
+                 scale_mismatch_blocks=int((~same).sum()))
+    assert n == 0 or ident / n >= REQUANT_IDENTICAL, stats
+    assert stats["max_step"] <= 1, stats
+    if stats["scale_mismatch_blocks"]:
+        assert np.all(np.abs(gs[~same].astype(np.int64) - rs[~same].astype(np.int64)) == 1), stats
+        h32 = np.asarray(r_h, dtype=np.float64).astype(np.float32)
+        amax = np.abs(h32.reshape(*h32.shape[:-1], -1, 16)).max(axis=-1)[~same]
+        d6 = np.float32(np.float32(6.0) * np.float32(g_h))
+        sf = (amax / d6).astype(np.float64)
+        mags = mxfp8.E4M3_MAGNITUDES
+        mids = (mags[:-1] + mags[1:]) / 2
+        nearest = mids[np.clip(np.searchsorted(mids, sf), 0, mids.size - 1)]
+        nearest2 = mids[np.clip(np.searchsorted(mids, sf) - 1, 0, mids.size - 1)]
+        rel = np.minimum(np.abs(sf / nearest - 1.0), np.abs(sf / nearest2 - 1.0))
         assert np.all(rel <= 1e-4), (stats, rel.max())
     return stats
 

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def header_symbols():
     text = open(os.path.join(ROOT, "include", "moe_w4a4.h")).read()
-    return sorted(set(re.findall(r"\b(moe_w4a4_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_w4a4_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
