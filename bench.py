@@ -1,6 +1,7 @@
 """Benchmark of the W4A4 MoE layer forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--mma-type {mxf4xmxf4,fp8xfp4}]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--mma-type {mxf4xmxf4,fp8xfp4,nvf4xnvf4}]
                     [--no-cpu-baseline] [--no-ceiling] [--no-prefill]
 
 A step is one whole forward of the layer (pre-dispatch quantization, routing,
@@ -14,10 +15,11 @@ Prints ONE JSON line.  `value` is the time of one layer forward in us (lower is
 better): K calls of moe_w4a4_forward, bracketed by synchronizations and HIP
 events on the stream the kernels run on.  Throughput in TFLOP/s and
 algorithmic HBM GB/s ride along.  "roofline" is GEMM1's, the dominant kernel
-(gemm1_swiglu_kernel up to 16 routed rows per expert, gemm_lds_kernel above),
-and "roofline_gemm2" GEMM2's, each against the HBM or the MFMA peak of the MMA
-type (MXFP4, or FP8 for the fp8xfp4 type), whichever bounds its algorithmic
-bytes and flops.  Their durations come from K further steps of the same
+(gemm1_swiglu_kernel up to 16 routed rows per expert, gemm_lds_kernel above;
+gemm1_nv_kernel for the NVFP4 type), and "roofline_gemm2" GEMM2's, each
+against the HBM or the MFMA peak of the MMA type (MXFP4, FP8 for the fp8xfp4
+type, fp16 for NVFP4, whose products run on the dense fp16 MFMA), whichever
+bounds its algorithmic bytes and flops.  Their durations come from K further steps of the same
 launches in which events on the same stream bracket each GEMM launch
 ("split_step_us" is the step time of that loop).  "forward_us" gives the
 median, minimum and maximum of K more forwards, each bracketed by its own
@@ -51,28 +53,39 @@ METRIC = "mega-MoE layer µs + TFLOPS + HBM GB/s at ntok=512/4096, DSV4-Flash sh
 HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E
 FP4_PEAK_TFLOPS = 10100.0         # MI355X dense MXFP4 MFMA
 FP8_PEAK_TFLOPS = 5000.0          # MI355X dense FP8 MFMA: the rate of the FP8 x FP4 mixed form
+F16_PEAK_TFLOPS = 2500.0          # MI355X dense fp16 / bf16 MFMA: the NVFP4 type's products
+# Tensor scales of the NVFP4 workload (calibration constants, like weights):
+# x ~ N(0, 1) stays below 6 * 448 * 2^-8 = 10.5, |h| below 64 (6 * 448 * g_h),
+# and the N(0, 0.02^2) weights below 0.164 (W1) and 0.142 (W2).
+NV_X_SCALE = 2.0 ** -8
+NV_H_SCALE = 64.0 / 2688.0
+NV_W_SCALES = (6.1e-5, 5.3e-5)
 COPY_BYTES = 256 << 20           # calibration copy size
 PAGES_US_NTOK512 = 537.6          # W4A4 mega-MoE kernel, 1 B200, 1-rank isolation, ntok=512 (context)
 PAGES_US_NTOK512_W4A8 = 753.2     # the same measurement of the W4A8 (FP8 activations) kernel
 
 
-def expert_bytes(H, I):
-    """MXFP4 bytes of one expert: W1 (2I x H) and W2 (H x I) codes + scales."""
-    return 2 * I * H // 2 + 2 * I * H // 32 + H * I // 2 + H * I // 32
+def expert_bytes(H, I, group=32):
+    """Bytes of one expert: W1 (2I x H) and W2 (H x I) E2M1 codes + one scale
+    byte per `group` elements (32 for MXFP4, 16 for NVFP4)."""
+    return 2 * I * H // 2 + 2 * I * H // group + H * I // 2 + H * I // group
 
 
-def algorithmic(cfg, counts, fp8=False):
-    """fp8: the fp8xfp4 MMA type, whose x-hat and h-hat take one byte per element."""
+def algorithmic(cfg, counts, fp8=False, nv=False):
+    """fp8: the fp8xfp4 MMA type, whose x-hat and h-hat take one byte per
+    element; nv: NVFP4, one scale byte per 16 elements everywhere (the tensor
+    scales are a few bytes)."""
     H, I, k, T = cfg.hidden, cfg.inter, cfg.topk, cfg.tokens
     cb = 1 if fp8 else 2          # elements per activation code byte
+    G = 16 if nv else 32          # elements per scale byte
     active = int((counts > 0).sum())
     R = int(counts.sum())
-    layer_bytes = active * expert_bytes(H, I) + T * (2 * H + 8 * k + 2 * H)
+    layer_bytes = active * expert_bytes(H, I, G) + T * (2 * H + 8 * k + 2 * H)
     flops = R * (2 * H * 2 * I + 2 * I * H)
-    w1 = 2 * I * H // 2 + 2 * I * H // 32
-    gemm1_bytes = active * w1 + T * (H // cb + H // 32) + R * (I // cb + I // 32)
-    w2 = H * I // 2 + H * I // 32
-    gemm2_bytes = active * w2 + R * (I // cb + I // 32) + R * 2 * H     # W2, h-hat in, y out (bf16)
+    w1 = 2 * I * H // 2 + 2 * I * H // G
+    gemm1_bytes = active * w1 + T * (H // cb + H // G) + R * (I // cb + I // G)
+    w2 = H * I // 2 + H * I // G
+    gemm2_bytes = active * w2 + R * (I // cb + I // G) + R * 2 * H      # W2, h-hat in, y out (bf16)
     return dict(active=active, R=R, layer_bytes=layer_bytes, flops=flops, gemm1_bytes=gemm1_bytes,
                 gemm1_flops=R * 2 * H * 2 * I, gemm2_bytes=gemm2_bytes, gemm2_flops=R * 2 * I * H)
 
@@ -91,11 +104,20 @@ KERNELS = {
                            ("gemm_lds.hip", "gemm_common.h", "epilogue.h", "device_common.h", "tiles.h")),
     ("gemm2", "prefill"): ("gemm_lds_kernel", "gemm_lds_kernel_gemm2",
                            ("gemm_lds.hip", "gemm_common.h", "epilogue.h", "device_common.h", "tiles.h")),
+    ("gemm1", "nv"): ("gemm1_nv_kernel", "gemm1_nv_kernel",
+                      ("gemm_nv.hip", "nvfp4.h", "gemm_common.h", "epilogue.h", "device_common.h", "tiles.h",
+                       "e4m3.h")),
+    ("gemm2", "nv"): ("gemm2_nv_kernel", "gemm2_nv_kernel",
+                      ("gemm_nv.hip", "nvfp4.h", "gemm_common.h", "epilogue.h", "device_common.h", "tiles.h",
+                       "e4m3.h")),
 }
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "{}_{}_hbm_counters.txt")
 
 
-def gemm_path(cfg):
+def gemm_path(cfg, nv=False):
+    """The GEMM kernels a workload runs on: the NVFP4 type has its own streaming kernels only."""
+    if nv:
+        return "nv"
     rows_hint = -(-cfg.tokens * cfg.topk // cfg.experts)
     return "stream" if rows_hint <= STREAM_MAX_ROWS else "prefill"
 
@@ -151,19 +173,26 @@ def cpu_baseline(cfg, x, ids, w, mma_type="mxf4xmxf4", weight_pool=2):
     experts' 3.4 GB with the oracle's brute-force quantizer would take tens of
     CPU-minutes)."""
     import synth
-    from oracle import mxfp4
+    from oracle import mxfp4, nvfp4
     from oracle.forward import forward
     from oracle.route import route
 
     threads, vendor = blas_info()
     counts = route(ids, cfg.experts)[0]
     active = int((counts > 0).sum())
+    nv = mma_type == "nvf4xnvf4"
     pool = []
     for e in range(weight_pool):
         w1, w2 = synth.expert_weights_f32(cfg, e)
-        pool.append(mxfp4.quantize_packed(w1) + mxfp4.quantize_packed(w2))
+        if nv:
+            pool.append(nvfp4.quantize_packed(w1, NV_W_SCALES[0]) + nvfp4.quantize_packed(w2, NV_W_SCALES[1]))
+        else:
+            pool.append(mxfp4.quantize_packed(w1) + mxfp4.quantize_packed(w2))
+    E = cfg.experts
+    ts = (NV_X_SCALE, NV_H_SCALE, np.full(E, NV_W_SCALES[0], np.float32),
+          np.full(E, NV_W_SCALES[1], np.float32)) if nv else None
     t0 = time.perf_counter()
-    forward(x, ids, w, lambda e: pool[e % weight_pool], cfg.experts, cfg.inter, mma_type=mma_type)
+    forward(x, ids, w, lambda e: pool[e % weight_pool], cfg.experts, cfg.inter, mma_type=mma_type, tensor_scales=ts)
     secs = time.perf_counter() - t0
     return {"value": round(secs * 1e6, 1), "unit": "us", "cores": threads, "kind": "oracle", "blas": vendor,
             "sample": f"one whole forward of the {cfg.name} workload ({cfg.tokens} tokens, {int(counts.sum())} "
@@ -172,10 +201,15 @@ def cpu_baseline(cfg, x, ids, w, mma_type="mxf4xmxf4", weight_pool=2):
             "measured_s": round(secs, 2)}
 
 
-def roofline(kernel, nbytes, flops, us, fp8, traffic):
+def mfma_peak_of(mma_type):
+    """Published dense MFMA peak (TFLOP/s) of the instruction an MMA type's GEMMs run on."""
+    return {"fp8xfp4": FP8_PEAK_TFLOPS, "nvf4xnvf4": F16_PEAK_TFLOPS}.get(mma_type, FP4_PEAK_TFLOPS)
+
+
+def roofline(kernel, nbytes, flops, us, mma_type, traffic):
     """Roofline object of one kernel: HBM-bound unless its flops take longer
     at the MFMA peak of the MMA type than its algorithmic bytes at the HBM peak."""
-    mfma_peak = FP8_PEAK_TFLOPS if fp8 else FP4_PEAK_TFLOPS
+    mfma_peak = mfma_peak_of(mma_type)
     mfma_bound = flops / (mfma_peak * 1e12) > nbytes / (HBM_PEAK_GBPS * 1e9)
     if mfma_bound:
         ach, peak, unit = flops / (us * 1e-6) / 1e12, mfma_peak, "TFLOP/s"
@@ -252,7 +286,7 @@ def measure(layer, cfg, x, ids, w, out, steps, warmup):
     return dict(us=us, wall=wall, gemm1_us=gemm1_us, gemm2_us=gemm2_us, split_us=split_us, fwd_us=fwd_us)
 
 
-def workload_record(layer, cfg, steps, warmup, fp8):
+def workload_record(layer, cfg, steps, warmup, mma_type):
     """Times one workload on `layer` and returns (its record, its inputs)."""
     import torch
 
@@ -266,12 +300,13 @@ def workload_record(layer, cfg, steps, warmup, fp8):
     torch.cuda.synchronize()
     m = measure(layer, cfg, x, ids, w, out, steps, warmup)
     counts = layer.ws("counts", (cfg.experts,), torch.int32).cpu().numpy()
-    alg = algorithmic(cfg, counts, fp8)
+    fp8, nv = mma_type == "fp8xfp4", mma_type == "nvf4xnvf4"
+    alg = algorithmic(cfg, counts, fp8, nv)
     us = m["us"]
-    mfma_peak = FP8_PEAK_TFLOPS if fp8 else FP4_PEAK_TFLOPS
+    mfma_peak = mfma_peak_of(mma_type)
     tflops = alg["flops"] / (us * 1e-6) / 1e12
     gbps = alg["layer_bytes"] / (us * 1e-6) / 1e9
-    path = gemm_path(cfg)
+    path = gemm_path(cfg, nv)
     rec = {
         "value": round(us, 2),
         "tflops": round(tflops, 2),
@@ -281,10 +316,10 @@ def workload_record(layer, cfg, steps, warmup, fp8):
         "split_step_us": round(m["split_us"], 2),
         "forward_us": {"median": round(float(np.median(m["fwd_us"])), 2), "min": round(float(m["fwd_us"].min()), 2),
                        "max": round(float(m["fwd_us"].max()), 2)},
-        "roofline": roofline(KERNELS[("gemm1", path)][0], alg["gemm1_bytes"], alg["gemm1_flops"], m["gemm1_us"], fp8,
-                             measured_traffic(cfg.name, "gemm1", path, fp8)),
+        "roofline": roofline(KERNELS[("gemm1", path)][0], alg["gemm1_bytes"], alg["gemm1_flops"], m["gemm1_us"],
+                             mma_type, measured_traffic(cfg.name, "gemm1", path, fp8)),
         "roofline_gemm2": roofline(KERNELS[("gemm2", path)][0], alg["gemm2_bytes"], alg["gemm2_flops"],
-                                   m["gemm2_us"], fp8, measured_traffic(cfg.name, "gemm2", path, fp8)),
+                                   m["gemm2_us"], mma_type, measured_traffic(cfg.name, "gemm2", path, fp8)),
         "wall_s": round(m["wall"], 3),
     }
     return rec, alg, (x_h, ids_h, w_h)
@@ -296,8 +331,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="dsv4flash_t512")
-    ap.add_argument("--mma-type", default="mxf4xmxf4", choices=("mxf4xmxf4", "fp8xfp4"),
-                    help="activation format: MXFP4 (the default, W4A4) or MXFP8 E4M3 (W4A8)")
+    ap.add_argument("--mma-type", default="mxf4xmxf4", choices=("mxf4xmxf4", "fp8xfp4", "nvf4xnvf4"),
+                    help="MXFP4 activations and weights (the default, W4A4), MXFP8 E4M3 activations "
+                         "(W4A8), or NVFP4 activations and weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the streaming-read and FP4 MFMA probes (libmoe_ceiling.so)")
@@ -322,14 +358,18 @@ def main():
     cfg = configs[args.workload]
     torch.cuda.set_device(0)
     t_setup = time.perf_counter()
-    fp8 = args.mma_type == "fp8xfp4"
-    layer = MoeW4A4Layer(cfg.hidden, cfg.inter, cfg.experts, cfg.topk, cfg.tokens,
-                         mma_type=_lib.MOE_MMA_FP8_X_MXF4 if fp8 else _lib.MOE_MMA_MXF4_X_MXF4)
-    layer.load_fp32(lambda e: synth.expert_weights_f32(cfg, e), threads=args.threads)
+    fp8, nv = args.mma_type == "fp8xfp4", args.mma_type == "nvf4xnvf4"
+    mma = {"mxf4xmxf4": _lib.MOE_MMA_MXF4_X_MXF4, "fp8xfp4": _lib.MOE_MMA_FP8_X_MXF4,
+           "nvf4xnvf4": _lib.MOE_MMA_NVF4_X_NVF4}[args.mma_type]
+    layer = MoeW4A4Layer(cfg.hidden, cfg.inter, cfg.experts, cfg.topk, cfg.tokens, mma_type=mma)
+    E = cfg.experts
+    ts = (NV_X_SCALE, NV_H_SCALE, np.full(E, NV_W_SCALES[0], np.float32),
+          np.full(E, NV_W_SCALES[1], np.float32)) if nv else None
+    layer.load_fp32(lambda e: synth.expert_weights_f32(cfg, e), threads=args.threads, tensor_scales=ts)
     torch.cuda.synchronize()
     print(f"[bench] setup {time.perf_counter() - t_setup:.1f}s workload={cfg.name}", file=sys.stderr, flush=True)
 
-    rec, alg, (x_h, ids_h, w_h) = workload_record(layer, cfg, args.steps, args.warmup, fp8)
+    rec, alg, (x_h, ids_h, w_h) = workload_record(layer, cfg, args.steps, args.warmup, args.mma_type)
     print(f"[bench] {cfg.name}: {rec['value']} us", file=sys.stderr, flush=True)
     us = rec["value"]
     pages_us = PAGES_US_NTOK512_W4A8 if fp8 else PAGES_US_NTOK512
@@ -346,14 +386,14 @@ def main():
         # The pages' figure was measured on another machine (one B200): it is
         # context, not the baseline (see "context" and "cpu_baseline").
         "vs_baseline": None,
-        "dtype": "mxfp8 x mxfp4" if fp8 else "mxfp4",
+        "dtype": {"mxf4xmxf4": "mxfp4", "fp8xfp4": "mxfp8 x mxfp4", "nvf4xnvf4": "nvfp4"}[args.mma_type],
         "data": "synthetic",
         "config": {"workload": cfg.name, "mma_type": args.mma_type, "tokens": cfg.tokens, "hidden": cfg.hidden,
                    "inter": cfg.inter, "experts": cfg.experts, "topk": cfg.topk, "routing": cfg.routing,
                    "active_experts": alg["active"], "routed_rows": alg["R"]},
     }
     res.update({k: v for k, v in rec.items() if k != "value"})
-    if cfg.name == "dsv4flash_t512":
+    if cfg.name == "dsv4flash_t512" and not nv:      # the pages give no NVFP4 figure
         res["context"] = {"pages_us": pages_us, "pages_hardware": "1x B200, 1-rank isolation",
                           "value_over_pages": round(us / pages_us, 4)}
     if not args.no_prefill and cfg.name == "dsv4flash_t512":
@@ -362,7 +402,7 @@ def main():
         # weights with a workspace for 4096 tokens.
         pcfg = configs[PREFILL]
         player = layer.with_capacity(pcfg.tokens)
-        prec, palg, _ = workload_record(player, pcfg, args.steps, args.warmup, fp8)
+        prec, palg, _ = workload_record(player, pcfg, args.steps, args.warmup, args.mma_type)
         prec = {("value_us" if k == "value" else k): v for k, v in prec.items()}
         prec["config"] = {"tokens": pcfg.tokens, "routing": pcfg.routing, "active_experts": palg["active"],
                           "routed_rows": palg["R"]}
@@ -384,7 +424,8 @@ def main():
         # roofline fraction uses.
         from block_scaled_fp4_pre_amd import ceiling
         ceil = ceiling.measure()
-        mfma_ref = ceil["mfma_fp8xfp4_TFLOPs" if fp8 else "mfma_fp4_TFLOPs"]
+        # the NVFP4 type's products run on the dense fp16 MFMA, whose rate is bf16's
+        mfma_ref = ceil["mfma_fp8xfp4_TFLOPs" if fp8 else "mfma_bf16_TFLOPs" if nv else "mfma_fp4_TFLOPs"]
         for r in [res] + ([res[PREFILL]] if PREFILL in res else []):
             # both GEMMs against the read ceiling or the MFMA rate (GEMM2
             # also writes y, which the read ceiling does not include)

@@ -22,7 +22,10 @@
 #include "validate.h"
 
 #ifndef MOE_NV_RING_DEPTH
-#define MOE_NV_RING_DEPTH 4       // weight-ring slots (divides the K steps)
+#define MOE_NV_RING_DEPTH 2       // weight-ring slots (divides the K steps)
+#endif
+#ifndef MOE_NV_TWO_TILES_ABOVE
+#define MOE_NV_TWO_TILES_ABOVE 16 // mean routed rows per expert above which a pass takes two token tiles
 #endif
 
 namespace moe {
@@ -394,7 +397,7 @@ hipError_t launch_gemm1_nv(const uint8_t* w1c, const uint8_t* w1s, const float* 
                            const uint8_t* xsf, const int32_t* counts, const int32_t* offsets,
                            const int32_t* sorted_rows, int H, int I, int E, int k, int rows_hint, int hrows,
                            uint8_t* hq, uint8_t* hsf, float* acc_out, hipStream_t stream) {
-  if (rows_hint > 8)
+  if (rows_hint > MOE_NV_TWO_TILES_ABOVE)
     return launch_gemm1_nv_nt<2>(w1c, w1s, gsc, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hrows, hq, hsf,
                                  acc_out, stream);
   return launch_gemm1_nv_nt<1>(w1c, w1s, gsc, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hrows, hq, hsf,
@@ -433,19 +436,18 @@ template <int NT>
 static hipError_t launch_gemm2_nv_nt(const uint8_t* w2c, const uint8_t* w2s, const float* gsc, const uint8_t* hq,
                                      const uint8_t* hsf, const int32_t* counts, const int32_t* offsets, int H, int I,
                                      int E, int hrows, uint16_t* y, hipStream_t stream) {
-  switch (ring_depth(I / kStepK)) {
-    case MOE_NV_RING_DEPTH:
-      return launch_gemm2_nv_d<NT, MOE_NV_RING_DEPTH>(w2c, w2s, gsc, hq, hsf, counts, offsets, H, I, E, hrows, y,
-                                                      stream);
-    case 2: return launch_gemm2_nv_d<NT, 2>(w2c, w2s, gsc, hq, hsf, counts, offsets, H, I, E, hrows, y, stream);
-    default: return launch_gemm2_nv_d<NT, 1>(w2c, w2s, gsc, hq, hsf, counts, offsets, H, I, E, hrows, y, stream);
-  }
+  const int d = ring_depth(I / kStepK);
+  if (d == MOE_NV_RING_DEPTH)
+    return launch_gemm2_nv_d<NT, MOE_NV_RING_DEPTH>(w2c, w2s, gsc, hq, hsf, counts, offsets, H, I, E, hrows, y,
+                                                    stream);
+  if (d == 2) return launch_gemm2_nv_d<NT, 2>(w2c, w2s, gsc, hq, hsf, counts, offsets, H, I, E, hrows, y, stream);
+  return launch_gemm2_nv_d<NT, 1>(w2c, w2s, gsc, hq, hsf, counts, offsets, H, I, E, hrows, y, stream);
 }
 
 hipError_t launch_gemm2_nv(const uint8_t* w2c, const uint8_t* w2s, const float* gsc, const uint8_t* hq,
                            const uint8_t* hsf, const int32_t* counts, const int32_t* offsets, int H, int I, int E,
                            int rows_hint, int hrows, uint16_t* y, hipStream_t stream) {
-  if (rows_hint > 8) return launch_gemm2_nv_nt<2>(w2c, w2s, gsc, hq, hsf, counts, offsets, H, I, E, hrows, y, stream);
+  if (rows_hint > MOE_NV_TWO_TILES_ABOVE) return launch_gemm2_nv_nt<2>(w2c, w2s, gsc, hq, hsf, counts, offsets, H, I, E, hrows, y, stream);
   return launch_gemm2_nv_nt<1>(w2c, w2s, gsc, hq, hsf, counts, offsets, H, I, E, hrows, y, stream);
 }
 

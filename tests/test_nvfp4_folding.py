@@ -11,7 +11,9 @@ as one of those elements times a power of two.  The enumeration below shows
 that v * s needs up to 6 significant bits, while every element format of that
 MFMA holds at most 4, so no folding of the E4M3 scale into the elements is
 exact; every v * s is exact in bfloat16 and in fp16, whose dense MFMAs are the
-ones left (the bf16 rate is measured by moe_ceiling_mfma_bf16)."""
+ones left.  The NVFP4 kernels (csrc/gemm_nv.hip) run on the fp16 one, with
+the products e2m1 * e4m3 formed in registers (the 16-bit MFMA rate is
+measured by moe_ceiling_mfma_bf16)."""
 from fractions import Fraction
 
 import numpy as np
