@@ -16,7 +16,8 @@ better): K calls of moe_w4a4_forward, bracketed by synchronizations and HIP
 events on the stream the kernels run on.  Throughput in TFLOP/s and
 algorithmic HBM GB/s ride along.  "roofline" is GEMM1's, the dominant kernel
 (gemm1_swiglu_kernel up to 16 routed rows per expert, gemm_lds_kernel above;
-gemm1_nv_kernel for the NVFP4 type), and "roofline_gemm2" GEMM2's, each
+gemm1_nv_kernel and gemm_lds_nv_kernel for the NVFP4 type), and
+"roofline_gemm2" GEMM2's, each
 against the HBM or the MFMA peak of the MMA type (MXFP4, FP8 for the fp8xfp4
 type, fp16 for NVFP4, whose products run on the dense fp16 MFMA), whichever
 bounds its algorithmic bytes and flops.  Their durations come from K further steps of the same
@@ -106,19 +107,28 @@ KERNELS = {
                            ("gemm_lds.hip", "gemm_common.h", "epilogue.h", "device_common.h", "tiles.h")),
     ("gemm1", "nv"): ("gemm1_nv_kernel", "gemm1_nv_kernel",
                       ("gemm_nv.hip", "nvfp4.h", "gemm_common.h", "epilogue.h", "device_common.h", "tiles.h",
-                       "e4m3.h")),
+                       "e4m3.h", "epilogue_nv.h")),
     ("gemm2", "nv"): ("gemm2_nv_kernel", "gemm2_nv_kernel",
                       ("gemm_nv.hip", "nvfp4.h", "gemm_common.h", "epilogue.h", "device_common.h", "tiles.h",
-                       "e4m3.h")),
+                       "e4m3.h", "epilogue_nv.h")),
+    ("gemm1", "nv_prefill"): ("gemm_lds_nv_kernel", "gemm_lds_nv_kernel",
+                              ("gemm_lds_nv.hip", "nvfp4.h", "gemm_common.h", "epilogue.h", "device_common.h",
+                               "tiles.h", "e4m3.h", "epilogue_nv.h")),
+    ("gemm2", "nv_prefill"): ("gemm_lds_nv_kernel", "gemm_lds_nv_kernel_gemm2",
+                              ("gemm_lds_nv.hip", "nvfp4.h", "gemm_common.h", "epilogue.h", "device_common.h",
+                               "tiles.h", "e4m3.h", "epilogue_nv.h")),
 }
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "{}_{}_hbm_counters.txt")
 
 
 def gemm_path(cfg, nv=False):
-    """The GEMM kernels a workload runs on: the NVFP4 type has its own streaming kernels only."""
-    if nv:
-        return "nv"
+    """The GEMM kernels a workload runs on: streaming or LDS-staged, each with
+    its own kernels for the NVFP4 type (whose LDS-staged form needs an even
+    number of weight blocks: hidden % 512 and inter % 256)."""
     rows_hint = -(-cfg.tokens * cfg.topk // cfg.experts)
+    if nv:
+        tiled = rows_hint > STREAM_MAX_ROWS and cfg.hidden % 512 == 0 and cfg.inter % 256 == 0
+        return "nv_prefill" if tiled else "nv"
     return "stream" if rows_hint <= STREAM_MAX_ROWS else "prefill"
 
 

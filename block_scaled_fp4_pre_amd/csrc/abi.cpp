@@ -175,10 +175,13 @@ int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t n
   // Few rows per expert: stream each expert's weights once with the whole
   // token tile in LDS.  Many rows, or a K too long for that tile to fit a
   // CU's LDS: tiled GEMMs over a device-built tile list, both operands staged
-  // through LDS one K step at a time.  NVFP4 has the streaming GEMMs only
-  // (several passes over the weights for many rows; check_cfg bounds K).
-  const bool tiled = !nv && (rows_hint > kStreamMaxRows || moe::stream_tile_lds(fp8, H, rows_hint) > moe::kCuLdsBytes ||
-                             moe::stream_tile_lds(fp8, I, rows_hint) > moe::kCuLdsBytes);
+  // through LDS one K step at a time.  NVFP4's tiled GEMMs pair weight
+  // blocks, so they need an even number of blocks (H % 512, I % 256); other
+  // NVFP4 shapes stream the weights once per pass of rows (check_cfg bounds K
+  // so that the streaming tile fits).
+  const bool tiled = nv ? rows_hint > kStreamMaxRows && H % 512 == 0 && I % 256 == 0
+                        : rows_hint > kStreamMaxRows || moe::stream_tile_lds(fp8, H, rows_hint) > moe::kCuLdsBytes ||
+                              moe::stream_tile_lds(fp8, I, rows_hint) > moe::kCuLdsBytes;
   const int tile_rows = tiled ? moe::lds_tile_rows(rows_hint) : 0;
   const int max_tiles = tiled ? moe::lds_max_tiles(R, E, tile_rows) : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -223,12 +226,16 @@ int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t n
   }
   if ((stages & MOE_STAGE_ROUTE) && tiled) {
     // the tiled GEMM1's token scales, in the sorted order the route just fixed
-    st = hip_status(moe::launch_sorted_scales(xsf, sorted_rows, offsets, E, R, H, k, hrows, xsf_planes, s));
+    st = hip_status(moe::launch_sorted_scales(xsf, sorted_rows, offsets, E, R, H / (nv ? 64 : 128), k, hrows,
+                                              xsf_planes, s));
     if (st != MOE_OK) return st;
   }
   if ((stages & MOE_STAGE_GEMM1) && nv) {
-    st = hip_status(moe::launch_gemm1_nv(pw + P.w1c, pw + P.w1s, gsc, xq, xsf, counts, offsets, sorted_rows, H, I, E,
-                                         k, rows_hint, hrows, hq, hsf, gemm1_acc, s));
+    st = hip_status(tiled ? moe::launch_gemm1_lds_nv(pw + P.w1c, pw + P.w1s, gsc, xq, xsf_planes, counts, offsets,
+                                                     sorted_rows, tiles, num_tiles, max_tiles, rows_hint, H, I, E, k,
+                                                     hrows, hq, hsf, gemm1_acc, s)
+                          : moe::launch_gemm1_nv(pw + P.w1c, pw + P.w1s, gsc, xq, xsf, counts, offsets, sorted_rows,
+                                                 H, I, E, k, rows_hint, hrows, hq, hsf, gemm1_acc, s));
     if (st != MOE_OK) return st;
   } else if (stages & MOE_STAGE_GEMM1) {
     st = hip_status(tiled ? moe::launch_gemm1_lds(fp8, pw + P.w1c, pw + P.w1s, xq, xsf_planes, counts, offsets,
@@ -239,8 +246,10 @@ int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t n
     if (st != MOE_OK) return st;
   }
   if ((stages & MOE_STAGE_GEMM2) && nv) {
-    st = hip_status(moe::launch_gemm2_nv(pw + P.w2c, pw + P.w2s, gsc, hq, hsf, counts, offsets, H, I, E, rows_hint,
-                                         hrows, y, s));
+    st = hip_status(tiled ? moe::launch_gemm2_lds_nv(pw + P.w2c, pw + P.w2s, gsc, hq, hsf, counts, offsets, tiles,
+                                                     num_tiles, max_tiles, rows_hint, H, I, E, hrows, y, s)
+                          : moe::launch_gemm2_nv(pw + P.w2c, pw + P.w2s, gsc, hq, hsf, counts, offsets, H, I, E,
+                                                 rows_hint, hrows, y, s));
     if (st != MOE_OK) return st;
   } else if (stages & MOE_STAGE_GEMM2) {
     st = hip_status(tiled ? moe::launch_gemm2_lds(fp8, pw + P.w2c, pw + P.w2s, hq, hsf, counts, offsets, tiles,

@@ -66,12 +66,14 @@ hipError_t launch_gemm2_lds(bool fp8, const uint8_t* w2c, const uint8_t* w2s, co
                             const int32_t* num_tiles, int max_tiles, int rows_hint, int H, int I, int hrows,
                             uint16_t* y, hipStream_t stream);
 
-// The token scales of the sorted rows [0, offsets[E]) in K-step planes:
-// plane c, row q = the 4 scale bytes of K step c of token sorted_rows[q] / k.
-// Read by the LDS-staged GEMM1, whose per-step token-scale loads then cover
+// The token scales of the sorted rows [0, offsets[E]) in dword planes: plane
+// d, row q = scale dword d of token sorted_rows[q] / k (sc_dwords per token:
+// H/128, one per K step, for MXFP4; H/64, two per K step, for NVFP4).  Read
+// by the LDS-staged GEMM1, whose per-step token-scale loads then cover
 // consecutive addresses.  rows_bound >= offsets[E] sizes the grid.
 hipError_t launch_sorted_scales(const uint8_t* xsf, const int32_t* sorted_rows, const int32_t* offsets, int E,
-                                int rows_bound, int H, int k, int hrows, uint8_t* xsf_planes, hipStream_t stream);
+                                int rows_bound, int sc_dwords, int k, int hrows, uint8_t* xsf_planes,
+                                hipStream_t stream);
 
 // Stage S2: grouped GEMM1 over the prepared W1 tiles + SwiGLU + MXFP4 requant
 // (fp8: E4M3 activations and requant, the fp8xfp4 MMA type).
@@ -85,6 +87,19 @@ hipError_t launch_gemm1(bool fp8, const uint8_t* w1_codes, const uint8_t* w1_sca
 hipError_t launch_gemm2(bool fp8, const uint8_t* w2_codes, const uint8_t* w2_scales, const uint8_t* hq,
                         const uint8_t* hsf, const int32_t* counts, const int32_t* offsets, int H,
                         int I, int E, int rows_hint, int hrows, uint16_t* y, hipStream_t stream);
+
+// Stages S2 and S3 of the NVFP4 type for many rows per expert
+// (gemm_lds_nv.hip): LDS-staged tiles of lds_tile_rows rows from the route's
+// tile list, token scales from the sorted dword planes (launch_sorted_scales).
+hipError_t launch_gemm1_lds_nv(const uint8_t* w1c, const uint8_t* w1s, const float* gsc, const uint8_t* xq,
+                               const uint8_t* xsf_planes, const int32_t* counts, const int32_t* offsets,
+                               const int32_t* sorted_rows, const int2* tiles, const int32_t* num_tiles,
+                               int max_tiles, int rows_hint, int H, int I, int E, int k, int hrows, uint8_t* hq,
+                               uint8_t* hsf, float* acc_out, hipStream_t stream);
+hipError_t launch_gemm2_lds_nv(const uint8_t* w2c, const uint8_t* w2s, const float* gsc, const uint8_t* hq,
+                               const uint8_t* hsf, const int32_t* counts, const int32_t* offsets, const int2* tiles,
+                               const int32_t* num_tiles, int max_tiles, int rows_hint, int H, int I, int E,
+                               int hrows, uint16_t* y, hipStream_t stream);
 
 // Stages S2 and S3 of the NVFP4 type (gemm_nv.hip): the weight-streaming
 // GEMMs on the dense bf16 MFMA, any rows per expert (passes of 16 rows, or of

@@ -84,17 +84,18 @@ __global__ void __launch_bounds__(kRouteRows) route_scatter_kernel(
   place_chunk(r < R ? ids[r] : -1, R, E, nbits, b * kRouteRows, base, wcnt, sorted_rows, pos);
 }
 
-// One thread per sorted row q < offsets[E]: its token's scale row (H/32
-// bytes) is read once and its dword for K step c goes to plane c; the lanes of
-// a wave write consecutive dwords of each plane.
+// One thread per sorted row q < offsets[E]: its token's scale row (dws
+// dwords: H/128 for MXFP4, one per K step; H/64 for NVFP4, two per K step) is
+// read once and its dword d goes to plane d; the lanes of a wave write
+// consecutive dwords of each plane.
 __global__ void __launch_bounds__(256) sorted_scales_kernel(const uint8_t* __restrict__ xsf,
                                                             const int32_t* __restrict__ sorted_rows,
-                                                            const int32_t* __restrict__ offsets, int E, int H, int k,
+                                                            const int32_t* __restrict__ offsets, int E, int dws, int k,
                                                             int hrows, uint32_t* __restrict__ planes) {
   const int q = blockIdx.x * 256 + threadIdx.x;
   if (q >= offsets[E]) return;
-  const uint2* src = reinterpret_cast<const uint2*>(xsf + (size_t)(sorted_rows[q] / k) * (H / 32));
-  for (int c2 = 0; c2 < H / 256; ++c2) {   // two K steps per 8-byte load (H % 256 == 0)
+  const uint2* src = reinterpret_cast<const uint2*>(xsf + (size_t)(sorted_rows[q] / k) * dws * 4);
+  for (int c2 = 0; c2 < dws / 2; ++c2) {   // two dwords per 8-byte load (dws is even)
     const uint2 v = src[c2];
     planes[(size_t)(2 * c2) * hrows + q] = v.x;
     planes[(size_t)(2 * c2 + 1) * hrows + q] = v.y;
@@ -102,10 +103,11 @@ __global__ void __launch_bounds__(256) sorted_scales_kernel(const uint8_t* __res
 }
 
 hipError_t launch_sorted_scales(const uint8_t* xsf, const int32_t* sorted_rows, const int32_t* offsets, int E,
-                                int rows_bound, int H, int k, int hrows, uint8_t* xsf_planes, hipStream_t stream) {
+                                int rows_bound, int sc_dwords, int k, int hrows, uint8_t* xsf_planes,
+                                hipStream_t stream) {
   if (rows_bound <= 0) return hipSuccess;
   hipLaunchKernelGGL(sorted_scales_kernel, dim3((rows_bound + 255) / 256), dim3(256), 0, stream, xsf, sorted_rows,
-                     offsets, E, H, k, hrows, reinterpret_cast<uint32_t*>(xsf_planes));
+                     offsets, E, sc_dwords, k, hrows, reinterpret_cast<uint32_t*>(xsf_planes));
   return hipGetLastError();
 }
 

@@ -72,7 +72,7 @@ def lazy_expert_weights_nv(cfg, scales):
 
 # Calibration bound of |h| per layer shape (hidden size): above the largest
 # |silu(gate) * up| of the synthetic layers, so no block of h saturates.
-H_AMAX = {256: 2.0, 512: 4.0, 1024: 8.0, 4096: 64.0}
+H_AMAX = {256: 2.0, 512: 4.0, 768: 6.0, 1024: 8.0, 4096: 64.0}
 
 # Tensor scales of the DSV4-shaped synthetic weights (N(0, 0.02^2): every
 # |w| is far below 6 * 448 * g), the same constants for every expert.
