@@ -9,22 +9,26 @@
 // tile list) x (two weight blocks of 4 units).  The 8 waves of a workgroup
 // own one unit each (64 weight rows, the 16-row MFMA A side) and share the
 // tile's 128 token rows (the B side).  Both operands go HBM/L2 -> LDS by
-// direct-to-LDS loads through a ring of 3 stages, one K step of 128 per stage:
+// direct-to-LDS loads through a ring of 2 stages, one K step of 128 per stage:
 //   weight codes   8 units x 4 KiB (tile order, tiles.h)
 //   weight scales  8 units x 512 B (nvfp4.h: lane l's 8 bytes at l * 8)
 //   token codes    128 rows x 64 B (16-byte piece c of row n at c ^ (n/4 % 4))
 //   token scales   2 dword planes x 128 rows (the sorted scales' dword planes
 //                  2s and 2s+1: bytes 2*kb + half of the row's K step)
-// 45 KiB per stage, 135 KiB per workgroup, one workgroup per CU.
+// 45 KiB per stage, plus a shared fp16 token tile of 32 KiB: 122 KiB per
+// workgroup, one workgroup per CU.
 //
-// Per step a wave turns its unit's four 16-byte weight operands into 16 fp16
-// operands of exact products e2m1 * e4m3 once, then for each of the 8 token
-// tiles converts the token operand the same way and runs 16 fp16 MFMAs
-// (4 weight blocks x 4 K pieces of 32).  The DMA of the stage two steps ahead
-// goes between those groups.  Synchronization as in gemm_lds.hip: before step
-// s a wave waits (vmcnt, in order) until only the DMAs of the stage after s
-// that it issued are in flight, then a barrier makes stage s whole and frees
-// the buffer of stage s-1.
+// Step s: wait for stage s, barrier, issue the DMAs of stage s+1 (they
+// overlap the rest of the step), then each wave converts 16 token rows of
+// stage s into exact fp16 products e2m1 * e4m3 in the shared tile, a second
+// barrier, and each wave turns its unit's four 16-byte weight operands into
+// 16 fp16 operands and runs, per 16-row token tile, 16 fp16 MFMAs (4 weight
+// blocks x 4 K pieces of 32) on operands read from the fp16 tile.  Converting
+// the tokens once per workgroup instead of once per wave measured 10 % faster
+// at 96 rows per expert (T = 4096 layer 1793-1801 -> 1630-1634 us).  The
+// per-wave form (MOE_NV_LDS_COOP=0: 3 stages, token conversion in every
+// wave, the next stage's DMAs between the MFMA groups) is kept for that
+// comparison.
 //
 // Block order as gemm_lds.hip's paired form: XCD x owns weight-block pairs
 // [x*q, x*q+q) and runs tile-major over them, so the q workgroups of a tile
@@ -38,10 +42,18 @@
 namespace moe {
 namespace {
 
+#ifndef MOE_NV_LDS_COOP
+#define MOE_NV_LDS_COOP 1   // 1: the waves convert the stage's tokens to fp16 once, into a shared LDS tile
+#endif
+
 constexpr int kNvLdsWaves = 8;                      // two weight blocks of 4 units
 constexpr int kNvLdsNT = 8;                         // 8 token tiles of 16 rows: 128-row work tiles
 constexpr int kNvLdsRows = kNvLdsNT * 16;
-constexpr int kNvLdsStages = 3;
+constexpr int kNvLdsStages = MOE_NV_LDS_COOP ? 2 : 3;
+// The shared fp16 token tile: 128 rows x 128 K elements x 2 bytes; 16-byte
+// chunk c (K elements 8c..8c+7) of row n at position c ^ (n % 16), so the
+// 16 rows one operand read touches fall on distinct banks.
+constexpr int kNvF16Tile = MOE_NV_LDS_COOP ? kNvLdsRows * 128 * 2 : 0;
 
 struct NvLdsStage {
   static constexpr int W_CODES = 0;                                           // 8 x 4 KiB
@@ -57,7 +69,7 @@ struct NvLdsStage {
 constexpr int kNvDmaPerStage = 8;
 static_assert(kNvLdsRows * 64 == kNvLdsWaves * 1024, "one token-code DMA per wave");
 static_assert(2 * kNvLdsRows == kNvLdsWaves * 32, "32 token-scale dwords per wave");
-static_assert(kNvDmaPerStage * (kNvLdsStages - 2) <= 63, "vmcnt range");
+static_assert(kNvLdsStages < 3 || kNvDmaPerStage * (kNvLdsStages - 2) <= 63, "vmcnt range");
 
 template <bool B>
 struct NvBool {
@@ -191,6 +203,21 @@ __global__ void __launch_bounds__(64 * kNvLdsWaves, 1) gemm_lds_nv_kernel(
   v4f acc[kNvLdsNT][4];
   zero_acc<kNvLdsNT>(acc);
   const int tok_lane = lane & 15, kb = lane >> 4;
+  uint8_t* const f16 = lds + P * L::BYTES;   // the shared fp16 token tile (MOE_NV_LDS_COOP)
+  // MOE_NV_LDS_COOP: wave w converts token rows 16w..16w+15 of stage s, lane
+  // (row, kb) the 32 K elements of its 16-byte operand, into the fp16 tile.
+  auto convert_tokens = [&](int s) {
+    const uint8_t* st = lds + (s % P) * L::BYTES;
+    const int n = wave * 16 + tok_lane;
+    const uint4 b = *reinterpret_cast<const uint4*>(st + L::T_CODES + n * 64 + nv_tok_pos(n, kb) * 16);
+    const uint32_t bs =
+        *reinterpret_cast<const uint16_t*>(st + L::T_SCALES + ((kb >> 1) * ROWS + n) * 4 + (kb & 1) * 2);
+    v8h bo[4];
+    nv_lds_operands(b, bs, bo);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<v8h*>(f16 + n * 256 + (((4 * kb + i) ^ (n & 15)) << 4)) = bo[i];
+  };
   auto step = [&](int s, auto with_dma) {
     constexpr bool WITH_DMA = decltype(with_dma)::value;
     const uint8_t* st = lds + (s % P) * L::BYTES;
@@ -205,15 +232,21 @@ __global__ void __launch_bounds__(64 * kNvLdsWaves, 1) gemm_lds_nv_kernel(
     }
 #pragma unroll
     for (int nt = 0; nt < kNvLdsNT; ++nt) {
-      if constexpr (WITH_DMA) {
+      if constexpr (WITH_DMA && !MOE_NV_LDS_COOP) {
         if (nt < kNvDmaPerStage) issue_one(s + P - 1, nt);
       }
       const int n = nt * 16 + tok_lane;
-      const uint4 b = *reinterpret_cast<const uint4*>(st + L::T_CODES + n * 64 + nv_tok_pos(n, kb) * 16);
-      const uint32_t bs =
-          *reinterpret_cast<const uint16_t*>(st + L::T_SCALES + ((kb >> 1) * ROWS + n) * 4 + (kb & 1) * 2);
       v8h bo[4];
-      nv_lds_operands(b, bs, bo);
+      if constexpr (MOE_NV_LDS_COOP) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          bo[i] = *reinterpret_cast<const v8h*>(f16 + n * 256 + (((4 * kb + i) ^ (n & 15)) << 4));
+      } else {
+        const uint4 b = *reinterpret_cast<const uint4*>(st + L::T_CODES + n * 64 + nv_tok_pos(n, kb) * 16);
+        const uint32_t bs =
+            *reinterpret_cast<const uint16_t*>(st + L::T_SCALES + ((kb >> 1) * ROWS + n) * 4 + (kb & 1) * 2);
+        nv_lds_operands(b, bs, bo);
+      }
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
@@ -221,19 +254,34 @@ __global__ void __launch_bounds__(64 * kNvLdsWaves, 1) gemm_lds_nv_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  int s = 0;
-  for (; s + P - 1 < S; ++s) {
-    nv_wait_vm<kNvDmaPerStage * (P - 2)>();
-    nv_stage_barrier();
-    step(s, NvBool<true>{});
-  }
-  for (; s < S; ++s) {                      // the last P-1 steps issue nothing
-    if (s + P - 2 < S)
-      nv_wait_vm<kNvDmaPerStage * (P - 2)>();
-    else
+  if constexpr (MOE_NV_LDS_COOP) {
+    // Two stages.  Step s: wait for stage s, barrier (every wave has left
+    // step s-1, so the other ring slot and the fp16 tile are free), issue
+    // stage s+1, convert this wave's share of stage s's tokens, barrier, then
+    // the MFMAs, which overlap stage s+1's DMA.
+    for (int s = 0; s < S; ++s) {
       nv_wait_vm<0>();
-    nv_stage_barrier();
-    step(s, NvBool<false>{});
+      nv_stage_barrier();
+      if (s + 1 < S) issue(s + 1);
+      convert_tokens(s);
+      nv_stage_barrier();
+      step(s, NvBool<false>{});
+    }
+  } else {
+    int s = 0;
+    for (; s + P - 1 < S; ++s) {
+      nv_wait_vm<kNvDmaPerStage * (P - 2)>();
+      nv_stage_barrier();
+      step(s, NvBool<true>{});
+    }
+    for (; s < S; ++s) {                      // the last P-1 steps issue nothing
+      if (s + P - 2 < S)
+        nv_wait_vm<kNvDmaPerStage * (P - 2)>();
+      else
+        nv_wait_vm<0>();
+      nv_stage_barrier();
+      step(s, NvBool<false>{});
+    }
   }
 
   if constexpr (G1) {
@@ -251,7 +299,7 @@ static hipError_t launch_lds_nv(const uint8_t* wc, const uint8_t* wsc, const flo
                                 int H, int I, int E, int k, int hrows, uint8_t* hq, uint8_t* hsf, float* acc_out,
                                 uint16_t* y, hipStream_t stream) {
   auto kern = gemm_lds_nv_kernel<G1, WNT>;
-  const size_t lds = (size_t)kNvLdsStages * NvLdsStage::BYTES;
+  const size_t lds = (size_t)kNvLdsStages * NvLdsStage::BYTES + kNvF16Tile;
   hipError_t err = raise_lds_limit(reinterpret_cast<const void*>(kern), lds);
   if (err != hipSuccess) return err;
   const int nwb = (G1 ? I / 128 : H / 256) / 2;
