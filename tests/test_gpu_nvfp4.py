@@ -11,7 +11,8 @@
     pass), empty experts, masked and duplicate ids; and on the LDS-staged
     form (gemm_lds_nv.hip) with one and several 128-row tiles per expert,
     Zipf routing, and the XCD-paired block order of the DSV4 shape;
-  - the DSV4 shape at 64, 512 and 4096 tokens with weights quantized on the device:
+  - the DSV4 shape at 64, 512, 4096 and 16384 (Zipf) tokens with weights
+    quantized on the device:
     the device's NVFP4 weights against the oracle's, and every routed row of
     sampled tokens against the oracle.
 Weights of the small layers are quantized by the oracle and loaded as
@@ -266,7 +267,7 @@ def dsv4_nv_layer():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("cfg_index", [1, 2, 3])
+@pytest.mark.parametrize("cfg_index", [1, 2, 3, 4])
 def test_nv_dsv4_sampled_tokens(dsv4_nv_layer, cfg_index):
     cfg = synth.CONFIGS[cfg_index]
     big, bufs, (gx, gh) = dsv4_nv_layer

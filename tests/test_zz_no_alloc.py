@@ -2,7 +2,7 @@
 callers that cannot allocate) against moe_w4a4_forward on a caller-owned
 workspace, through the C ABI: two calls in a row, the second with fewer
 tokens, on both GEMM paths (many rows per expert: LDS-staged tiles; few:
-weight streaming), for both MMA types.  The forward is deterministic, so the
+weight streaming), for all three MMA types.  The forward is deterministic, so the
 outputs must be bit-identical.  A size past the scratch is refused on the
 host with MOE_ESCRATCH."""
 import numpy as np
@@ -26,13 +26,23 @@ def _inputs(T, seed):
     return dev_bf16(x), dev(ids), dev(w)
 
 
-@pytest.mark.parametrize("mma", [_lib.MOE_MMA_MXF4_X_MXF4, _lib.MOE_MMA_FP8_X_MXF4], ids=["mxf4xmxf4", "fp8xfp4"])
+# NVFP4 tensor scales (x, h, W1, W2): calibration constants above the
+# synthetic data's absolute maxima
+NV_SCALES = (2.0 ** -8, 8.0 / 2688, 6.1e-5, 5.3e-5)
+
+
+@pytest.mark.parametrize("mma", [_lib.MOE_MMA_MXF4_X_MXF4, _lib.MOE_MMA_FP8_X_MXF4, _lib.MOE_MMA_NVF4_X_NVF4],
+                         ids=["mxf4xmxf4", "fp8xfp4", "nvf4xnvf4"])
 def test_noalloc_forward_matches_the_workspace_forward(mma):
     log(f"[test] no-alloc forward, mma_type {mma}")
     layer = layer_for(CFG.hidden, CFG.inter, CFG.experts, CFG.topk, CFG.tokens, mma_type=mma)
-    layer.load_fp32(lambda e: synth.expert_weights_f32(CFG, e), threads=4)
+    ts = None
+    if mma == _lib.MOE_MMA_NVF4_X_NVF4:
+        gx, gh, g1, g2 = NV_SCALES
+        ts = (gx, gh, np.full(CFG.experts, g1, np.float32), np.full(CFG.experts, g2, np.float32))
+    layer.load_fp32(lambda e: synth.expert_weights_f32(CFG, e), threads=4, tensor_scales=ts)
     torch.cuda.synchronize()
-    for T, seed in ((2000, 1), (100, 2)):       # 250 then 25 rows per expert: tiled, then streaming
+    for T, seed in ((2000, 1), (50, 2)):        # 250 then 13 rows per expert: tiled, then streaming
         x, ids, w = _inputs(T, seed)
         log(f"    T={T}")
         ref = layer.forward(x, ids, w)
