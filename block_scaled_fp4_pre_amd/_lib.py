@@ -19,6 +19,9 @@ MOE_MMA_MXF4_X_MXF4, MOE_MMA_FP8_X_MXF4, MOE_MMA_NVF4_X_NVF4 = 0, 1, 2
 MOE_ACT_SWIGLU = 0
 MOE_STAGE_QUANT, MOE_STAGE_ROUTE, MOE_STAGE_GEMM1, MOE_STAGE_GEMM2, MOE_STAGE_COMBINE = 1, 2, 4, 8, 16
 MOE_STAGE_ALL = 31
+MOE_MEGA_MAX_ROWS = 256          # routed rows the single-launch forward takes
+MOE_MEGA_STATE_BYTES = 144 << 10  # its workspace state region (offset 0), zero before its first call
+MOE_MEGA_ERR_WORD = 800           # uint64 word of that region that a wait which gave up sets
 
 # Every symbol include/moe_w4a4.h declares.
 EXPORTED = (
@@ -28,6 +31,7 @@ EXPORTED = (
     "moe_w4a4_prepare_weights",
     "moe_w4a4_prepare_weights_nvfp4",
     "moe_w4a4_forward",
+    "moe_w4a4_forward_mega",
     "moe_w4a4_forward_noalloc",
     "moe_w4a4_status_string",
     "moe_w4a4_workspace_layout",
@@ -49,7 +53,7 @@ class moe_w4a4_cfg(ctypes.Structure):
 class moe_w4a4_ws_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "xq", "xsf", "counts", "offsets", "sorted_rows", "pos", "hist", "hq", "hsf", "y", "tiles",
-        "num_tiles", "xsf_planes", "total")]
+        "num_tiles", "xsf_planes", "mega", "total")]
 
 
 if not os.path.exists(LIB_PATH):
@@ -73,6 +77,7 @@ _lib.moe_w4a4_prepare_weights.argtypes = [_CFG, _P, _P, _P, _P, _P, _sz, _P]
 _lib.moe_w4a4_prepare_weights_nvfp4.argtypes = [_CFG, _P, _P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_float, _P,
                                                 _sz, _P]
 _lib.moe_w4a4_forward.argtypes = [_CFG, _P, _i32, _P, _P, _P, _P, _P, _sz, _P]
+_lib.moe_w4a4_forward_mega.argtypes = [_CFG, _P, _i32, _P, _P, _P, _P, _P, _sz, _P]
 _lib.moe_w4a4_forward_noalloc.argtypes = [_CFG, _P, _i32, _P, _P, _P, _P, _P]
 _lib.moe_w4a4_status_string.argtypes = [ctypes.c_int]
 _lib.moe_w4a4_status_string.restype = ctypes.c_char_p
@@ -260,6 +265,16 @@ def moe_w4a4_forward(cfg, prepared, num_tokens: int, x, topk_ids, topk_weights, 
                                  _ptr(topk_weights), _ptr(out), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream)),
            "moe_w4a4_forward")
+
+
+def moe_w4a4_forward_mega(cfg, prepared, num_tokens: int, x, topk_ids, topk_weights, out, workspace,
+                          stream=None) -> None:
+    """The forward as one kernel launch (decode sizes); arguments as moe_w4a4_forward."""
+    _check_forward_tensors(cfg, num_tokens, x, topk_ids, topk_weights, out, workspace, prepared)
+    _check(_lib.moe_w4a4_forward_mega(ctypes.byref(cfg), _ptr(prepared), int(num_tokens), _ptr(x), _ptr(topk_ids),
+                                      _ptr(topk_weights), _ptr(out), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(stream)),
+           "moe_w4a4_forward_mega")
 
 
 def moe_w4a4_forward_noalloc(cfg, prepared, num_tokens: int, x, topk_ids, topk_weights, out,

@@ -29,7 +29,7 @@ ARCH = "gfx950"
 
 DEVICE_SOURCES = ("quant.hip", "route.hip", "predispatch.hip", "gemm1.hip", "gemm2.hip", "gemm_lds.hip",
                   "gemm_nv.hip", "gemm_lds_nv.hip", "combine.hip",
-                  "prepare.hip", "noalloc.hip")
+                  "prepare.hip", "noalloc.hip", "mega.hip")
 HOST_SOURCES = ("abi.cpp", "validate.cpp")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include")]
 # Packed fp32 VALU ops are kept out of the device code.

@@ -25,6 +25,10 @@ constexpr int kMaxDevices = 64;
 #define MOE_STREAM_MAX_ROWS 16   // mean routed rows per expert up to which the VGPR-streaming GEMMs run
 #endif
 constexpr int kStreamMaxRows = MOE_STREAM_MAX_ROWS;
+// Polls of a wait in the single-launch forward before it gives up: about a
+// microsecond each (a sleep of 64 cycles and a load from memory), so about
+// 0.1 s, against waits of a few to a few hundred microseconds.
+constexpr uint32_t kMegaPollLimit = 1u << 16;
 
 std::atomic<int> g_is_gfx950[kMaxDevices];  // 0 unknown, 1 yes, 2 no
 
@@ -265,9 +269,37 @@ int moe_w4a4_run_stages(const moe_w4a4_cfg* cfg, const void* prepared, int32_t n
   return MOE_OK;
 }
 
+int moe_w4a4_forward_mega(const moe_w4a4_cfg* cfg, const void* prepared, int32_t num_tokens, const uint16_t* x,
+                          const int32_t* topk_ids, const float* topk_weights, uint16_t* out, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  bool noop = false;
+  int st = moe::check_stage_args(cfg, prepared, num_tokens, x, topk_ids, topk_weights, out, workspace,
+                                 workspace_bytes, MOE_STAGE_ALL, nullptr, &noop);
+  if (st != MOE_OK) return st;
+  st = moe::check_mega_args(cfg, num_tokens);
+  if (st != MOE_OK || noop) return st;
+  st = moe::check_device();
+  if (st != MOE_OK) return st;
+  const moe_w4a4_ws_layout L = moe::ws_layout(cfg);
+  const moe::PreparedLayout P = moe::prepared_layout(cfg);
+  const uint8_t* pw = static_cast<const uint8_t*>(prepared);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  return hip_status(moe::launch_mega(
+      pw + P.w1c, pw + P.w1s, pw + P.w2c, pw + P.w2s, x, topk_ids, topk_weights, out, num_tokens, cfg->hidden,
+      cfg->inter, cfg->num_experts, cfg->topk, cfg->max_tokens * cfg->topk, ws + L.xq, ws + L.xsf, ws + L.hq,
+      ws + L.hsf, reinterpret_cast<uint16_t*>(ws + L.y), reinterpret_cast<uint64_t*>(ws + L.mega),
+      reinterpret_cast<int32_t*>(ws + L.counts), reinterpret_cast<int32_t*>(ws + L.offsets),
+      reinterpret_cast<int32_t*>(ws + L.sorted_rows), reinterpret_cast<int32_t*>(ws + L.pos), kMegaPollLimit,
+      static_cast<hipStream_t>(stream)));
+}
+
 int moe_w4a4_forward(const moe_w4a4_cfg* cfg, const void* prepared, int32_t num_tokens, const uint16_t* x,
                      const int32_t* topk_ids, const float* topk_weights, uint16_t* out, void* workspace,
                      size_t workspace_bytes, void* stream) {
+  if (cfg != nullptr && moe::check_cfg(cfg) == MOE_OK && moe::check_mega_args(cfg, num_tokens) == MOE_OK &&
+      (int64_t)num_tokens * cfg->topk <= MOE_MEGA_AUTO_ROWS)
+    return moe_w4a4_forward_mega(cfg, prepared, num_tokens, x, topk_ids, topk_weights, out, workspace,
+                                 workspace_bytes, stream);
   return moe_w4a4_run_stages(cfg, prepared, num_tokens, x, topk_ids, topk_weights, out, workspace,
                              workspace_bytes, MOE_STAGE_ALL, nullptr, stream);
 }

@@ -9,6 +9,20 @@
 
 namespace moe {
 
+// Store policies of the epilogues.  PlainStore: ordinary stores, made visible
+// to other workgroups by the kernel's end.  CoherentStore: agent-scope stores
+// (the sc1 policy on gfx950), visible to the agent-scope loads of any
+// workgroup on the device once they complete, for results that another
+// workgroup of the same launch reads (mega.hip).
+struct PlainStore {
+  template <class T>
+  __device__ static void put(T* p, T v) { *p = v; }
+};
+struct CoherentStore {
+  template <class T>
+  __device__ static void put(T* p, T v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+};
+
 // SwiGLU in fp32: silu(g) * u, silu(g) = g / (1 + e^-g).  e^-g is the hardware
 // 2^x of -g * log2(e) and the quotient goes through the hardware reciprocal:
 // a few ulp from the correctly rounded value, against ~20 instructions per
@@ -33,7 +47,7 @@ __device__ __forceinline__ float swiglu(float g, float u) {
 // hrows being the rows of a plane.  A tile of consecutive rows then reads one
 // contiguous run per K step.  Unit u is PB / 4 code bytes and scale byte u % 4
 // of plane u / 4.
-template <int NT, bool F8 = false>
+template <int NT, bool F8 = false, class St = PlainStore>
 __device__ __forceinline__ void gemm1_epilogue(v4f (&acc)[NT][4], int u, int row0, int nrows, int I, int hrows,
                                                int lane, uint8_t* __restrict__ hq, uint8_t* __restrict__ hsf,
                                                float* __restrict__ acc_out) {
@@ -63,17 +77,17 @@ __device__ __forceinline__ void gemm1_epilogue(v4f (&acc)[NT][4], int u, int row
         // columns 4kb..4kb+3 and 16+4kb..16+4kb+3 of the unit's 32 bytes
         const float inv = e4m3_exp2(-ex);
         uint8_t* row = hq + pr * 128 + (u & 3) * 32;
-        *reinterpret_cast<uint32_t*>(row + 4 * kb) = e4m3_pack4(h[0], h[1], h[2], h[3], inv);
-        *reinterpret_cast<uint32_t*>(row + 16 + 4 * kb) = e4m3_pack4(h[4], h[5], h[6], h[7], inv);
+        St::put(reinterpret_cast<uint32_t*>(row + 4 * kb), e4m3_pack4(h[0], h[1], h[2], h[3], inv));
+        St::put(reinterpret_cast<uint32_t*>(row + 16 + 4 * kb), e4m3_pack4(h[4], h[5], h[6], h[7], inv));
       } else {
         const float sc = exp2_scale(ex);
         const uint32_t lo = e2m1_pack2<1>(e2m1_pack2<0>(0u, h[0], h[1], sc), h[2], h[3], sc);
         const uint32_t hi = e2m1_pack2<1>(e2m1_pack2<0>(0u, h[4], h[5], sc), h[6], h[7], sc);
         uint8_t* row = hq + pr * 64 + (u & 3) * 16;
-        *reinterpret_cast<uint16_t*>(row + 2 * kb) = (uint16_t)lo;
-        *reinterpret_cast<uint16_t*>(row + 8 + 2 * kb) = (uint16_t)hi;
+        St::put(reinterpret_cast<uint16_t*>(row + 2 * kb), (uint16_t)lo);
+        St::put(reinterpret_cast<uint16_t*>(row + 8 + 2 * kb), (uint16_t)hi);
       }
-      if (kb == 0) hsf[pr * 4 + (u & 3)] = (uint8_t)(ex + 127);
+      if (kb == 0) St::put(hsf + pr * 4 + (u & 3), (uint8_t)(ex + 127));
       if (acc_out != nullptr) {
         float* arow = acc_out + (size_t)p * (2 * I) + 32 * u + 4 * kb;
 #pragma unroll
@@ -91,7 +105,7 @@ __device__ __forceinline__ void gemm1_epilogue(v4f (&acc)[NT][4], int u, int row
 // GEMM2 unit v (hidden rows [64v, 64v+64)): y rows in sorted order, the fp32
 // accumulators rounded to bfloat16 (nearest even) -- half the bytes of the
 // y round trip to the combine.
-template <int NT>
+template <int NT, class St = PlainStore>
 __device__ __forceinline__ void gemm2_epilogue(const v4f (&acc)[NT][4], int v, int row0, int nrows, int H,
                                                int lane, uint16_t* __restrict__ y) {
   const int tok_lane = lane & 15, kb = lane >> 4;
@@ -102,9 +116,9 @@ __device__ __forceinline__ void gemm2_epilogue(const v4f (&acc)[NT][4], int v, i
       uint16_t* yrow = y + (size_t)(row0 + n) * H + 64 * v + 4 * kb;
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
-        *reinterpret_cast<uint2*>(yrow + 16 * rb) =
-            make_uint2(f32_to_bf16(acc[nt][rb][0]) | (f32_to_bf16(acc[nt][rb][1]) << 16),
-                       f32_to_bf16(acc[nt][rb][2]) | (f32_to_bf16(acc[nt][rb][3]) << 16));
+        St::put(reinterpret_cast<uint64_t*>(yrow + 16 * rb),
+                (uint64_t)(f32_to_bf16(acc[nt][rb][0]) | (f32_to_bf16(acc[nt][rb][1]) << 16)) |
+                    ((uint64_t)(f32_to_bf16(acc[nt][rb][2]) | (f32_to_bf16(acc[nt][rb][3]) << 16)) << 32));
     }
   }
 }

@@ -1,0 +1,617 @@
+// The whole forward of the layer in one launch, for decode-sized batches: the
+// pages' single fused "mega" MoE kernel ([P1] sglang PR "[deepseek-v4] Bump
+// sgl-deep-gemm for packed FP4xFP4 mega-MoE (W4A4)", title and section B,
+// where one kernel runs the routed experts' layer).  MXFP4 x MXFP4, at most
+// kMegaMaxRows routed rows, hidden and inter multiples of 512 up to 4096
+// (validate.h).
+//
+// Stage S1 inside the work items.  Every workgroup routes the T*k ids itself
+// (the stable counting sort of route_common.h in LDS, one thread per routed
+// row), so no workgroup waits for a routing stage, and the GEMM1 items
+// quantize the token rows they need straight from x with the quantize
+// kernel's encoder (quant_group.h).
+//
+// Work items, in two phases:
+//   GEMM1 (active expert, W1 unit u of 64 rows): the 4 waves split K into 4
+//     slices.  Each wave loads its slice of the unit's weights into VGPRs at
+//     once (every load in flight together); the workgroup quantizes the
+//     expert's token rows into an LDS tile (kept for the next item when that
+//     is of the same expert); each wave runs 4 MFMAs per K step of its slice.
+//     The slices' partial sums meet in LDS in a fixed order; wave 0 runs the
+//     SwiGLU + requant epilogue (epilogue.h) with agent-scope stores, waits
+//     for them, and adds one to the expert's h counter.  A GEMM1 item never
+//     waits.
+//   GEMM2 (active expert, W2 unit v of 64 hidden rows): the weights as above,
+//     loaded before the wait for the expert's h counter to reach its number of
+//     GEMM1 items; then each wave's slice of h by agent-scope loads, the
+//     MFMAs, the reduction, and y (bf16) by agent-scope stores.  For each of its rows the item then adds
+//     one to the (token, v) combine counter; the item that brings it to the
+//     token's number of valid slots combines those 64 columns of the token
+//     (stage S4), in slot order, as combine.hip does.
+// Each phase's items are dealt round-robin over kMegaQueues ticket counters
+// (one fetch-and-add per item, spread over as many addresses, since
+// same-address atomics from every CU serialize in the memory system).  A
+// workgroup starts on the queue of its own index, moves on to the others,
+// and takes GEMM2 items only once it has seen every GEMM1 queue run out:
+// every GEMM1 item a GEMM2 item waits for has then been handed to a running
+// workgroup, whatever order the hardware dispatches workgroups in.
+//
+// Hand-off between workgroups: the producer stores with the agent-scope
+// policy, waits for those stores to complete (vmcnt), then adds to the
+// counter with an agent-scope atomic; the consumer reads the counter and then
+// the data with agent-scope loads.  Data that only moves through agent-scope
+// accesses needs no L2 write-back or invalidate.
+//
+// The state region (queues, counters) must be zero at the launch; the last
+// workgroup to finish, found by a two-level count, zeroes it again, so a
+// zeroed workspace stays valid for every later call (a replayed graph
+// included).  Every wait gives up after poll_limit polls: it sets the error
+// word (which the kernel never clears) and the abort word, after which no wait
+// waits, so the launch always drains.
+#include <climits>
+
+#include "epilogue.h"
+#include "gemm_common.h"
+#include "launch.h"
+#include "quant_group.h"
+#include "tiles.h"
+#include "validate.h"
+
+namespace moe {
+namespace {
+
+constexpr int kMegaThreads = 256;
+constexpr int kMegaWaves = kMegaThreads / kWave;   // K slices of a work item
+constexpr int kMegaMaxL = 8;                        // K steps per slice, at most (1, 2, 4 or 8)
+static_assert(kMegaMaxRows <= kMegaThreads, "one routed row per thread");
+static_assert(kMegaMaxK / kStepK <= kMegaWaves * kMegaMaxL, "K slices");
+
+// The state region (validate.h: kMegaStateBytes), in 8-byte words: each
+// ticket and done counter on a 128-byte line of its own.
+constexpr int kLine = 16;                                   // words per 128 bytes
+constexpr int kQueueA = 0;                                  // GEMM1 ticket counters
+constexpr int kQueueB = kQueueA + kMegaQueues * kLine;      // GEMM2 ticket counters
+constexpr int kDone1 = kQueueB + kMegaQueues * kLine;       // finished workgroups, by blockIdx % kMegaQueues
+constexpr int kDone2 = kDone1 + kMegaQueues * kLine;        // finished groups of kDone1
+constexpr int kAbort = kDone2 + kLine;                      // nonzero: waits give up at once
+constexpr int kErr = kAbort + kLine;                        // nonzero: a wait gave up (never cleared here)
+constexpr int kCounters = kErr + kLine;                     // h counters [E], then combine counters
+static_assert((uint64_t)(kCounters + kMaxExperts + kMegaMaxRows * (kMegaMaxK / 64)) * 8 <= kMegaStateBytes,
+              "state region");
+static_assert(kErr == MOE_MEGA_ERR_WORD, "error word documented in moe_w4a4.h");
+
+constexpr int kTokStride = kMegaMaxK / 2 + 16;
+constexpr int kTscStride = kMegaMaxK / 32 + 4;
+
+struct MegaLds {
+  int wcnt[kMegaWaves][kMaxExperts];   // route: rows of each expert per wave
+  int off[kMaxExperts + 1];            // sorted position of each expert's first row
+  int act[kMaxExperts];                // active experts, ascending
+  int sorted[kMegaMaxRows];            // flat row t*k+j at each sorted position
+  int pos[kMegaMaxRows];               // sorted position of each flat row, or -1
+  int wave_tot[kMegaWaves];
+  int nact;
+  int item;
+  int last;
+  int tok_key;                         // (expert, first row) of the token tile, or -1
+  float red[kMegaWaves - 1][kWave][16];   // partial sums of K slices 1..3
+  // GEMM1's token tile: 16 quantized token rows of one expert over all of K,
+  // rows kTokStride bytes apart (16 bytes of padding put the 16 rows one MFMA
+  // operand read touches on distinct banks), and their scale bytes.
+  uint8_t tok[16 * kTokStride];
+  uint8_t tsc[16 * kTscStride];
+};
+
+__device__ __forceinline__ uint64_t ld_agent(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t add_agent(uint64_t* p, uint64_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Polls *p until it equals want; false after `limit` polls, or as soon as
+// the error word *err is set (err may be null), so that once one wait has
+// given up the launch drains without waiting again.
+__device__ __forceinline__ bool wait_eq(const uint64_t* p, uint64_t want, const uint64_t* err, uint32_t limit) {
+  for (uint32_t i = 0; i < limit; ++i) {
+    if (ld_agent(p) == want) return true;
+    if (err != nullptr && ld_agent(err) != 0) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return ld_agent(p) == want;
+}
+
+struct MegaArgs {
+  const uint8_t* w1c;
+  const uint8_t* w1s;
+  const uint8_t* w2c;
+  const uint8_t* w2s;
+  const uint16_t* x;
+  uint8_t* xq;
+  uint8_t* xsf;
+  const int32_t* ids;
+  const float* tw;
+  uint16_t* out;
+  uint8_t* hq;
+  uint8_t* hsf;
+  uint16_t* y;
+  uint64_t* state;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_rows;
+  int32_t* pos;
+  int T, H, I, E, k, nbits, hrows;
+  uint32_t poll_limit;
+};
+
+// The workgroup's own route: counts, offsets, the active experts and both
+// directions of the permutation, as the route stage computes them.
+__device__ void mega_route(const MegaArgs& A, MegaLds& sh) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const int R = A.T * A.k, E = A.E;
+  int e = -1;
+  if (tid < R) {
+    const int id = A.ids[tid];
+    e = id >= 0 && id < E ? id : -1;
+  }
+  for (int i = tid; i < E; i += kMegaThreads)
+#pragma unroll
+    for (int ww = 0; ww < kMegaWaves; ++ww) sh.wcnt[ww][i] = 0;
+  __syncthreads();
+  const bool valid = e >= 0;
+  uint64_t match = __ballot(valid);
+  for (int bit = 0; bit < A.nbits; ++bit) {
+    const uint64_t m1 = __ballot(valid && ((e >> bit) & 1));
+    match &= ((e >> bit) & 1) ? m1 : ~m1;
+  }
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+  const int rank_w = __popcll(match & below);
+  if (valid && rank_w == 0) sh.wcnt[w][e] = __popcll(match);
+  __syncthreads();
+  // Thread t scans experts 2t and 2t+1 (E <= 512): row count in the low 16
+  // bits, 1 << 16 per active expert above.
+  const int e0 = 2 * tid, e1 = 2 * tid + 1;
+  int c0 = 0, c1 = 0;
+#pragma unroll
+  for (int ww = 0; ww < kMegaWaves; ++ww) {
+    if (e0 < E) c0 += sh.wcnt[ww][e0];
+    if (e1 < E) c1 += sh.wcnt[ww][e1];
+  }
+  const int v0 = c0 | (c0 > 0 ? 1 << 16 : 0), v1 = c1 | (c1 > 0 ? 1 << 16 : 0);
+  int incl = v0 + v1;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int o = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += o;
+  }
+  if (lane == kWave - 1) sh.wave_tot[w] = incl;
+  __syncthreads();
+  for (int ww = 0; ww < w; ++ww) incl += sh.wave_tot[ww];
+  const int ex0 = incl - v0 - v1, ex1 = ex0 + v0;
+  if (e0 < E) {
+    sh.off[e0] = ex0 & 0xFFFF;
+    if (c0 > 0) sh.act[ex0 >> 16] = e0;
+  }
+  if (e1 < E) {
+    sh.off[e1] = ex1 & 0xFFFF;
+    if (c1 > 0) sh.act[ex1 >> 16] = e1;
+  }
+  if (tid == kMegaThreads - 1) {
+    sh.off[E] = incl & 0xFFFF;
+    sh.nact = incl >> 16;
+  }
+  __syncthreads();
+  if (tid < R) {
+    if (valid) {
+      int rank = rank_w;
+      for (int ww = 0; ww < w; ++ww) rank += sh.wcnt[ww][e];
+      const int p = sh.off[e] + rank;
+      sh.pos[tid] = p;
+      sh.sorted[p] = tid;
+    } else {
+      sh.pos[tid] = -1;
+    }
+  }
+  __syncthreads();
+}
+
+// Writes the route to the workspace and zeroes the output rows of tokens with
+// no valid slot (nothing else writes them).  Called by one workgroup.
+__device__ void mega_route_out(const MegaArgs& A, const MegaLds& sh) {
+  const int tid = threadIdx.x, R = A.T * A.k;
+  for (int e = tid; e <= A.E; e += kMegaThreads) {
+    A.offsets[e] = sh.off[e];
+    if (e < A.E) A.counts[e] = sh.off[e + 1] - sh.off[e];
+  }
+  if (tid < R) {
+    A.pos[tid] = sh.pos[tid];
+    if (tid < sh.off[A.E]) A.sorted_rows[tid] = sh.sorted[tid];
+  }
+  const int pieces = A.H / 8;
+  for (int i = tid; i < A.T * pieces; i += kMegaThreads) {
+    const int t = i / pieces;
+    bool any = false;
+    for (int j = 0; j < A.k; ++j) any |= sh.pos[t * A.k + j] >= 0;
+    if (!any) reinterpret_cast<uint4*>(A.out + (size_t)t * A.H)[i - t * pieces] = make_uint4(0, 0, 0, 0);
+  }
+}
+
+// K-slice w's weights of one unit: all L steps in flight at once.
+template <int L>
+__device__ __forceinline__ void mega_load_weights(const uint8_t* codes, const uint8_t* scales, int lane,
+                                                  uint4 (&a)[L][4], uint32_t (&sa)[L]) {
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(codes, (uint32_t)(L - 1) * kUnitStepStride + kStepCodeBytes);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales, (uint32_t)(L - 1) * kUnitScaleStride + kStepScaleBytes);
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) a[i][rb] = buf_load16(wr, lane * 16 + rb * 1024, i * kUnitStepStride);
+    sa[i] = buf_load4(sr, lane * 4, i * kUnitScaleStride);
+  }
+}
+
+// Sums the K slices into wave 0's acc, slice 0 first.  Ends with a barrier:
+// the caller's wave 0 then owns the sums, and the other waves may go on.
+__device__ __forceinline__ void mega_reduce(MegaLds& sh, int w, int lane, v4f (&acc)[1][4]) {
+  if (w > 0) {
+    float4* d = reinterpret_cast<float4*>(&sh.red[w - 1][lane][0]);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) d[rb] = make_float4(acc[0][rb][0], acc[0][rb][1], acc[0][rb][2], acc[0][rb][3]);
+  }
+  __syncthreads();
+  if (w == 0) {
+#pragma unroll
+    for (int q = 0; q < kMegaWaves - 1; ++q) {
+      const float4* s = reinterpret_cast<const float4*>(&sh.red[q][lane][0]);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const float4 v = s[rb];
+        acc[0][rb][0] += v.x;
+        acc[0][rb][1] += v.y;
+        acc[0][rb][2] += v.z;
+        acc[0][rb][3] += v.w;
+      }
+    }
+  }
+}
+
+// MXFP4 of the 32-element group g of the bf16 row src: the quantize stage's
+// encoder (quant_group.h).
+__device__ __forceinline__ void mega_quantize_group(const uint16_t* src, int g, uint4& codes, uint32_t& scale) {
+  uint32_t w[16];
+  load_bf16_words(src, g, w);
+  scale = mx_encode_bf16_group(w, codes);
+}
+
+// The quantized tokens as the quantize stage writes them (xq [T, H/2], xsf
+// [T, H/32]), for inspection only: the GEMM1 items quantize their own rows.
+__device__ void mega_tokens_out(const MegaArgs& A) {
+  const int groups = A.H / 32;
+  for (int i = threadIdx.x; i < A.T * groups; i += kMegaThreads) {
+    const int t = i / groups, g = i - t * groups;
+    uint4 c;
+    uint32_t sc;
+    mega_quantize_group(A.x + (size_t)t * A.H, g, c, sc);
+    reinterpret_cast<uint4*>(A.xq + (size_t)t * (A.H / 2))[g] = c;
+    A.xsf[(size_t)t * groups + g] = (uint8_t)sc;
+  }
+}
+
+// Combines the 64 columns of block v of token t (stage S4, as combine.hip:
+// slots in order, fp32 from +0, one rounding to bf16); lane c takes column
+// 64v + c.  y by agent-scope loads.
+__device__ void mega_combine(const MegaArgs& A, const MegaLds& sh, int t, int v, int lane) {
+  const int col = 64 * v + lane;
+  float s = 0.f;
+  for (int j0 = 0; j0 < A.k; j0 += 4) {
+    uint32_t yv[4];
+    float wj[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int j = j0 + q;
+      const int pj = j < A.k ? sh.pos[t * A.k + j] : -1;
+      wj[q] = pj >= 0 ? A.tw[(size_t)t * A.k + j] : 0.f;
+      yv[q] = pj >= 0 ? __hip_atomic_load(A.y + (size_t)pj * A.H + col, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                      : 0u;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int j = j0 + q;
+      if (j < A.k && sh.pos[t * A.k + j] >= 0) s += wj[q] * bf16_to_f32(yv[q]);
+    }
+  }
+  A.out[(size_t)t * A.H + col] = (uint16_t)f32_to_bf16(s);
+}
+
+// Issues this wave's weight loads of item i: expert act[i / N], unit i % N,
+// the wave's K slice.
+template <bool G1, int L>
+__device__ __forceinline__ void mega_item_weights(const MegaArgs& A, const MegaLds& sh, int i, int N, int w,
+                                                  int lane, uint4 (&a)[L][4], uint32_t (&sa)[L]) {
+  const int e = sh.act[i / N], unit = i % N, s0 = w * L;
+  if constexpr (G1)
+    mega_load_weights<L>(A.w1c + w1_code_offset(e, unit, s0, A.H, A.I),
+                         A.w1s + w1_scale_offset(e, unit, s0, A.H, A.I), lane, a, sa);
+  else
+    mega_load_weights<L>(A.w2c + w2_code_offset(e, unit, s0, A.H, A.I),
+                         A.w2s + w2_scale_offset(e, unit, s0, A.H, A.I), lane, a, sa);
+}
+
+// GEMM1's token tile for a pass over the sorted rows p0 .. p0 + nrows - 1:
+// the rows of x quantized by the workgroup with the quantize stage's encoder
+// (quant_group.h) into LDS, 16 rows over all of K (rows kTokStride bytes
+// apart, 16 bytes of padding putting the 16 rows one MFMA operand read
+// touches on distinct banks; scale bytes kTscStride apart).  The tile is kept
+// while the pass stays the same (key: its first sorted row).  All threads
+// call it.
+__device__ __forceinline__ void mega_token_tile(const MegaArgs& A, MegaLds& sh, int p0, int nrows) {
+  if (sh.tok_key == p0) return;
+  const int groups = A.H / 32;
+  for (int i = threadIdx.x; i < nrows * groups; i += kMegaThreads) {
+    const int r = i / groups, g = i - r * groups;
+    uint32_t w[16];
+    load_bf16_words(A.x + (size_t)(sh.sorted[p0 + r] / A.k) * A.H, g, w);
+    uint4 c;
+    sh.tsc[r * kTscStride + g] = (uint8_t)mx_encode_bf16_group(w, c);
+    *reinterpret_cast<uint4*>(sh.tok + r * kTokStride + g * 16) = c;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) sh.tok_key = p0;   // read again only after a later barrier
+}
+
+// The 16 code bytes at p and the scale byte kb of the dword at s4, by
+// agent-scope loads.
+__device__ __forceinline__ void ld_operand(const uint8_t* p, const uint8_t* s4, int kb, uint4& b, uint32_t& sb) {
+  const uint64_t* c = reinterpret_cast<const uint64_t*>(p);
+  const uint64_t lo = ld_agent(c), hi = ld_agent(c + 1);
+  b = make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32));
+  const uint32_t w = __hip_atomic_load(reinterpret_cast<const uint32_t*>(s4), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  sb = (w >> (8 * kb)) & 0xFFu;
+}
+
+// One pass of a wave over its K slice (from step s0), rows p0 .. p0 + nrows
+// - 1 (row min(r, nrows - 1) for lane row r: rows past the expert's last
+// re-read it, their results are not stored): per step the token operand, then
+// 4 MFMAs (one per 16-row weight block).  GEMM1: the operand from the LDS
+// token tile.  GEMM2: h by agent-scope loads (K-step planes of hrows rows,
+// epilogue.h).
+template <bool G1, int L>
+__device__ __forceinline__ void mega_pass(const MegaArgs& A, const MegaLds& sh, int p0, int nrows, int s0,
+                                          int lane, const uint4 (&a)[L][4], const uint32_t (&sa)[L],
+                                          v4f (&acc)[1][4]) {
+  const int r = lane & 15, kb = lane >> 4;
+  const int rr = min(r, nrows - 1);
+  const size_t pp = (size_t)s0 * A.hrows + p0 + rr;
+  zero_acc<1>(acc);
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    uint4 b;
+    uint32_t sb;
+    if constexpr (G1) {
+      b = *reinterpret_cast<const uint4*>(sh.tok + rr * kTokStride + (s0 + i) * 64 + kb * 16);
+      sb = sh.tsc[rr * kTscStride + (s0 + i) * 4 + kb];
+    } else {
+      const size_t pr = pp + (size_t)i * A.hrows;
+      ld_operand(A.hq + pr * 64 + kb * 16, A.hsf + pr * 4, kb, b, sb);
+    }
+    acc[0][0] = mfma_fp4<0, 0>(a[i][0], b, acc[0][0], (int)sa[i], (int)sb);
+    acc[0][1] = mfma_fp4<1, 0>(a[i][1], b, acc[0][1], (int)sa[i], (int)sb);
+    acc[0][2] = mfma_fp4<2, 0>(a[i][2], b, acc[0][2], (int)sa[i], (int)sb);
+    acc[0][3] = mfma_fp4<3, 0>(a[i][3], b, acc[0][3], (int)sa[i], (int)sb);
+  }
+}
+
+// Wave 0's end of a pass.  GEMM1: the SwiGLU + requant epilogue (h).  GEMM2:
+// y, then for each row one more on its token's combine counter of block v,
+// and the combines this completes.
+template <bool G1>
+__device__ void mega_finish_pass(const MegaArgs& A, const MegaLds& sh, int unit, int p0, int nrows, int lane,
+                                 v4f (&acc)[1][4]) {
+  if constexpr (G1) {
+    gemm1_epilogue<1, false, CoherentStore>(acc, unit, p0, nrows, A.I, A.hrows, lane, A.hq, A.hsf, nullptr);
+  } else {
+    gemm2_epilogue<1, CoherentStore>(acc, unit, p0, nrows, A.H, lane, A.y);
+    wait_vmem_all();   // y stores complete before the combine counters say so
+    const int r = lane & 15, kb = lane >> 4;
+    int tok = 0;
+    bool last = false;
+    if (r < nrows && kb == 0) {
+      tok = sh.sorted[p0 + r] / A.k;
+      int nvalid = 0;
+      for (int j = 0; j < A.k; ++j) nvalid += sh.pos[tok * A.k + j] >= 0;
+      uint64_t* ccnt = A.state + kCounters + A.E;
+      last = (int)add_agent(ccnt + (size_t)tok * (A.H / 64) + unit, 1) + 1 == nvalid;
+    }
+    uint64_t m = __ballot(last);
+    while (m) {
+      const int src = __ffsll((long long)m) - 1;
+      m &= m - 1;
+      mega_combine(A, sh, __shfl(tok, src, kWave), unit, lane);
+    }
+  }
+}
+
+// One queue of a phase (the counter at ctr hands out items q, q +
+// kMegaQueues, ... below n), pipelined: the next item's ticket is taken while
+// the current item runs, and each wave issues the next item's weights as soon
+// as its MFMAs have consumed the current ones, before the epilogue.
+template <bool G1, int L>
+__device__ void mega_queue(const MegaArgs& A, MegaLds& sh, uint64_t* ctr, int q, int n) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int N = G1 ? A.I / 32 : A.H / 64, s0 = w * L;
+  if (tid == 0) sh.item = (int)min(add_agent(ctr, 1) * kMegaQueues + q, (uint64_t)INT_MAX);
+  __syncthreads();
+  int cur = sh.item;
+  __syncthreads();
+  if (cur >= n) return;
+  uint4 a[L][4];
+  uint32_t sa[L];
+  mega_item_weights<G1, L>(A, sh, cur, N, w, lane, a, sa);
+  for (;;) {
+    uint64_t next_raw = 0;
+    if (tid == 0) next_raw = add_agent(ctr, 1);
+    // An opaque copy of the lane index per item: the lane-derived addresses
+    // are recomputed here instead of being hoisted out of the loops and held
+    // (or spilled) across them.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int e = sh.act[cur / N], unit = cur % N;
+    const int base = sh.off[e], n_e = sh.off[e + 1] - base;
+    if constexpr (!G1) {
+      // h of the expert is complete once each of its I/32 GEMM1 items has counted
+      if (!wait_eq(A.state + kCounters + e, (uint64_t)(A.I / 32), A.state + kAbort, A.poll_limit) && ln == 0) {
+        st_agent(A.state + kErr, 1);
+        st_agent(A.state + kAbort, 1);
+      }
+    }
+    int nxt = INT_MAX;
+    for (int t0 = 0; t0 < n_e; t0 += 16) {
+      const int nrows = min(16, n_e - t0);
+      const bool last = t0 + 16 >= n_e;
+      if constexpr (G1) mega_token_tile(A, sh, base + t0, nrows);
+      v4f acc[1][4];
+      mega_pass<G1, L>(A, sh, base + t0, nrows, s0, ln, a, sa, acc);
+      if (last && tid == 0) sh.item = (int)min(next_raw * kMegaQueues + q, (uint64_t)INT_MAX);
+      mega_reduce(sh, w, ln, acc);   // a barrier: sh.item is published
+      if (last) nxt = sh.item;
+      // (Separate paths for "no next item" and "next item", each loading the
+      // weights unconditionally, so that the spent weights are dead during
+      // the epilogue instead of being kept for a merge with the new ones.)
+      if (last && nxt >= n) {
+        if (w == 0) {
+          mega_finish_pass<G1>(A, sh, unit, base + t0, nrows, ln, acc);
+          if constexpr (G1) {
+            wait_vmem_all();   // h stores complete before the counter says so
+            if (ln == 0) add_agent(A.state + kCounters + e, 1);
+          }
+        }
+        __syncthreads();
+        return;
+      }
+      if (w == 0) {
+        mega_finish_pass<G1>(A, sh, unit, base + t0, nrows, ln, acc);
+        if (last) {
+          if constexpr (G1) {
+            wait_vmem_all();
+            if (ln == 0) add_agent(A.state + kCounters + e, 1);
+          }
+          mega_item_weights<G1, L>(A, sh, nxt, N, 0, ln, a, sa);
+        }
+      } else if (last) {
+        mega_item_weights<G1, L>(A, sh, nxt, N, w, ln, a, sa);
+      }
+      __syncthreads();   // the partial sums' LDS and sh.item are free again
+    }
+    cur = nxt;
+  }
+}
+
+// Takes the items of one phase (n of them, item i on queue i % kMegaQueues)
+// until every queue has run out: first the workgroup's own queue, then,
+// after one read of all the queue counters at once, any queue still open.
+template <bool G1, int L>
+__device__ void mega_phase(const MegaArgs& A, MegaLds& sh, uint64_t* q0, int n) {
+  const int tid = threadIdx.x;
+  int q = blockIdx.x % kMegaQueues;
+  for (;;) {
+    mega_queue<G1, L>(A, sh, q0 + q * kLine, q, n);
+    if (tid < kWave) {
+      const bool open = tid < kMegaQueues && ld_agent(q0 + tid * kLine) * kMegaQueues + tid < (uint64_t)n;
+      const uint64_t m = __ballot(open);
+      if (tid == 0) sh.item = (int)m;
+    }
+    __syncthreads();
+    const uint32_t mask = (uint32_t)sh.item;
+    __syncthreads();
+    if (mask == 0) break;
+    // the next open queue after q, cyclically
+    const uint32_t rot = ((mask >> (q + 1)) | (mask << (kMegaQueues - q - 1))) & ((1u << kMegaQueues) - 1);
+    q = (q + 1 + __builtin_ctz(rot)) % kMegaQueues;
+  }
+}
+
+// A phase with its K-slice length as a compile-time constant.
+template <bool G1>
+__device__ __forceinline__ void mega_phase_l(const MegaArgs& A, MegaLds& sh, uint64_t* q0, int n) {
+  switch ((G1 ? A.H : A.I) / kStepK / kMegaWaves) {
+    case 8: mega_phase<G1, 8>(A, sh, q0, n); break;
+    case 4: mega_phase<G1, 4>(A, sh, q0, n); break;
+    case 2: mega_phase<G1, 2>(A, sh, q0, n); break;
+    default: mega_phase<G1, 1>(A, sh, q0, n); break;
+  }
+}
+
+}  // namespace
+
+__global__ void __launch_bounds__(kMegaThreads, 2) mega_moe_kernel(MegaArgs A) {
+  __shared__ MegaLds sh;
+  const int tid = threadIdx.x;
+  mega_route(A, sh);
+  if (tid == 0) sh.tok_key = -1;   // ordered before its first read by the barriers of the phases
+  if (blockIdx.x == 0) {
+    mega_route_out(A, sh);
+    mega_tokens_out(A);
+  }
+  mega_phase_l<true>(A, sh, A.state + kQueueA, sh.nact * (A.I / 32));
+  mega_phase_l<false>(A, sh, A.state + kQueueB, sh.nact * (A.H / 64));
+
+  // Two-level count of finished workgroups; the last one zeroes the state.
+  if (tid == 0) {
+    wait_vmem_all();   // this workgroup's counter updates are done
+    const int g = blockIdx.x % kMegaQueues;
+    const int in_group = (int)(gridDim.x / kMegaQueues) + (g < (int)(gridDim.x % kMegaQueues) ? 1 : 0);
+    const int groups = min((int)gridDim.x, kMegaQueues);
+    int last = 0;
+    if ((int)add_agent(A.state + kDone1 + g * kLine, 1) + 1 == in_group)
+      last = (int)add_agent(A.state + kDone2, 1) + 1 == groups;
+    sh.last = last;
+  }
+  __syncthreads();
+  if (sh.last) {
+    const int nwords = kCounters + A.E + (kMegaMaxRows / A.k) * (A.H / 64);
+    for (int i = tid; i < nwords; i += kMegaThreads)
+      if (i != kErr) st_agent(A.state + i, 0);
+  }
+}
+
+namespace {
+int g_mega_grid[64];   // workgroups per launch on each device: CUs x resident workgroups per CU
+}
+
+hipError_t launch_mega(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* w2c, const uint8_t* w2s,
+                       const uint16_t* x, const int32_t* ids, const float* tw, uint16_t* out, int T, int H, int I,
+                       int E, int k, int hrows, uint8_t* xq, uint8_t* xsf, uint8_t* hq, uint8_t* hsf, uint16_t* y,
+                       uint64_t* state, int32_t* counts, int32_t* offsets, int32_t* sorted_rows, int32_t* pos,
+                       uint32_t poll_limit, hipStream_t stream) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  int grid = dev < 64 ? __atomic_load_n(&g_mega_grid[dev], __ATOMIC_RELAXED) : 0;
+  if (grid == 0) {
+    int cus = 0, per_cu = 0;
+    err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return err;
+    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(mega_moe_kernel),
+                                                       kMegaThreads, 0);
+    if (err != hipSuccess) return err;
+    grid = cus * (per_cu > 0 ? per_cu : 1);
+    if (dev < 64) __atomic_store_n(&g_mega_grid[dev], grid, __ATOMIC_RELAXED);
+  }
+  const int R = T * k;
+  const int64_t items = (int64_t)(R < E ? R : E) * (I / 32);
+  if (items < grid) grid = (int)items;
+  if (grid < 1) grid = 1;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  MegaArgs A{w1c, w1s, w2c, w2s, x, xq, xsf, ids, tw, out, hq, hsf, y, state, counts, offsets, sorted_rows, pos,
+             T, H, I, E, k, nbits, hrows, poll_limit};
+  hipLaunchKernelGGL(mega_moe_kernel, dim3(grid), dim3(kMegaThreads), 0, stream, A);
+  return hipGetLastError();
+}
+
+}  // namespace moe

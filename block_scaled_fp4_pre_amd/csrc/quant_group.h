@@ -38,9 +38,71 @@ __device__ __forceinline__ void load_group(const void* __restrict__ src, int64_t
   }
 }
 
+// MXFP4 codes of 32 values whose absolute maximum has the fp32 bits amax:
+// 16 bytes, two codes per byte with the even element in the low nibble; the
+// return value is the scale byte.
+__device__ __forceinline__ uint32_t mx_encode_group(const float (&v)[32], uint32_t amax, uint4& codes) {
+  const int e = mx_scale_exp(amax);
+  const float sc = exp2_scale(e);
+  uint32_t packed[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t w = e2m1_pack2<0>(0u, v[8 * q], v[8 * q + 1], sc);
+    w = e2m1_pack2<1>(w, v[8 * q + 2], v[8 * q + 3], sc);
+    w = e2m1_pack2<2>(w, v[8 * q + 4], v[8 * q + 5], sc);
+    packed[q] = e2m1_pack2<3>(w, v[8 * q + 6], v[8 * q + 7], sc);
+  }
+  codes = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  return (uint32_t)(e + 127);
+}
+
+// The same for 32 bf16 values as 16 words (element 2i in the low half of
+// word i), without widening them all to fp32 at once: the absolute maximum
+// is taken on the bit patterns (bf16 magnitudes order as their low 15 bits),
+// each value widened only for its conversion.
+__device__ __forceinline__ uint32_t mx_encode_bf16_group(const uint32_t (&w)[16], uint4& codes) {
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = max(amax, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+  const int e = mx_scale_exp(amax << 16);
+  const float sc = exp2_scale(e);
+  uint32_t packed[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t* x = w + 4 * q;
+    uint32_t p = e2m1_pack2<0>(0u, bf16_to_f32(x[0] & 0xFFFFu), bf16_to_f32(x[0] >> 16), sc);
+    p = e2m1_pack2<1>(p, bf16_to_f32(x[1] & 0xFFFFu), bf16_to_f32(x[1] >> 16), sc);
+    p = e2m1_pack2<2>(p, bf16_to_f32(x[2] & 0xFFFFu), bf16_to_f32(x[2] >> 16), sc);
+    packed[q] = e2m1_pack2<3>(p, bf16_to_f32(x[3] & 0xFFFFu), bf16_to_f32(x[3] >> 16), sc);
+  }
+  codes = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  return (uint32_t)(e + 127);
+}
+
+// The 16 words of group g of a bf16 row-major source.
+__device__ __forceinline__ void load_bf16_words(const void* __restrict__ src, int64_t g, uint32_t (&w)[16]) {
+  const uint4* p = reinterpret_cast<const uint4*>(src) + g * 4;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 v = p[q];
+    w[4 * q] = v.x;
+    w[4 * q + 1] = v.y;
+    w[4 * q + 2] = v.z;
+    w[4 * q + 3] = v.w;
+  }
+}
+
 template <bool BF16, bool F8 = false>
 __device__ __forceinline__ void quantize_group(const void* __restrict__ src, int64_t g,
                                                uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  if constexpr (BF16 && !F8) {
+    uint32_t w[16];
+    load_bf16_words(src, g, w);
+    uint4 c;
+    scales[g] = (uint8_t)mx_encode_bf16_group(w, c);
+    reinterpret_cast<uint4*>(codes)[g] = c;
+    return;
+  }
   float v[32];
   load_group<BF16>(src, g, v);
   uint32_t amax = 0;
@@ -58,18 +120,9 @@ __device__ __forceinline__ void quantize_group(const void* __restrict__ src, int
     scales[g] = (uint8_t)(e + 127);
     return;
   }
-  const int e = mx_scale_exp(amax);
-  const float sc = exp2_scale(e);
-  uint32_t packed[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    uint32_t w = e2m1_pack2<0>(0u, v[8 * q], v[8 * q + 1], sc);
-    w = e2m1_pack2<1>(w, v[8 * q + 2], v[8 * q + 3], sc);
-    w = e2m1_pack2<2>(w, v[8 * q + 4], v[8 * q + 5], sc);
-    packed[q] = e2m1_pack2<3>(w, v[8 * q + 6], v[8 * q + 7], sc);
-  }
-  reinterpret_cast<uint4*>(codes)[g] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-  scales[g] = (uint8_t)(e + 127);
+  uint4 c;
+  scales[g] = (uint8_t)mx_encode_group(v, amax, c);
+  reinterpret_cast<uint4*>(codes)[g] = c;
 }
 
 // NVFP4 (nvfp4.h): group g of 32 values -> 16 bytes of packed E2M1 codes at

@@ -43,12 +43,25 @@ PreparedLayout prepared_layout(const moe_w4a4_cfg* c) {
   return p;
 }
 
+bool mega_shape_ok(const moe_w4a4_cfg* c) {
+  return c->mma_type == MOE_MMA_MXF4_X_MXF4 && c->hidden % 512 == 0 && c->inter % 512 == 0 &&
+         c->hidden <= kMegaMaxK && c->inter <= kMegaMaxK;
+}
+
+int check_mega_args(const moe_w4a4_cfg* c, int32_t num_tokens) {
+  if (!mega_shape_ok(c) || (int64_t)num_tokens * c->topk > kMegaMaxRows) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
 moe_w4a4_ws_layout ws_layout(const moe_w4a4_cfg* c) {
   const uint64_t H = c->hidden, I = c->inter, E = c->num_experts, M = c->max_tokens, G = scale_group(c);
   const uint64_t R = M * c->topk;
   const uint64_t nb = (R + kRouteRowsPerBlock - 1) / kRouteRowsPerBlock;
   moe_w4a4_ws_layout L{};
   uint64_t off = 0;
+  // First and of one size for every configuration, so that it stays put in
+  // the allocation-free forward's scratch, which is laid out per call.
+  L.mega = off; off = align256(off + kMegaStateBytes);
   const uint64_t ab = c->mma_type == MOE_MMA_FP8_X_MXF4 ? 2 : 1;   // activation bytes per 2 elements
   L.xq = off; off = align256(off + M * H / 2 * ab);
   L.xsf = off; off = align256(off + M * H / G);

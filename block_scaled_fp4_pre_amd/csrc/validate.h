@@ -25,6 +25,24 @@ constexpr int kNvMaxK = 12032;
 constexpr float kNvScaleMin = 0x1p-100f;
 constexpr float kNvScaleMax = 0x1p100f;
 
+// The single-launch forward (mega.hip): MXFP4 x MXFP4 only, at most
+// kMegaMaxRows routed rows (num_tokens * topk; one thread each in the
+// workgroup's own route), hidden and inter multiples of 512 up to kMegaMaxK
+// (each of a work item's 4 waves takes a quarter of K, at most 8 steps of 128).
+constexpr int kMegaMaxRows = MOE_MEGA_MAX_ROWS;
+constexpr int kMegaMaxK = 4096;
+// Ticket counters per work phase of the single-launch forward.
+constexpr int kMegaQueues = 16;
+// Its state region, the first region of every workspace whatever the
+// configuration (so that it stays put in the allocation-free forward's
+// scratch): queue, done and error words, one h counter per expert, and one
+// combine counter per (token, 64 hidden columns).
+constexpr uint64_t kMegaStateBytes = MOE_MEGA_STATE_BYTES;
+bool mega_shape_ok(const moe_w4a4_cfg* c);     // c must pass check_cfg
+// MOE_OK when the single-launch forward supports cfg and num_tokens (c must
+// pass check_cfg), else MOE_EUNSUPPORTED.
+int check_mega_args(const moe_w4a4_cfg* c, int32_t num_tokens);
+
 // Bytes after the last region of the prepared weights.  The streaming GEMMs
 // keep a ring of up to 4 K steps of weight loads in flight per wave and issue
 // the ring's refills past a unit's last step without a branch; for the last

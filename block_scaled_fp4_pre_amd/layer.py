@@ -39,6 +39,10 @@ class MoeW4A4Layer:
         self.prepared = prepared
         self.workspace = torch.empty(wb, dtype=torch.uint8, device=self.device)
         self.layout = _lib.moe_w4a4_workspace_layout(self.cfg)
+        # the single-launch forward's state region: zero before its first call
+        # (every call leaves it zero)
+        m = self.layout["mega"]
+        self.workspace[m:m + _lib.MOE_MEGA_STATE_BYTES].zero_()
 
     @property
     def nvfp4(self) -> bool:
@@ -120,6 +124,17 @@ class MoeW4A4Layer:
         with torch.cuda.device(self.device):
             _lib.moe_w4a4_forward(self.cfg, self.prepared, T, x, topk_ids, topk_weights, out, self.workspace,
                                   stream=stream)
+        return out
+
+    def forward_mega(self, x, topk_ids, topk_weights, out=None, stream=None):
+        """The forward as one kernel launch (moe_w4a4_forward_mega: MXFP4, at
+        most 256 routed rows); arguments as forward."""
+        T = x.shape[0]
+        if out is None:
+            out = torch.empty((T, self.H), dtype=torch.bfloat16, device=self.device)
+        with torch.cuda.device(self.device):
+            _lib.moe_w4a4_forward_mega(self.cfg, self.prepared, T, x, topk_ids, topk_weights, out, self.workspace,
+                                       stream=stream)
         return out
 
     def run_stages(self, stages, num_tokens, x=None, topk_ids=None, topk_weights=None, out=None,

@@ -213,6 +213,41 @@ int moe_w4a4_forward(const moe_w4a4_cfg* cfg, const void* prepared, int32_t num_
                      const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
                      uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The same forward as ONE kernel launch, for decode-sized batches: the pages'
+ * single fused mega-MoE kernel ([P1] sglang PR "[deepseek-v4] Bump
+ * sgl-deep-gemm for packed FP4xFP4 mega-MoE (W4A4)", title and section B; [P3]
+ * "Key source snippets", _run_mega_routed, which runs one fused kernel per
+ * forward after pre_dispatch).  Every workgroup routes the top-k ids itself;
+ * work items (quantizing one token row, a 64-row unit of W1 for one expert, a
+ * 64-row unit of W2 for one expert) come from a device-side ticket counter in
+ * that order; a GEMM1 item waits for the token rows, a GEMM2 item for its
+ * expert's h, each through counters in the workspace; the GEMM2 item that
+ * completes a token's 64 hidden columns combines them.
+ * Supported: MOE_MMA_MXF4_X_MXF4, num_tokens * topk <= MOE_MEGA_MAX_ROWS,
+ * hidden and inter multiples of 512 up to 4096; otherwise MOE_EUNSUPPORTED
+ * and nothing is enqueued.  Arguments, other errors and the workspace as for
+ * moe_w4a4_forward, plus: the workspace's `mega` region (its first
+ * MOE_MEGA_STATE_BYTES) must be zero before the first call on it, and every
+ * call leaves it zero (so zero it once after allocating the workspace); calls
+ * that share a workspace must not overlap.  A wait inside the kernel that runs
+ * out of polls (about 0.1 s; none does unless the state was not zero) sets the
+ * error word, uint64 number MOE_MEGA_ERR_WORD of the region, which the kernel
+ * never clears; that call's results are then unspecified.  Afterwards the workspace holds the same
+ * intermediates as after moe_w4a4_forward (xq, xsf, counts, offsets,
+ * sorted_rows, pos, hq, hsf, y).  Numerics as moe_w4a4_forward except the
+ * order of the fp32 sums of both GEMMs (each sum is four partial sums over
+ * quarters of K, added in order), so the two paths agree to the parity bar
+ * rather than bit for bit; the result is deterministic.
+ * moe_w4a4_forward takes this path by itself when it is supported and
+ * num_tokens * topk <= MOE_MEGA_AUTO_ROWS. */
+#define MOE_MEGA_MAX_ROWS 256
+#define MOE_MEGA_AUTO_ROWS 96
+#define MOE_MEGA_STATE_BYTES (144u << 10)
+#define MOE_MEGA_ERR_WORD 800
+int moe_w4a4_forward_mega(const moe_w4a4_cfg* cfg, const void* prepared, int32_t num_tokens,
+                          const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
+                          uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* The same forward with no workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  The intermediates live in a static
@@ -259,6 +294,9 @@ typedef struct moe_w4a4_ws_layout {
   uint64_t num_tiles;    /* int32  [1]                 number of valid tiles        */
   uint64_t xsf_planes;   /* uint8  [H/128, R, 4]       token scales of the sorted rows
                                                         (planes; the tiled GEMM1's input) */
+  uint64_t mega;         /* MOE_MEGA_STATE_BYTES at offset 0: the single-launch forward's
+                                                        work queues and counters; must be zero
+                                                        before its first call, left zero by each */
   uint64_t total;        /* == workspace_bytes                                      */
 } moe_w4a4_ws_layout;
 

@@ -106,7 +106,8 @@ void layout_checks() {
       expect(p.total >= end + moe::kPreparedTailBytes, 1, "prepared tail", s[0]);
       const moe_w4a4_ws_layout L = moe::ws_layout(&c);
       const uint64_t R = (uint64_t)c.max_tokens * c.topk, ab = mma ? 2 : 1;
-      const uint64_t wr[][2] = {{L.xq, c.max_tokens * H / 2 * ab}, {L.xsf, c.max_tokens * H / 32},
+      const uint64_t wr[][2] = {{L.mega, moe::kMegaStateBytes}, {L.xq, c.max_tokens * H / 2 * ab},
+                                {L.xsf, c.max_tokens * H / 32},
                                 {L.counts, E * 4}, {L.offsets, (E + 1) * 4}, {L.sorted_rows, R * 4},
                                 {L.pos, R * 4}, {L.hist, (R + 1023) / 1024 * E * 4}, {L.hq, R * I / 2 * ab},
                                 {L.hsf, R * I / 32}, {L.y, R * H * 2}, {L.tiles, (R / 16 + E + 1) * 8},
@@ -117,6 +118,7 @@ void layout_checks() {
         end = r[0] + r[1];
       }
       expect(L.total >= end && L.total % 256 == 0, 1, "workspace total", s[0]);
+      expect(L.mega == 0, 1, "the single-launch state region comes first", s[0]);
     }
   }
 }
@@ -212,6 +214,39 @@ void stage_checks() {
          MOE_EINVAL);
 }
 
+void mega_checks() {
+  // The single-launch forward: MXFP4, H and I multiples of 512 up to 4096, at
+  // most MOE_MEGA_MAX_ROWS routed rows.
+  moe_w4a4_cfg c = base_cfg();
+  c.hidden = 4096;
+  c.inter = 2048;
+  c.num_experts = 256;
+  c.topk = 6;
+  c.max_tokens = 64;
+  EXPECT(moe::check_mega_args(&c, 42), MOE_OK);               // 252 rows
+  EXPECT(moe::check_mega_args(&c, 43), MOE_EUNSUPPORTED);     // 258 rows
+  EXPECT(moe::check_mega_args(&c, 0), MOE_OK);
+  c.topk = 1;
+  EXPECT(moe::check_mega_args(&c, 256), MOE_OK);
+  EXPECT(moe::check_mega_args(&c, 257), MOE_EUNSUPPORTED);
+  c.topk = 6;
+  c.mma_type = MOE_MMA_FP8_X_MXF4;
+  EXPECT(moe::check_mega_args(&c, 1), MOE_EUNSUPPORTED);
+  c.mma_type = MOE_MMA_MXF4_X_MXF4;
+  const int shapes[][2] = {{4096, 2048}, {512, 512}, {2048, 1024}, {4096, 4096}};
+  for (const auto& s : shapes) {
+    c.hidden = s[0];
+    c.inter = s[1];
+    expect(moe::check_mega_args(&c, 1), MOE_OK, "supported shape", s[0] + s[1]);
+  }
+  const int bad[][2] = {{768, 512}, {512, 384}, {8192, 512}, {512, 8192}, {256, 512}};
+  for (const auto& s : bad) {
+    c.hidden = s[0];
+    c.inter = s[1];
+    expect(moe::check_mega_args(&c, 1), MOE_EUNSUPPORTED, "unsupported shape", s[0] + s[1]);
+  }
+}
+
 }  // namespace
 
 int main() {
@@ -220,6 +255,7 @@ int main() {
   quantize_checks();
   prepare_checks();
   stage_checks();
+  mega_checks();
   // A heap copy of a layout, read back: gives the address sanitizer real
   // allocations to watch next to the stack-only checks above.
   std::vector<moe_w4a4_ws_layout> v(3);

@@ -58,11 +58,12 @@ def synth_layer(weight_set_cfg_index: int, max_tokens: int, mma_type: int = 0):
     return _weights_layer(weight_set_cfg_index).with_capacity(max_tokens, mma_type=mma_type)
 
 
-def run_inputs(layer, x, ids, w, acc=False, acc_rows=None):
+def run_inputs(layer, x, ids, w, acc=False, acc_rows=None, mega=False):
     """Forward of host inputs on `layer`; returns host copies of every
     intermediate.  acc: run the same launches through moe_w4a4_run_stages
     with GEMM1's raw accumulators captured as "acc" (sorted-row order; only
-    the rows acc_rows, default all, are copied back)."""
+    the rows acc_rows, default all, are copied back).  mega: through the
+    single-launch forward (moe_w4a4_forward_mega) instead."""
     from block_scaled_fp4_pre_amd import _lib
     T = x.shape[0]
     xd, idd, wd = dev_bf16(x), dev(ids), dev(w)
@@ -81,16 +82,16 @@ def run_inputs(layer, x, ids, w, acc=False, acc_rows=None):
         res["acc"] = a
         del buf
     else:
-        out = layer.forward(xd, idd, wd)
+        out = layer.forward_mega(xd, idd, wd) if mega else layer.forward(xd, idd, wd)
     torch.cuda.synchronize()
     return dict(x=x, ids=ids, w=w, out=host_bits(out), **res, **workspace_host(layer, T))
 
 
-def run_config(layer, cfg, tokens=None, acc=False, acc_rows=None):
+def run_config(layer, cfg, tokens=None, acc=False, acc_rows=None, mega=False):
     """Forward of config cfg on `layer`; returns host copies of every intermediate."""
     x = synth.make_tokens(cfg, tokens)
     ids, w = synth.make_routing(cfg, tokens)
-    return run_inputs(layer, x, ids, w, acc=acc, acc_rows=acc_rows)
+    return run_inputs(layer, x, ids, w, acc=acc, acc_rows=acc_rows, mega=mega)
 
 
 def rows_from_planes(planes, nrows):

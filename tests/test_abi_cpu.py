@@ -90,6 +90,32 @@ def test_forward_validation_before_any_hip_call():
     assert _lib.status_string(_lib.MOE_ECAPACITY).startswith("num_tokens")
 
 
+def test_single_launch_forward_validation():
+    """moe_w4a4_forward_mega checks its arguments as moe_w4a4_forward does and
+    then refuses what it does not support, before any HIP call."""
+    from block_scaled_fp4_pre_amd import _lib
+    L = _lib.lib()
+    P = ctypes.c_void_p
+    fake = P(1 << 20)
+    cfg = _lib.make_cfg(4096, 2048, 256, 6, 64)
+    _, ws = _lib.moe_w4a4_query(cfg)
+    fwd = lambda c, T, wsb=ws: L.moe_w4a4_forward_mega(ctypes.byref(c), fake, T, fake, fake, fake, fake, fake,
+                                                         wsb, None)
+    assert fwd(cfg, 43) == _lib.MOE_EUNSUPPORTED               # 258 routed rows
+    assert fwd(cfg, 65) == _lib.MOE_ECAPACITY
+    assert fwd(cfg, 4, ws - 1) == _lib.MOE_EWORKSPACE
+    assert fwd(cfg, 0) == _lib.MOE_OK
+    assert fwd(cfg, 4) == _lib.MOE_ENODEVICE                    # valid: only the device is missing
+    fp8 = _lib.make_cfg(4096, 2048, 256, 6, 64, mma_type=_lib.MOE_MMA_FP8_X_MXF4)
+    _, ws8 = _lib.moe_w4a4_query(fp8)
+    assert fwd(fp8, 4, ws8) == _lib.MOE_EUNSUPPORTED
+    odd = _lib.make_cfg(768, 512, 8, 2, 16)
+    _, wso = _lib.moe_w4a4_query(odd)
+    assert fwd(odd, 4, wso) == _lib.MOE_EUNSUPPORTED
+    lay = _lib.moe_w4a4_workspace_layout(cfg)
+    assert lay["mega"] == 0 and lay["xq"] >= _lib.MOE_MEGA_STATE_BYTES
+
+
 def test_fp8_activations_double_the_token_regions():
     """mma_type fp8xfp4: x and h take one E4M3 byte per element instead of half."""
     from block_scaled_fp4_pre_amd import _lib

@@ -1,0 +1,194 @@
+"""GPU tier for the single-launch forward (moe_w4a4_forward_mega), compared
+with the oracle on every token and every intermediate it leaves in the
+workspace (quantized tokens, route, requantized h, y, output):
+
+  mega_h512_i512_e8_k2_t16         K slices of one step (H = I = 512)
+  mega_h1024_i512_e16_k2_t64_zipf  experts with more than 16 rows (several
+                                   passes per work item) and experts with none
+  mega_h2048_i1024_e64_k6_t42      252 routed rows
+  DSV4-Flash shape, T = 1, 8, 42   the 8- and 4-step slices of hidden 4096 and
+                                   inter 2048 (6, 48 and 252 routed rows)
+
+plus routing edge cases (masked, out-of-range and duplicate ids, a token with
+no valid slot, one token, 256 routed rows), determinism, back-to-back calls
+with different token counts on one workspace interleaved with the multi-launch
+forward, a HIP graph replayed on new inputs, and the error word of the
+kernel's bounded waits staying 0."""
+import dataclasses
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle.forward import forward
+from tests.gpu_support import dev, dev_bf16, host_bits, layer_for, log, run_config, run_inputs, synth_layer
+from tests.oracle_inputs import all_expert_weights, all_experts_parallel
+from tests.test_gpu_layer import check_all_stages
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [
+    synth.LayerConfig(140, "mega_h512_i512_e8_k2_t16", 16, 512, 512, 8, 2, "uniform", 140),
+    synth.LayerConfig(141, "mega_h1024_i512_e16_k2_t64_zipf", 64, 1024, 512, 16, 2, "zipf", 141, 2.0),
+    synth.LayerConfig(142, "mega_h2048_i1024_e64_k6_t42", 42, 2048, 1024, 64, 6, "uniform", 142),
+]
+DSV4_TOKENS = [1, 8, 42]
+
+
+def err_word(layer):
+    """The kernel's error word (a wait that ran out of polls sets it); the
+    rest of the state region must be back at zero after every call."""
+    from block_scaled_fp4_pre_amd import _lib
+    st = layer.ws("mega", (_lib.MOE_MEGA_STATE_BYTES // 8,), torch.int64).cpu().numpy()
+    err = int(st[_lib.MOE_MEGA_ERR_WORD])
+    st[_lib.MOE_MEGA_ERR_WORD] = 0
+    assert not st.any(), np.nonzero(st)[0][:8]
+    return err
+
+
+@pytest.fixture(scope="module")
+def layers():
+    out = {}
+    for cfg in SHAPES:
+        layer = layer_for(cfg.hidden, cfg.inter, cfg.experts, cfg.topk, cfg.tokens)
+        layer.load_fp32(lambda e, c=cfg: synth.expert_weights_f32(c, e), threads=4)
+        out[cfg.name] = layer
+    return out
+
+
+@pytest.mark.parametrize("cfg", SHAPES, ids=lambda c: c.name)
+def test_mega_all_tokens(cfg, layers):
+    log(f"[test] mega {cfg.name}")
+    layer = layers[cfg.name]
+    got = run_config(layer, cfg, mega=True)
+    counts = got["counts"]
+    log(f"    rows per expert: max {counts.max()}, empty {(counts == 0).sum()}")
+    if "zipf" in cfg.name:
+        assert counts.max() > 16 and (counts == 0).any()
+    ref = forward(got["x"], got["ids"], got["w"], all_expert_weights(cfg), cfg.experts, cfg.inter)
+    check_all_stages(got, ref, cfg.topk)
+    assert err_word(layer) == 0
+
+
+@pytest.mark.parametrize("T", DSV4_TOKENS)
+def test_mega_dsv4_every_row(T):
+    cfg = dataclasses.replace(synth.CONFIGS[1], name=f"dsv4flash_t{T}", tokens=T)
+    log(f"[test] mega DSV4-Flash T={T}")
+    layer = synth_layer(1, T)
+    got = run_config(layer, cfg, mega=True)
+    log(f"    {int((got['counts'] > 0).sum())} active experts; oracle")
+    ref = forward(got["x"], got["ids"], got["w"], all_experts_parallel(synth.CONFIGS[1]), cfg.experts, cfg.inter)
+    check_all_stages(got, ref, cfg.topk)
+    assert err_word(layer) == 0
+
+
+@pytest.mark.parametrize("case", ["T1", "masked_dups", "no_valid_slot", "rows256"])
+def test_mega_edge_cases(case, layers):
+    log(f"[test] mega edge case {case}")
+    cfg = SHAPES[0]
+    E, k = cfg.experts, cfg.topk
+    rng = np.random.default_rng(zlib.crc32(case.encode()))
+    T = {"T1": 1, "rows256": 128}.get(case, 16)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((T, cfg.hidden)).astype(np.float32))
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    w /= w.sum(axis=1, keepdims=True)
+    if case == "masked_dups":
+        ids[::3, 1] = -1
+        ids[1::3, 1] = ids[1::3, 0]
+        ids[7, 0] = E + 3
+    if case == "no_valid_slot":
+        ids[4, :] = -1
+        ids[9, :] = E
+    layer = layers[cfg.name] if T <= cfg.tokens else layer_for(cfg.hidden, cfg.inter, E, k, T)
+    if T > cfg.tokens:
+        layer.load_fp32(lambda e: synth.expert_weights_f32(cfg, e), threads=4)
+    got = run_inputs(layer, x, ids, w, mega=True)
+    ref = forward(x, ids, w, all_expert_weights(cfg), E, cfg.inter)
+    check_all_stages(got, ref, k)
+    if case == "no_valid_slot":
+        assert np.all(got["out"][4] == 0) and np.all(got["out"][9] == 0)
+    assert err_word(layer) == 0
+
+
+def test_mega_deterministic_and_reusable(layers):
+    """Two identical calls give identical bits; calls with other token counts
+    and multi-launch forwards in between leave the next call unaffected."""
+    log("[test] mega determinism and workspace reuse")
+    cfg = SHAPES[2]
+    layer = layers[cfg.name]
+    x = synth.make_tokens(cfg)
+    ids, w = synth.make_routing(cfg)
+    xd, idd, wd = dev_bf16(x), dev(ids), dev(w)
+    first = host_bits(layer.forward_mega(xd, idd, wd))
+    for T in (1, 5, 42, 17):
+        layer.forward_mega(xd[:T], idd[:T], wd[:T])
+        layer.forward(xd[:T], idd[:T], wd[:T])
+    again = host_bits(layer.forward_mega(xd, idd, wd))
+    torch.cuda.synchronize()
+    assert np.array_equal(first, again)
+    multi = host_bits(layer.forward(xd, idd, wd))
+    log(f"    multi-launch vs single-launch outputs bit-identical on {float(np.mean(multi == first)):.4f}")
+    assert err_word(layer) == 0
+
+
+def test_forward_takes_the_single_launch_path_for_few_rows(layers):
+    """moe_w4a4_forward runs the single-launch kernel up to MOE_MEGA_AUTO_ROWS
+    routed rows (its output then equals moe_w4a4_forward_mega's bit for bit),
+    and so does the allocation-free forward on the library's static scratch."""
+    from block_scaled_fp4_pre_amd import _lib
+    log("[test] automatic single-launch path")
+    cfg = SHAPES[2]
+    layer = layers[cfg.name]
+    T = 96 // cfg.topk
+    x = synth.make_tokens(cfg)[:T]
+    ids, w = synth.make_routing(cfg)
+    xd, idd, wd = dev_bf16(x), dev(ids[:T]), dev(w[:T])
+    mega = host_bits(layer.forward_mega(xd, idd, wd))
+    auto = host_bits(layer.forward(xd, idd, wd))
+    out = torch.empty((T, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+    for _ in range(2):                          # the scratch's state region is left zero for the next call
+        _lib.moe_w4a4_forward_noalloc(layer.cfg, layer.prepared, T, xd, idd, wd, out)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(out), mega)
+    assert np.array_equal(auto, mega)
+    assert err_word(layer) == 0
+
+
+def test_mega_graph_replays_equal_eager(layers):
+    log("[test] mega graph capture and replay")
+    cfg = SHAPES[1]
+    layer = layers[cfg.name]
+    sets = []
+    for i in range(2):
+        c = dataclasses.replace(cfg, index=cfg.index + 500 * i)
+        ids, w = synth.make_routing(c)
+        sets.append((dev_bf16(synth.make_tokens(c)), dev(ids), dev(w)))
+    eager = [host_bits(layer.forward_mega(*s)) for s in sets]
+    torch.cuda.synchronize()
+    assert not np.array_equal(eager[0], eager[1])
+    x_s, ids_s, w_s = (t.clone() for t in sets[0])
+    out_s = torch.empty((cfg.tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.forward_mega(x_s, ids_s, w_s, out=out_s)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward_mega(x_s, ids_s, w_s, out=out_s)
+    torch.cuda.synchronize()
+    for i, which in enumerate((1, 0, 1)):
+        for dst, src in zip((x_s, ids_s, w_s), sets[which]):
+            dst.copy_(src)
+        g.replay()
+        torch.cuda.synchronize()
+        got = host_bits(out_s)
+        log(f"    replay {i} on input set {which}: bit-identical {np.array_equal(got, eager[which])}")
+        assert np.array_equal(got, eager[which])
+        assert np.array_equal(host_bits(layer.forward_mega(*sets[1 - which])), eager[1 - which])
+        torch.cuda.synchronize()
+    assert err_word(layer) == 0
