@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--mma-type {mxf4xmxf4,fp8xfp4,nvf4xnvf4}]
-                    [--no-cpu-baseline] [--no-ceiling] [--no-prefill]
+                    [--no-cpu-baseline] [--no-ceiling] [--no-prefill] [--no-decode]
 
 A step is one whole forward of the layer (pre-dispatch quantization, routing,
 GEMM1 + SwiGLU + requant, GEMM2, combine) on one batch of synthetic tokens whose
@@ -26,7 +26,10 @@ launches in which events on the same stream bracket each GEMM launch
 median, minimum and maximum of K more forwards, each bracketed by its own
 events.  With the default workload the metric's second operating point,
 ntok = 4096, rides along as the object "dsv4flash_t4096_prefill" (same
-weights, same measurements).  "context" holds the pages' own figure for
+weights, same measurements), and a decode batch of 8 tokens, which
+moe_w4a4_forward runs as one kernel launch (mega_moe_kernel), as
+"dsv4flash_t8_decode_single_launch", with the same forward's time as four
+launches beside it.  "context" holds the pages' own figure for
 ntok = 512 (another machine: not a baseline, so "vs_baseline" is null).
 "ceiling" holds this GPU's measured ceilings (libmoe_ceiling.so): the
 streaming-read rate of a 2 GiB buffer with non-temporal and with default loads
@@ -92,6 +95,7 @@ def algorithmic(cfg, counts, fp8=False, nv=False):
 
 
 PREFILL = "dsv4flash_t4096_prefill"   # the metric's second operating point
+DECODE_TOKENS = 8                 # decode batch of the single-launch record (48 routed rows)
 STREAM_MAX_ROWS = 16              # mean routed rows per expert up to which the GEMMs are the streaming kernels
 # Each GEMM's kernel on each path, with the sources its code comes from.  The
 # label names the committed HBM-counter file of that kernel
@@ -335,6 +339,53 @@ def workload_record(layer, cfg, steps, warmup, mma_type):
     return rec, alg, (x_h, ids_h, w_h)
 
 
+def decode_record(layer, cfg, steps, warmup):
+    """The DeepSeek-V4-Flash layer at a decode batch (cfg: its shape and
+    routing recipe, cfg.tokens tokens) through moe_w4a4_forward, which takes
+    the single-launch kernel at that size (mega_moe_kernel), beside the same
+    forward as the four launches of the stage sequence (moe_w4a4_run_stages)."""
+    import torch
+
+    import synth
+    from block_scaled_fp4_pre_amd import _lib
+    T = cfg.tokens
+    x_h = synth.make_tokens(cfg)
+    ids_h, w_h = synth.make_routing(cfg)
+    x = torch.from_numpy(x_h.view(np.int16)).cuda().view(torch.bfloat16)
+    ids = torch.from_numpy(ids_h).cuda()
+    w = torch.from_numpy(w_h).cuda()
+    out = torch.empty((T, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps * 1e3
+
+    us = timed(lambda: layer.forward(x, ids, w, out))
+    multi = timed(lambda: layer.run_stages(_lib.MOE_STAGE_ALL, T, x=x, topk_ids=ids, topk_weights=w, out=out))
+    counts = layer.ws("counts", (cfg.experts,), torch.int32).cpu().numpy()
+    alg = algorithmic(cfg, counts)
+    gbps = alg["layer_bytes"] / (us * 1e-6) / 1e9
+    return {
+        "value_us": round(us, 2),
+        "multi_launch_us": round(multi, 2),
+        "speedup_over_multi_launch": round(multi / us, 3),
+        "hbm_gbps": round(gbps, 1),
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "roofline": {"kernel": "mega_moe_kernel", "bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None, "avg_us": round(us, 2),
+                     "bytes_per_launch": int(alg["layer_bytes"])},
+        "config": {"tokens": T, "routing": cfg.routing, "active_experts": alg["active"], "routed_rows": alg["R"]},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -347,6 +398,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the streaming-read and FP4 MFMA probes (libmoe_ceiling.so)")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode-batch record of the single-launch forward")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the ntok=4096 prefill record that rides along with the ntok=512 headline")
     ap.add_argument("--threads", type=int, default=16)
@@ -420,6 +473,17 @@ def main():
         print(f"[bench] {pcfg.name}: {prec['value_us']} us", file=sys.stderr, flush=True)
         del player
         torch.cuda.synchronize()
+    if not args.no_decode and cfg.name == "dsv4flash_t512" and args.mma_type == "mxf4xmxf4":
+        # A decode batch, which runs as one kernel launch (the single-launch
+        # forward), on the same prepared weights.
+        import dataclasses
+        dcfg = dataclasses.replace(configs["dsv4flash_t64_decode"], name=f"dsv4flash_t{DECODE_TOKENS}_decode",
+                                   tokens=DECODE_TOKENS)
+        dlayer = layer.with_capacity(DECODE_TOKENS)
+        res[dcfg.name + "_single_launch"] = decode_record(dlayer, dcfg, args.steps, args.warmup)
+        print(f"[bench] {dcfg.name}: {res[dcfg.name + '_single_launch']['value_us']} us", file=sys.stderr,
+              flush=True)
+        del dlayer
     if args.calibrate_copy:
         # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE per dispatch
         # calibrate the counters read for the layer's kernels.

@@ -1,8 +1,8 @@
 """bench.py's command-line contract: more than one GPU is refused with a
 message (CPU tier), and one short run prints exactly one JSON line with the
 fields and types the benchmark record needs, plus the per-forward spread,
-both GEMMs' rooflines, the ntok=4096 record and the measured ceilings (GPU
-tier); the CPU baseline is the oracle over one whole forward (CPU tier, at the
+both GEMMs' rooflines, the ntok=4096 record, the decode record of the
+single-launch forward and the measured ceilings (GPU tier); the CPU baseline is the oracle over one whole forward (CPU tier, at the
 tiny size)."""
 import json
 import os
@@ -50,6 +50,12 @@ def test_one_json_line_with_the_record_fields(mma):
     assert pre["config"]["tokens"] == 4096 and pre["value_us"] > 0
     assert pre["roofline"]["kernel"] == "gemm_lds_kernel" and pre["roofline_gemm2"]["avg_us"] > 0
     assert "cpu_baseline" not in d
+    dec = d.get("dsv4flash_t8_decode_single_launch")     # MXFP4 only: a decode batch as one launch
+    assert (dec is not None) == (mma == "mxf4xmxf4")
+    if dec is not None:
+        assert dec["config"]["tokens"] == 8 and dec["roofline"]["kernel"] == "mega_moe_kernel"
+        assert 0 < dec["value_us"] and 0 < dec["multi_launch_us"]
+        assert abs(dec["roofline"]["frac"] - dec["roofline"]["achieved"] / dec["roofline"]["peak"]) < 1e-3
     fw = d["forward_us"]
     assert 0 < fw["min"] <= fw["median"] <= fw["max"]
     ceil = d["ceiling"]                                         # measured ceilings beside the published peaks
