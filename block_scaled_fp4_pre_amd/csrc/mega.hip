@@ -18,16 +18,18 @@
 //     expert's token rows into an LDS tile (kept for the next item when that
 //     is of the same expert); each wave runs 4 MFMAs per K step of its slice.
 //     The slices' partial sums meet in LDS in a fixed order; wave 0 runs the
-//     SwiGLU + requant epilogue (epilogue.h) with agent-scope stores, waits
-//     for them, and adds one to the expert's h counter.  A GEMM1 item never
+//     SwiGLU + requant epilogue (epilogue.h) with agent-scope stores, and
+//     once they are complete (one pass later, when the wave has nothing else
+//     outstanding) adds one to the expert's h counter.  A GEMM1 item never
 //     waits.
 //   GEMM2 (active expert, W2 unit v of 64 hidden rows): the weights as above,
 //     loaded before the wait for the expert's h counter to reach its number of
 //     GEMM1 items; then each wave's slice of h by agent-scope loads, the
-//     MFMAs, the reduction, and y (bf16) by agent-scope stores.  For each of its rows the item then adds
-//     one to the (token, v) combine counter; the item that brings it to the
-//     token's number of valid slots combines those 64 columns of the token
-//     (stage S4), in slot order, as combine.hip does.
+//     MFMAs, the reduction, and y (bf16) by agent-scope stores.  Once they
+//     are complete (again one pass later), one more on each row's (token, v)
+//     combine counter; the item that brings it to the token's number of valid
+//     slots combines those 64 columns of the token (stage S4), in slot order,
+//     as combine.hip does.
 // Each phase's items are dealt round-robin over kMegaQueues ticket counters
 // (one fetch-and-add per item, spread over as many addresses, since
 // same-address atomics from every CU serialize in the memory system).  A
@@ -37,9 +39,10 @@
 // workgroup, whatever order the hardware dispatches workgroups in.
 //
 // Hand-off between workgroups: the producer stores with the agent-scope
-// policy, waits for those stores to complete (vmcnt), then adds to the
-// counter with an agent-scope atomic; the consumer reads the counter and then
-// the data with agent-scope loads.  Data that only moves through agent-scope
+// policy, waits until none of its memory operations is outstanding (vmcnt
+// 0: those stores have completed), then adds to the counter with an
+// agent-scope atomic; the consumer reads the counter and then the data with
+// agent-scope loads.  Data that only moves through agent-scope
 // accesses needs no L2 write-back or invalidate.
 //
 // The state region (queues, counters) must be zero at the launch; the last
@@ -405,33 +408,71 @@ __device__ __forceinline__ void mega_pass(const MegaArgs& A, const MegaLds& sh, 
   }
 }
 
-// Wave 0's end of a pass.  GEMM1: the SwiGLU + requant epilogue (h).  GEMM2:
-// y, then for each row one more on its token's combine counter of block v,
-// and the combines this completes.
+// Wave 0's end of a pass: GEMM1's SwiGLU + requant epilogue (h) or GEMM2's
+// y, by agent-scope stores.  Their completion is waited for later
+// (mega_publish), when the wave has nothing else outstanding.
 template <bool G1>
-__device__ void mega_finish_pass(const MegaArgs& A, const MegaLds& sh, int unit, int p0, int nrows, int lane,
-                                 v4f (&acc)[1][4]) {
-  if constexpr (G1) {
+__device__ __forceinline__ void mega_epilogue(const MegaArgs& A, int unit, int p0, int nrows, int lane,
+                                              v4f (&acc)[1][4]) {
+  if constexpr (G1)
     gemm1_epilogue<1, false, CoherentStore>(acc, unit, p0, nrows, A.I, A.hrows, lane, A.hq, A.hsf, nullptr);
-  } else {
+  else
     gemm2_epilogue<1, CoherentStore>(acc, unit, p0, nrows, A.H, lane, A.y);
-    wait_vmem_all();   // y stores complete before the combine counters say so
+}
+
+// What wave 0 still owes for the stores of an earlier pass: the expert's h
+// counter (GEMM1, once per item), or the combine counters of the pass's rows
+// (GEMM2: unit v, sorted rows p0 .. p0 + nrows - 1).  Published once the
+// wave has waited for all its memory operations, one pass later, so that no
+// wave waits for a store's completion on the item's critical path.
+struct MegaPending {
+  int e = -1, unit = 0, p0 = 0, nrows = 0;
+  int tok = 0;        // GEMM2, lane r < nrows (kb == 0): the row's token
+  uint64_t old = 0;   //   and the combine counter's value before this row's count
+  bool counted = false;
+};
+
+// First half of a publication (wave 0): wait for every outstanding memory
+// operation of the wave (the pending stores included), then count.  GEMM1
+// adds one to the expert's h counter; GEMM2 adds one to each row's (token,
+// block) combine counter, keeping the old values for mega_publish_end.
+template <bool G1>
+__device__ __forceinline__ void mega_publish(const MegaArgs& A, const MegaLds& sh, MegaPending& pd, int lane) {
+  if (pd.e < 0) return;
+  wait_vmem_all();
+  if constexpr (G1) {
+    if (lane == 0) add_agent(A.state + kCounters + pd.e, 1);
+    pd.e = -1;
+  } else {
     const int r = lane & 15, kb = lane >> 4;
-    int tok = 0;
+    pd.counted = r < pd.nrows && kb == 0;
+    if (pd.counted) {
+      pd.tok = sh.sorted[pd.p0 + r] / A.k;
+      pd.old = add_agent(A.state + kCounters + A.E + (size_t)pd.tok * (A.H / 64) + pd.unit, 1);
+    }
+  }
+}
+
+// Second half (GEMM2): the tokens whose last row this was get their block
+// combined.
+template <bool G1>
+__device__ __forceinline__ void mega_publish_end(const MegaArgs& A, const MegaLds& sh, MegaPending& pd,
+                                                 int lane) {
+  if constexpr (!G1) {
+    if (pd.e < 0) return;
     bool last = false;
-    if (r < nrows && kb == 0) {
-      tok = sh.sorted[p0 + r] / A.k;
+    if (pd.counted) {
       int nvalid = 0;
-      for (int j = 0; j < A.k; ++j) nvalid += sh.pos[tok * A.k + j] >= 0;
-      uint64_t* ccnt = A.state + kCounters + A.E;
-      last = (int)add_agent(ccnt + (size_t)tok * (A.H / 64) + unit, 1) + 1 == nvalid;
+      for (int j = 0; j < A.k; ++j) nvalid += sh.pos[pd.tok * A.k + j] >= 0;
+      last = (int)pd.old + 1 == nvalid;
     }
     uint64_t m = __ballot(last);
     while (m) {
       const int src = __ffsll((long long)m) - 1;
       m &= m - 1;
-      mega_combine(A, sh, __shfl(tok, src, kWave), unit, lane);
+      mega_combine(A, sh, __shfl(pd.tok, src, kWave), pd.unit, lane);
     }
+    pd.e = -1;
   }
 }
 
@@ -452,6 +493,7 @@ __device__ void mega_queue(const MegaArgs& A, MegaLds& sh, uint64_t* ctr, int q,
   uint4 a[L][4];
   uint32_t sa[L];
   mega_item_weights<G1, L>(A, sh, cur, N, w, lane, a, sa);
+  MegaPending pd;   // wave 0's
   for (;;) {
     uint64_t next_raw = 0;
     if (tid == 0) next_raw = add_agent(ctr, 1);
@@ -476,6 +518,9 @@ __device__ void mega_queue(const MegaArgs& A, MegaLds& sh, uint64_t* ctr, int q,
       if constexpr (G1) mega_token_tile(A, sh, base + t0, nrows);
       v4f acc[1][4];
       mega_pass<G1, L>(A, sh, base + t0, nrows, s0, ln, a, sa, acc);
+      // The previous pass's stores are long done: wave 0 publishes them
+      // while the other waves reach the reduction.
+      if (w == 0) mega_publish<G1>(A, sh, pd, ln);
       if (last && tid == 0) sh.item = (int)min(next_raw * kMegaQueues + q, (uint64_t)INT_MAX);
       mega_reduce(sh, w, ln, acc);   // a barrier: sh.item is published
       if (last) nxt = sh.item;
@@ -484,24 +529,20 @@ __device__ void mega_queue(const MegaArgs& A, MegaLds& sh, uint64_t* ctr, int q,
       // the epilogue instead of being kept for a merge with the new ones.)
       if (last && nxt >= n) {
         if (w == 0) {
-          mega_finish_pass<G1>(A, sh, unit, base + t0, nrows, ln, acc);
-          if constexpr (G1) {
-            wait_vmem_all();   // h stores complete before the counter says so
-            if (ln == 0) add_agent(A.state + kCounters + e, 1);
-          }
+          mega_epilogue<G1>(A, unit, base + t0, nrows, ln, acc);
+          mega_publish_end<G1>(A, sh, pd, ln);
+          pd.e = e, pd.unit = unit, pd.p0 = base + t0, pd.nrows = nrows;
+          mega_publish<G1>(A, sh, pd, ln);   // the queue's last: published at once
+          mega_publish_end<G1>(A, sh, pd, ln);
         }
         __syncthreads();
         return;
       }
       if (w == 0) {
-        mega_finish_pass<G1>(A, sh, unit, base + t0, nrows, ln, acc);
-        if (last) {
-          if constexpr (G1) {
-            wait_vmem_all();
-            if (ln == 0) add_agent(A.state + kCounters + e, 1);
-          }
-          mega_item_weights<G1, L>(A, sh, nxt, N, 0, ln, a, sa);
-        }
+        mega_epilogue<G1>(A, unit, base + t0, nrows, ln, acc);
+        mega_publish_end<G1>(A, sh, pd, ln);
+        if (!G1 || last) pd.e = e, pd.unit = unit, pd.p0 = base + t0, pd.nrows = nrows;
+        if (last) mega_item_weights<G1, L>(A, sh, nxt, N, 0, ln, a, sa);
       } else if (last) {
         mega_item_weights<G1, L>(A, sh, nxt, N, w, ln, a, sa);
       }
