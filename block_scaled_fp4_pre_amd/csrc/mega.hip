@@ -494,6 +494,9 @@ __device__ void mega_queue(const MegaArgs& A, MegaLds& sh, uint64_t* ctr, int q,
   uint32_t sa[L];
   mega_item_weights<G1, L>(A, sh, cur, N, w, lane, a, sa);
   MegaPending pd;   // wave 0's
+  // GEMM2: the next item's h counter, read as soon as the item is known; a
+  // count already complete spares the wait's first load
+  uint64_t hc_next = 0;
   for (;;) {
     uint64_t next_raw = 0;
     if (tid == 0) next_raw = add_agent(ctr, 1);
@@ -505,8 +508,10 @@ __device__ void mega_queue(const MegaArgs& A, MegaLds& sh, uint64_t* ctr, int q,
     const int e = sh.act[cur / N], unit = cur % N;
     const int base = sh.off[e], n_e = sh.off[e + 1] - base;
     if constexpr (!G1) {
-      // h of the expert is complete once each of its I/32 GEMM1 items has counted
-      if (!wait_eq(A.state + kCounters + e, (uint64_t)(A.I / 32), A.state + kAbort, A.poll_limit) && ln == 0) {
+      // h of the expert is complete once each of its I/32 GEMM1 items has
+      // counted (counts only grow within a launch)
+      if (hc_next != (uint64_t)(A.I / 32) &&
+          !wait_eq(A.state + kCounters + e, (uint64_t)(A.I / 32), A.state + kAbort, A.poll_limit) && ln == 0) {
         st_agent(A.state + kErr, 1);
         st_agent(A.state + kAbort, 1);
       }
@@ -524,6 +529,9 @@ __device__ void mega_queue(const MegaArgs& A, MegaLds& sh, uint64_t* ctr, int q,
       if (last && tid == 0) sh.item = (int)min(next_raw * kMegaQueues + q, (uint64_t)INT_MAX);
       mega_reduce(sh, w, ln, acc);   // a barrier: sh.item is published
       if (last) nxt = sh.item;
+      if constexpr (!G1) {
+        if (last && nxt < n) hc_next = ld_agent(A.state + kCounters + sh.act[nxt / N]);
+      }
       // (Separate paths for "no next item" and "next item", each loading the
       // weights unconditionally, so that the spent weights are dead during
       // the epilogue instead of being kept for a merge with the new ones.)
