@@ -473,7 +473,7 @@ def main():
         print(f"[bench] {pcfg.name}: {prec['value_us']} us", file=sys.stderr, flush=True)
         del player
         torch.cuda.synchronize()
-    if not args.no_decode and cfg.name == "dsv4flash_t512" and args.mma_type == "mxf4xmxf4":
+    if not args.no_decode and cfg.name == "dsv4flash_t512" and args.mma_type != "nvf4xnvf4":
         # A decode batch, which runs as one kernel launch (the single-launch
         # forward), on the same prepared weights.
         import dataclasses

@@ -289,15 +289,16 @@ int moe_w4a4_forward_mega(const moe_w4a4_cfg* cfg, const void* prepared, int32_t
       cfg->inter, cfg->num_experts, cfg->topk, cfg->max_tokens * cfg->topk, ws + L.xq, ws + L.xsf, ws + L.hq,
       ws + L.hsf, reinterpret_cast<uint16_t*>(ws + L.y), reinterpret_cast<uint64_t*>(ws + L.mega),
       reinterpret_cast<int32_t*>(ws + L.counts), reinterpret_cast<int32_t*>(ws + L.offsets),
-      reinterpret_cast<int32_t*>(ws + L.sorted_rows), reinterpret_cast<int32_t*>(ws + L.pos), kMegaPollLimit,
-      static_cast<hipStream_t>(stream)));
+      reinterpret_cast<int32_t*>(ws + L.sorted_rows), reinterpret_cast<int32_t*>(ws + L.pos),
+      cfg->mma_type == MOE_MMA_FP8_X_MXF4, kMegaPollLimit, static_cast<hipStream_t>(stream)));
 }
 
 int moe_w4a4_forward(const moe_w4a4_cfg* cfg, const void* prepared, int32_t num_tokens, const uint16_t* x,
                      const int32_t* topk_ids, const float* topk_weights, uint16_t* out, void* workspace,
                      size_t workspace_bytes, void* stream) {
   if (cfg != nullptr && moe::check_cfg(cfg) == MOE_OK && moe::check_mega_args(cfg, num_tokens) == MOE_OK &&
-      (int64_t)num_tokens * cfg->topk <= MOE_MEGA_AUTO_ROWS)
+      (int64_t)num_tokens * cfg->topk <=
+          (cfg->mma_type == MOE_MMA_FP8_X_MXF4 ? MOE_MEGA_AUTO_ROWS_FP8 : MOE_MEGA_AUTO_ROWS))
     return moe_w4a4_forward_mega(cfg, prepared, num_tokens, x, topk_ids, topk_weights, out, workspace,
                                  workspace_bytes, stream);
   return moe_w4a4_run_stages(cfg, prepared, num_tokens, x, topk_ids, topk_weights, out, workspace,

@@ -49,15 +49,16 @@ hipError_t launch_predispatch(int act, const uint16_t* x, int64_t ngroups, const
                               hipStream_t stream);
 
 // The whole forward in one launch (mega.hip) for at most kMegaMaxRows routed
-// rows, MXFP4, H and I multiples of 512 up to 4096: route, quantization, both
-// GEMMs and the combine.  state: the workspace's `mega` region (zero at the
-// launch, left zero); xq/xsf, counts, offsets, sorted_rows, pos, hq/hsf and y
-// receive what the stages write.  poll_limit bounds every wait.
+// rows, H and I multiples of 512 up to 4096: route, quantization, both GEMMs
+// and the combine; MXFP4 tokens and h, or E4M3 (f8, the fp8xfp4 MMA type).
+// state: the workspace's `mega` region (zero at the launch, left zero);
+// xq/xsf, counts, offsets, sorted_rows, pos, hq/hsf and y receive what the
+// stages write.  poll_limit bounds every wait.
 hipError_t launch_mega(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* w2c, const uint8_t* w2s,
                        const uint16_t* x, const int32_t* ids, const float* tw, uint16_t* out, int T, int H, int I,
                        int E, int k, int hrows, uint8_t* xq, uint8_t* xsf, uint8_t* hq, uint8_t* hsf, uint16_t* y,
                        uint64_t* state, int32_t* counts, int32_t* offsets, int32_t* sorted_rows, int32_t* pos,
-                       uint32_t poll_limit, hipStream_t stream);
+                       bool f8, uint32_t poll_limit, hipStream_t stream);
 
 // Prefill GEMMs with both operands staged in LDS (gemm_lds.hip): tiles of
 // lds_tile_rows(mean rows per expert) routed rows; rows_hint (the mean) also

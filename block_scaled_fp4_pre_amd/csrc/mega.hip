@@ -1,9 +1,10 @@
 // The whole forward of the layer in one launch, for decode-sized batches: the
 // pages' single fused "mega" MoE kernel ([P1] sglang PR "[deepseek-v4] Bump
 // sgl-deep-gemm for packed FP4xFP4 mega-MoE (W4A4)", title and section B,
-// where one kernel runs the routed experts' layer).  MXFP4 x MXFP4, at most
-// kMegaMaxRows routed rows, hidden and inter multiples of 512 up to 4096
-// (validate.h).
+// where one kernel runs the routed experts' layer).  MXFP4 x MXFP4 and the
+// fp8xfp4 MMA type (E4M3 tokens and h, [P3] "Implementation breakdown" items
+// 1-3), at most kMegaMaxRows routed rows, hidden and inter multiples of 512
+// up to 4096 (validate.h).
 //
 // Stage S1 inside the work items.  Every workgroup routes the T*k ids itself
 // (the stable counting sort of route_common.h in LDS, one thread per routed
@@ -21,7 +22,8 @@
 //     SwiGLU + requant epilogue (epilogue.h) with agent-scope stores, and
 //     once they are complete (one pass later, when the wave has nothing else
 //     outstanding) adds one to the expert's h counter.  A GEMM1 item never
-//     waits.
+//     waits.  A pass takes 16 of the expert's rows (E4M3 tokens: 8, so that
+//     the tile of twice the bytes per row keeps its LDS size).
 //   GEMM2 (active expert, W2 unit v of 64 hidden rows): the weights as above,
 //     loaded before the wait for the expert's h counter to reach its number of
 //     GEMM1 items; then each wave's slice of h by agent-scope loads, the
@@ -83,8 +85,14 @@ static_assert((uint64_t)(kCounters + kMaxExperts + kMegaMaxRows * (kMegaMaxK / 6
               "state region");
 static_assert(kErr == MOE_MEGA_ERR_WORD, "error word documented in moe_w4a4.h");
 
-constexpr int kTokStride = kMegaMaxK / 2 + 16;
+constexpr int kTokStride = kMegaMaxK / 2 + 16;    // E2M1 tile: 16 rows
+constexpr int kTokStride8 = kMegaMaxK + 16;       // E4M3 tile: 8 rows
 constexpr int kTscStride = kMegaMaxK / 32 + 4;
+static_assert(8 * kTokStride8 <= 16 * kTokStride, "the E4M3 tile fits the E2M1 tile's bytes");
+
+// Token rows of a GEMM1 pass (the LDS tile) and of a GEMM2 pass.
+template <bool G1, bool F8>
+constexpr int pass_rows() { return G1 && F8 ? 8 : 16; }
 
 struct MegaLds {
   int wcnt[kMegaWaves][kMaxExperts];   // route: rows of each expert per wave
@@ -100,7 +108,8 @@ struct MegaLds {
   float red[kMegaWaves - 1][kWave][16];   // partial sums of K slices 1..3
   // GEMM1's token tile: 16 quantized token rows of one expert over all of K,
   // rows kTokStride bytes apart (16 bytes of padding put the 16 rows one MFMA
-  // operand read touches on distinct banks), and their scale bytes.
+  // operand read touches on distinct banks), and their scale bytes; E4M3: 8
+  // rows kTokStride8 bytes apart.
   uint8_t tok[16 * kTokStride];
   uint8_t tsc[16 * kTscStride];
 };
@@ -281,24 +290,28 @@ __device__ __forceinline__ void mega_reduce(MegaLds& sh, int w, int lane, v4f (&
   }
 }
 
-// MXFP4 of the 32-element group g of the bf16 row src: the quantize stage's
-// encoder (quant_group.h).
-__device__ __forceinline__ void mega_quantize_group(const uint16_t* src, int g, uint4& codes, uint32_t& scale) {
-  uint32_t w[16];
-  load_bf16_words(src, g, w);
-  scale = mx_encode_bf16_group(w, codes);
-}
-
-// The quantized tokens as the quantize stage writes them (xq [T, H/2], xsf
-// [T, H/32]), for inspection only: the GEMM1 items quantize their own rows.
+// The quantized tokens as the quantize stage writes them (xq [T, H/2], E4M3:
+// [T, H]; xsf [T, H/32]), for inspection only: the GEMM1 items quantize
+// their own rows.
+template <bool F8>
 __device__ void mega_tokens_out(const MegaArgs& A) {
   const int groups = A.H / 32;
   for (int i = threadIdx.x; i < A.T * groups; i += kMegaThreads) {
     const int t = i / groups, g = i - t * groups;
-    uint4 c;
+    uint32_t w[16];
+    load_bf16_words(A.x + (size_t)t * A.H, g, w);
     uint32_t sc;
-    mega_quantize_group(A.x + (size_t)t * A.H, g, c, sc);
-    reinterpret_cast<uint4*>(A.xq + (size_t)t * (A.H / 2))[g] = c;
+    if constexpr (F8) {
+      uint4 lo, hi;
+      sc = mx8_encode_bf16_group(w, lo, hi);
+      uint4* d = reinterpret_cast<uint4*>(A.xq + (size_t)t * A.H) + 2 * g;
+      d[0] = lo;
+      d[1] = hi;
+    } else {
+      uint4 c;
+      sc = mx_encode_bf16_group(w, c);
+      reinterpret_cast<uint4*>(A.xq + (size_t)t * (A.H / 2))[g] = c;
+    }
     A.xsf[(size_t)t * groups + g] = (uint8_t)sc;
   }
 }
@@ -347,9 +360,10 @@ __device__ __forceinline__ void mega_item_weights(const MegaArgs& A, const MegaL
 // the rows of x quantized by the workgroup with the quantize stage's encoder
 // (quant_group.h) into LDS, 16 rows over all of K (rows kTokStride bytes
 // apart, 16 bytes of padding putting the 16 rows one MFMA operand read
-// touches on distinct banks; scale bytes kTscStride apart).  The tile is kept
-// while the pass stays the same (key: its first sorted row).  All threads
-// call it.
+// touches on distinct banks; scale bytes kTscStride apart); E4M3: 8 rows,
+// kTokStride8 bytes apart, element order.  The tile is kept while the pass
+// stays the same (key: its first sorted row).  All threads call it.
+template <bool F8>
 __device__ __forceinline__ void mega_token_tile(const MegaArgs& A, MegaLds& sh, int p0, int nrows) {
   if (sh.tok_key == p0) return;
   const int groups = A.H / 32;
@@ -357,9 +371,17 @@ __device__ __forceinline__ void mega_token_tile(const MegaArgs& A, MegaLds& sh, 
     const int r = i / groups, g = i - r * groups;
     uint32_t w[16];
     load_bf16_words(A.x + (size_t)(sh.sorted[p0 + r] / A.k) * A.H, g, w);
-    uint4 c;
-    sh.tsc[r * kTscStride + g] = (uint8_t)mx_encode_bf16_group(w, c);
-    *reinterpret_cast<uint4*>(sh.tok + r * kTokStride + g * 16) = c;
+    if constexpr (F8) {
+      uint4 lo, hi;
+      sh.tsc[r * kTscStride + g] = (uint8_t)mx8_encode_bf16_group(w, lo, hi);
+      uint4* d = reinterpret_cast<uint4*>(sh.tok + r * kTokStride8 + g * 32);
+      d[0] = lo;
+      d[1] = hi;
+    } else {
+      uint4 c;
+      sh.tsc[r * kTscStride + g] = (uint8_t)mx_encode_bf16_group(w, c);
+      *reinterpret_cast<uint4*>(sh.tok + r * kTokStride + g * 16) = c;
+    }
   }
   __syncthreads();
   if (threadIdx.x == 0) sh.tok_key = p0;   // read again only after a later barrier
@@ -376,13 +398,27 @@ __device__ __forceinline__ void ld_operand(const uint8_t* p, const uint8_t* s4, 
   sb = (w >> (8 * kb)) & 0xFFu;
 }
 
+// The E4M3 operand of lane group kb in the 128-byte step row at p (elements
+// [16kb, 16kb+16) and [64+16kb, 64+16kb+16), device_common.h) and its scale
+// byte, by agent-scope loads.
+__device__ __forceinline__ void ld_operand8(const uint8_t* p, const uint8_t* s4, int kb, uint4& lo, uint4& hi,
+                                            uint32_t& sb) {
+  const uint64_t* c = reinterpret_cast<const uint64_t*>(p + kb * 16);
+  const uint64_t a0 = ld_agent(c), a1 = ld_agent(c + 1), b0 = ld_agent(c + 8), b1 = ld_agent(c + 9);
+  lo = make_uint4((uint32_t)a0, (uint32_t)(a0 >> 32), (uint32_t)a1, (uint32_t)(a1 >> 32));
+  hi = make_uint4((uint32_t)b0, (uint32_t)(b0 >> 32), (uint32_t)b1, (uint32_t)(b1 >> 32));
+  const uint32_t w = __hip_atomic_load(reinterpret_cast<const uint32_t*>(s4), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  sb = (w >> (8 * kb)) & 0xFFu;
+}
+
 // One pass of a wave over its K slice (from step s0), rows p0 .. p0 + nrows
 // - 1 (row min(r, nrows - 1) for lane row r: rows past the expert's last
 // re-read it, their results are not stored): per step the token operand, then
 // 4 MFMAs (one per 16-row weight block).  GEMM1: the operand from the LDS
 // token tile.  GEMM2: h by agent-scope loads (K-step planes of hrows rows,
-// epilogue.h).
-template <bool G1, int L>
+// epilogue.h).  F8: E4M3 operands of 32 bytes a lane (the FP8 MFMA form).
+template <bool G1, bool F8, int L>
 __device__ __forceinline__ void mega_pass(const MegaArgs& A, const MegaLds& sh, int p0, int nrows, int s0,
                                           int lane, const uint4 (&a)[L][4], const uint32_t (&sa)[L],
                                           v4f (&acc)[1][4]) {
@@ -392,30 +428,47 @@ __device__ __forceinline__ void mega_pass(const MegaArgs& A, const MegaLds& sh, 
   zero_acc<1>(acc);
 #pragma unroll
   for (int i = 0; i < L; ++i) {
-    uint4 b;
     uint32_t sb;
-    if constexpr (G1) {
-      b = *reinterpret_cast<const uint4*>(sh.tok + rr * kTokStride + (s0 + i) * 64 + kb * 16);
-      sb = sh.tsc[rr * kTscStride + (s0 + i) * 4 + kb];
+    if constexpr (F8) {
+      uint4 lo, hi;
+      if constexpr (G1) {
+        const uint8_t* row = sh.tok + rr * kTokStride8 + (s0 + i) * 128 + kb * 16;
+        lo = *reinterpret_cast<const uint4*>(row);
+        hi = *reinterpret_cast<const uint4*>(row + 64);
+        sb = sh.tsc[rr * kTscStride + (s0 + i) * 4 + kb];
+      } else {
+        const size_t pr = pp + (size_t)i * A.hrows;
+        ld_operand8(A.hq + pr * 128, A.hsf + pr * 4, kb, lo, hi, sb);
+      }
+      acc[0][0] = mfma_fp4_fp8<0, 0>(a[i][0], lo, hi, acc[0][0], (int)sa[i], (int)sb);
+      acc[0][1] = mfma_fp4_fp8<1, 0>(a[i][1], lo, hi, acc[0][1], (int)sa[i], (int)sb);
+      acc[0][2] = mfma_fp4_fp8<2, 0>(a[i][2], lo, hi, acc[0][2], (int)sa[i], (int)sb);
+      acc[0][3] = mfma_fp4_fp8<3, 0>(a[i][3], lo, hi, acc[0][3], (int)sa[i], (int)sb);
     } else {
-      const size_t pr = pp + (size_t)i * A.hrows;
-      ld_operand(A.hq + pr * 64 + kb * 16, A.hsf + pr * 4, kb, b, sb);
+      uint4 b;
+      if constexpr (G1) {
+        b = *reinterpret_cast<const uint4*>(sh.tok + rr * kTokStride + (s0 + i) * 64 + kb * 16);
+        sb = sh.tsc[rr * kTscStride + (s0 + i) * 4 + kb];
+      } else {
+        const size_t pr = pp + (size_t)i * A.hrows;
+        ld_operand(A.hq + pr * 64 + kb * 16, A.hsf + pr * 4, kb, b, sb);
+      }
+      acc[0][0] = mfma_fp4<0, 0>(a[i][0], b, acc[0][0], (int)sa[i], (int)sb);
+      acc[0][1] = mfma_fp4<1, 0>(a[i][1], b, acc[0][1], (int)sa[i], (int)sb);
+      acc[0][2] = mfma_fp4<2, 0>(a[i][2], b, acc[0][2], (int)sa[i], (int)sb);
+      acc[0][3] = mfma_fp4<3, 0>(a[i][3], b, acc[0][3], (int)sa[i], (int)sb);
     }
-    acc[0][0] = mfma_fp4<0, 0>(a[i][0], b, acc[0][0], (int)sa[i], (int)sb);
-    acc[0][1] = mfma_fp4<1, 0>(a[i][1], b, acc[0][1], (int)sa[i], (int)sb);
-    acc[0][2] = mfma_fp4<2, 0>(a[i][2], b, acc[0][2], (int)sa[i], (int)sb);
-    acc[0][3] = mfma_fp4<3, 0>(a[i][3], b, acc[0][3], (int)sa[i], (int)sb);
   }
 }
 
 // Wave 0's end of a pass: GEMM1's SwiGLU + requant epilogue (h) or GEMM2's
 // y, by agent-scope stores.  Their completion is waited for later
 // (mega_publish), when the wave has nothing else outstanding.
-template <bool G1>
+template <bool G1, bool F8>
 __device__ __forceinline__ void mega_epilogue(const MegaArgs& A, int unit, int p0, int nrows, int lane,
                                               v4f (&acc)[1][4]) {
   if constexpr (G1)
-    gemm1_epilogue<1, false, CoherentStore>(acc, unit, p0, nrows, A.I, A.hrows, lane, A.hq, A.hsf, nullptr);
+    gemm1_epilogue<1, F8, CoherentStore>(acc, unit, p0, nrows, A.I, A.hrows, lane, A.hq, A.hsf, nullptr);
   else
     gemm2_epilogue<1, CoherentStore>(acc, unit, p0, nrows, A.H, lane, A.y);
 }
@@ -480,8 +533,9 @@ __device__ __forceinline__ void mega_publish_end(const MegaArgs& A, const MegaLd
 // kMegaQueues, ... below n), pipelined: the next item's ticket is taken while
 // the current item runs, and each wave issues the next item's weights as soon
 // as its MFMAs have consumed the current ones, before the epilogue.
-template <bool G1, int L>
+template <bool G1, bool F8, int L>
 __device__ void mega_queue(const MegaArgs& A, MegaLds& sh, uint64_t* ctr, int q, int n) {
+  constexpr int P = pass_rows<G1, F8>();
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int N = G1 ? A.I / 32 : A.H / 64, s0 = w * L;
@@ -517,12 +571,12 @@ __device__ void mega_queue(const MegaArgs& A, MegaLds& sh, uint64_t* ctr, int q,
       }
     }
     int nxt = INT_MAX;
-    for (int t0 = 0; t0 < n_e; t0 += 16) {
-      const int nrows = min(16, n_e - t0);
-      const bool last = t0 + 16 >= n_e;
-      if constexpr (G1) mega_token_tile(A, sh, base + t0, nrows);
+    for (int t0 = 0; t0 < n_e; t0 += P) {
+      const int nrows = min(P, n_e - t0);
+      const bool last = t0 + P >= n_e;
+      if constexpr (G1) mega_token_tile<F8>(A, sh, base + t0, nrows);
       v4f acc[1][4];
-      mega_pass<G1, L>(A, sh, base + t0, nrows, s0, ln, a, sa, acc);
+      mega_pass<G1, F8, L>(A, sh, base + t0, nrows, s0, ln, a, sa, acc);
       // The previous pass's stores are long done: wave 0 publishes them
       // while the other waves reach the reduction.
       if (w == 0) mega_publish<G1>(A, sh, pd, ln);
@@ -537,7 +591,7 @@ __device__ void mega_queue(const MegaArgs& A, MegaLds& sh, uint64_t* ctr, int q,
       // the epilogue instead of being kept for a merge with the new ones.)
       if (last && nxt >= n) {
         if (w == 0) {
-          mega_epilogue<G1>(A, unit, base + t0, nrows, ln, acc);
+          mega_epilogue<G1, F8>(A, unit, base + t0, nrows, ln, acc);
           mega_publish_end<G1>(A, sh, pd, ln);
           pd.e = e, pd.unit = unit, pd.p0 = base + t0, pd.nrows = nrows;
           mega_publish<G1>(A, sh, pd, ln);   // the queue's last: published at once
@@ -547,7 +601,7 @@ __device__ void mega_queue(const MegaArgs& A, MegaLds& sh, uint64_t* ctr, int q,
         return;
       }
       if (w == 0) {
-        mega_epilogue<G1>(A, unit, base + t0, nrows, ln, acc);
+        mega_epilogue<G1, F8>(A, unit, base + t0, nrows, ln, acc);
         mega_publish_end<G1>(A, sh, pd, ln);
         if (!G1 || last) pd.e = e, pd.unit = unit, pd.p0 = base + t0, pd.nrows = nrows;
         if (last) mega_item_weights<G1, L>(A, sh, nxt, N, 0, ln, a, sa);
@@ -563,12 +617,12 @@ __device__ void mega_queue(const MegaArgs& A, MegaLds& sh, uint64_t* ctr, int q,
 // Takes the items of one phase (n of them, item i on queue i % kMegaQueues)
 // until every queue has run out: first the workgroup's own queue, then,
 // after one read of all the queue counters at once, any queue still open.
-template <bool G1, int L>
+template <bool G1, bool F8, int L>
 __device__ void mega_phase(const MegaArgs& A, MegaLds& sh, uint64_t* q0, int n) {
   const int tid = threadIdx.x;
   int q = blockIdx.x % kMegaQueues;
   for (;;) {
-    mega_queue<G1, L>(A, sh, q0 + q * kLine, q, n);
+    mega_queue<G1, F8, L>(A, sh, q0 + q * kLine, q, n);
     if (tid < kWave) {
       const bool open = tid < kMegaQueues && ld_agent(q0 + tid * kLine) * kMegaQueues + tid < (uint64_t)n;
       const uint64_t m = __ballot(open);
@@ -584,19 +638,12 @@ __device__ void mega_phase(const MegaArgs& A, MegaLds& sh, uint64_t* q0, int n) 
   }
 }
 
-// A phase with its K-slice length as a compile-time constant.
-template <bool G1>
-__device__ __forceinline__ void mega_phase_l(const MegaArgs& A, MegaLds& sh, uint64_t* q0, int n) {
-  switch ((G1 ? A.H : A.I) / kStepK / kMegaWaves) {
-    case 8: mega_phase<G1, 8>(A, sh, q0, n); break;
-    case 4: mega_phase<G1, 4>(A, sh, q0, n); break;
-    case 2: mega_phase<G1, 2>(A, sh, q0, n); break;
-    default: mega_phase<G1, 1>(A, sh, q0, n); break;
-  }
-}
-
 }  // namespace
 
+// One kernel per token format and K-slice lengths (L1 = H / 512 steps for
+// GEMM1, L2 = I / 512 for GEMM2), so that each holds only its own two phase
+// bodies and their registers.
+template <bool F8, int L1, int L2>
 __global__ void __launch_bounds__(kMegaThreads, 2) mega_moe_kernel(MegaArgs A) {
   __shared__ MegaLds sh;
   const int tid = threadIdx.x;
@@ -604,10 +651,10 @@ __global__ void __launch_bounds__(kMegaThreads, 2) mega_moe_kernel(MegaArgs A) {
   if (tid == 0) sh.tok_key = -1;   // ordered before its first read by the barriers of the phases
   if (blockIdx.x == 0) {
     mega_route_out(A, sh);
-    mega_tokens_out(A);
+    mega_tokens_out<F8>(A);
   }
-  mega_phase_l<true>(A, sh, A.state + kQueueA, sh.nact * (A.I / 32));
-  mega_phase_l<false>(A, sh, A.state + kQueueB, sh.nact * (A.H / 64));
+  mega_phase<true, F8, L1>(A, sh, A.state + kQueueA, sh.nact * (A.I / 32));
+  mega_phase<false, F8, L2>(A, sh, A.state + kQueueB, sh.nact * (A.H / 64));
 
   // Two-level count of finished workgroups; the last one zeroes the state.
   if (tid == 0) {
@@ -629,27 +676,53 @@ __global__ void __launch_bounds__(kMegaThreads, 2) mega_moe_kernel(MegaArgs A) {
 }
 
 namespace {
-int g_mega_grid[64];   // workgroups per launch on each device: CUs x resident workgroups per CU
+// Workgroups per launch of each kernel on each device: CUs x resident
+// workgroups per CU.
+int g_mega_grid[2][4][4][64];
+
+int log2_slice(int steps) { return steps >= 8 ? 3 : steps >= 4 ? 2 : steps >= 2 ? 1 : 0; }
+
+template <bool F8, int L1>
+const void* mega_kernel_l2(int l2) {
+  switch (l2) {
+    case 3: return reinterpret_cast<const void*>(mega_moe_kernel<F8, L1, 8>);
+    case 2: return reinterpret_cast<const void*>(mega_moe_kernel<F8, L1, 4>);
+    case 1: return reinterpret_cast<const void*>(mega_moe_kernel<F8, L1, 2>);
+    default: return reinterpret_cast<const void*>(mega_moe_kernel<F8, L1, 1>);
+  }
 }
+
+template <bool F8>
+const void* mega_kernel_l1(int l1, int l2) {
+  switch (l1) {
+    case 3: return mega_kernel_l2<F8, 8>(l2);
+    case 2: return mega_kernel_l2<F8, 4>(l2);
+    case 1: return mega_kernel_l2<F8, 2>(l2);
+    default: return mega_kernel_l2<F8, 1>(l2);
+  }
+}
+}  // namespace
 
 hipError_t launch_mega(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* w2c, const uint8_t* w2s,
                        const uint16_t* x, const int32_t* ids, const float* tw, uint16_t* out, int T, int H, int I,
                        int E, int k, int hrows, uint8_t* xq, uint8_t* xsf, uint8_t* hq, uint8_t* hsf, uint16_t* y,
                        uint64_t* state, int32_t* counts, int32_t* offsets, int32_t* sorted_rows, int32_t* pos,
-                       uint32_t poll_limit, hipStream_t stream) {
+                       bool f8, uint32_t poll_limit, hipStream_t stream) {
   int dev = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
-  int grid = dev < 64 ? __atomic_load_n(&g_mega_grid[dev], __ATOMIC_RELAXED) : 0;
+  const int l1 = log2_slice(H / kStepK / kMegaWaves), l2 = log2_slice(I / kStepK / kMegaWaves);
+  const void* kern = f8 ? mega_kernel_l1<true>(l1, l2) : mega_kernel_l1<false>(l1, l2);
+  int* cached = &g_mega_grid[f8][l1][l2][dev < 64 ? dev : 0];
+  int grid = dev < 64 ? __atomic_load_n(cached, __ATOMIC_RELAXED) : 0;
   if (grid == 0) {
     int cus = 0, per_cu = 0;
     err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (err != hipSuccess) return err;
-    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(mega_moe_kernel),
-                                                       kMegaThreads, 0);
+    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kMegaThreads, 0);
     if (err != hipSuccess) return err;
     grid = cus * (per_cu > 0 ? per_cu : 1);
-    if (dev < 64) __atomic_store_n(&g_mega_grid[dev], grid, __ATOMIC_RELAXED);
+    if (dev < 64) __atomic_store_n(cached, grid, __ATOMIC_RELAXED);
   }
   const int R = T * k;
   const int64_t items = (int64_t)(R < E ? R : E) * (I / 32);
@@ -659,7 +732,9 @@ hipError_t launch_mega(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* w2
   while ((1 << nbits) < E) ++nbits;
   MegaArgs A{w1c, w1s, w2c, w2s, x, xq, xsf, ids, tw, out, hq, hsf, y, state, counts, offsets, sorted_rows, pos,
              T, H, I, E, k, nbits, hrows, poll_limit};
-  hipLaunchKernelGGL(mega_moe_kernel, dim3(grid), dim3(kMegaThreads), 0, stream, A);
+  void* args[] = {&A};
+  err = hipLaunchKernel(kern, dim3(grid), dim3(kMegaThreads), args, 0, stream);
+  if (err != hipSuccess) return err;
   return hipGetLastError();
 }
 

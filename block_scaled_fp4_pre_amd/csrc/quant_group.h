@@ -79,6 +79,26 @@ __device__ __forceinline__ uint32_t mx_encode_bf16_group(const uint32_t (&w)[16]
   return (uint32_t)(e + 127);
 }
 
+// MXFP8 E4M3 codes (e4m3.h) of 32 bf16 values as 16 words: elements 0..15
+// in lo, 16..31 in hi, one byte each in element order; the return value is
+// the scale byte.  The same rule and arithmetic as quantize_group's F8 branch
+// (the absolute maximum on the bit patterns, as above).
+__device__ __forceinline__ uint32_t mx8_encode_bf16_group(const uint32_t (&w)[16], uint4& lo, uint4& hi) {
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = max(amax, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+  const int e = mx8_scale_exp(amax << 16);
+  const float inv = e4m3_exp2(-e);
+  uint32_t c[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    c[q] = e4m3_pack4(bf16_to_f32(w[2 * q] & 0xFFFFu), bf16_to_f32(w[2 * q] >> 16),
+                      bf16_to_f32(w[2 * q + 1] & 0xFFFFu), bf16_to_f32(w[2 * q + 1] >> 16), inv);
+  lo = make_uint4(c[0], c[1], c[2], c[3]);
+  hi = make_uint4(c[4], c[5], c[6], c[7]);
+  return (uint32_t)(e + 127);
+}
+
 // The 16 words of group g of a bf16 row-major source.
 __device__ __forceinline__ void load_bf16_words(const void* __restrict__ src, int64_t g, uint32_t (&w)[16]) {
   const uint4* p = reinterpret_cast<const uint4*>(src) + g * 4;

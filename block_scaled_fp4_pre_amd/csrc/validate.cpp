@@ -44,7 +44,7 @@ PreparedLayout prepared_layout(const moe_w4a4_cfg* c) {
 }
 
 bool mega_shape_ok(const moe_w4a4_cfg* c) {
-  return c->mma_type == MOE_MMA_MXF4_X_MXF4 && c->hidden % 512 == 0 && c->inter % 512 == 0 &&
+  return (c->mma_type == MOE_MMA_MXF4_X_MXF4 || c->mma_type == MOE_MMA_FP8_X_MXF4) && c->hidden % 512 == 0 && c->inter % 512 == 0 &&
          c->hidden <= kMegaMaxK && c->inter <= kMegaMaxK;
 }
 

@@ -127,8 +127,8 @@ class MoeW4A4Layer:
         return out
 
     def forward_mega(self, x, topk_ids, topk_weights, out=None, stream=None):
-        """The forward as one kernel launch (moe_w4a4_forward_mega: MXFP4, at
-        most 256 routed rows); arguments as forward."""
+        """The forward as one kernel launch (moe_w4a4_forward_mega: MXFP4 or
+        fp8xfp4, at most 256 routed rows); arguments as forward."""
         T = x.shape[0]
         if out is None:
             out = torch.empty((T, self.H), dtype=torch.bfloat16, device=self.device)

@@ -218,12 +218,13 @@ int moe_w4a4_forward(const moe_w4a4_cfg* cfg, const void* prepared, int32_t num_
  * sgl-deep-gemm for packed FP4xFP4 mega-MoE (W4A4)", title and section B; [P3]
  * "Key source snippets", _run_mega_routed, which runs one fused kernel per
  * forward after pre_dispatch).  Every workgroup routes the top-k ids itself;
- * work items (quantizing one token row, a 64-row unit of W1 for one expert, a
- * 64-row unit of W2 for one expert) come from a device-side ticket counter in
- * that order; a GEMM1 item waits for the token rows, a GEMM2 item for its
- * expert's h, each through counters in the workspace; the GEMM2 item that
- * completes a token's 64 hidden columns combines them.
- * Supported: MOE_MMA_MXF4_X_MXF4, num_tokens * topk <= MOE_MEGA_MAX_ROWS,
+ * work items (a 64-row unit of W1 for one expert, which quantizes the token
+ * rows it needs; a 64-row unit of W2 for one expert) come from device-side
+ * ticket counters, all W1 units before any W2 unit; a W2 item waits for its
+ * expert's h through a counter in the workspace; the W2 item that completes a
+ * token's 64 hidden columns combines them.
+ * Supported: MOE_MMA_MXF4_X_MXF4 and MOE_MMA_FP8_X_MXF4,
+ * num_tokens * topk <= MOE_MEGA_MAX_ROWS,
  * hidden and inter multiples of 512 up to 4096; otherwise MOE_EUNSUPPORTED
  * and nothing is enqueued.  Arguments, other errors and the workspace as for
  * moe_w4a4_forward, plus: the workspace's `mega` region (its first
@@ -239,9 +240,12 @@ int moe_w4a4_forward(const moe_w4a4_cfg* cfg, const void* prepared, int32_t num_
  * quarters of K, added in order), so the two paths agree to the parity bar
  * rather than bit for bit; the result is deterministic.
  * moe_w4a4_forward takes this path by itself when it is supported and
- * num_tokens * topk <= MOE_MEGA_AUTO_ROWS. */
+ * num_tokens * topk <= MOE_MEGA_AUTO_ROWS (MXFP4) or MOE_MEGA_AUTO_ROWS_FP8
+ * (fp8xfp4), the sizes up to which it measured faster than the stage
+ * sequence at the DeepSeek-V4-Flash shape. */
 #define MOE_MEGA_MAX_ROWS 256
 #define MOE_MEGA_AUTO_ROWS 96
+#define MOE_MEGA_AUTO_ROWS_FP8 48
 #define MOE_MEGA_STATE_BYTES (144u << 10)
 #define MOE_MEGA_ERR_WORD 800
 int moe_w4a4_forward_mega(const moe_w4a4_cfg* cfg, const void* prepared, int32_t num_tokens,

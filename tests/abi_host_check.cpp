@@ -215,8 +215,8 @@ void stage_checks() {
 }
 
 void mega_checks() {
-  // The single-launch forward: MXFP4, H and I multiples of 512 up to 4096, at
-  // most MOE_MEGA_MAX_ROWS routed rows.
+  // The single-launch forward: MXFP4 or fp8xfp4, H and I multiples of 512 up
+  // to 4096, at most MOE_MEGA_MAX_ROWS routed rows.  NVFP4: refused.
   moe_w4a4_cfg c = base_cfg();
   c.hidden = 4096;
   c.inter = 2048;
@@ -231,6 +231,9 @@ void mega_checks() {
   EXPECT(moe::check_mega_args(&c, 257), MOE_EUNSUPPORTED);
   c.topk = 6;
   c.mma_type = MOE_MMA_FP8_X_MXF4;
+  EXPECT(moe::check_mega_args(&c, 42), MOE_OK);
+  EXPECT(moe::check_mega_args(&c, 43), MOE_EUNSUPPORTED);
+  c.mma_type = MOE_MMA_NVF4_X_NVF4;
   EXPECT(moe::check_mega_args(&c, 1), MOE_EUNSUPPORTED);
   c.mma_type = MOE_MMA_MXF4_X_MXF4;
   const int shapes[][2] = {{4096, 2048}, {512, 512}, {2048, 1024}, {4096, 4096}};

@@ -108,7 +108,11 @@ def test_single_launch_forward_validation():
     assert fwd(cfg, 4) == _lib.MOE_ENODEVICE                    # valid: only the device is missing
     fp8 = _lib.make_cfg(4096, 2048, 256, 6, 64, mma_type=_lib.MOE_MMA_FP8_X_MXF4)
     _, ws8 = _lib.moe_w4a4_query(fp8)
-    assert fwd(fp8, 4, ws8) == _lib.MOE_EUNSUPPORTED
+    assert fwd(fp8, 4, ws8) == _lib.MOE_ENODEVICE               # fp8xfp4: supported
+    assert fwd(fp8, 43, ws8) == _lib.MOE_EUNSUPPORTED
+    nv = _lib.make_cfg(4096, 2048, 256, 6, 64, mma_type=_lib.MOE_MMA_NVF4_X_NVF4)
+    _, wsn = _lib.moe_w4a4_query(nv)
+    assert fwd(nv, 4, wsn) == _lib.MOE_EUNSUPPORTED
     odd = _lib.make_cfg(768, 512, 8, 2, 16)
     _, wso = _lib.moe_w4a4_query(odd)
     assert fwd(odd, 4, wso) == _lib.MOE_EUNSUPPORTED

@@ -50,8 +50,8 @@ def test_one_json_line_with_the_record_fields(mma):
     assert pre["config"]["tokens"] == 4096 and pre["value_us"] > 0
     assert pre["roofline"]["kernel"] == "gemm_lds_kernel" and pre["roofline_gemm2"]["avg_us"] > 0
     assert "cpu_baseline" not in d
-    dec = d.get("dsv4flash_t8_decode_single_launch")     # MXFP4 only: a decode batch as one launch
-    assert (dec is not None) == (mma == "mxf4xmxf4")
+    dec = d.get("dsv4flash_t8_decode_single_launch")     # the MX types: a decode batch as one launch
+    assert (dec is not None) == (mma != "nvf4xnvf4")
     if dec is not None:
         assert dec["config"]["tokens"] == 8 and dec["roofline"]["kernel"] == "mega_moe_kernel"
         assert 0 < dec["value_us"] and 0 < dec["multi_launch_us"]

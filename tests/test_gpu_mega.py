@@ -13,8 +13,11 @@ plus routing edge cases (masked, out-of-range and duplicate ids, a token with
 no valid slot, one token, 256 routed rows), determinism, back-to-back calls
 with different token counts on one workspace interleaved with the multi-launch
 forward, a HIP graph replayed on new inputs, and the error word of the
-kernel's bounded waits staying 0."""
+kernel's bounded waits staying 0.  The fp8xfp4 type (E4M3 tokens and h, 8-row
+GEMM1 passes) on the same shapes, the DSV4 sizes and two edge cases, held to
+its oracle and the MFMA model's element rules on every row."""
 import dataclasses
+import functools
 import zlib
 
 import numpy as np
@@ -28,6 +31,7 @@ from tests.oracle_inputs import all_expert_weights, all_experts_parallel
 from tests.test_gpu_layer import check_all_stages
 
 pytestmark = pytest.mark.gpu
+FP8 = 1   # MOE_MMA_FP8_X_MXF4
 
 SHAPES = [
     synth.LayerConfig(140, "mega_h512_i512_e8_k2_t16", 16, 512, 512, 8, 2, "uniform", 140),
@@ -35,6 +39,18 @@ SHAPES = [
     synth.LayerConfig(142, "mega_h2048_i1024_e64_k6_t42", 42, 2048, 1024, 64, 6, "uniform", 142),
 ]
 DSV4_TOKENS = [1, 8, 42]
+
+
+@functools.lru_cache(maxsize=1)
+def dsv4_weights():
+    """e -> the oracle's MXFP4 weights of DSV4 expert e (both MMA types)."""
+    return all_experts_parallel(synth.CONFIGS[1])
+
+
+@functools.lru_cache(maxsize=4)
+def stacked_weights(cfg):
+    W = all_expert_weights(cfg)
+    return W, (lambda e: (W[0][e], W[1][e], W[2][e], W[3][e]))
 
 
 def err_word(layer):
@@ -79,14 +95,45 @@ def test_mega_dsv4_every_row(T):
     layer = synth_layer(1, T)
     got = run_config(layer, cfg, mega=True)
     log(f"    {int((got['counts'] > 0).sum())} active experts; oracle")
-    ref = forward(got["x"], got["ids"], got["w"], all_experts_parallel(synth.CONFIGS[1]), cfg.experts, cfg.inter)
+    ref = forward(got["x"], got["ids"], got["w"], dsv4_weights(), cfg.experts, cfg.inter)
     check_all_stages(got, ref, cfg.topk)
     assert err_word(layer) == 0
 
 
-@pytest.mark.parametrize("case", ["T1", "masked_dups", "no_valid_slot", "rows256"])
+@pytest.mark.parametrize("cfg", SHAPES, ids=lambda c: c.name)
+def test_mega_fp8_all_tokens(cfg, layers):
+    log(f"[test] mega fp8xfp4 {cfg.name}")
+    layer = layers[cfg.name].with_capacity(cfg.tokens, mma_type=FP8)
+    got = run_config(layer, cfg, mega=True)
+    counts = got["counts"]
+    log(f"    rows per expert: max {counts.max()}, empty {(counts == 0).sum()}")
+    if "zipf" in cfg.name:
+        assert counts.max() > 16 and (counts == 0).any()    # several 8-row GEMM1 passes
+    W, getter = stacked_weights(cfg)
+    ref = forward(got["x"], got["ids"], got["w"], W, cfg.experts, cfg.inter, mma_type="fp8xfp4")
+    check_all_stages(got, ref, cfg.topk, weights=getter)
+    assert err_word(layer) == 0
+
+
+@pytest.mark.parametrize("T", DSV4_TOKENS)
+def test_mega_fp8_dsv4_every_row(T):
+    cfg = dataclasses.replace(synth.CONFIGS[1], name=f"dsv4flash_t{T}", tokens=T)
+    log(f"[test] mega fp8xfp4 DSV4-Flash T={T}")
+    layer = synth_layer(1, T, FP8)
+    got = run_config(layer, cfg, mega=True)
+    log(f"    {int((got['counts'] > 0).sum())} active experts; oracle")
+    W = dsv4_weights()
+    ref = forward(got["x"], got["ids"], got["w"], W, cfg.experts, cfg.inter, mma_type="fp8xfp4")
+    check_all_stages(got, ref, cfg.topk, weights=W)
+    assert err_word(layer) == 0
+
+
+@pytest.mark.parametrize("case", ["T1", "masked_dups", "no_valid_slot", "rows256", "fp8_masked_dups",
+                                  "fp8_rows256"])
 def test_mega_edge_cases(case, layers):
     log(f"[test] mega edge case {case}")
+    fp8 = case.startswith("fp8_")
+    case = case[4:] if fp8 else case
     cfg = SHAPES[0]
     E, k = cfg.experts, cfg.topk
     rng = np.random.default_rng(zlib.crc32(case.encode()))
@@ -102,12 +149,11 @@ def test_mega_edge_cases(case, layers):
     if case == "no_valid_slot":
         ids[4, :] = -1
         ids[9, :] = E
-    layer = layers[cfg.name] if T <= cfg.tokens else layer_for(cfg.hidden, cfg.inter, E, k, T)
-    if T > cfg.tokens:
-        layer.load_fp32(lambda e: synth.expert_weights_f32(cfg, e), threads=4)
+    layer = layers[cfg.name].with_capacity(max(T, cfg.tokens), mma_type=FP8 if fp8 else 0)
     got = run_inputs(layer, x, ids, w, mega=True)
-    ref = forward(x, ids, w, all_expert_weights(cfg), E, cfg.inter)
-    check_all_stages(got, ref, k)
+    W, getter = stacked_weights(cfg)
+    ref = forward(x, ids, w, W, E, cfg.inter, mma_type="fp8xfp4" if fp8 else "mxf4xmxf4")
+    check_all_stages(got, ref, k, weights=getter if fp8 else None)
     if case == "no_valid_slot":
         assert np.all(got["out"][4] == 0) and np.all(got["out"][9] == 0)
     assert err_word(layer) == 0
@@ -153,6 +199,26 @@ def test_forward_takes_the_single_launch_path_for_few_rows(layers):
         _lib.moe_w4a4_forward_noalloc(layer.cfg, layer.prepared, T, xd, idd, wd, out)
         torch.cuda.synchronize()
         assert np.array_equal(host_bits(out), mega)
+    assert np.array_equal(auto, mega)
+    assert err_word(layer) == 0
+
+
+def test_fp8_forward_takes_the_single_launch_path_for_few_rows(layers):
+    """The same for the fp8xfp4 type, up to MOE_MEGA_AUTO_ROWS_FP8 routed rows."""
+    from block_scaled_fp4_pre_amd import _lib
+    log("[test] automatic single-launch path, fp8xfp4")
+    cfg = SHAPES[2]
+    layer = layers[cfg.name].with_capacity(cfg.tokens, mma_type=FP8)
+    T = 48 // cfg.topk
+    x = synth.make_tokens(cfg)[:T]
+    ids, w = synth.make_routing(cfg)
+    xd, idd, wd = dev_bf16(x), dev(ids[:T]), dev(w[:T])
+    mega = host_bits(layer.forward_mega(xd, idd, wd))
+    auto = host_bits(layer.forward(xd, idd, wd))
+    out = torch.empty((T, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+    _lib.moe_w4a4_forward_noalloc(layer.cfg, layer.prepared, T, xd, idd, wd, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(out), mega)
     assert np.array_equal(auto, mega)
     assert err_word(layer) == 0
 
