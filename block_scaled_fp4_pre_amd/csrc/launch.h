@@ -49,7 +49,7 @@ hipError_t launch_predispatch(int act, const uint16_t* x, int64_t ngroups, const
                               hipStream_t stream);
 
 // The whole forward in one launch (mega.hip) for at most kMegaMaxRows routed
-// rows, H and I multiples of 512 up to 4096: route, quantization, both GEMMs
+// rows, H and I each 512, 1024, 2048 or 4096: route, quantization, both GEMMs
 // and the combine; MXFP4 tokens and h, or E4M3 (f8, the fp8xfp4 MMA type).
 // state: the workspace's `mega` region (zero at the launch, left zero);
 // xq/xsf, counts, offsets, sorted_rows, pos, hq/hsf and y receive what the

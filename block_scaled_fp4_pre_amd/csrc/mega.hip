@@ -3,8 +3,8 @@
 // sgl-deep-gemm for packed FP4xFP4 mega-MoE (W4A4)", title and section B,
 // where one kernel runs the routed experts' layer).  MXFP4 x MXFP4 and the
 // fp8xfp4 MMA type (E4M3 tokens and h, [P3] "Implementation breakdown" items
-// 1-3), at most kMegaMaxRows routed rows, hidden and inter multiples of 512
-// up to 4096 (validate.h).
+// 1-3), at most kMegaMaxRows routed rows, hidden and inter each 512, 1024,
+// 2048 or 4096 (validate.h).
 //
 // Stage S1 inside the work items.  Every workgroup routes the T*k ids itself
 // (the stable counting sort of route_common.h in LDS, one thread per routed

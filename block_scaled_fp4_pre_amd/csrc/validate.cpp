@@ -43,9 +43,13 @@ PreparedLayout prepared_layout(const moe_w4a4_cfg* c) {
   return p;
 }
 
+// Hidden and inter of 512, 1024, 2048 or 4096: K splits into 4 slices of 1,
+// 2, 4 or 8 steps of 128, the slice lengths the kernel is built for.
+static bool mega_k_ok(int64_t K) { return K >= 512 && K <= kMegaMaxK && (K & (K - 1)) == 0; }
+
 bool mega_shape_ok(const moe_w4a4_cfg* c) {
-  return (c->mma_type == MOE_MMA_MXF4_X_MXF4 || c->mma_type == MOE_MMA_FP8_X_MXF4) && c->hidden % 512 == 0 && c->inter % 512 == 0 &&
-         c->hidden <= kMegaMaxK && c->inter <= kMegaMaxK;
+  return (c->mma_type == MOE_MMA_MXF4_X_MXF4 || c->mma_type == MOE_MMA_FP8_X_MXF4) && mega_k_ok(c->hidden) &&
+         mega_k_ok(c->inter);
 }
 
 int check_mega_args(const moe_w4a4_cfg* c, int32_t num_tokens) {

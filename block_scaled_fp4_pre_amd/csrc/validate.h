@@ -25,10 +25,11 @@ constexpr int kNvMaxK = 12032;
 constexpr float kNvScaleMin = 0x1p-100f;
 constexpr float kNvScaleMax = 0x1p100f;
 
-// The single-launch forward (mega.hip): MXFP4 x MXFP4 only, at most
+// The single-launch forward (mega.hip): MXFP4 x MXFP4 or fp8xfp4, at most
 // kMegaMaxRows routed rows (num_tokens * topk; one thread each in the
-// workgroup's own route), hidden and inter multiples of 512 up to kMegaMaxK
-// (each of a work item's 4 waves takes a quarter of K, at most 8 steps of 128).
+// workgroup's own route), hidden and inter each 512, 1024, 2048 or kMegaMaxK
+// (each of a work item's 4 waves takes a quarter of K: 1, 2, 4 or 8 steps of
+// 128, the slice lengths the kernel is built for).
 constexpr int kMegaMaxRows = MOE_MEGA_MAX_ROWS;
 constexpr int kMegaMaxK = 4096;
 // Ticket counters per work phase of the single-launch forward.

@@ -225,7 +225,7 @@ int moe_w4a4_forward(const moe_w4a4_cfg* cfg, const void* prepared, int32_t num_
  * token's 64 hidden columns combines them.
  * Supported: MOE_MMA_MXF4_X_MXF4 and MOE_MMA_FP8_X_MXF4,
  * num_tokens * topk <= MOE_MEGA_MAX_ROWS,
- * hidden and inter multiples of 512 up to 4096; otherwise MOE_EUNSUPPORTED
+ * hidden and inter each 512, 1024, 2048 or 4096; otherwise MOE_EUNSUPPORTED
  * and nothing is enqueued.  Arguments, other errors and the workspace as for
  * moe_w4a4_forward, plus: the workspace's `mega` region (its first
  * MOE_MEGA_STATE_BYTES) must be zero before the first call on it, and every

@@ -215,8 +215,8 @@ void stage_checks() {
 }
 
 void mega_checks() {
-  // The single-launch forward: MXFP4 or fp8xfp4, H and I multiples of 512 up
-  // to 4096, at most MOE_MEGA_MAX_ROWS routed rows.  NVFP4: refused.
+  // The single-launch forward: MXFP4 or fp8xfp4, H and I of 512, 1024, 2048
+  // or 4096, at most MOE_MEGA_MAX_ROWS routed rows.  NVFP4: refused.
   moe_w4a4_cfg c = base_cfg();
   c.hidden = 4096;
   c.inter = 2048;
@@ -242,7 +242,8 @@ void mega_checks() {
     c.inter = s[1];
     expect(moe::check_mega_args(&c, 1), MOE_OK, "supported shape", s[0] + s[1]);
   }
-  const int bad[][2] = {{768, 512}, {512, 384}, {8192, 512}, {512, 8192}, {256, 512}};
+  const int bad[][2] = {{768, 512}, {512, 384}, {8192, 512}, {512, 8192}, {256, 512},
+                        {1536, 512}, {512, 1536}, {3072, 2048}, {4096, 2560}, {3584, 512}};
   for (const auto& s : bad) {
     c.hidden = s[0];
     c.inter = s[1];

@@ -113,9 +113,10 @@ def test_single_launch_forward_validation():
     nv = _lib.make_cfg(4096, 2048, 256, 6, 64, mma_type=_lib.MOE_MMA_NVF4_X_NVF4)
     _, wsn = _lib.moe_w4a4_query(nv)
     assert fwd(nv, 4, wsn) == _lib.MOE_EUNSUPPORTED
-    odd = _lib.make_cfg(768, 512, 8, 2, 16)
-    _, wso = _lib.moe_w4a4_query(odd)
-    assert fwd(odd, 4, wso) == _lib.MOE_EUNSUPPORTED
+    for H, I in ((768, 512), (1536, 512), (512, 1536), (3072, 2048)):   # K slices of 1, 2, 4 or 8 steps only
+        odd = _lib.make_cfg(H, I, 8, 2, 16)
+        _, wso = _lib.moe_w4a4_query(odd)
+        assert fwd(odd, 4, wso) == _lib.MOE_EUNSUPPORTED, (H, I)
     lay = _lib.moe_w4a4_workspace_layout(cfg)
     assert lay["mega"] == 0 and lay["xq"] >= _lib.MOE_MEGA_STATE_BYTES
 
