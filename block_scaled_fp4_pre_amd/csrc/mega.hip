@@ -89,6 +89,8 @@ constexpr int kTokStride = kMegaMaxK / 2 + 16;    // E2M1 tile: 16 rows
 constexpr int kTokStride8 = kMegaMaxK + 16;       // E4M3 tile: 8 rows
 constexpr int kTscStride = kMegaMaxK / 32 + 4;
 static_assert(8 * kTokStride8 <= 16 * kTokStride, "the E4M3 tile fits the E2M1 tile's bytes");
+static_assert(2 * (kMegaWaves - 1) * kWave * 16 * 4 <= 16 * kTokStride,
+              "GEMM2's partial sums of two units fit the token tile's bytes");
 
 // Token rows of a GEMM1 pass (the LDS tile) and of a GEMM2 pass.
 template <bool G1, bool F8>
@@ -105,12 +107,12 @@ struct MegaLds {
   int item;
   int last;
   int tok_key;                         // (expert, first row) of the token tile, or -1
-  float red[kMegaWaves - 1][kWave][16];   // partial sums of K slices 1..3
+  float red[kMegaWaves - 1][kWave][16];   // partial sums of the other K slices, one unit per item
   // GEMM1's token tile: 16 quantized token rows of one expert over all of K,
   // rows kTokStride bytes apart (16 bytes of padding put the 16 rows one MFMA
   // operand read touches on distinct banks), and their scale bytes; E4M3: 8
   // rows kTokStride8 bytes apart.
-  uint8_t tok[16 * kTokStride];
+  alignas(16) uint8_t tok[16 * kTokStride];
   uint8_t tsc[16 * kTscStride];
 };
 
@@ -265,26 +267,39 @@ __device__ __forceinline__ void mega_load_weights(const uint8_t* codes, const ui
   }
 }
 
-// Sums the K slices into wave 0's acc, slice 0 first.  Ends with a barrier:
-// the caller's wave 0 then owns the sums, and the other waves may go on.
-__device__ __forceinline__ void mega_reduce(MegaLds& sh, int w, int lane, v4f (&acc)[1][4]) {
-  if (w > 0) {
-    float4* d = reinterpret_cast<float4*>(&sh.red[w - 1][lane][0]);
+// Sums the K slices of unit u into wave u's acc[u], slice 0 first (wave u's
+// own slice enters in its place: fp32 addition commutes).  red: [U][waves -
+// 1][kWave][16] floats, wave w's partial sums of unit u in slot w - (w > u).
+// Ends with a barrier: waves u < U then own the sums, and the others may go
+// on.
+template <int U>
+__device__ __forceinline__ void mega_reduce(float* red, int w, int lane, v4f (&acc)[U][1][4]) {
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) d[rb] = make_float4(acc[0][rb][0], acc[0][rb][1], acc[0][rb][2], acc[0][rb][3]);
+  for (int u = 0; u < U; ++u) {
+    if (w != u) {
+      float4* d = reinterpret_cast<float4*>(red + ((u * (kMegaWaves - 1) + w - (w > u)) * kWave + lane) * 16);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+        d[rb] = make_float4(acc[u][0][rb][0], acc[u][0][rb][1], acc[u][0][rb][2], acc[u][0][rb][3]);
+    }
   }
   __syncthreads();
-  if (w == 0) {
 #pragma unroll
-    for (int q = 0; q < kMegaWaves - 1; ++q) {
-      const float4* s = reinterpret_cast<const float4*>(&sh.red[q][lane][0]);
+  for (int u = 0; u < U; ++u) {
+    if (w == u) {
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const float4 v = s[rb];
-        acc[0][rb][0] += v.x;
-        acc[0][rb][1] += v.y;
-        acc[0][rb][2] += v.z;
-        acc[0][rb][3] += v.w;
+      for (int q = 0; q < kMegaWaves; ++q) {
+        if (q == u) continue;
+        const float4* s =
+            reinterpret_cast<const float4*>(red + ((u * (kMegaWaves - 1) + q - (q > u)) * kWave + lane) * 16);
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          const float4 v = s[rb];
+          acc[u][0][rb][0] += v.x;
+          acc[u][0][rb][1] += v.y;
+          acc[u][0][rb][2] += v.z;
+          acc[u][0][rb][3] += v.w;
+        }
       }
     }
   }
@@ -342,18 +357,21 @@ __device__ void mega_combine(const MegaArgs& A, const MegaLds& sh, int t, int v,
   A.out[(size_t)t * A.H + col] = (uint16_t)f32_to_bf16(s);
 }
 
-// Issues this wave's weight loads of item i: expert act[i / N], unit i % N,
-// the wave's K slice.
-template <bool G1, int L>
+// Issues this wave's weight loads of item i: expert act[i / N], units
+// (i % N) * U .. + U - 1, the wave's K slice of each.
+template <bool G1, int U, int L>
 __device__ __forceinline__ void mega_item_weights(const MegaArgs& A, const MegaLds& sh, int i, int N, int w,
-                                                  int lane, uint4 (&a)[L][4], uint32_t (&sa)[L]) {
-  const int e = sh.act[i / N], unit = i % N, s0 = w * L;
-  if constexpr (G1)
-    mega_load_weights<L>(A.w1c + w1_code_offset(e, unit, s0, A.H, A.I),
-                         A.w1s + w1_scale_offset(e, unit, s0, A.H, A.I), lane, a, sa);
-  else
-    mega_load_weights<L>(A.w2c + w2_code_offset(e, unit, s0, A.H, A.I),
-                         A.w2s + w2_scale_offset(e, unit, s0, A.H, A.I), lane, a, sa);
+                                                  int lane, uint4 (&a)[U][L][4], uint32_t (&sa)[U][L]) {
+  const int e = sh.act[i / N], unit0 = (i % N) * U, s0 = w * L;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if constexpr (G1)
+      mega_load_weights<L>(A.w1c + w1_code_offset(e, unit0 + u, s0, A.H, A.I),
+                           A.w1s + w1_scale_offset(e, unit0 + u, s0, A.H, A.I), lane, a[u], sa[u]);
+    else
+      mega_load_weights<L>(A.w2c + w2_code_offset(e, unit0 + u, s0, A.H, A.I),
+                           A.w2s + w2_scale_offset(e, unit0 + u, s0, A.H, A.I), lane, a[u], sa[u]);
+  }
 }
 
 // GEMM1's token tile for a pass over the sorted rows p0 .. p0 + nrows - 1:
@@ -418,14 +436,15 @@ __device__ __forceinline__ void ld_operand8(const uint8_t* p, const uint8_t* s4,
 // 4 MFMAs (one per 16-row weight block).  GEMM1: the operand from the LDS
 // token tile.  GEMM2: h by agent-scope loads (K-step planes of hrows rows,
 // epilogue.h).  F8: E4M3 operands of 32 bytes a lane (the FP8 MFMA form).
-template <bool G1, bool F8, int L>
+template <bool G1, bool F8, int U, int L>
 __device__ __forceinline__ void mega_pass(const MegaArgs& A, const MegaLds& sh, int p0, int nrows, int s0,
-                                          int lane, const uint4 (&a)[L][4], const uint32_t (&sa)[L],
-                                          v4f (&acc)[1][4]) {
+                                          int lane, const uint4 (&a)[U][L][4], const uint32_t (&sa)[U][L],
+                                          v4f (&acc)[U][1][4]) {
   const int r = lane & 15, kb = lane >> 4;
   const int rr = min(r, nrows - 1);
   const size_t pp = (size_t)s0 * A.hrows + p0 + rr;
-  zero_acc<1>(acc);
+#pragma unroll
+  for (int u = 0; u < U; ++u) zero_acc<1>(acc[u]);
 #pragma unroll
   for (int i = 0; i < L; ++i) {
     uint32_t sb;
@@ -440,10 +459,13 @@ __device__ __forceinline__ void mega_pass(const MegaArgs& A, const MegaLds& sh, 
         const size_t pr = pp + (size_t)i * A.hrows;
         ld_operand8(A.hq + pr * 128, A.hsf + pr * 4, kb, lo, hi, sb);
       }
-      acc[0][0] = mfma_fp4_fp8<0, 0>(a[i][0], lo, hi, acc[0][0], (int)sa[i], (int)sb);
-      acc[0][1] = mfma_fp4_fp8<1, 0>(a[i][1], lo, hi, acc[0][1], (int)sa[i], (int)sb);
-      acc[0][2] = mfma_fp4_fp8<2, 0>(a[i][2], lo, hi, acc[0][2], (int)sa[i], (int)sb);
-      acc[0][3] = mfma_fp4_fp8<3, 0>(a[i][3], lo, hi, acc[0][3], (int)sa[i], (int)sb);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        acc[u][0][0] = mfma_fp4_fp8<0, 0>(a[u][i][0], lo, hi, acc[u][0][0], (int)sa[u][i], (int)sb);
+        acc[u][0][1] = mfma_fp4_fp8<1, 0>(a[u][i][1], lo, hi, acc[u][0][1], (int)sa[u][i], (int)sb);
+        acc[u][0][2] = mfma_fp4_fp8<2, 0>(a[u][i][2], lo, hi, acc[u][0][2], (int)sa[u][i], (int)sb);
+        acc[u][0][3] = mfma_fp4_fp8<3, 0>(a[u][i][3], lo, hi, acc[u][0][3], (int)sa[u][i], (int)sb);
+      }
     } else {
       uint4 b;
       if constexpr (G1) {
@@ -453,10 +475,13 @@ __device__ __forceinline__ void mega_pass(const MegaArgs& A, const MegaLds& sh, 
         const size_t pr = pp + (size_t)i * A.hrows;
         ld_operand(A.hq + pr * 64 + kb * 16, A.hsf + pr * 4, kb, b, sb);
       }
-      acc[0][0] = mfma_fp4<0, 0>(a[i][0], b, acc[0][0], (int)sa[i], (int)sb);
-      acc[0][1] = mfma_fp4<1, 0>(a[i][1], b, acc[0][1], (int)sa[i], (int)sb);
-      acc[0][2] = mfma_fp4<2, 0>(a[i][2], b, acc[0][2], (int)sa[i], (int)sb);
-      acc[0][3] = mfma_fp4<3, 0>(a[i][3], b, acc[0][3], (int)sa[i], (int)sb);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        acc[u][0][0] = mfma_fp4<0, 0>(a[u][i][0], b, acc[u][0][0], (int)sa[u][i], (int)sb);
+        acc[u][0][1] = mfma_fp4<1, 0>(a[u][i][1], b, acc[u][0][1], (int)sa[u][i], (int)sb);
+        acc[u][0][2] = mfma_fp4<2, 0>(a[u][i][2], b, acc[u][0][2], (int)sa[u][i], (int)sb);
+        acc[u][0][3] = mfma_fp4<3, 0>(a[u][i][3], b, acc[u][0][3], (int)sa[u][i], (int)sb);
+      }
     }
   }
 }
@@ -471,6 +496,15 @@ __device__ __forceinline__ void mega_epilogue(const MegaArgs& A, int unit, int p
     gemm1_epilogue<1, F8, CoherentStore>(acc, unit, p0, nrows, A.I, A.hrows, lane, A.hq, A.hsf, nullptr);
   else
     gemm2_epilogue<1, CoherentStore>(acc, unit, p0, nrows, A.H, lane, A.y);
+}
+
+// Wave w (< U)'s epilogue: that of unit w of the item, whose sums it holds.
+template <bool G1, bool F8, int U>
+__device__ __forceinline__ void mega_epilogue_u(const MegaArgs& A, int unit, int p0, int nrows, int w, int lane,
+                                                v4f (&acc)[U][1][4]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (w == u) mega_epilogue<G1, F8>(A, unit, p0, nrows, lane, acc[u]);
 }
 
 // What wave 0 still owes for the stores of an earlier pass: the expert's h
@@ -532,22 +566,28 @@ __device__ __forceinline__ void mega_publish_end(const MegaArgs& A, const MegaLd
 // One queue of a phase (the counter at ctr hands out items q, q +
 // kMegaQueues, ... below n), pipelined: the next item's ticket is taken while
 // the current item runs, and each wave issues the next item's weights as soon
-// as its MFMAs have consumed the current ones, before the epilogue.
-template <bool G1, bool F8, int L>
+// as its MFMAs have consumed the current ones, before the epilogue.  An item
+// covers U weight units (GEMM2: 1 or 2); wave u < U reduces unit u, runs its
+// epilogue and publishes it.
+template <bool G1, bool F8, int U, int L>
 __device__ void mega_queue(const MegaArgs& A, MegaLds& sh, uint64_t* ctr, int q, int n) {
   constexpr int P = pass_rows<G1, F8>();
+  static_assert(U == 1 || (!G1 && U == 2), "two units per item: GEMM2 only");
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int N = G1 ? A.I / 32 : A.H / 64, s0 = w * L;
+  const int N = G1 ? A.I / 32 : A.H / 64 / U, s0 = w * L;
+  // Partial sums of the K slices: GEMM2 with two units puts them in the
+  // token tile's bytes, which only GEMM1 uses.
+  float* red = U == 1 ? &sh.red[0][0][0] : reinterpret_cast<float*>(sh.tok);
   if (tid == 0) sh.item = (int)min(add_agent(ctr, 1) * kMegaQueues + q, (uint64_t)INT_MAX);
   __syncthreads();
   int cur = sh.item;
   __syncthreads();
   if (cur >= n) return;
-  uint4 a[L][4];
-  uint32_t sa[L];
-  mega_item_weights<G1, L>(A, sh, cur, N, w, lane, a, sa);
-  MegaPending pd;   // wave 0's
+  uint4 a[U][L][4];
+  uint32_t sa[U][L];
+  mega_item_weights<G1, U, L>(A, sh, cur, N, w, lane, a, sa);
+  MegaPending pd;   // waves u < U: unit u's
   // GEMM2: the next item's h counter, read as soon as the item is known; a
   // count already complete spares the wait's first load
   uint64_t hc_next = 0;
@@ -559,7 +599,7 @@ __device__ void mega_queue(const MegaArgs& A, MegaLds& sh, uint64_t* ctr, int q,
     // (or spilled) across them.
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    const int e = sh.act[cur / N], unit = cur % N;
+    const int e = sh.act[cur / N], unit = (cur % N) * U + min(w, U - 1);   // the wave's unit, if it has one
     const int base = sh.off[e], n_e = sh.off[e + 1] - base;
     if constexpr (!G1) {
       // h of the expert is complete once each of its I/32 GEMM1 items has
@@ -575,13 +615,13 @@ __device__ void mega_queue(const MegaArgs& A, MegaLds& sh, uint64_t* ctr, int q,
       const int nrows = min(P, n_e - t0);
       const bool last = t0 + P >= n_e;
       if constexpr (G1) mega_token_tile<F8>(A, sh, base + t0, nrows);
-      v4f acc[1][4];
-      mega_pass<G1, F8, L>(A, sh, base + t0, nrows, s0, ln, a, sa, acc);
-      // The previous pass's stores are long done: wave 0 publishes them
+      v4f acc[U][1][4];
+      mega_pass<G1, F8, U, L>(A, sh, base + t0, nrows, s0, ln, a, sa, acc);
+      // The previous pass's stores are long done: waves u < U publish them
       // while the other waves reach the reduction.
-      if (w == 0) mega_publish<G1>(A, sh, pd, ln);
+      if (w < U) mega_publish<G1>(A, sh, pd, ln);
       if (last && tid == 0) sh.item = (int)min(next_raw * kMegaQueues + q, (uint64_t)INT_MAX);
-      mega_reduce(sh, w, ln, acc);   // a barrier: sh.item is published
+      mega_reduce<U>(red, w, ln, acc);   // a barrier: sh.item is published
       if (last) nxt = sh.item;
       if constexpr (!G1) {
         if (last && nxt < n) hc_next = ld_agent(A.state + kCounters + sh.act[nxt / N]);
@@ -590,8 +630,8 @@ __device__ void mega_queue(const MegaArgs& A, MegaLds& sh, uint64_t* ctr, int q,
       // weights unconditionally, so that the spent weights are dead during
       // the epilogue instead of being kept for a merge with the new ones.)
       if (last && nxt >= n) {
-        if (w == 0) {
-          mega_epilogue<G1, F8>(A, unit, base + t0, nrows, ln, acc);
+        if (w < U) {
+          mega_epilogue_u<G1, F8, U>(A, unit, base + t0, nrows, w, ln, acc);
           mega_publish_end<G1>(A, sh, pd, ln);
           pd.e = e, pd.unit = unit, pd.p0 = base + t0, pd.nrows = nrows;
           mega_publish<G1>(A, sh, pd, ln);   // the queue's last: published at once
@@ -600,13 +640,13 @@ __device__ void mega_queue(const MegaArgs& A, MegaLds& sh, uint64_t* ctr, int q,
         __syncthreads();
         return;
       }
-      if (w == 0) {
-        mega_epilogue<G1, F8>(A, unit, base + t0, nrows, ln, acc);
+      if (w < U) {
+        mega_epilogue_u<G1, F8, U>(A, unit, base + t0, nrows, w, ln, acc);
         mega_publish_end<G1>(A, sh, pd, ln);
         if (!G1 || last) pd.e = e, pd.unit = unit, pd.p0 = base + t0, pd.nrows = nrows;
-        if (last) mega_item_weights<G1, L>(A, sh, nxt, N, 0, ln, a, sa);
+        if (last) mega_item_weights<G1, U, L>(A, sh, nxt, N, w, ln, a, sa);
       } else if (last) {
-        mega_item_weights<G1, L>(A, sh, nxt, N, w, ln, a, sa);
+        mega_item_weights<G1, U, L>(A, sh, nxt, N, w, ln, a, sa);
       }
       __syncthreads();   // the partial sums' LDS and sh.item are free again
     }
@@ -617,12 +657,12 @@ __device__ void mega_queue(const MegaArgs& A, MegaLds& sh, uint64_t* ctr, int q,
 // Takes the items of one phase (n of them, item i on queue i % kMegaQueues)
 // until every queue has run out: first the workgroup's own queue, then,
 // after one read of all the queue counters at once, any queue still open.
-template <bool G1, bool F8, int L>
+template <bool G1, bool F8, int U, int L>
 __device__ void mega_phase(const MegaArgs& A, MegaLds& sh, uint64_t* q0, int n) {
   const int tid = threadIdx.x;
   int q = blockIdx.x % kMegaQueues;
   for (;;) {
-    mega_queue<G1, F8, L>(A, sh, q0 + q * kLine, q, n);
+    mega_queue<G1, F8, U, L>(A, sh, q0 + q * kLine, q, n);
     if (tid < kWave) {
       const bool open = tid < kMegaQueues && ld_agent(q0 + tid * kLine) * kMegaQueues + tid < (uint64_t)n;
       const uint64_t m = __ballot(open);
@@ -640,10 +680,10 @@ __device__ void mega_phase(const MegaArgs& A, MegaLds& sh, uint64_t* q0, int n) 
 
 }  // namespace
 
-// One kernel per token format and K-slice lengths (L1 = H / 512 steps for
-// GEMM1, L2 = I / 512 for GEMM2), so that each holds only its own two phase
-// bodies and their registers.
-template <bool F8, int L1, int L2>
+// One kernel per token format, K-slice lengths (L1 = H / 512 steps for
+// GEMM1, L2 = I / 512 for GEMM2) and W2 units per GEMM2 item (U2), so that
+// each holds only its own two phase bodies and their registers.
+template <bool F8, int L1, int L2, int U2>
 __global__ void __launch_bounds__(kMegaThreads, 2) mega_moe_kernel(MegaArgs A) {
   __shared__ MegaLds sh;
   const int tid = threadIdx.x;
@@ -653,8 +693,8 @@ __global__ void __launch_bounds__(kMegaThreads, 2) mega_moe_kernel(MegaArgs A) {
     mega_route_out(A, sh);
     mega_tokens_out<F8>(A);
   }
-  mega_phase<true, F8, L1>(A, sh, A.state + kQueueA, sh.nact * (A.I / 32));
-  mega_phase<false, F8, L2>(A, sh, A.state + kQueueB, sh.nact * (A.H / 64));
+  mega_phase<true, F8, 1, L1>(A, sh, A.state + kQueueA, sh.nact * (A.I / 32));
+  mega_phase<false, F8, U2, L2>(A, sh, A.state + kQueueB, sh.nact * (A.H / 64 / U2));
 
   // Two-level count of finished workgroups; the last one zeroes the state.
   if (tid == 0) {
@@ -678,27 +718,37 @@ __global__ void __launch_bounds__(kMegaThreads, 2) mega_moe_kernel(MegaArgs A) {
 namespace {
 // Workgroups per launch of each kernel on each device: CUs x resident
 // workgroups per CU.
-int g_mega_grid[2][4][4][64];
+int g_mega_grid[2][4][4][2][64];
 
 int log2_slice(int steps) { return steps >= 8 ? 3 : steps >= 4 ? 2 : steps >= 2 ? 1 : 0; }
 
+// Two W2 units per GEMM2 item (twice the weights per item, half the items)
+// from this many routed rows on, when the wave's two slices fit its
+// registers (at most 4 steps each: inter up to 2048).
+#ifndef MOE_MEGA_PAIR_ROWS
+#define MOE_MEGA_PAIR_ROWS 24
+#endif
+
 template <bool F8, int L1>
-const void* mega_kernel_l2(int l2) {
+const void* mega_kernel_l2(int l2, bool pair) {
   switch (l2) {
-    case 3: return reinterpret_cast<const void*>(mega_moe_kernel<F8, L1, 8>);
-    case 2: return reinterpret_cast<const void*>(mega_moe_kernel<F8, L1, 4>);
-    case 1: return reinterpret_cast<const void*>(mega_moe_kernel<F8, L1, 2>);
-    default: return reinterpret_cast<const void*>(mega_moe_kernel<F8, L1, 1>);
+    case 3: return reinterpret_cast<const void*>(mega_moe_kernel<F8, L1, 8, 1>);
+    case 2: return pair ? reinterpret_cast<const void*>(mega_moe_kernel<F8, L1, 4, 2>)
+                        : reinterpret_cast<const void*>(mega_moe_kernel<F8, L1, 4, 1>);
+    case 1: return pair ? reinterpret_cast<const void*>(mega_moe_kernel<F8, L1, 2, 2>)
+                        : reinterpret_cast<const void*>(mega_moe_kernel<F8, L1, 2, 1>);
+    default: return pair ? reinterpret_cast<const void*>(mega_moe_kernel<F8, L1, 1, 2>)
+                         : reinterpret_cast<const void*>(mega_moe_kernel<F8, L1, 1, 1>);
   }
 }
 
 template <bool F8>
-const void* mega_kernel_l1(int l1, int l2) {
+const void* mega_kernel_l1(int l1, int l2, bool pair) {
   switch (l1) {
-    case 3: return mega_kernel_l2<F8, 8>(l2);
-    case 2: return mega_kernel_l2<F8, 4>(l2);
-    case 1: return mega_kernel_l2<F8, 2>(l2);
-    default: return mega_kernel_l2<F8, 1>(l2);
+    case 3: return mega_kernel_l2<F8, 8>(l2, pair);
+    case 2: return mega_kernel_l2<F8, 4>(l2, pair);
+    case 1: return mega_kernel_l2<F8, 2>(l2, pair);
+    default: return mega_kernel_l2<F8, 1>(l2, pair);
   }
 }
 }  // namespace
@@ -712,8 +762,9 @@ hipError_t launch_mega(const uint8_t* w1c, const uint8_t* w1s, const uint8_t* w2
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
   const int l1 = log2_slice(H / kStepK / kMegaWaves), l2 = log2_slice(I / kStepK / kMegaWaves);
-  const void* kern = f8 ? mega_kernel_l1<true>(l1, l2) : mega_kernel_l1<false>(l1, l2);
-  int* cached = &g_mega_grid[f8][l1][l2][dev < 64 ? dev : 0];
+  const bool pair = l2 < 3 && T * k >= MOE_MEGA_PAIR_ROWS;
+  const void* kern = f8 ? mega_kernel_l1<true>(l1, l2, pair) : mega_kernel_l1<false>(l1, l2, pair);
+  int* cached = &g_mega_grid[f8][l1][l2][pair][dev < 64 ? dev : 0];
   int grid = dev < 64 ? __atomic_load_n(cached, __ATOMIC_RELAXED) : 0;
   if (grid == 0) {
     int cus = 0, per_cu = 0;
