@@ -121,6 +121,10 @@ KERNELS = {
     ("gemm2", "nv_prefill"): ("gemm_lds_nv_kernel", "gemm_lds_nv_kernel_gemm2",
                               ("gemm_lds_nv.hip", "nvfp4.h", "gemm_common.h", "epilogue.h", "device_common.h",
                                "tiles.h", "e4m3.h", "epilogue_nv.h")),
+    # the single-launch forward: the whole layer in one kernel
+    ("layer", "single"): ("mega_moe_kernel", "mega_moe_kernel",
+                          ("mega.hip", "epilogue.h", "gemm_common.h", "quant_group.h", "nvfp4.h", "tiles.h",
+                           "device_common.h", "e4m3.h")),
 }
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "{}_{}_hbm_counters.txt")
 
@@ -341,9 +345,11 @@ def workload_record(layer, cfg, steps, warmup, mma_type):
 
 def decode_record(layer, cfg, steps, warmup):
     """The DeepSeek-V4-Flash layer at a decode batch (cfg: its shape and
-    routing recipe, cfg.tokens tokens) through moe_w4a4_forward, which takes
-    the single-launch kernel at that size (mega_moe_kernel), beside the same
-    forward as the four launches of the stage sequence (moe_w4a4_run_stages)."""
+    routing recipe, cfg.tokens tokens) as the single-launch kernel
+    (moe_w4a4_forward_mega, mega_moe_kernel), beside the same forward as the
+    four launches of the stage sequence (moe_w4a4_run_stages).
+    "forward_takes_single_launch": whether moe_w4a4_forward runs the single
+    launch at this size."""
     import torch
 
     import synth
@@ -368,19 +374,22 @@ def decode_record(layer, cfg, steps, warmup):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / steps * 1e3
 
-    us = timed(lambda: layer.forward(x, ids, w, out))
+    us = timed(lambda: layer.forward_mega(x, ids, w, out))
     multi = timed(lambda: layer.run_stages(_lib.MOE_STAGE_ALL, T, x=x, topk_ids=ids, topk_weights=w, out=out))
     counts = layer.ws("counts", (cfg.experts,), torch.int32).cpu().numpy()
     alg = algorithmic(cfg, counts)
     gbps = alg["layer_bytes"] / (us * 1e-6) / 1e9
+    traffic = measured_traffic(cfg.name, "layer", "single", layer.mma_type == _lib.MOE_MMA_FP8_X_MXF4)
     return {
         "value_us": round(us, 2),
         "multi_launch_us": round(multi, 2),
         "speedup_over_multi_launch": round(multi / us, 3),
+        "forward_takes_single_launch": T * cfg.topk <= (_lib.MOE_MEGA_AUTO_ROWS_FP8 if layer.mma_type == 1
+                                                        else _lib.MOE_MEGA_AUTO_ROWS),
         "hbm_gbps": round(gbps, 1),
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"kernel": "mega_moe_kernel", "bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None, "avg_us": round(us, 2),
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic, "avg_us": round(us, 2),
                      "bytes_per_launch": int(alg["layer_bytes"])},
         "config": {"tokens": T, "routing": cfg.routing, "active_experts": alg["active"], "routed_rows": alg["R"]},
     }

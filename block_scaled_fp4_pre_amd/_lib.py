@@ -20,6 +20,8 @@ MOE_ACT_SWIGLU = 0
 MOE_STAGE_QUANT, MOE_STAGE_ROUTE, MOE_STAGE_GEMM1, MOE_STAGE_GEMM2, MOE_STAGE_COMBINE = 1, 2, 4, 8, 16
 MOE_STAGE_ALL = 31
 MOE_MEGA_MAX_ROWS = 256          # routed rows the single-launch forward takes
+MOE_MEGA_AUTO_ROWS = 48          # routed rows up to which moe_w4a4_forward takes it (MXFP4)
+MOE_MEGA_AUTO_ROWS_FP8 = 24      # the same for fp8xfp4
 MOE_MEGA_STATE_BYTES = 144 << 10  # its workspace state region (offset 0), zero before its first call
 MOE_MEGA_ERR_WORD = 800           # uint64 word of that region that a wait which gave up sets
 

@@ -244,8 +244,8 @@ int moe_w4a4_forward(const moe_w4a4_cfg* cfg, const void* prepared, int32_t num_
  * (fp8xfp4), the sizes up to which it measured faster than the stage
  * sequence at the DeepSeek-V4-Flash shape. */
 #define MOE_MEGA_MAX_ROWS 256
-#define MOE_MEGA_AUTO_ROWS 96
-#define MOE_MEGA_AUTO_ROWS_FP8 48
+#define MOE_MEGA_AUTO_ROWS 48
+#define MOE_MEGA_AUTO_ROWS_FP8 24
 #define MOE_MEGA_STATE_BYTES (144u << 10)
 #define MOE_MEGA_ERR_WORD 800
 int moe_w4a4_forward_mega(const moe_w4a4_cfg* cfg, const void* prepared, int32_t num_tokens,

@@ -235,3 +235,16 @@ def test_binding_rejects_bad_weight_and_quantize_buffers():
         _lib.moe_w4a4_quantize(_t((4, 64), torch.float32), _t((4, 31), torch.uint8), _t((4, 2), torch.uint8))
     with pytest.raises(ValueError):
         _lib.moe_w4a4_quantize(_t((4, 64), torch.float64), _t((4, 32), torch.uint8), _t((4, 2), torch.uint8))
+
+
+def test_binding_constants_match_the_header():
+    """The binding's copies of the header's #define values."""
+    import re
+    from block_scaled_fp4_pre_amd import _lib
+    text = open(os.path.join(os.path.dirname(__file__), "..", "include", "moe_w4a4.h")).read()
+    for name in ("MOE_MEGA_MAX_ROWS", "MOE_MEGA_AUTO_ROWS", "MOE_MEGA_AUTO_ROWS_FP8", "MOE_MEGA_ERR_WORD", "MOE_NOALLOC_SCRATCH_BYTES",
+                 "MOE_MEGA_STATE_BYTES"):
+        m = re.search(rf"#define {name} \(?(\d+)u?(?: << (\d+))?\)?", text)
+        assert m, name
+        value = int(m.group(1)) << int(m.group(2) or 0)
+        assert getattr(_lib, name) == value, name

@@ -188,7 +188,7 @@ def test_forward_takes_the_single_launch_path_for_few_rows(layers):
     log("[test] automatic single-launch path")
     cfg = SHAPES[2]
     layer = layers[cfg.name]
-    T = 96 // cfg.topk
+    T = _lib.MOE_MEGA_AUTO_ROWS // cfg.topk
     x = synth.make_tokens(cfg)[:T]
     ids, w = synth.make_routing(cfg)
     xd, idd, wd = dev_bf16(x), dev(ids[:T]), dev(w[:T])
@@ -209,7 +209,7 @@ def test_fp8_forward_takes_the_single_launch_path_for_few_rows(layers):
     log("[test] automatic single-launch path, fp8xfp4")
     cfg = SHAPES[2]
     layer = layers[cfg.name].with_capacity(cfg.tokens, mma_type=FP8)
-    T = 48 // cfg.topk
+    T = _lib.MOE_MEGA_AUTO_ROWS_FP8 // cfg.topk
     x = synth.make_tokens(cfg)[:T]
     ids, w = synth.make_routing(cfg)
     xd, idd, wd = dev_bf16(x), dev(ids[:T]), dev(w[:T])
