@@ -183,7 +183,7 @@ static hipError_t launch_gemm1_t(const uint8_t* w1c, const uint8_t* w1s, const u
                                  uint8_t* hsf, float* acc_out, hipStream_t stream) {
   constexpr int ROWS = NT == 1 ? 16 : MOE_STREAM_ROWS2;
   size_t lds = (size_t)ROWS * (F8 ? H : H / 2) + (size_t)ROWS * (H / 32);
-  if (NT == 1 && lds < kOneTileMinLds) lds = kOneTileMinLds;   // at most two workgroups per CU (stream_ring.h)
+  if (lds < kStreamMinLds) lds = kStreamMinLds;   // at most two workgroups per CU (stream_ring.h)
   auto kern = gemm1_swiglu_kernel<NT, D, SWZ, F8, WAVES>;
   const int upw = units_per_wave(I / 32 / WAVES, MOE_GEMM1_UNITS_PER_WAVE);
   if (lds > 65536) {

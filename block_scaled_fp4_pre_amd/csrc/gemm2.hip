@@ -167,7 +167,7 @@ static hipError_t launch_gemm2_t(const uint8_t* w2c, const uint8_t* w2s, const u
                                  int H, int I, int E, int hrows, uint16_t* y, hipStream_t stream) {
   constexpr int ROWS = NT == 1 ? 16 : MOE_STREAM_ROWS2;
   size_t lds = (size_t)ROWS * (F8 ? I : I / 2) + (size_t)ROWS * (I / 32);
-  if (NT == 1 && lds < kOneTileMinLds) lds = kOneTileMinLds;   // at most two workgroups per CU (stream_ring.h)
+  if (lds < kStreamMinLds) lds = kStreamMinLds;   // at most two workgroups per CU (stream_ring.h)
   auto kern = gemm2_kernel<NT, D, SWZ, F8>;
   const int upw = units_per_wave(H / kUnitRows / 4, MOE_GEMM2_UNITS_PER_WAVE);
   if (lds > 65536) {

@@ -8,14 +8,15 @@
 
 namespace moe {
 
-// Dynamic LDS of a one-tile launch (16 token rows per pass) at least this
-// much, so that at most two of its 4-wave workgroups share a CU.  At decode
-// sizes most workgroups belong to experts without rows and exit at once; the
-// few live ones were placed up to four to a CU when their registers and a
-// small token tile allowed it, and streamed their weights more slowly than
-// two to a CU: at 8 tokens (DeepSeek-V4-Flash shape, top-6, MXFP4) the two
-// GEMMs took 99 us instead of 132 per layer, at 64 tokens 397 instead of 403.
-constexpr size_t kOneTileMinLds = 56u << 10;
+// Dynamic LDS of a streaming launch at least this much, so that at most two
+// of its 4-wave workgroups share a CU.  At decode sizes most workgroups
+// belong to experts without rows and exit at once; the few live ones were
+// placed up to four to a CU when their registers and a small token tile
+// allowed it, and streamed their weights more slowly than two to a CU: at 8
+// tokens (DeepSeek-V4-Flash shape, top-6, MXFP4) the two GEMMs took 99 us
+// instead of 132 per layer, at 64 tokens 397 instead of 403; at 512 tokens
+// (two token tiles, three to a CU before) the layer took 534 instead of 538.
+constexpr size_t kStreamMinLds = 56u << 10;
 
 // Fill the ring with the wave's first D K steps.
 // The ring's refills run up to D steps past a wave's last one (gemm1.hip,
