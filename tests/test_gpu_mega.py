@@ -15,7 +15,8 @@ with different token counts on one workspace interleaved with the multi-launch
 forward, a HIP graph replayed on new inputs, and the error word of the
 kernel's bounded waits staying 0.  The fp8xfp4 type (E4M3 tokens and h, 8-row
 GEMM1 passes) on the same shapes, the DSV4 sizes and two edge cases, held to
-its oracle and the MFMA model's element rules on every row."""
+its oracle and the MFMA model's element rules on every row.  The kernel's
+token encoder of both types on every finite bf16 pattern."""
 import dataclasses
 import functools
 import zlib
@@ -125,6 +126,41 @@ def test_mega_fp8_dsv4_every_row(T):
     W = dsv4_weights()
     ref = forward(got["x"], got["ids"], got["w"], W, cfg.experts, cfg.inter, mma_type="fp8xfp4")
     check_all_stages(got, ref, cfg.topk, weights=W)
+    assert err_word(layer) == 0
+
+
+@pytest.mark.parametrize("mma", [0, FP8], ids=["mxf4xmxf4", "fp8xfp4"])
+def test_mega_quantizes_every_bf16_pattern(mma):
+    """The kernel's token encoder (the one its GEMM1 items use for their
+    tiles; block 0 writes its x-hat to the workspace) on every finite bf16
+    pattern as a lone value of its 32-group, at positions 0 and 17: codes and
+    scales bit-exact against the oracle's quantizer, in two calls of 255
+    tokens of hidden 4096."""
+    from oracle import bf16, mxfp4, mxfp8
+    log(f"[test] mega quantize: every finite bf16 pattern, mma_type {mma}")
+    H, I, E = 4096, 512, 8
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    vals = bits[((bits >> 7) & 0xFF) != 0xFF].astype(np.uint16)      # 65280 finite patterns
+    grp = np.zeros((vals.size, 32), np.uint16)
+    grp[:, 0] = vals
+    grp[:, 17] = vals[::-1]
+    T = 255
+    x_all = grp.reshape(-1, T, H)                                     # 2 calls of 255 tokens x 128 groups
+    assert x_all.shape[0] == 2
+    rng = np.random.default_rng(5)
+    layer = layer_for(H, I, E, 1, T, mma_type=mma)
+    layer.load_fp32(lambda e: ((rng.standard_normal((2 * I, H)) * 0.02).astype(np.float32),
+                               (rng.standard_normal((H, I)) * 0.02).astype(np.float32)), threads=1)
+    ids = (np.arange(T, dtype=np.int32) % E).reshape(T, 1)
+    w = np.ones((T, 1), np.float32)
+    for x in x_all:
+        layer.forward_mega(dev_bf16(x), dev(ids), dev(w))
+        torch.cuda.synchronize()
+        xq = layer.ws("xq", (T, H if mma else H // 2), torch.uint8).cpu().numpy()
+        xsf = layer.ws("xsf", (T, H // 32), torch.uint8).cpu().numpy()
+        rc, rs = (mxfp8.quantize if mma else mxfp4.quantize_packed)(bf16.decode(x))
+        assert np.array_equal(xsf, rs)
+        assert np.array_equal(xq, rc)
     assert err_word(layer) == 0
 
 
