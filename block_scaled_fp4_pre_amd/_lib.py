@@ -24,6 +24,7 @@ MOE_MEGA_AUTO_ROWS = 48          # routed rows up to which moe_w4a4_forward take
 MOE_MEGA_AUTO_ROWS_FP8 = 24      # the same for fp8xfp4
 MOE_MEGA_STATE_BYTES = 144 << 10  # its workspace state region (offset 0), zero before its first call
 MOE_MEGA_ERR_WORD = 800           # uint64 word of that region that a wait which gave up sets
+MOE_MEGA_HCOUNT_WORD = 816        # first per-expert h count of that region (words hcount + e)
 
 # Every symbol include/moe_w4a4.h declares.
 EXPORTED = (

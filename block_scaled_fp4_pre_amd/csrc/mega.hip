@@ -84,6 +84,7 @@ constexpr int kCounters = kErr + kLine;                     // h counters [E], t
 static_assert((uint64_t)(kCounters + kMaxExperts + kMegaMaxRows * (kMegaMaxK / 64)) * 8 <= kMegaStateBytes,
               "state region");
 static_assert(kErr == MOE_MEGA_ERR_WORD, "error word documented in moe_w4a4.h");
+static_assert(kCounters == MOE_MEGA_HCOUNT_WORD, "h counters documented in moe_w4a4.h");
 
 constexpr int kTokStride = kMegaMaxK / 2 + 16;    // E2M1 tile: 16 rows
 constexpr int kTokStride8 = kMegaMaxK + 16;       // E4M3 tile: 8 rows

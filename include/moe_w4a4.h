@@ -233,7 +233,10 @@ int moe_w4a4_forward(const moe_w4a4_cfg* cfg, const void* prepared, int32_t num_
  * that share a workspace must not overlap.  A wait inside the kernel that runs
  * out of polls (about 0.1 s; none does unless the state was not zero) sets the
  * error word, uint64 number MOE_MEGA_ERR_WORD of the region, which the kernel
- * never clears; that call's results are then unspecified.  Afterwards the workspace holds the same
+ * never clears; that call's results are then unspecified, and the rest of the
+ * region is still left zero.  Words MOE_MEGA_HCOUNT_WORD + e (e < num_experts)
+ * hold the per-expert counts that the W2 items wait for (tests force a wait
+ * to give up by setting them beforehand).  Afterwards the workspace holds the same
  * intermediates as after moe_w4a4_forward (xq, xsf, counts, offsets,
  * sorted_rows, pos, hq, hsf, y).  Numerics as moe_w4a4_forward except the
  * order of the fp32 sums of both GEMMs (each sum is four partial sums over
@@ -248,6 +251,7 @@ int moe_w4a4_forward(const moe_w4a4_cfg* cfg, const void* prepared, int32_t num_
 #define MOE_MEGA_AUTO_ROWS_FP8 24
 #define MOE_MEGA_STATE_BYTES (144u << 10)
 #define MOE_MEGA_ERR_WORD 800
+#define MOE_MEGA_HCOUNT_WORD 816
 int moe_w4a4_forward_mega(const moe_w4a4_cfg* cfg, const void* prepared, int32_t num_tokens,
                           const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
                           uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);

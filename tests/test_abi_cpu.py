@@ -242,7 +242,8 @@ def test_binding_constants_match_the_header():
     import re
     from block_scaled_fp4_pre_amd import _lib
     text = open(os.path.join(os.path.dirname(__file__), "..", "include", "moe_w4a4.h")).read()
-    for name in ("MOE_MEGA_MAX_ROWS", "MOE_MEGA_AUTO_ROWS", "MOE_MEGA_AUTO_ROWS_FP8", "MOE_MEGA_ERR_WORD", "MOE_NOALLOC_SCRATCH_BYTES",
+    for name in ("MOE_MEGA_MAX_ROWS", "MOE_MEGA_AUTO_ROWS", "MOE_MEGA_AUTO_ROWS_FP8", "MOE_MEGA_ERR_WORD",
+                 "MOE_MEGA_HCOUNT_WORD", "MOE_NOALLOC_SCRATCH_BYTES",
                  "MOE_MEGA_STATE_BYTES"):
         m = re.search(rf"#define {name} \(?(\d+)u?(?: << (\d+))?\)?", text)
         assert m, name

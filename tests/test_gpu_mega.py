@@ -259,6 +259,36 @@ def test_fp8_forward_takes_the_single_launch_path_for_few_rows(layers):
     assert err_word(layer) == 0
 
 
+def test_mega_wait_that_gives_up_sets_the_error_word_and_drains(layers):
+    """Failure handling, forced from the host: the per-expert h counts are
+    set beforehand to a value they can never count to, so every GEMM2 item's
+    bounded wait gives up.  The launch still ends (the first wait to give up
+    sets the abort word, after which no wait waits), the error word reads 1
+    and the rest of the state region is back at zero; with the error word
+    cleared, the next call gives the clean call's bits again."""
+    from block_scaled_fp4_pre_amd import _lib
+    log("[test] mega: a wait that gives up")
+    cfg = SHAPES[0]
+    layer = layers[cfg.name].with_capacity(cfg.tokens)
+    x = synth.make_tokens(cfg)
+    ids, w = synth.make_routing(cfg)
+    xd, idd, wd = dev_bf16(x), dev(ids), dev(w)
+    clean = host_bits(layer.forward_mega(xd, idd, wd))
+    torch.cuda.synchronize()
+    assert err_word(layer) == 0
+    st = layer.ws("mega", (_lib.MOE_MEGA_STATE_BYTES // 8,), torch.int64)
+    st[_lib.MOE_MEGA_HCOUNT_WORD:_lib.MOE_MEGA_HCOUNT_WORD + cfg.experts] = 1 << 40
+    torch.cuda.synchronize()
+    layer.forward_mega(xd, idd, wd)
+    torch.cuda.synchronize()
+    assert err_word(layer) == 1                 # and every other word zero again
+    st[_lib.MOE_MEGA_ERR_WORD] = 0
+    again = host_bits(layer.forward_mega(xd, idd, wd))
+    torch.cuda.synchronize()
+    assert err_word(layer) == 0
+    assert np.array_equal(again, clean)
+
+
 def test_mega_graph_replays_equal_eager(layers):
     log("[test] mega graph capture and replay")
     cfg = SHAPES[1]
