@@ -24,14 +24,16 @@
 //     outstanding) adds one to the expert's h counter.  A GEMM1 item never
 //     waits.  A pass takes 16 of the expert's rows (E4M3 tokens: 8, so that
 //     the tile of twice the bytes per row keeps its LDS size).
-//   GEMM2 (active expert, W2 unit v of 64 hidden rows): the weights as above,
-//     loaded before the wait for the expert's h counter to reach its number of
-//     GEMM1 items; then each wave's slice of h by agent-scope loads, the
-//     MFMAs, the reduction, and y (bf16) by agent-scope stores.  Once they
-//     are complete (again one pass later), one more on each row's (token, v)
-//     combine counter; the item that brings it to the token's number of valid
-//     slots combines those 64 columns of the token (stage S4), in slot order,
-//     as combine.hip does.
+//   GEMM2 (active expert, one or two W2 units v of 64 hidden rows; two from
+//     MOE_MEGA_PAIR_ROWS routed rows on, when both 4-step slices fit a wave's
+//     registers): the weights as above, loaded before the wait for the
+//     expert's h counter to reach its number of GEMM1 items; then each wave's
+//     slice of h by agent-scope loads (one operand for both units), the
+//     MFMAs, the reduction (wave u sums unit u), and y (bf16) by agent-scope
+//     stores.  Once they are complete (again one pass later), one more on
+//     each row's (token, v) combine counter; the item that brings it to the
+//     token's number of valid slots combines those 64 columns of the token
+//     (stage S4), in slot order, as combine.hip does.
 // Each phase's items are dealt round-robin over kMegaQueues ticket counters
 // (one fetch-and-add per item, spread over as many addresses, since
 // same-address atomics from every CU serialize in the memory system).  A
