@@ -26,10 +26,11 @@ launches in which events on the same stream bracket each GEMM launch
 median, minimum and maximum of K more forwards, each bracketed by its own
 events.  With the default workload the metric's second operating point,
 ntok = 4096, rides along as the object "dsv4flash_t4096_prefill" (same
-weights, same measurements), and a decode batch of 8 tokens, which
-moe_w4a4_forward runs as one kernel launch (mega_moe_kernel), as
+weights, same measurements), and (MX types) a decode batch of 8 tokens run
+as one kernel launch (moe_w4a4_forward_mega, mega_moe_kernel), as
 "dsv4flash_t8_decode_single_launch", with the same forward's time as four
-launches beside it.  "context" holds the pages' own figure for
+launches beside it and whether moe_w4a4_forward takes the single launch at
+that size.  "context" holds the pages' own figure for
 ntok = 512 (another machine: not a baseline, so "vs_baseline" is null).
 "ceiling" holds this GPU's measured ceilings (libmoe_ceiling.so): the
 streaming-read rate of a 2 GiB buffer with non-temporal and with default loads
@@ -483,8 +484,8 @@ def main():
         del player
         torch.cuda.synchronize()
     if not args.no_decode and cfg.name == "dsv4flash_t512" and args.mma_type != "nvf4xnvf4":
-        # A decode batch, which runs as one kernel launch (the single-launch
-        # forward), on the same prepared weights.
+        # A decode batch as one kernel launch (the single-launch forward) and
+        # as the four launches, on the same prepared weights.
         import dataclasses
         dcfg = dataclasses.replace(configs["dsv4flash_t64_decode"], name=f"dsv4flash_t{DECODE_TOKENS}_decode",
                                    tokens=DECODE_TOKENS)
