@@ -6,6 +6,8 @@ workspace (quantized tokens, route, requantized h, y, output):
   mega_h1024_i512_e16_k2_t64_zipf  experts with more than 16 rows (several
                                    passes per work item) and experts with none
   mega_h2048_i1024_e64_k6_t42      252 routed rows
+  mega_h512_i4096_e8_k2_t24        8-step GEMM2 slices (one W2 unit per item)
+  mega_h4096_i512_e16_k4_t16       8-step GEMM1 slices, 1-step GEMM2 slices
   DSV4-Flash shape, T = 1, 8, 42   the 8- and 4-step slices of hidden 4096 and
                                    inter 2048 (6, 48 and 252 routed rows)
 
@@ -38,6 +40,8 @@ SHAPES = [
     synth.LayerConfig(140, "mega_h512_i512_e8_k2_t16", 16, 512, 512, 8, 2, "uniform", 140),
     synth.LayerConfig(141, "mega_h1024_i512_e16_k2_t64_zipf", 64, 1024, 512, 16, 2, "zipf", 141, 2.0),
     synth.LayerConfig(142, "mega_h2048_i1024_e64_k6_t42", 42, 2048, 1024, 64, 6, "uniform", 142),
+    synth.LayerConfig(143, "mega_h512_i4096_e8_k2_t24", 24, 512, 4096, 8, 2, "uniform", 143),
+    synth.LayerConfig(144, "mega_h4096_i512_e16_k4_t16", 16, 4096, 512, 16, 4, "uniform", 144),
 ]
 DSV4_TOKENS = [1, 8, 42]
 
