@@ -279,9 +279,10 @@ template <int NT, int D, int SWZ>
 static hipError_t launch_gemm1_nv_t(const uint8_t* w1c, const uint8_t* w1s, const float* gsc, const uint8_t* xq,
                                     const uint8_t* xsf, const int32_t* counts, const int32_t* offsets,
                                     const int32_t* sorted_rows, int H, int I, int E, int k, int hrows, uint8_t* hq,
-                                    uint8_t* hsf, float* acc_out, hipStream_t stream) {
+                                    uint8_t* hsf, float* acc_out, size_t min_lds, hipStream_t stream) {
   constexpr int ROWS = NT == 1 ? 16 : kNvStreamRows;
-  const size_t lds = (size_t)ROWS * (H / 2 + H / 16);
+  size_t lds = (size_t)ROWS * (H / 2 + H / 16);
+  if (lds < min_lds) lds = min_lds;
   auto kern = gemm1_nv_kernel<NT, D, SWZ>;
   const int upw = units_per_wave(I / 32 / 4, 2);
   hipError_t err = allow_lds(kern, lds);
@@ -294,12 +295,12 @@ template <int NT, int D>
 static hipError_t launch_gemm1_nv_d(const uint8_t* w1c, const uint8_t* w1s, const float* gsc, const uint8_t* xq,
                                     const uint8_t* xsf, const int32_t* counts, const int32_t* offsets,
                                     const int32_t* sorted_rows, int H, int I, int E, int k, int hrows, uint8_t* hq,
-                                    uint8_t* hsf, float* acc_out, hipStream_t stream) {
+                                    uint8_t* hsf, float* acc_out, size_t min_lds, hipStream_t stream) {
   switch (swizzle(H / 2)) {
     case 16: return launch_gemm1_nv_t<NT, D, 16>(w1c, w1s, gsc, xq, xsf, counts, offsets, sorted_rows, H, I, E, k,
-                                                 hrows, hq, hsf, acc_out, stream);
+                                                 hrows, hq, hsf, acc_out, min_lds, stream);
     default: return launch_gemm1_nv_t<NT, D, 8>(w1c, w1s, gsc, xq, xsf, counts, offsets, sorted_rows, H, I, E, k,
-                                                hrows, hq, hsf, acc_out, stream);
+                                                hrows, hq, hsf, acc_out, min_lds, stream);
   }
 }
 
@@ -307,24 +308,30 @@ template <int NT>
 static hipError_t launch_gemm1_nv_nt(const uint8_t* w1c, const uint8_t* w1s, const float* gsc, const uint8_t* xq,
                                      const uint8_t* xsf, const int32_t* counts, const int32_t* offsets,
                                      const int32_t* sorted_rows, int H, int I, int E, int k, int hrows, uint8_t* hq,
-                                     uint8_t* hsf, float* acc_out, hipStream_t stream) {
+                                     uint8_t* hsf, float* acc_out, size_t min_lds, hipStream_t stream) {
   // H % 256 == 0: the K steps are even
   if (ring_depth(H / kStepK) == MOE_NV_RING_DEPTH)
     return launch_gemm1_nv_d<NT, MOE_NV_RING_DEPTH>(w1c, w1s, gsc, xq, xsf, counts, offsets, sorted_rows, H, I, E, k,
-                                                    hrows, hq, hsf, acc_out, stream);
+                                                    hrows, hq, hsf, acc_out, min_lds, stream);
   return launch_gemm1_nv_d<NT, 2>(w1c, w1s, gsc, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hrows, hq, hsf,
-                                  acc_out, stream);
+                                  acc_out, min_lds, stream);
 }
 
 hipError_t launch_gemm1_nv(const uint8_t* w1c, const uint8_t* w1s, const float* gsc, const uint8_t* xq,
                            const uint8_t* xsf, const int32_t* counts, const int32_t* offsets,
                            const int32_t* sorted_rows, int H, int I, int E, int k, int rows_hint, int hrows,
                            uint8_t* hq, uint8_t* hsf, float* acc_out, hipStream_t stream) {
+  // With more than 8 rows per expert on average (most workgroups live), at
+  // most two one-tile workgroups per CU: 56 KiB of LDS each.  At 512 tokens
+  // (DeepSeek-V4-Flash shape, 12 rows per expert) GEMM1 473 -> 455 us; at
+  // 64 tokens (2 rows) the same cap measured slower (310 -> 327 us), and
+  // GEMM2 slower at both, so they keep the tile's own LDS size.
+  const size_t min_lds = rows_hint > 8 ? (size_t)56 << 10 : 0;
   if (rows_hint > MOE_NV_TWO_TILES_ABOVE)
     return launch_gemm1_nv_nt<2>(w1c, w1s, gsc, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hrows, hq, hsf,
-                                 acc_out, stream);
+                                 acc_out, min_lds, stream);
   return launch_gemm1_nv_nt<1>(w1c, w1s, gsc, xq, xsf, counts, offsets, sorted_rows, H, I, E, k, hrows, hq, hsf,
-                               acc_out, stream);
+                               acc_out, min_lds, stream);
 }
 
 #undef NV_G1_ARGS
