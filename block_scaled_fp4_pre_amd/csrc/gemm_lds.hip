@@ -314,10 +314,39 @@ __global__ void __launch_bounds__(256 * WB, WB == 1 ? MOE_LDS_BLOCKS : 1) gemm_l
     step(s, BoolConst<false>{});
   }
 
-  if constexpr (G1)
+  constexpr int kYStride = 144;
+  if constexpr (G1) {
     gemm1_epilogue<NT, F8>(acc, unit, row0, nrows, I, hrows, lane, hq, hsf, acc_out);
-  else
-    gemm2_epilogue<NT>(acc, unit, row0, nrows, H, lane, y);
+  } else if constexpr (WAVES * ROWS * kYStride > P * L::BYTES) {
+    gemm2_epilogue<NT>(acc, unit, row0, nrows, H, lane, y);   // (8-wave tiles: the ring is too small)
+  } else {
+    // y through LDS, so that every store writes whole 128-byte lines: a
+    // unit's 64 bf16 columns of a row are one aligned line, and the
+    // accumulator layout gives each lane 8 bytes of it (4 pieces, 16 rows
+    // apart in the store pattern of gemm2_epilogue).  Each wave puts its
+    // ROWS x 64 tile into the ring's bytes (rows kYStride apart: the 16 rows a
+    // write touches start on different bank groups), then stores 8 rows per
+    // instruction, 16 bytes a lane.  Writing the pieces directly cost GEMM2
+    // about 30 % of its time at 4096 tokens.
+    __syncthreads();                                   // every wave is done with the ring
+    uint8_t* ytile = lds + wave * ROWS * kYStride;
+    const int tok_lane = lane & 15, kb = lane >> 4;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+        *reinterpret_cast<uint64_t*>(ytile + (nt * 16 + tok_lane) * kYStride + (16 * rb + 4 * kb) * 2) =
+            (uint64_t)(f32_to_bf16(acc[nt][rb][0]) | (f32_to_bf16(acc[nt][rb][1]) << 16)) |
+            ((uint64_t)(f32_to_bf16(acc[nt][rb][2]) | (f32_to_bf16(acc[nt][rb][3]) << 16)) << 32);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < ROWS / 8; ++i) {
+      const int r = i * 8 + (lane >> 3), c = lane & 7;
+      if (r < nrows)
+        *reinterpret_cast<uint4*>(y + (size_t)(row0 + r) * H + 64 * unit + 8 * c) =
+            *reinterpret_cast<const uint4*>(ytile + r * kYStride + 16 * c);
+    }
+  }
 }
 
 #ifndef MOE_LDS_STAGES
